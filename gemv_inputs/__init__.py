@@ -1,0 +1,272 @@
+"""Seeded synthetic inputs for GEMV, shared by the tests, the smoke check and
+the benchmark.
+
+This module holds no GEMV arithmetic: it only draws random numbers, rounds
+them to the stored element types, and lays them out.  Both the HIP path and
+the CPU oracle consume the arrays it returns, so they see the same bits.
+
+Element encodings: ``"f32"`` arrays are ``float32``; ``"f16"`` and ``"bf16"``
+arrays are ``uint16`` bit patterns.
+
+Workloads (no public dataset or weights are involved; every input is drawn
+from a seeded ``numpy.random.default_rng`` in the order A, then x, then bias):
+
+* ``sgemv_1024x128``: fp32, M=1024, K=128, A and x uniform on [-1, 1], no
+  bias; the shape timed on page "SGEMV CUDA代码学习" (its opening timing table
+  and the benchmark script in section "完整代码"), seed 61.
+* ``skinny_k{16,32,128}``: fp32, M=2^20 rows, K in {16, 32, 128}, A, x and
+  bias uniform on [-1, 1]; the short-row regime of that page's section
+  "Kernel 3: k16" scaled up, seed 62.
+* ``decode_f16_4096``: fp16, M=K=4096, A ~ N(0,1)/sqrt(K), x ~ N(0,1), no
+  bias; the 4096x4096 fp16 decode (m = 1) run of page "GEMM、GEMV、dtype 与
+  算术强度", section "可运行 CUDA 实验", seed 63.
+* ``sweep_{q,k,v,o,gate,up,down}``: bf16 decode-layer projections with
+  weights ~ N(0, 0.02^2) (0.02 is the standard deviation) and x ~ N(0,1), no
+  bias, seeds 640..646.
+* ``batched_f16_4096x16``: fp16 W 4096x4096 ~ N(0,1)/sqrt(K), X with 16
+  columns (K x 16, column-major) ~ N(0,1), no bias; the m = 16
+  small_batch_decode run of the same section, seed 65.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+DTYPES = ("f32", "f16", "bf16")
+ELEMENT_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+# ---------------------------------------------------------------------------
+# rounding float64 draws to the stored encodings (round to nearest, ties even)
+# ---------------------------------------------------------------------------
+
+def to_f32(v) -> np.ndarray:
+    return np.asarray(v, dtype=np.float64).astype(np.float32)
+
+
+def to_f16_bits(v) -> np.ndarray:
+    return np.asarray(v, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def f32_to_bf16_bits(f) -> np.ndarray:
+    """Round binary32 values to bfloat16 (ties to even), returning the bits."""
+    u = np.asarray(f, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    nan = np.isnan(np.asarray(f, dtype=np.float32))
+    if nan.any():
+        sign = ((u >> 16) & 0x8000).astype(np.uint16)
+        rounded = np.where(nan, sign | np.uint16(0x7FC0), rounded)
+    return rounded.astype(np.uint16)
+
+
+def to_bf16_bits(v) -> np.ndarray:
+    """float64 -> binary32 (ties even) -> bfloat16 (ties even)."""
+    return f32_to_bf16_bits(to_f32(v))
+
+
+def quantise(dtype: str, v) -> np.ndarray:
+    if dtype == "f32":
+        return to_f32(v)
+    if dtype == "f16":
+        return to_f16_bits(v)
+    if dtype == "bf16":
+        return to_bf16_bits(v)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def storage_dtype(dtype: str):
+    return np.float32 if dtype == "f32" else np.uint16
+
+
+# ---------------------------------------------------------------------------
+# a problem instance
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class Case:
+    """One GEMV problem: A is (M, lda) stored row-major (columns K..lda-1 are
+    padding), X is (nvec, K) (column j of the K x nvec column-major matrix is
+    row j here), bias is float32 (M,) or None."""
+
+    name: str
+    dtype: str
+    M: int
+    K: int
+    A: np.ndarray
+    X: np.ndarray
+    bias: np.ndarray | None
+    lda: int
+    nvec: int = 1
+    seed: int | None = None
+
+    def algorithmic_bytes(self) -> int:
+        return workload_bytes(self.dtype, self.M, self.K, self.nvec,
+                              self.bias is not None)
+
+
+def workload_bytes(dtype: str, M: int, K: int, nvec: int = 1,
+                   has_bias: bool = False) -> int:
+    """Minimum HBM bytes of one call: A read once, every x column read once,
+    y written once as fp32, bias read once if present."""
+    s = ELEMENT_BYTES[dtype]
+    return M * K * s + nvec * K * s + 4 * M * nvec + (4 * M if has_bias else 0)
+
+
+def workload_flops(M: int, K: int, nvec: int = 1, has_bias: bool = False) -> int:
+    return 2 * M * K * nvec + (M * nvec if has_bias else 0)
+
+
+def _pad(A: np.ndarray, lda: int, fill) -> np.ndarray:
+    M, K = A.shape
+    if lda == K:
+        return np.ascontiguousarray(A)
+    out = np.full((M, lda), fill, dtype=A.dtype)
+    out[:, :K] = A
+    return out
+
+
+def _padding_value(dtype: str):
+    """A quiet NaN in the stored encoding: padding that must never be read."""
+    if dtype == "f32":
+        return np.float32(np.nan)
+    if dtype == "f16":
+        return np.uint16(0x7E00)
+    return np.uint16(0x7FC0)
+
+
+def make_random(dtype: str, M: int, K: int, *, seed: int, nvec: int = 1,
+                lda: int | None = None, bias: bool = False,
+                dist: str = "uniform", scale: float = 1.0,
+                name: str | None = None) -> Case:
+    """Random case: ``dist`` is "uniform" (on [-scale, scale]) or "normal"
+    (standard deviation ``scale`` for A; x and bias are drawn like A but with
+    scale 1 for "normal")."""
+    rng = np.random.default_rng(seed)
+    lda = K if lda is None else lda
+    if dist == "uniform":
+        a = rng.uniform(-scale, scale, size=(M, K))
+        x = rng.uniform(-1.0, 1.0, size=(nvec, K))
+        b = rng.uniform(-1.0, 1.0, size=M) if bias else None
+    elif dist == "normal":
+        a = rng.standard_normal(size=(M, K)) * scale
+        x = rng.standard_normal(size=(nvec, K))
+        b = rng.standard_normal(size=M) if bias else None
+    else:
+        raise ValueError(dist)
+    A = _pad(quantise(dtype, a), lda, _padding_value(dtype))
+    X = np.ascontiguousarray(quantise(dtype, x))
+    return Case(name or f"rand_{dtype}_{M}x{K}", dtype, M, K, A, X,
+                None if b is None else to_f32(b), lda, nvec, seed)
+
+
+# ---------------------------------------------------------------------------
+# the named workloads
+# ---------------------------------------------------------------------------
+
+SWEEP_SHAPES = {           # name: (M, K)
+    "q": (4096, 4096),
+    "k": (1024, 4096),
+    "v": (1024, 4096),
+    "o": (4096, 4096),
+    "gate": (14336, 4096),
+    "up": (14336, 4096),
+    "down": (4096, 14336),
+}
+
+WORKLOADS = {
+    # name: (dtype, M, K, nvec, bias, dist, scale rule, seed)
+    "sgemv_1024x128": ("f32", 1024, 128, 1, False, "uniform", None, 61),
+    "skinny_k16": ("f32", 1 << 20, 16, 1, True, "uniform", None, 62),
+    "skinny_k32": ("f32", 1 << 20, 32, 1, True, "uniform", None, 62),
+    "skinny_k128": ("f32", 1 << 20, 128, 1, True, "uniform", None, 62),
+    "decode_f16_4096": ("f16", 4096, 4096, 1, False, "normal", "1/sqrtK", 63),
+    "batched_f16_4096x16": ("f16", 4096, 4096, 16, False, "normal", "1/sqrtK", 65),
+}
+for _i, (_n, (_m, _k)) in enumerate(SWEEP_SHAPES.items()):
+    WORKLOADS[f"sweep_{_n}"] = ("bf16", _m, _k, 1, False, "normal", 0.02, 640 + _i)
+
+
+def workload_shape(name: str):
+    dtype, M, K, nvec, bias, _, _, _ = WORKLOADS[name]
+    return dtype, M, K, nvec, bias
+
+
+def make_workload(name: str, lda: int | None = None) -> Case:
+    dtype, M, K, nvec, bias, dist, rule, seed = WORKLOADS[name]
+    if rule is None:
+        scale = 1.0
+    elif rule == "1/sqrtK":
+        scale = 1.0 / math.sqrt(K)
+    else:
+        scale = float(rule)
+    return make_random(dtype, M, K, seed=seed, nvec=nvec, lda=lda, bias=bias,
+                       dist=dist, scale=scale, name=name)
+
+
+# ---------------------------------------------------------------------------
+# structured inputs whose products are known in closed form
+# ---------------------------------------------------------------------------
+
+def make_integer(dtype: str, M: int, K: int, *, seed: int, nvec: int = 1,
+                 lda: int | None = None, bias: bool = False,
+                 lo: int = -8, hi: int = 8) -> Case:
+    """Integer-valued A, x (and bias) in [lo, hi]: exact in every encoding, and
+    for K <= 16384 every partial sum stays below 2^24, so any fp32 summation
+    order gives the exact result."""
+    rng = np.random.default_rng(seed)
+    lda = K if lda is None else lda
+    a = rng.integers(lo, hi + 1, size=(M, K)).astype(np.float64)
+    x = rng.integers(lo, hi + 1, size=(nvec, K)).astype(np.float64)
+    b = rng.integers(lo, hi + 1, size=M).astype(np.float64) if bias else None
+    A = _pad(quantise(dtype, a), lda, _padding_value(dtype))
+    return Case(f"int_{dtype}_{M}x{K}", dtype, M, K, A,
+                np.ascontiguousarray(quantise(dtype, x)),
+                None if b is None else to_f32(b), lda, nvec, seed)
+
+
+def make_worked_example(dtype: str, bias: bool = False) -> Case:
+    """M=3, K=1024 with A[m,k] = (m+1)·(-1)^k and x[k] = k mod 8, and bias
+    [0.5, -0.25, 1] when requested: the shape walked through on page "第 3 课：
+    GEMV 与行级并行", section "具体演示与数值推演" (the page prints no values;
+    these entries are chosen so every value is exact in every encoding)."""
+    M, K = 3, 1024
+    k = np.arange(K)
+    a = np.array([(m + 1) * np.where(k % 2 == 0, 1.0, -1.0) for m in range(M)])
+    x = (k % 8).astype(np.float64)[None, :]
+    b = np.array([0.5, -0.25, 1.0]) if bias else None
+    return Case(f"worked_{dtype}", dtype, M, K, quantise(dtype, a),
+                quantise(dtype, x), None if b is None else to_f32(b), K)
+
+
+def make_identity(dtype: str, n: int, *, seed: int, bias: bool = False) -> Case:
+    """A = I (n x n), x random integer-valued in [-1000, 1000] (exact in fp16
+    and fp32; bf16 rounds x once at quantisation, which is the stored x)."""
+    rng = np.random.default_rng(seed)
+    a = np.eye(n)
+    x = rng.integers(-1000, 1001, size=(1, n)).astype(np.float64)
+    b = rng.integers(-50, 51, size=n).astype(np.float64) if bias else None
+    return Case(f"identity_{dtype}_{n}", dtype, n, n, quantise(dtype, a),
+                quantise(dtype, x), None if b is None else to_f32(b), n, 1, seed)
+
+
+def make_one_hot(dtype: str, M: int, K: int, *, seed: int, nvec: int = 1,
+                 lda: int | None = None) -> Case:
+    """Row m of A has one non-zero entry c_m (a power of two in
+    [2^-3, 2^3], random sign) at column pi(m), a random column; x is random
+    integer-valued.  Then y[m] = c_m · x[pi(m)] exactly."""
+    rng = np.random.default_rng(seed)
+    lda = K if lda is None else lda
+    cols = rng.integers(0, K, size=M)
+    coef = (2.0 ** rng.integers(-3, 4, size=M)) * rng.choice([-1.0, 1.0], size=M)
+    a = np.zeros((M, K))
+    a[np.arange(M), cols] = coef
+    x = rng.integers(-64, 65, size=(nvec, K)).astype(np.float64)
+    A = _pad(quantise(dtype, a), lda, _padding_value(dtype))
+    case = Case(f"onehot_{dtype}_{M}x{K}", dtype, M, K, A,
+                np.ascontiguousarray(quantise(dtype, x)), None, lda, nvec, seed)
+    case.cols = cols          # the column of each row's non-zero entry
+    case.coef = coef          # and its value
+    return case

@@ -1,0 +1,383 @@
+#!/usr/bin/env python3
+"""Benchmark libgemv on one MI355X.
+
+One step is one GEMV call (the whole hot path: stage x, stream A once,
+multiply-accumulate in fp32, reduce, add bias, write y) on the workload named
+by ``--workload``; the default is the bf16 4096×4096 GEMV (the q/o
+projection of the decode-layer sweep).  Inputs are seeded synthetic data
+(no dataset or weights) and are resident in HBM before timing starts.
+
+Cache defeat: ``R`` copies of A (and x, y) are allocated so that together
+they exceed twice the 256 MB Infinity Cache, and consecutive steps cycle
+through them, so every step streams its A from HBM.
+
+Timed region: ``--steps`` back-to-back calls issued as replays of a HIP graph
+that holds one launch per rotation set (host launch cost would otherwise
+exceed the ~5 µs kernel), bracketed by ``torch.cuda.synchronize()`` and a
+pair of HIP events on the launch stream.  ``value`` is algorithmic bytes ×
+steps ÷ elapsed.  Also measured:
+  * eager calls through the C ABI (one ctypes call per step);
+  * per-launch kernel durations from an event pair around each launch, the
+    figure ``roofline.achieved`` divides by, to compare with rocprofv3;
+  * µs/call, GB/s and GFLOP/s for every other configured shape;
+  * the CPU oracle on the host cores (``cpu_baseline``).
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+INFINITY_CACHE_BYTES = 256 << 20
+METRIC = "achieved HBM GB/s (% of 8 TB/s) for 4096x4096 bf16 GEMV; µs/call per shape"
+DEFAULT_WORKLOAD = "sweep_q"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--shapes", default="all",
+                    help="comma-separated workloads for the per-shape table, 'all' or 'none'")
+    ap.add_argument("--shape-steps", type=int, default=400)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall-clock budget of the CPU oracle timing (0 = skip)")
+    ap.add_argument("--kernel-only", action="store_true",
+                    help="only run the timed graph loop of --workload (for profilers)")
+    return ap.parse_args()
+
+
+class Rotation:
+    """R device copies of one case's inputs/outputs, R chosen so that the
+    copies of A together exceed 2× the Infinity Cache."""
+
+    def __init__(self, case, torch, min_bytes=2 * INFINITY_CACHE_BYTES):
+        import numpy as np
+        self.case = case
+        a_bytes = case.A.nbytes
+        self.R = max(2, math.ceil(min_bytes / max(a_bytes, 1)) + 1)
+        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[case.dtype]
+        if case.dtype == "f32":
+            hA = torch.from_numpy(case.A.astype(np.float32))
+            hX = torch.from_numpy(case.X.astype(np.float32))
+        else:
+            hA = torch.from_numpy(case.A.view(np.int16)).view(tdt)
+            hX = torch.from_numpy(case.X.view(np.int16)).view(tdt)
+        self.A, self.X, self.Y = [], [], []
+        for _ in range(self.R):
+            self.A.append(hA.to("cuda"))
+            self.X.append(hX.to("cuda"))
+            self.Y.append(torch.empty((case.nvec, case.M), dtype=torch.float32, device="cuda"))
+        self.bias = None
+        if case.bias is not None:
+            self.bias = torch.from_numpy(case.bias).to("cuda")
+        self.bytes_resident = self.R * (a_bytes + case.X.nbytes + 4 * case.M * case.nvec)
+
+    def callers(self, lg, stream_handle):
+        """One zero-argument callable per set that enqueues one call through
+        the C ABI (arguments pre-marshalled, so a call is one ctypes call)."""
+        c = self.case
+        fns = []
+        bias = self.bias.data_ptr() if self.bias is not None else None
+        for i in range(self.R):
+            A, X, Y = self.A[i].data_ptr(), self.X[i].data_ptr(), self.Y[i].data_ptr()
+            if c.nvec > 1:
+                f = {"f16": lg.gemv_batched_f16, "bf16": lg.gemv_batched_bf16}[c.dtype]
+                args = (A, c.lda, X, bias, Y, c.M, c.K, c.nvec, stream_handle)
+            else:
+                f = {"f32": lg.gemv_f32, "f16": lg.gemv_f16, "bf16": lg.gemv_bf16}[c.dtype]
+                args = (A, c.lda, X, bias, Y, c.M, c.K, stream_handle)
+            fns.append((f, args))
+        return fns
+
+
+def call(fn_args):
+    f, args = fn_args
+    rc = f(*args)
+    if rc != 0:
+        raise RuntimeError(f"{f.__name__} returned {rc}")
+
+
+def build_graph(torch, rot, lg, launches):
+    """A HIP graph of ``launches`` back-to-back calls cycling through the
+    rotation sets (captured from the C-ABI launches on a side stream)."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fns = rot.callers(lg, s.cuda_stream)
+        call(fns[0])  # warm the launch path outside capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(launches):
+                call(fns[i % len(fns)])
+    torch.cuda.synchronize()
+    return g
+
+
+class GraphLoop:
+    """Exactly ``steps`` launches as replays of a main graph (``per`` calls)
+    plus one tail graph for the remainder."""
+
+    def __init__(self, torch, rot, lg, steps, per):
+        self.torch = torch
+        self.per = min(per, steps)
+        self.replays, rem = divmod(steps, self.per)
+        self.main = build_graph(torch, rot, lg, self.per)
+        self.tail = build_graph(torch, rot, lg, rem) if rem else None
+        self.steps = steps
+
+    def run(self):
+        for _ in range(self.replays):
+            self.main.replay()
+        if self.tail is not None:
+            self.tail.replay()
+
+    def time(self, warmup):
+        torch = self.torch
+        for _ in range(max(1, math.ceil(warmup / self.per))):
+            self.main.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        self.run()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+
+def time_eager(torch, fns, steps, warmup):
+    for i in range(warmup):
+        call(fns[i % len(fns)])
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        call(fns[i % len(fns)])
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def time_per_launch(torch, fns, n):
+    """Kernel durations from an event pair around each launch (ms each)."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for i in range(n):
+        starts[i].record()
+        call(fns[i % len(fns)])
+        ends[i].record()
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+
+def parity_check(case, rot, torch):
+    """Set 0's output against the CPU oracle (every row)."""
+    import numpy as np
+    import oracle
+    ref, absdot = oracle.gemv(case.dtype, case.A, case.X, case.bias, case.M, case.K,
+                              lda=case.lda, nvec=case.nvec)
+    y = rot.Y[0].cpu().numpy().astype(np.float64)
+    err = np.abs(y - ref)
+    ok = bool(np.all(err <= 1e-5 * absdot + 1e-6))
+    worst = float(np.max(err / (1e-5 * absdot + 1e-6))) if err.size else 0.0
+    return ok, worst
+
+
+def measure_shape(name, torch, lg, gi, steps):
+    case = gi.make_workload(name)
+    rot = Rotation(case, torch)
+    loop = GraphLoop(torch, rot, lg, steps, per=rot.R * max(1, 64 // rot.R))
+    ms, n = loop.time(warmup=loop.per), steps
+    fns = rot.callers(lg, torch.cuda.current_stream().cuda_stream)
+    eager_ms = time_eager(torch, fns, steps, warmup=rot.R)
+    durs = time_per_launch(torch, fns, min(steps, 200))
+    nbytes = case.algorithmic_bytes()
+    flops = gi.workload_flops(case.M, case.K, case.nvec, case.bias is not None)
+    us = 1e3 * ms / n
+    kus = 1e3 * statistics.median(durs)
+    plan = lg.plan(case.dtype, case.M, case.K, case.lda, case.nvec,
+                   rot.A[0].data_ptr(), rot.X[0].data_ptr())
+    del loop, rot
+    torch.cuda.empty_cache()
+    return {
+        "dtype": case.dtype, "M": case.M, "K": case.K, "nvec": case.nvec,
+        "bias": case.bias is not None, "bytes": nbytes,
+        "family": lg.FAMILY_NAMES[plan["family"]],
+        "us_per_call_graph": round(us, 3),
+        "us_per_call_eager": round(1e3 * eager_ms / steps, 3),
+        "us_kernel_event_median": round(kus, 3),
+        "GBps": round(nbytes / us / 1e3, 1),
+        "GBps_kernel": round(nbytes / kus / 1e3, 1),
+        "frac_of_8TBps": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+        "GFLOPps": round(flops / us / 1e3, 1),
+    }
+
+
+def cpu_baseline(case, seconds):
+    """The CPU oracle, as it stands, on the same workload: 1 warmup, then
+    repeats until ``seconds`` of wall time; median."""
+    import oracle
+    o = oracle.default()
+    o.gemv(case.dtype, case.A, case.X, case.bias, case.M, case.K, lda=case.lda, nvec=case.nvec)
+    times = []
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end or len(times) < 3:
+        t0 = time.perf_counter()
+        o.gemv(case.dtype, case.A, case.X, case.bias, case.M, case.K, lda=case.lda, nvec=case.nvec)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    return {
+        "value": round(case.algorithmic_bytes() / med / 1e9, 3),
+        "unit": "GB/s",
+        "cores": o.num_threads(),
+        "kind": "oracle",
+        "sample": (f"the whole {case.dtype} {case.M}x{case.K} workload, {len(times)} repeats "
+                   f"in {seconds:.0f} s after 1 warmup, median {med * 1e3:.2f} ms per call; "
+                   "fp64 C loop, OpenMP over rows"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: every box in this setup has a single MI355X, "
+              f"so --gpus {args.gpus} is not supported (the row-sharded multi-GPU layout is "
+              f"described in the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np  # noqa: F401
+    import torch
+
+    import gemv_inputs as gi
+    import memory_bound_gemv_f32_amd as lg
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    log(f"device {torch.cuda.get_device_name(0)} ({torch.cuda.get_device_properties(0).gcnArchName})")
+
+    case = gi.make_workload(args.workload)
+    rot = Rotation(case, torch)
+    log(f"workload {args.workload}: {case.dtype} M={case.M} K={case.K} nvec={case.nvec} "
+        f"rotation sets {rot.R} ({rot.bytes_resident / 2**20:.0f} MiB resident)")
+    loop = GraphLoop(torch, rot, lg, args.steps, per=rot.R * max(1, 256 // rot.R))
+
+    if args.kernel_only:
+        ms = loop.time(args.warmup)
+        log(f"kernel-only: {args.steps} launches, {1e3 * ms / args.steps:.3f} us per launch")
+        return
+
+    ok, worst = parity_check(case, rot, torch)
+    log(f"parity vs oracle (set 0, every row): {'ok' if ok else 'FAILED'}; "
+        f"worst error / bound = {worst:.3g}")
+    if not ok:
+        sys.exit(1)
+
+    # timed region: graph replays, exactly --steps launches
+    torch.cuda.synchronize()
+    ms, launches = loop.time(args.warmup), args.steps
+    nbytes = case.algorithmic_bytes()
+    us_step = 1e3 * ms / launches
+    value = nbytes / us_step / 1e3  # GB/s
+    log(f"graph: {launches} launches in {ms:.3f} ms -> {us_step:.3f} us/step, {value:.1f} GB/s")
+
+    fns = rot.callers(lg, torch.cuda.current_stream().cuda_stream)
+    eager_ms = time_eager(torch, fns, args.steps, args.warmup)
+    log(f"eager: {1e3 * eager_ms / args.steps:.3f} us/step")
+    durs = time_per_launch(torch, fns, min(args.steps, 1000))
+    k_mean = 1e3 * statistics.fmean(durs)
+    k_med = 1e3 * statistics.median(durs)
+    log(f"per-launch events: mean {k_mean:.3f} us, median {k_med:.3f} us")
+    achieved = nbytes / k_mean / 1e3
+
+    plan = lg.plan(case.dtype, case.M, case.K, case.lda, case.nvec,
+                   rot.A[0].data_ptr(), rot.X[0].data_ptr())
+    del loop, rot
+    torch.cuda.empty_cache()
+
+    shapes = {}
+    names = [] if args.shapes == "none" else (
+        list(gi.WORKLOADS) if args.shapes == "all" else args.shapes.split(","))
+    for name in names:
+        shapes[name] = measure_shape(name, torch, lg, gi, args.shape_steps)
+        log(f"  {name}: {shapes[name]}")
+    sweep = [n for n in shapes if n.startswith("sweep_")]
+    sweep_agg = None
+    if len(sweep) == len(gi.SWEEP_SHAPES):
+        tb = sum(shapes[n]["bytes"] for n in sweep)
+        tus = sum(shapes[n]["us_per_call_graph"] for n in sweep)
+        tk = sum(shapes[n]["us_kernel_event_median"] for n in sweep)
+        sweep_agg = {"bytes": tb, "us": round(tus, 3), "GBps": round(tb / tus / 1e3, 1),
+                     "frac_of_8TBps": round(tb / tus / 1e3 / HBM_PEAK_GBS, 4),
+                     "GBps_kernel": round(tb / tk / 1e3, 1)}
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("timing the CPU oracle ...")
+        cpu = cpu_baseline(case, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": launches,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms / launches, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic (seeded, resident in HBM, rotated over >2x the Infinity Cache)",
+        "config": {
+            "workload": f"{case.dtype} GEMV y=A·x, A {case.M}x{case.K} row-major, fp32 "
+                        f"accumulate and output, no bias ({args.workload})",
+            "M": case.M, "K": case.K, "nvec": case.nvec,
+            "family": lg.FAMILY_NAMES[plan["family"]],
+            "timing": "HIP graph replays of back-to-back launches; event pair on the launch stream",
+            "us_per_call": round(us_step, 3),
+            "us_per_call_eager": round(1e3 * eager_ms / args.steps, 3),
+            "frac_of_8TBps": round(value / HBM_PEAK_GBS, 4),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel_us_mean": round(k_mean, 3),
+            "kernel_us_median": round(k_med, 3),
+            "bytes_per_launch": nbytes,
+        },
+        "cpu_baseline": cpu,
+        "per_shape": shapes,
+        "sweep_aggregate": sweep_agg,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

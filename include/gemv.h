@@ -1,0 +1,159 @@
+/*
+ * libgemv — dense matrix-vector products on AMD Instinct MI355X (gfx950).
+ *
+ *   y = A·x (+ bias)                 gemv_f32 / gemv_f16 / gemv_bf16
+ *   Y = A·X (+ bias), 1..16 vectors   gemv_batched_f16 / gemv_batched_bf16
+ *
+ * The operation.  Output m is the dot product of row m of A with x (page
+ * "SGEMV CUDA代码学习", section "问题定义: 一行一个点积": A is M×K, x is K×1,
+ * y is M×1), plus bias[m] when a bias is given; the bias may be absent, in
+ * which case nothing is added (page "第 3 课：GEMV 与行级并行", section
+ * "核心心智模型" item 1 for y = A x + bias, section "3. 正确性边界与指针安全性"
+ * for the absent bias).  The batched form applies one pass over A to up to 16
+ * right-hand vectors, the small-batch decode case measured on page "GEMM、
+ * GEMV、dtype 与算术强度", section "可运行 CUDA 实验" (m = 16), below the batch
+ * size at which page "第 3 课" section "4. 性能与工程权舍" moves to GEMM.
+ *
+ * Arithmetic.  fp16 and bf16 elements are multiplied and summed in fp32, the
+ * wider accumulator that page "GEMM、GEMV、dtype 与算术强度", section "dtype
+ * 改变什么", calls for; fp32 is true IEEE fp32 (never a reduced-precision
+ * matrix mode).  Products may be fused (FMA) and the summation order is the
+ * library's own, so results differ from a sequential sum by rounding only:
+ * for every output |y − exact| <= 1e-5·Σ_k|A[m,k]·x[k]| + 1e-6.  Results are
+ * deterministic: the same inputs give the same bits on every call.  No
+ * atomics are used; each output is written by exactly one lane.
+ *
+ * Layouts.
+ *   A     row-major: element (m, k) at A[(int64)m·lda + k], lda >= K.
+ *         Elements K..lda-1 of each row are never read.
+ *   x     K contiguous elements.
+ *   X     K×nvec column-major: column j at X + (int64)j·K.
+ *   bias  M contiguous fp32 values, or NULL.
+ *   y     M contiguous fp32 values (written, never read).
+ *   Y     M×nvec column-major fp32: column j at Y + (int64)j·M.
+ *   fp16 / bf16 elements are passed as their raw 16-bit patterns (uint16_t):
+ *   IEEE binary16, and bfloat16 (the upper half of a binary32 word).
+ *   Outputs and bias are fp32 for every input type.
+ *
+ * Pointers and ownership.  A, x/X, bias and y/Y are device pointers (memory
+ * from hipMalloc or a device allocator such as PyTorch's), owned by the
+ * caller.  The library never allocates, frees, retains or synchronises: a
+ * call only enqueues one kernel on `stream` (NULL = the null stream) and
+ * returns.  y/Y must not overlap A, x/X or bias.  Pointers must be aligned
+ * to their element size; any further alignment is optional (16-byte aligned
+ * A, x and row pitch lda·element_size select the widest loads).
+ *
+ * Errors.  Every entry point validates its arguments before touching the
+ * GPU.  GEMV_ERROR_INVALID_VALUE (nothing enqueued, y untouched) for:
+ * M < 0, K < 0, lda < K, nvec outside [1, 16], a NULL A or x when
+ * M > 0 and K > 0, a NULL y when M > 0, or a pointer not aligned to its
+ * element size.  M == 0 succeeds without enqueuing anything.  K == 0 writes
+ * y = bias (or 0): the empty sum.  GEMV_ERROR_LAUNCH_FAILURE if the HIP
+ * runtime refuses the launch.  The library is stateless and reentrant.
+ */
+#ifndef LIBGEMV_GEMV_H
+#define LIBGEMV_GEMV_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GEMV_SUCCESS = 0,
+    GEMV_ERROR_INVALID_VALUE = 1,
+    GEMV_ERROR_LAUNCH_FAILURE = 2
+} gemv_status_t;
+
+/* Static, NUL-terminated description of a status code. */
+const char *gemv_status_string(gemv_status_t status);
+
+/* y = A·x (+ bias); A, x fp32. */
+gemv_status_t gemv_f32(const float *A, int lda, const float *x,
+                       const float *bias, float *y, int M, int K,
+                       hipStream_t stream);
+
+/* y = A·x (+ bias); A, x IEEE binary16 bit patterns; fp32 accumulate/output. */
+gemv_status_t gemv_f16(const uint16_t *A, int lda, const uint16_t *x,
+                       const float *bias, float *y, int M, int K,
+                       hipStream_t stream);
+
+/* y = A·x (+ bias); A, x bfloat16 bit patterns; fp32 accumulate/output. */
+gemv_status_t gemv_bf16(const uint16_t *A, int lda, const uint16_t *x,
+                        const float *bias, float *y, int M, int K,
+                        hipStream_t stream);
+
+/* Y = A·X (+ bias added to every column); 1 <= nvec <= 16; A is read from
+ * memory once for all nvec vectors.  nvec == 1 computes what gemv_f16 does. */
+gemv_status_t gemv_batched_f16(const uint16_t *A, int lda, const uint16_t *X,
+                               const float *bias, float *Y, int M, int K,
+                               int nvec, hipStream_t stream);
+
+/* As gemv_batched_f16, for bfloat16 A and X. */
+gemv_status_t gemv_batched_bf16(const uint16_t *A, int lda, const uint16_t *X,
+                                const float *bias, float *Y, int M, int K,
+                                int nvec, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Introspection and testing.  These do not change what the entry points
+ * above compute; they expose how the library maps a problem onto the GPU so
+ * that the mapping can be checked without a GPU and every kernel family can
+ * be exercised at every shape it supports.
+ * ------------------------------------------------------------------------ */
+
+typedef enum { GEMV_DTYPE_F32 = 0, GEMV_DTYPE_F16 = 1, GEMV_DTYPE_BF16 = 2 } gemv_dtype_t;
+
+/* Kernel families.  Page "SGEMV CUDA代码学习", section "三 kernel 的设计空间
+ * 总结", frames GEMV's only design choice as how many lanes share one row;
+ * these are the gfx950 (64-lane wavefront) points on that axis. */
+typedef enum {
+    GEMV_FAMILY_AUTO = -1,
+    GEMV_FAMILY_ROWS_PER_WAVE = 0, /* 64/L rows per wavefront, L lanes per row */
+    GEMV_FAMILY_WAVE_PER_ROW = 1,  /* one 64-lane wavefront per row */
+    GEMV_FAMILY_GROUP_PER_ROW = 2, /* one workgroup per row, LDS reduction */
+    GEMV_FAMILY_BATCHED = 3        /* several rows × nvec vectors per wave */
+} gemv_family_t;
+
+typedef struct {
+    int family;          /* gemv_family_t */
+    int vector_loads;    /* 1: 16-byte loads; 0: one element per load */
+    int chunk_elems;     /* elements per load (16/size, or 1) */
+    int lanes_per_row;   /* lanes that share one row's dot product */
+    int rows_per_wave;   /* rows one wavefront covers per row tile */
+    int row_tiles;       /* row tiles each wavefront takes in one pass */
+    int waves_per_group; /* wavefronts per workgroup */
+    int rows_per_group;  /* rows one workgroup produces */
+    int batch;           /* loads per lane kept in flight per row */
+    int passes;          /* loop trips per lane over one row's full chunks */
+    int block;           /* threads per workgroup */
+    int lds_bytes;       /* static + dynamic LDS per workgroup */
+    int64_t grid;        /* workgroups */
+} gemv_plan_t;
+
+/* Compute, on the host only, the mapping a call with these arguments would
+ * launch (family = GEMV_FAMILY_AUTO), or the mapping of a forced family.
+ * The pointer arguments are inspected for alignment only (they may be any
+ * value, including host addresses or NULL).  Returns GEMV_ERROR_INVALID_VALUE
+ * for arguments the entry points would reject or a family that cannot run
+ * this shape (e.g. GEMV_FAMILY_BATCHED for fp32, or a single-vector family
+ * with nvec > 1). */
+gemv_status_t gemv_plan(gemv_dtype_t dtype, int M, int K, int lda, int nvec,
+                        const void *A, const void *X, int family,
+                        gemv_plan_t *plan);
+
+/* Run with a forced family (GEMV_FAMILY_AUTO = what the entry points do).
+ * Same arguments, validation and results contract as the entry points;
+ * for tests and benchmarks. */
+gemv_status_t gemv_run_family(gemv_dtype_t dtype, int family, const void *A,
+                              int lda, const void *X, const float *bias,
+                              float *Y, int M, int K, int nvec,
+                              hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBGEMV_GEMV_H */

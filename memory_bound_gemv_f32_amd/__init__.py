@@ -1,0 +1,223 @@
+"""Python binding of libgemv (dense GEMV for MI355X / gfx950).
+
+Marshalling only: every step of the computation runs in the HIP kernels of
+``libgemv.so``; this module passes device pointers, sizes and the current
+HIP stream through ctypes.  There is no CPU fallback: importing this package
+without a built ``libgemv.so`` raises ``ImportError``.
+
+Two levels:
+
+* the C ABI under the same names (``gemv_f32``, ``gemv_f16``, ``gemv_bf16``,
+  ``gemv_batched_f16``, ``gemv_batched_bf16``, ``gemv_plan``,
+  ``gemv_run_family``, ``gemv_status_string``), taking integer addresses and
+  returning the ``gemv_status_t`` code;
+* tensor helpers ``gemv`` and ``gemv_batched`` that check dtype, shape,
+  strides and device, call the matching entry point on
+  ``torch.cuda.current_stream()`` and raise ``GemvError`` on a failure code.
+
+Layout of the tensor helpers: ``A`` is (M, K) with unit column stride and row
+stride ``lda = A.stride(0) >= K`` (so a column slice of a wider matrix works);
+``x`` is (K,); for the batched form ``X`` is (nvec, K) contiguous, which is the
+K×nvec column-major matrix of the C ABI, and the result is (nvec, M)
+contiguous, i.e. Y as M×nvec column-major.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+PACKAGE = Path(__file__).resolve().parent
+LIBRARY = PACKAGE / "libgemv.so"
+
+if not LIBRARY.exists():
+    raise ImportError(
+        f"{LIBRARY} is not built; run `python -m memory_bound_gemv_f32_amd.build` "
+        "(there is no fallback implementation)")
+
+_lib = ctypes.CDLL(str(LIBRARY))
+
+GEMV_SUCCESS = 0
+GEMV_ERROR_INVALID_VALUE = 1
+GEMV_ERROR_LAUNCH_FAILURE = 2
+
+DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
+DTYPE_CODES = {"f32": DTYPE_F32, "f16": DTYPE_F16, "bf16": DTYPE_BF16}
+
+FAMILY_AUTO = -1
+FAMILY_ROWS_PER_WAVE = 0
+FAMILY_WAVE_PER_ROW = 1
+FAMILY_GROUP_PER_ROW = 2
+FAMILY_BATCHED = 3
+FAMILY_NAMES = {
+    FAMILY_ROWS_PER_WAVE: "rows_per_wave",
+    FAMILY_WAVE_PER_ROW: "wave_per_row",
+    FAMILY_GROUP_PER_ROW: "group_per_row",
+    FAMILY_BATCHED: "batched",
+}
+
+
+class GemvPlan(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int) for name in (
+        "family", "vector_loads", "chunk_elems", "lanes_per_row",
+        "rows_per_wave", "row_tiles", "waves_per_group", "rows_per_group",
+        "batch", "passes", "block", "lds_bytes")] + [("grid", ctypes.c_int64)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+_vp, _i, _st = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p
+
+
+def _bind(name, argtypes, restype=ctypes.c_int):
+    fn = getattr(_lib, name)
+    fn.argtypes = argtypes
+    fn.restype = restype
+    return fn
+
+
+gemv_status_string = _bind("gemv_status_string", [_i], ctypes.c_char_p)
+gemv_f32 = _bind("gemv_f32", [_vp, _i, _vp, _vp, _vp, _i, _i, _st])
+gemv_f16 = _bind("gemv_f16", [_vp, _i, _vp, _vp, _vp, _i, _i, _st])
+gemv_bf16 = _bind("gemv_bf16", [_vp, _i, _vp, _vp, _vp, _i, _i, _st])
+gemv_batched_f16 = _bind("gemv_batched_f16", [_vp, _i, _vp, _vp, _vp, _i, _i, _i, _st])
+gemv_batched_bf16 = _bind("gemv_batched_bf16", [_vp, _i, _vp, _vp, _vp, _i, _i, _i, _st])
+gemv_plan = _bind("gemv_plan", [_i, _i, _i, _i, _i, _vp, _vp, _i, ctypes.POINTER(GemvPlan)])
+gemv_run_family = _bind("gemv_run_family", [_i, _i, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _st])
+
+EXPORTED = ("gemv_status_string", "gemv_f32", "gemv_f16", "gemv_bf16",
+            "gemv_batched_f16", "gemv_batched_bf16", "gemv_plan",
+            "gemv_run_family")
+
+
+class GemvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {gemv_status_string(status).decode()}")
+
+
+def plan(dtype: str, M: int, K: int, lda: int | None = None, nvec: int = 1,
+         A_addr: int = 0, X_addr: int = 0, family: int = FAMILY_AUTO) -> dict:
+    """The mapping libgemv would launch (host-only; no GPU needed)."""
+    out = GemvPlan()
+    rc = gemv_plan(DTYPE_CODES[dtype], M, K, K if lda is None else lda, nvec,
+                   A_addr, X_addr, family, ctypes.byref(out))
+    if rc != GEMV_SUCCESS:
+        raise GemvError(rc, "gemv_plan")
+    return out.as_dict()
+
+
+# ---------------------------------------------------------------------------
+# tensor helpers
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch  # noqa: PLC0415 - torch only allocates memory and streams
+    return torch
+
+
+def _dtype_name(t) -> str:
+    torch = _torch()
+    names = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+    if t.dtype not in names:
+        raise TypeError(f"unsupported dtype {t.dtype}; expected float32, float16 or bfloat16")
+    return names[t.dtype]
+
+
+def _stream_handle(stream=None) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _check_matrix(A):
+    if A.dim() != 2:
+        raise ValueError("A must be 2-D (M, K)")
+    if not A.is_cuda:
+        raise ValueError("A must be a device tensor")
+    M, K = A.shape
+    if K > 1 and A.stride(1) != 1:
+        raise ValueError("A must have unit column stride")
+    lda = A.stride(0) if M > 1 else max(K, 1)
+    if lda < K:
+        raise ValueError("A's row stride is smaller than K")
+    return M, K, lda
+
+
+def _check_out(out, shape, device):
+    torch = _torch()
+    if out is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    if out.dtype != torch.float32 or tuple(out.shape) != tuple(shape) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous float32 tensor of shape {tuple(shape)}")
+    if out.device != device:
+        raise ValueError("out is on another device")
+    return out
+
+
+def _check_bias(bias, M, device):
+    torch = _torch()
+    if bias is None:
+        return None
+    if bias.dtype != torch.float32 or bias.dim() != 1 or bias.shape[0] != M or not bias.is_contiguous():
+        raise ValueError("bias must be a contiguous float32 tensor of shape (M,)")
+    if bias.device != device:
+        raise ValueError("bias is on another device")
+    return bias
+
+
+def gemv(A, x, bias=None, out=None, *, family: int = FAMILY_AUTO, stream=None):
+    """y = A @ x (+ bias) in fp32 on A's device; returns y (M,) float32."""
+    M, K, lda = _check_matrix(A)
+    dt = _dtype_name(A)
+    if x.dtype != A.dtype or x.dim() != 1 or x.shape[0] != K or not x.is_contiguous():
+        raise ValueError("x must be a contiguous (K,) tensor of A's dtype")
+    if x.device != A.device:
+        raise ValueError("x is on another device")
+    bias = _check_bias(bias, M, A.device)
+    y = _check_out(out, (M,), A.device)
+    args = (A.data_ptr(), lda, x.data_ptr(),
+            bias.data_ptr() if bias is not None else None, y.data_ptr(), M, K)
+    if family == FAMILY_AUTO:
+        fn = {"f32": gemv_f32, "f16": gemv_f16, "bf16": gemv_bf16}[dt]
+        rc = fn(*args, _stream_handle(stream))
+        where = fn.__name__
+    else:
+        rc = gemv_run_family(DTYPE_CODES[dt], family, args[0], lda, args[2],
+                             args[3], args[4], M, K, 1, _stream_handle(stream))
+        where = "gemv_run_family"
+    if rc != GEMV_SUCCESS:
+        raise GemvError(rc, where)
+    return y
+
+
+def gemv_batched(A, X, bias=None, out=None, *, family: int = FAMILY_AUTO,
+                 stream=None):
+    """Y = A @ X (+ bias) for X of shape (nvec, K), 1 <= nvec <= 16, fp16 or
+    bf16; returns Y of shape (nvec, M) float32 (column j = output for X[j])."""
+    M, K, lda = _check_matrix(A)
+    dt = _dtype_name(A)
+    if X.dtype != A.dtype or X.dim() != 2 or X.shape[1] != K or not X.is_contiguous():
+        raise ValueError("X must be a contiguous (nvec, K) tensor of A's dtype")
+    if X.device != A.device:
+        raise ValueError("X is on another device")
+    nvec = X.shape[0]
+    bias = _check_bias(bias, M, A.device)
+    Y = _check_out(out, (nvec, M), A.device)
+    bptr = bias.data_ptr() if bias is not None else None
+    if family == FAMILY_AUTO:
+        if dt == "f32":
+            raise TypeError("the batched entry points take float16 or bfloat16")
+        fn = {"f16": gemv_batched_f16, "bf16": gemv_batched_bf16}[dt]
+        rc = fn(A.data_ptr(), lda, X.data_ptr(), bptr, Y.data_ptr(), M, K, nvec,
+                _stream_handle(stream))
+        where = fn.__name__
+    else:
+        rc = gemv_run_family(DTYPE_CODES[dt], family, A.data_ptr(), lda,
+                             X.data_ptr(), bptr, Y.data_ptr(), M, K, nvec,
+                             _stream_handle(stream))
+        where = "gemv_run_family"
+    if rc != GEMV_SUCCESS:
+        raise GemvError(rc, where)
+    return Y

@@ -1,0 +1,122 @@
+// Device building blocks for the gfx950 GEMV kernels: element types, loads,
+// per-chunk dot products and wavefront segment reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gemvdev {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Element types.  `storage` is what sits in memory; products are formed and
+// summed in fp32 (page "GEMM、GEMV、dtype 与算术强度", section "dtype 改变什么":
+// half-precision inputs with a wider accumulator).
+struct TF32 {
+    using storage = float;
+    static constexpr int bytes = 4;
+};
+struct TF16 {
+    using storage = uint16_t;
+    static constexpr int bytes = 2;
+};
+struct TBF16 {
+    using storage = uint16_t;
+    static constexpr int bytes = 2;
+};
+
+// One stored element widened to fp32 (exact for all three types).
+__device__ __forceinline__ float widen(TF32, float v) { return v; }
+__device__ __forceinline__ float widen(TF16, uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+__device__ __forceinline__ float widen(TBF16, uint16_t h) {
+    return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+__device__ __forceinline__ float f32_of(uint32_t w) { return __builtin_bit_cast(float, w); }
+
+// acc + Σ a_i·x_i over one 16-byte chunk (4 fp32 or 8 half-width elements).
+// fp32: fused multiply-adds.  fp16 / bf16: the packed two-element dot
+// products with fp32 accumulation (v_dot2_f32_f16 / v_dot2_f32_bf16), whose
+// half-width products are exact in fp32.
+__device__ __forceinline__ float chunk_dot(TF32, uint4 a, uint4 x, float acc) {
+    acc = __builtin_fmaf(f32_of(a.x), f32_of(x.x), acc);
+    acc = __builtin_fmaf(f32_of(a.y), f32_of(x.y), acc);
+    acc = __builtin_fmaf(f32_of(a.z), f32_of(x.z), acc);
+    acc = __builtin_fmaf(f32_of(a.w), f32_of(x.w), acc);
+    return acc;
+}
+__device__ __forceinline__ float chunk_dot(TF16, uint4 a, uint4 x, float acc) {
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a.x), __builtin_bit_cast(f16x2, x.x), acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a.y), __builtin_bit_cast(f16x2, x.y), acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a.z), __builtin_bit_cast(f16x2, x.z), acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a.w), __builtin_bit_cast(f16x2, x.w), acc, false);
+    return acc;
+}
+__device__ __forceinline__ float chunk_dot(TBF16, uint4 a, uint4 x, float acc) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.x), __builtin_bit_cast(bf16x2, x.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.y), __builtin_bit_cast(bf16x2, x.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.z), __builtin_bit_cast(bf16x2, x.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w), __builtin_bit_cast(bf16x2, x.w), acc, false);
+    return acc;
+}
+
+// Chunk = one 16-byte load (VEC) or one element.
+template <class D, bool VEC>
+struct Chunk;
+template <class D>
+struct Chunk<D, true> {
+    using type = uint4;
+    static constexpr int elems = 16 / D::bytes;
+    __device__ __forceinline__ static type load(const typename D::storage* p, int64_t c) {
+        return *reinterpret_cast<const uint4*>(p + c * elems);
+    }
+    __device__ __forceinline__ static type zero() { return make_uint4(0u, 0u, 0u, 0u); }
+    __device__ __forceinline__ static float dot(type a, type x, float acc) {
+        return chunk_dot(D{}, a, x, acc);
+    }
+};
+template <class D>
+struct Chunk<D, false> {
+    using type = typename D::storage;
+    static constexpr int elems = 1;
+    __device__ __forceinline__ static type load(const typename D::storage* p, int64_t c) {
+        return p[c];
+    }
+    __device__ __forceinline__ static type zero() { return type(0); }
+    __device__ __forceinline__ static float dot(type a, type x, float acc) {
+        return __builtin_fmaf(widen(D{}, a), widen(D{}, x), acc);
+    }
+};
+
+// DPP lane exchange within 16-lane rows (bound_ctrl: no lane is disabled).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+constexpr int kDppSwapAdjacent = 0xB1;   // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppSwapPairs = 0x4E;      // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppHalfRowMirror = 0x141; // lane i <- 7 - i within 8 lanes
+constexpr int kDppRowMirror = 0x140;     // lane i <- 15 - i within 16 lanes
+
+// Sum over each aligned segment of L lanes (L a power of two, 1..64); every
+// lane of the segment receives the same, bit-identical total.  Every lane of
+// the wavefront must execute this (no lane may be inactive).  After the two
+// quad steps all four lanes of a quad hold the quad sum, so the mirrors act
+// as the xor-4 and xor-8 butterfly steps; the 32- and 64-lane steps cross DPP
+// rows through the LDS crossbar (ds_bpermute), which uses no LDS storage.
+template <int L>
+__device__ __forceinline__ float segment_sum(float v) {
+    if constexpr (L >= 2) v += dpp<kDppSwapAdjacent>(v);
+    if constexpr (L >= 4) v += dpp<kDppSwapPairs>(v);
+    if constexpr (L >= 8) v += dpp<kDppHalfRowMirror>(v);
+    if constexpr (L >= 16) v += dpp<kDppRowMirror>(v);
+    if constexpr (L >= 32) v += __shfl_xor(v, 16, 64);
+    if constexpr (L >= 64) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+}  // namespace gemvdev

@@ -1,0 +1,192 @@
+// Host-side mapping of a GEMV problem onto gfx950 workgroups.
+//
+// Pure C++ (no HIP headers): the same function decides what the entry points
+// launch and what gemv_plan() reports, so the mapping table can be checked on
+// a machine without a GPU.
+//
+// The one design axis is how many lanes cooperate on one row's dot product
+// (page "SGEMV CUDA代码学习", section "三 kernel 的设计空间总结": elements per
+// lane times rows per warp equals the warp width, so that no lane idles).  On
+// a 64-lane wavefront with 16-byte loads, one load instruction covers 1 KiB
+// of A, so:
+//   * rows shorter than 32 loads (fp32 K <= 128, fp16/bf16 K <= 256) share a
+//     wavefront: L lanes per row, L the next power of two of the row's load
+//     count, 64/L rows per wavefront (the page's section "Kernel 3: k16", two
+//     rows per warp, generalised);
+//   * mid-length rows get one wavefront each (its sections "Kernel 1: k32"
+//     and "Kernel 2: k128 + Vec4");
+//   * long rows when there are too few rows to fill the chip get a whole
+//     workgroup each with a cross-wavefront reduction in LDS (page "第 3 课：
+//     GEMV 与行级并行", section "2. 行级并行与 Block 映射架构" and the
+//     threshold discussion of its section "4. 性能与工程权舍").
+// The thresholds are this library's own, set for 256 CUs.
+#pragma once
+
+#include <stdint.h>
+
+namespace gemvplan {
+
+enum Dtype { F32 = 0, F16 = 1, BF16 = 2 };
+enum Family { AUTO = -1, ROWS_PER_WAVE = 0, WAVE_PER_ROW = 1, GROUP_PER_ROW = 2, BATCHED = 3 };
+enum Status { OK = 0, INVALID = 1 };
+
+constexpr int kWave = 64;
+constexpr int kLoadBytes = 16;
+constexpr int kMaxVectors = 16;
+
+// Rows-per-wave family: lanes per row is a power of two up to this.
+constexpr int kRowsPerWaveMaxLanes = 32;
+// Workgroup-per-row family: wavefronts per workgroup, and when it is chosen
+// automatically (few rows, long rows).
+constexpr int kGroupWaves = 4;
+constexpr int64_t kGroupMaxRows = 2048;
+constexpr int64_t kGroupMinLoadsPerRow = 512;
+// Wave-per-row family: loads per lane kept in flight per row.
+constexpr int kWaveBatch = 8;
+constexpr int kGroupBatch = 4;
+// Batched family: loads in flight per row, and rows per wavefront, fewer as
+// the number of vectors grows so that rows × vectors accumulators plus the
+// loaded chunks fit the register budget of four wavefronts per SIMD.
+constexpr int kBatchedBatch = 1;
+constexpr int batched_rows(int nvec) { return nvec <= 2 ? 4 : (nvec <= 4 ? 2 : 1); }
+// Threads per workgroup of the rows/wave and batched families.
+constexpr int kBlock = 256;
+// Below this many workgroups the rows-per-wave family stops giving each
+// wavefront several row tiles, so that small problems still spread out.
+constexpr int64_t kTargetGroups = 1024;
+
+struct Plan {
+    int family = -1;
+    int vector_loads = 0;
+    int chunk_elems = 1;
+    int lanes_per_row = 0;
+    int rows_per_wave = 0;
+    int row_tiles = 0;
+    int waves_per_group = 0;
+    int rows_per_group = 0;
+    int batch = 0;
+    int passes = 0;
+    int block = 0;
+    int lds_bytes = 0;
+    int64_t grid = 0;
+};
+
+inline int element_bytes(int dtype) { return dtype == F32 ? 4 : 2; }
+
+inline int next_pow2(int64_t v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Argument checks shared by every entry point (see the header's "Errors").
+inline int validate(int dtype, int M, int K, int lda, int nvec, uintptr_t A,
+                    uintptr_t X, uintptr_t bias, uintptr_t Y) {
+    if (dtype < F32 || dtype > BF16) return INVALID;
+    if (M < 0 || K < 0 || lda < K) return INVALID;
+    if (nvec < 1 || nvec > kMaxVectors) return INVALID;
+    const uintptr_t s = (uintptr_t)element_bytes(dtype);
+    if (M > 0 && K > 0 && (A == 0 || X == 0)) return INVALID;
+    if (M > 0 && Y == 0) return INVALID;
+    if (A % s != 0 || X % s != 0 || bias % 4 != 0 || Y % 4 != 0) return INVALID;
+    return OK;
+}
+
+// 16-byte loads need 16-byte aligned A, x (and every X column) and row pitch.
+inline bool vector_ok(int dtype, int K, int lda, int nvec, uintptr_t A, uintptr_t X) {
+    const int64_t s = element_bytes(dtype);
+    if (A % kLoadBytes != 0 || X % kLoadBytes != 0) return false;
+    if (((int64_t)lda * s) % kLoadBytes != 0) return false;
+    if (nvec > 1 && ((int64_t)K * s) % kLoadBytes != 0) return false;
+    return true;
+}
+
+inline int make_plan(int dtype, int M, int K, int lda, int nvec, uintptr_t A,
+                     uintptr_t X, int family, Plan* out) {
+    // Shape checks only: planning accepts any pointer value, NULL included.
+    if (dtype < F32 || dtype > BF16 || M < 0 || K < 0 || lda < K || nvec < 1 ||
+        nvec > kMaxVectors)
+        return INVALID;
+
+    Plan p;
+    p.vector_loads = vector_ok(dtype, K, lda, nvec, A, X) ? 1 : 0;
+    p.chunk_elems = p.vector_loads ? kLoadBytes / element_bytes(dtype) : 1;
+    // loads needed to cover one row (the last may be a partial, element-wise tail)
+    const int64_t loads = ceil_div(K, p.chunk_elems);
+    const int64_t full = K / p.chunk_elems;
+
+    int fam = family;
+    if (fam == AUTO) {
+        if (nvec > 1)
+            fam = BATCHED;
+        else if (loads <= kRowsPerWaveMaxLanes)
+            fam = ROWS_PER_WAVE;
+        else if (M <= kGroupMaxRows && loads >= kGroupMinLoadsPerRow)
+            fam = GROUP_PER_ROW;
+        else
+            fam = WAVE_PER_ROW;
+    }
+    if (fam != BATCHED && nvec != 1) return INVALID;
+    if (fam == BATCHED && dtype == F32) return INVALID;
+
+    p.family = fam;
+    switch (fam) {
+    case ROWS_PER_WAVE: {
+        if (loads > kRowsPerWaveMaxLanes) return INVALID;
+        p.lanes_per_row = next_pow2(loads < 1 ? 1 : loads);
+        p.rows_per_wave = kWave / p.lanes_per_row;
+        p.waves_per_group = kBlock / kWave;
+        p.batch = 1;
+        // as many row tiles per wavefront as keeps >= kTargetGroups groups
+        p.row_tiles = 1;
+        if (p.vector_loads) {
+            for (int u = 8; u > 1; u >>= 1) {
+                const int64_t rows = (int64_t)u * p.rows_per_wave * p.waves_per_group;
+                if (ceil_div(M, rows) >= kTargetGroups) {
+                    p.row_tiles = u;
+                    break;
+                }
+            }
+        }
+        break;
+    }
+    case WAVE_PER_ROW:
+        p.lanes_per_row = kWave;
+        p.rows_per_wave = 1;
+        p.waves_per_group = kBlock / kWave;
+        p.batch = kWaveBatch;
+        p.row_tiles = 1;
+        break;
+    case GROUP_PER_ROW:
+        p.lanes_per_row = kWave * kGroupWaves;
+        p.rows_per_wave = 0;  // a row spans the whole workgroup
+        p.waves_per_group = kGroupWaves;
+        p.batch = kGroupBatch;
+        p.row_tiles = 1;
+        p.lds_bytes = (int)(kGroupWaves * sizeof(float));
+        break;
+    case BATCHED:
+        p.lanes_per_row = kWave;
+        p.rows_per_wave = batched_rows(nvec);
+        p.waves_per_group = kBlock / kWave;
+        p.batch = kBatchedBatch;
+        p.row_tiles = 1;
+        break;
+    default:
+        return INVALID;
+    }
+    p.block = p.waves_per_group * kWave;
+    if (fam == GROUP_PER_ROW)
+        p.rows_per_group = 1;
+    else
+        p.rows_per_group = p.rows_per_wave * p.row_tiles * p.waves_per_group;
+    p.grid = ceil_div(M, p.rows_per_group);
+    p.passes = (int)ceil_div(full, (int64_t)p.lanes_per_row);
+    if (p.grid > 0x7fffffff) return INVALID;
+    *out = p;
+    return OK;
+}
+
+}  // namespace gemvplan

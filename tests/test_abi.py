@@ -1,0 +1,181 @@
+"""libgemv's C ABI on the host: the library loads, exports what the header
+declares, validates arguments before touching the GPU, and maps shapes onto
+kernel families as designed.  No GPU and no compute call is needed."""
+
+import ctypes
+import json
+import re
+from pathlib import Path
+
+import pytest
+
+import memory_bound_gemv_f32_amd as lg
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "gemv.h"
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemv_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("gemv_f32", "gemv_f16", "gemv_bf16", "gemv_batched_f16",
+                 "gemv_batched_bf16", "gemv_status_string", "gemv_plan",
+                 "gemv_run_family"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(str(lg.LIBRARY))
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) <= set(lg.EXPORTED)
+
+
+def test_status_strings():
+    for code in (lg.GEMV_SUCCESS, lg.GEMV_ERROR_INVALID_VALUE, lg.GEMV_ERROR_LAUNCH_FAILURE):
+        assert lg.gemv_status_string(code).startswith(b"GEMV_")
+    assert b"unknown" in lg.gemv_status_string(99)
+
+
+# Invalid arguments are rejected before any HIP call, so these run without a
+# GPU.  Pointers here are dummies that must never be dereferenced.
+GOOD = 0x10000
+
+
+@pytest.mark.parametrize("args", [
+    dict(M=-1), dict(K=-1), dict(lda=3, K=4), dict(A=0), dict(x=0), dict(y=0),
+    dict(A=GOOD + 2), dict(x=GOOD + 1), dict(y=GOOD + 2), dict(bias=GOOD + 1),
+])
+def test_f32_validation(args):
+    a = dict(A=GOOD, lda=8, x=GOOD, bias=None, y=GOOD, M=4, K=8)
+    a.update(args)
+    rc = lg.gemv_f32(a["A"] or None, a["lda"], a["x"] or None, a["bias"],
+                     a["y"] or None, a["M"], a["K"], None)
+    assert rc == lg.GEMV_ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("fn", [lg.gemv_f16, lg.gemv_bf16])
+def test_half_validation(fn):
+    assert fn(GOOD + 1, 8, GOOD, None, GOOD, 4, 8, None) == lg.GEMV_ERROR_INVALID_VALUE
+    assert fn(GOOD, 7, GOOD, None, GOOD, 4, 8, None) == lg.GEMV_ERROR_INVALID_VALUE
+    assert fn(None, 8, GOOD, None, GOOD, 4, 8, None) == lg.GEMV_ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("fn", [lg.gemv_batched_f16, lg.gemv_batched_bf16])
+@pytest.mark.parametrize("nvec", [0, 17, -3])
+def test_batched_rejects_nvec(fn, nvec):
+    assert fn(GOOD, 8, GOOD, None, GOOD, 4, 8, nvec, None) == lg.GEMV_ERROR_INVALID_VALUE
+
+
+def test_empty_M_is_a_successful_no_op():
+    # M == 0: nothing to compute and nothing enqueued
+    assert lg.gemv_f32(None, 8, None, None, None, 0, 8, None) == lg.GEMV_SUCCESS
+    assert lg.gemv_batched_bf16(None, 8, None, None, None, 0, 8, 4, None) == lg.GEMV_SUCCESS
+
+
+def test_forced_family_must_fit_the_shape():
+    r = lg.gemv_run_family(lg.DTYPE_F32, lg.FAMILY_BATCHED, GOOD, 8, GOOD, None,
+                           GOOD, 4, 8, 2, None)
+    assert r == lg.GEMV_ERROR_INVALID_VALUE
+    r = lg.gemv_run_family(lg.DTYPE_F16, lg.FAMILY_WAVE_PER_ROW, GOOD, 8, GOOD,
+                           None, GOOD, 4, 8, 2, None)
+    assert r == lg.GEMV_ERROR_INVALID_VALUE
+    with pytest.raises(lg.GemvError):
+        lg.plan("f32", 4, 8, family=17)
+
+
+# ---------------------------------------------------------------------------
+# mapping table
+# ---------------------------------------------------------------------------
+
+ALIGNED = 1 << 20
+
+
+def p(dtype, M, K, lda=None, nvec=1, A=ALIGNED, X=ALIGNED, family=lg.FAMILY_AUTO):
+    return lg.plan(dtype, M, K, lda, nvec, A, X, family)
+
+
+@pytest.mark.parametrize("dtype,K,lanes", [
+    ("f32", 16, 4), ("f32", 32, 8), ("f32", 128, 32), ("f32", 4, 1),
+    ("f32", 20, 8), ("bf16", 16, 2), ("bf16", 256, 32), ("f16", 64, 8),
+    ("f32", 0, 1), ("f32", 3, 1),
+])
+def test_short_rows_share_a_wavefront(dtype, K, lanes):
+    per16 = 4 if dtype == "f32" else 8
+    lda = max(per16, -(-K // per16) * per16)  # 16-byte row pitch
+    q = p(dtype, 1 << 20, K, lda=lda)
+    assert q["family"] == lg.FAMILY_ROWS_PER_WAVE
+    assert q["vector_loads"] == 1
+    assert q["lanes_per_row"] == lanes
+    assert q["rows_per_wave"] * q["lanes_per_row"] == 64
+    # no lane idles beyond rounding the row's loads up to a power of two
+    loads = -(-K // q["chunk_elems"])
+    assert loads <= lanes < 2 * max(loads, 1) or lanes == 1
+    assert q["grid"] * q["rows_per_group"] >= 1 << 20
+
+
+def test_skinny_k16_geometry():
+    q = p("f32", 1 << 20, 16)
+    assert (q["lanes_per_row"], q["rows_per_wave"], q["row_tiles"]) == (4, 16, 8)
+    assert q["rows_per_group"] == 16 * 8 * 4
+    assert q["grid"] == (1 << 20) // q["rows_per_group"]
+
+
+def test_small_problem_spreads_out():
+    q = p("f32", 1024, 128)  # the 1024 x 128 timing shape: launch-bound
+    assert q["family"] == lg.FAMILY_ROWS_PER_WAVE and q["row_tiles"] == 1
+    assert q["grid"] == 1024 // 8
+
+
+def test_mid_rows_get_a_wavefront_each():
+    q = p("bf16", 4096, 4096)
+    assert q["family"] == lg.FAMILY_WAVE_PER_ROW
+    assert q["lanes_per_row"] == 64 and q["rows_per_group"] == 4
+    assert q["grid"] == 1024 and q["passes"] == 8
+    q = p("bf16", 4096, 14336)
+    assert q["family"] == lg.FAMILY_WAVE_PER_ROW and q["passes"] == 28
+
+
+def test_few_long_rows_get_a_workgroup_each():
+    q = p("bf16", 1024, 4096)
+    assert q["family"] == lg.FAMILY_GROUP_PER_ROW
+    assert q["grid"] == 1024 and q["block"] == 256 and q["rows_per_group"] == 1
+
+
+def test_worked_example_mapping():
+    """Page "第 3 课：GEMV 与行级并行", section "具体演示与数值推演": M=3,
+    N=1024 on 256 threads per row is 3 workgroups, each thread taking 4
+    strided passes of one element.  The workgroup-per-row family with
+    element loads (a misaligned A forces them) reproduces that geometry."""
+    fx = json.loads((ROOT / "tests" / "golden" / "worked_example_m3_k1024.json").read_text())
+    pg = fx["printed_by_the_page"]
+    q = p("f32", pg["M"], pg["N"], A=ALIGNED + 4, family=lg.FAMILY_GROUP_PER_ROW)
+    assert q["vector_loads"] == 0
+    assert q["grid"] == pg["blocks"]
+    assert q["lanes_per_row"] == pg["threads_per_block"] == q["block"]
+    assert q["passes"] == pg["column_passes_per_row"]
+    # with 16-byte loads the same row is one pass
+    q = p("f32", pg["M"], pg["N"], family=lg.FAMILY_GROUP_PER_ROW)
+    assert q["vector_loads"] == 1 and q["passes"] == 1
+
+
+@pytest.mark.parametrize("kw", [dict(A=ALIGNED + 4), dict(X=ALIGNED + 8),
+                                dict(lda=4097)])
+def test_misaligned_falls_back_to_element_loads(kw):
+    q = p("f32", 4096, 4096, **kw)
+    assert q["vector_loads"] == 0 and q["chunk_elems"] == 1
+
+
+def test_batched_plans():
+    q = p("f16", 4096, 4096, nvec=16)
+    assert q["family"] == lg.FAMILY_BATCHED
+    q1 = p("f16", 4096, 4096, nvec=1)
+    assert q1["family"] != lg.FAMILY_BATCHED   # nvec 1 is plain GEMV
+    assert p("f16", 4096, 4095, nvec=4)["vector_loads"] == 0  # X columns misaligned
+    with pytest.raises(lg.GemvError):
+        p("f16", 4096, 4096, nvec=17)

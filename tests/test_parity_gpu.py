@@ -1,0 +1,241 @@
+"""Parity of libgemv's HIP kernels with the CPU oracle (needs an MI355X).
+
+Every case goes through the C ABI (ctypes), compares element by element with
+the fp64 oracle on the same seeded inputs, and checks canary words around
+the output.  Integer-valued, identity, one-hot and worked-example inputs
+must match bit for bit (every partial sum is exact in fp32, whatever the
+order); random inputs must satisfy |y - y_ref| <= 1e-5·Σ|A·x| + 1e-6.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import gemv_inputs as gi
+import memory_bound_gemv_f32_amd as lg
+from gpu_helpers import (assert_bit_exact, assert_within_bound, run_gpu,
+                         run_oracle)
+from oracle_pins import lib_decode
+
+pytestmark = pytest.mark.gpu
+
+SINGLE_FAMILIES = [lg.FAMILY_AUTO, lg.FAMILY_ROWS_PER_WAVE, lg.FAMILY_WAVE_PER_ROW,
+                   lg.FAMILY_GROUP_PER_ROW]
+
+
+def families_for(case: gi.Case, misalign: int = 0):
+    """Every family the planner accepts for this shape and alignment."""
+    out = []
+    fams = SINGLE_FAMILIES if case.nvec == 1 else [lg.FAMILY_AUTO]
+    if case.dtype != "f32":
+        fams = fams + [lg.FAMILY_BATCHED]
+    addr = (1 << 20) + misalign * gi.ELEMENT_BYTES[case.dtype]
+    for fam in fams:
+        try:
+            lg.plan(case.dtype, case.M, case.K, case.lda, case.nvec, addr, addr, fam)
+        except lg.GemvError:
+            continue
+        out.append(fam)
+    return out
+
+
+def pad16(dtype, K):
+    per = 16 // gi.ELEMENT_BYTES[dtype]
+    return max(per, -(-K // per) * per)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    name = torch.cuda.get_device_properties(0).gcnArchName
+    print(f"device: {torch.cuda.get_device_name(0)} arch {name}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# bit-exact pins
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", gi.DTYPES)
+@pytest.mark.parametrize("bias", [False, True])
+@pytest.mark.parametrize("misalign", [0, 1])
+def test_worked_example(dtype, bias, misalign):
+    """M=3, K=1024 (page "第 3 课：GEMV 与行级并行", section "具体演示与数值推演"):
+    y = -512·(m+1) (+ bias), bit-exact on every family that can run it."""
+    case = gi.make_worked_example(dtype, bias=bias)
+    want = np.array([[-512.0, -1024.0, -1536.0]])
+    if bias:
+        want = want + np.array([[0.5, -0.25, 1.0]])
+    for fam in families_for(case, misalign):
+        y = run_gpu(case, fam, misalign=misalign)
+        assert_bit_exact(y, want, f"{dtype} family {fam} misalign {misalign}")
+
+
+@pytest.mark.parametrize("dtype", gi.DTYPES)
+@pytest.mark.parametrize("n", [1, 7, 64, 300, 1024, 4096])
+def test_identity(dtype, n):
+    case = gi.make_identity(dtype, n, seed=n, bias=True)
+    ref, _ = run_oracle(case)
+    for fam in families_for(case):
+        assert_bit_exact(run_gpu(case, fam), ref, f"{dtype} n={n} family {fam}")
+
+
+@pytest.mark.parametrize("dtype", gi.DTYPES)
+@pytest.mark.parametrize("M,K,extra", [(1000, 16, 0), (999, 100, 4), (513, 777, 9),
+                                       (300, 4096, 0), (64, 14336, 8)])
+def test_one_hot(dtype, M, K, extra):
+    case = gi.make_one_hot(dtype, M, K, seed=K, lda=K + extra)
+    ref, _ = run_oracle(case)
+    for fam in families_for(case):
+        assert_bit_exact(run_gpu(case, fam), ref, f"{dtype} {M}x{K} family {fam}")
+
+
+INT_SHAPES = [(1, 1), (5, 3), (63, 8), (64, 15), (65, 16), (130, 17), (257, 31),
+              (33, 32), (17, 33), (9, 127), (300, 128), (31, 129), (7, 255),
+              (129, 256), (3, 257), (70, 1000), (40, 1024), (5, 4097), (3, 14337)]
+
+
+@pytest.mark.parametrize("dtype", gi.DTYPES)
+@pytest.mark.parametrize("M,K", INT_SHAPES)
+def test_integer_every_family(dtype, M, K):
+    """Exact-integer regime: every family, with bias, tight and padded row
+    pitch, aligned and element-aligned pointers; all bit-exact."""
+    for lda, misalign in ((K, 0), (pad16(dtype, K), 0), (K + 3, 0), (pad16(dtype, K), 1)):
+        case = gi.make_integer(dtype, M, K, seed=M * 7 + K, lda=lda, bias=True)
+        ref, _ = run_oracle(case)
+        for fam in families_for(case, misalign):
+            y = run_gpu(case, fam, misalign=misalign)
+            assert_bit_exact(y, ref, f"{dtype} {M}x{K} lda={lda} misalign={misalign} family {fam}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("nvec", list(range(1, 17)))
+def test_integer_batched(dtype, nvec):
+    for M, K, lda in ((67, 512, 512), (130, 1000, 1000), (9, 4104, 4104), (33, 77, 80)):
+        case = gi.make_integer(dtype, M, K, seed=nvec * 100 + K, nvec=nvec, lda=lda,
+                               bias=nvec % 2 == 0)
+        ref, _ = run_oracle(case)
+        y = run_gpu(case, lg.FAMILY_AUTO, batched=True)
+        assert_bit_exact(y, ref, f"{dtype} nvec={nvec} {M}x{K}")
+        y1 = run_gpu(case, lg.FAMILY_BATCHED, batched=True, misalign=1)
+        assert_bit_exact(y1, ref, f"{dtype} nvec={nvec} {M}x{K} element loads")
+
+
+def test_empty_reduction_gives_bias():
+    for dtype in gi.DTYPES:
+        for bias in (False, True):
+            case = gi.make_integer(dtype, 100, 0, seed=1, bias=bias)
+            want = case.bias.astype(np.float64)[None, :] if bias else np.zeros((1, 100))
+            for fam in families_for(case):
+                assert_bit_exact(run_gpu(case, fam), want, f"K=0 {dtype} family {fam}")
+
+
+def test_nan_stays_in_its_row():
+    for dtype in gi.DTYPES:
+        case = gi.make_random(dtype, 300, 1000, seed=3, lda=1000)
+        nan = gi.quantise(dtype, np.array([np.nan]))[0]
+        case.A = case.A.copy()
+        case.A[123, 456] = nan
+        for fam in families_for(case):
+            y = run_gpu(case, fam)[0]
+            assert np.isnan(y[123]), (dtype, fam)
+            assert np.all(np.isfinite(np.delete(y, 123))), (dtype, fam)
+
+
+def test_f16_subnormals_are_kept():
+    """fp16 subnormal A (2^-20 · small integers) times integer x: exact sums."""
+    rng = np.random.default_rng(5)
+    M, K = 256, 4096
+    a = rng.integers(-7, 8, size=(M, K)) * 2.0 ** -20
+    x = rng.integers(-7, 8, size=(1, K)).astype(np.float64)
+    case = gi.Case("sub_f16", "f16", M, K, gi.quantise("f16", a), gi.quantise("f16", x), None, K)
+    ref, _ = run_oracle(case)
+    for fam in families_for(case):
+        assert_bit_exact(run_gpu(case, fam), ref, f"subnormal family {fam}")
+    case.nvec = 4
+    case.X = gi.quantise("f16", np.repeat(x, 4, axis=0))
+    ref, _ = run_oracle(case)
+    assert_bit_exact(run_gpu(case, lg.FAMILY_AUTO, batched=True), ref, "subnormal batched")
+
+
+# ---------------------------------------------------------------------------
+# random data within the bound
+# ---------------------------------------------------------------------------
+
+RANDOM_SHAPES = [(1, 5), (777, 16), (1000, 37), (513, 128), (100, 255), (257, 1000),
+                 (2048, 4096), (1024, 4096), (31, 14336), (4097, 300)]
+
+
+@pytest.mark.parametrize("dtype", gi.DTYPES)
+@pytest.mark.parametrize("M,K", RANDOM_SHAPES)
+def test_random_every_family(dtype, M, K):
+    for lda in (K, pad16(dtype, K) + 8):
+        case = gi.make_random(dtype, M, K, seed=M + K, lda=lda, bias=True, dist="normal")
+        ref, absdot = run_oracle(case)
+        for fam in families_for(case):
+            y = run_gpu(case, fam)
+            assert_within_bound(y, ref, absdot, f"{dtype} {M}x{K} lda={lda} family {fam}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("nvec", [2, 3, 8, 13, 16])
+def test_random_batched(dtype, nvec):
+    for M, K in ((4096, 4096), (1000, 1000), (64, 14336)):
+        case = gi.make_random(dtype, M, K, seed=nvec + K, nvec=nvec, bias=True,
+                              dist="normal", scale=1 / np.sqrt(K))
+        ref, absdot = run_oracle(case)
+        y = run_gpu(case, lg.FAMILY_AUTO, batched=True)
+        assert_within_bound(y, ref, absdot, f"{dtype} nvec={nvec} {M}x{K}")
+
+
+# ---------------------------------------------------------------------------
+# invariants
+# ---------------------------------------------------------------------------
+
+def test_scaling_negation_permutation_determinism():
+    for dtype in gi.DTYPES:
+        case = gi.make_random(dtype, 1111, 3000, seed=9, dist="normal")
+        y = run_gpu(case, lg.FAMILY_AUTO)
+        assert_bit_exact(run_gpu(case, lg.FAMILY_AUTO), y, "repeat")
+        # doubling and negating are exact in every encoding at these magnitudes
+        X2 = gi.quantise(dtype, 2.0 * lib_decode(dtype, case.X))
+        Xn = gi.quantise(dtype, -1.0 * lib_decode(dtype, case.X))
+        for X, factor in ((X2, 2.0), (Xn, -1.0)):
+            c2 = gi.Case(case.name, dtype, case.M, case.K, case.A, X.astype(case.X.dtype),
+                         None, case.lda)
+            assert_bit_exact(run_gpu(c2, lg.FAMILY_AUTO), factor * y, f"{dtype} x*{factor}")
+        perm = np.random.default_rng(1).permutation(case.M)
+        cp = gi.Case(case.name, dtype, case.M, case.K, case.A[perm], case.X, None, case.lda)
+        assert_bit_exact(run_gpu(cp, lg.FAMILY_AUTO), y[:, perm], f"{dtype} row permutation")
+
+
+def test_batched_columns_and_single_vector_agree():
+    for dtype in ("f16", "bf16"):
+        case = gi.make_random(dtype, 2000, 2048, seed=4, nvec=11, bias=True, dist="normal")
+        Y = run_gpu(case, lg.FAMILY_AUTO, batched=True)
+        ref, absdot = run_oracle(case)
+        assert_within_bound(Y, ref, absdot, "batched")
+        perm = np.random.default_rng(2).permutation(case.nvec)
+        cp = gi.Case(case.name, dtype, case.M, case.K, case.A, case.X[perm], case.bias,
+                     case.lda, case.nvec)
+        assert_bit_exact(run_gpu(cp, lg.FAMILY_AUTO, batched=True), Y[perm], "column permutation")
+        for j in (0, 5, 10):
+            c1 = gi.Case(case.name, dtype, case.M, case.K, case.A, case.X[j:j + 1], case.bias,
+                         case.lda)
+            assert_within_bound(run_gpu(c1, lg.FAMILY_AUTO), ref[j:j + 1], absdot[j:j + 1],
+                                f"single vector {j}")
+
+
+# ---------------------------------------------------------------------------
+# the full-size workloads, in the launch configuration the benchmark times
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(gi.WORKLOADS))
+def test_full_size_workload(name):
+    case = gi.make_workload(name)
+    print(f"workload {name}: {case.dtype} M={case.M} K={case.K} nvec={case.nvec}", flush=True)
+    ref, absdot = run_oracle(case)
+    y = run_gpu(case, lg.FAMILY_AUTO, batched=case.nvec > 1)
+    assert_within_bound(y, ref, absdot, name)

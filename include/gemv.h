@@ -71,6 +71,12 @@ typedef enum {
 /* Static, NUL-terminated description of a status code. */
 const char *gemv_status_string(gemv_status_t status);
 
+/* The hipError_t value behind the calling thread's most recent
+ * GEMV_ERROR_LAUNCH_FAILURE (0 = hipSuccess if there was none), and the HIP
+ * runtime's name for it.  Thread-local; other calls do not reset it. */
+int gemv_last_hip_error(void);
+const char *gemv_last_hip_error_string(void);
+
 /* y = A·x (+ bias); A, x fp32. */
 gemv_status_t gemv_f32(const float *A, int lda, const float *x,
                        const float *bias, float *y, int M, int K,

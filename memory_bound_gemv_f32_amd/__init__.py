@@ -27,12 +27,21 @@ from __future__ import annotations
 import ctypes
 from pathlib import Path
 
+# torch ships its own HIP runtime under the same soname (libamdhip64.so.7) as
+# the system one that libgemv is linked against.  Whichever loads first is the
+# one the process uses, so torch goes first: libgemv then launches on the
+# runtime that owns torch's streams and allocations.
+try:
+    import torch as _torch_runtime  # noqa: F401
+except ImportError:  # a C-only user of the library has no torch
+    _torch_runtime = None
+
 PACKAGE = Path(__file__).resolve().parent
 LIBRARY = PACKAGE / "libgemv.so"
 
 if not LIBRARY.exists():
     raise ImportError(
-        f"{LIBRARY} is not built; run `python -m memory_bound_gemv_f32_amd.build` "
+        f"{LIBRARY} is not built; run `python memory_bound_gemv_f32_amd/build.py` "
         "(there is no fallback implementation)")
 
 _lib = ctypes.CDLL(str(LIBRARY))
@@ -78,6 +87,8 @@ def _bind(name, argtypes, restype=ctypes.c_int):
 
 
 gemv_status_string = _bind("gemv_status_string", [_i], ctypes.c_char_p)
+gemv_last_hip_error = _bind("gemv_last_hip_error", [])
+gemv_last_hip_error_string = _bind("gemv_last_hip_error_string", [], ctypes.c_char_p)
 gemv_f32 = _bind("gemv_f32", [_vp, _i, _vp, _vp, _vp, _i, _i, _st])
 gemv_f16 = _bind("gemv_f16", [_vp, _i, _vp, _vp, _vp, _i, _i, _st])
 gemv_bf16 = _bind("gemv_bf16", [_vp, _i, _vp, _vp, _vp, _i, _i, _st])
@@ -86,7 +97,8 @@ gemv_batched_bf16 = _bind("gemv_batched_bf16", [_vp, _i, _vp, _vp, _vp, _i, _i, 
 gemv_plan = _bind("gemv_plan", [_i, _i, _i, _i, _i, _vp, _vp, _i, ctypes.POINTER(GemvPlan)])
 gemv_run_family = _bind("gemv_run_family", [_i, _i, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _st])
 
-EXPORTED = ("gemv_status_string", "gemv_f32", "gemv_f16", "gemv_bf16",
+EXPORTED = ("gemv_status_string", "gemv_last_hip_error",
+            "gemv_last_hip_error_string", "gemv_f32", "gemv_f16", "gemv_bf16",
             "gemv_batched_f16", "gemv_batched_bf16", "gemv_plan",
             "gemv_run_family")
 
@@ -94,7 +106,10 @@ EXPORTED = ("gemv_status_string", "gemv_f32", "gemv_f16", "gemv_bf16",
 class GemvError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
-        super().__init__(f"{where}: {gemv_status_string(status).decode()}")
+        msg = f"{where}: {gemv_status_string(status).decode()}"
+        if status == GEMV_ERROR_LAUNCH_FAILURE:
+            msg += f" ({gemv_last_hip_error_string().decode()})"
+        super().__init__(msg)
 
 
 def plan(dtype: str, M: int, K: int, lda: int | None = None, nvec: int = 1,

@@ -1,7 +1,9 @@
 """Build libgemv.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
-Run as ``python -m memory_bound_gemv_f32_amd.build``; ``__graft_entry__.build``
-calls :func:`build`.  The library is written next to this file, in-tree.
+Run as ``python memory_bound_gemv_f32_amd/build.py`` (a standalone script: it
+does not import the package, whose import needs the built library);
+``__graft_entry__.build`` loads this file by path and calls :func:`build`.
+The library is written next to this file, in-tree.
 """
 
 from __future__ import annotations

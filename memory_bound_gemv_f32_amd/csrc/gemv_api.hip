@@ -12,6 +12,8 @@
 
 namespace {
 
+thread_local hipError_t g_last_launch_error = hipSuccess;
+
 using gemvdev::TBF16;
 using gemvdev::TF16;
 using gemvdev::TF32;
@@ -148,7 +150,12 @@ gemv_status_t run(int dtype, int family, const void* A, int lda, const void* X,
     }
     if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;
     const Args args{A, (int64_t)lda, X, bias, Y, M, K};
-    return launch(fn, p, stream, args) == hipSuccess ? GEMV_SUCCESS : GEMV_ERROR_LAUNCH_FAILURE;
+    const hipError_t err = launch(fn, p, stream, args);
+    if (err != hipSuccess) {
+        g_last_launch_error = err;
+        return GEMV_ERROR_LAUNCH_FAILURE;
+    }
+    return GEMV_SUCCESS;
 }
 
 }  // namespace
@@ -163,6 +170,10 @@ const char* gemv_status_string(gemv_status_t status) {
     default: return "unknown gemv_status_t value";
     }
 }
+
+int gemv_last_hip_error(void) { return (int)g_last_launch_error; }
+
+const char* gemv_last_hip_error_string(void) { return hipGetErrorName(g_last_launch_error); }
 
 gemv_status_t gemv_f32(const float* A, int lda, const float* x, const float* bias, float* y,
                        int M, int K, hipStream_t stream) {

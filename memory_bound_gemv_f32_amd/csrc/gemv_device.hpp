@@ -37,10 +37,20 @@ __device__ __forceinline__ float widen(TBF16, uint16_t h) {
 
 __device__ __forceinline__ float f32_of(uint32_t w) { return __builtin_bit_cast(float, w); }
 
-// acc + Σ a_i·x_i over one 16-byte chunk (4 fp32 or 8 half-width elements).
-// fp32: fused multiply-adds.  fp16 / bf16: the packed two-element dot
-// products with fp32 accumulation (v_dot2_f32_f16 / v_dot2_f32_bf16), whose
-// half-width products are exact in fp32.
+// acc + Σ a_i·x_i over one 16-byte chunk (4 fp32 or 8 half-width elements),
+// as a chain of IEEE fp32 fused multiply-adds in element order.  Half-width
+// elements are widened exactly first (fp16 -> fp32 folds into v_fma_mix_f32;
+// bf16 -> fp32 is a 16-bit shift or mask), so the arithmetic is plain fp32
+// with round-to-nearest-even: sign-symmetric and the same on every family.
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+__device__ __forceinline__ float lo_f16(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float hi_f16(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
 __device__ __forceinline__ float chunk_dot(TF32, uint4 a, uint4 x, float acc) {
     acc = __builtin_fmaf(f32_of(a.x), f32_of(x.x), acc);
     acc = __builtin_fmaf(f32_of(a.y), f32_of(x.y), acc);
@@ -48,19 +58,45 @@ __device__ __forceinline__ float chunk_dot(TF32, uint4 a, uint4 x, float acc) {
     acc = __builtin_fmaf(f32_of(a.w), f32_of(x.w), acc);
     return acc;
 }
-__device__ __forceinline__ float chunk_dot(TF16, uint4 a, uint4 x, float acc) {
+__device__ __forceinline__ float pair_dot(TF16, uint32_t a, uint32_t x, float acc) {
+    acc = __builtin_fmaf(lo_f16(a), lo_f16(x), acc);
+    return __builtin_fmaf(hi_f16(a), hi_f16(x), acc);
+}
+__device__ __forceinline__ float pair_dot(TBF16, uint32_t a, uint32_t x, float acc) {
+    acc = __builtin_fmaf(lo_bf16(a), lo_bf16(x), acc);
+    return __builtin_fmaf(hi_bf16(a), hi_bf16(x), acc);
+}
+template <class D>
+__device__ __forceinline__ float chunk_dot(D, uint4 a, uint4 x, float acc) {
+    acc = pair_dot(D{}, a.x, x.x, acc);
+    acc = pair_dot(D{}, a.y, x.y, acc);
+    acc = pair_dot(D{}, a.z, x.z, acc);
+    acc = pair_dot(D{}, a.w, x.w, acc);
+    return acc;
+}
+
+// The packed two-element dot products with fp32 accumulation
+// (v_dot2_f32_f16 / v_dot2_f32_bf16): one instruction per element pair, for
+// the batched kernel where every A element meets up to 16 vectors and VALU
+// issue, not memory, is the limit.  Their products are exact, but their
+// internal rounding is not IEEE round-to-nearest (measured: negating x does
+// not exactly negate the result), which the tolerance absorbs.
+__device__ __forceinline__ float chunk_dot2(TF16, uint4 a, uint4 x, float acc) {
     acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a.x), __builtin_bit_cast(f16x2, x.x), acc, false);
     acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a.y), __builtin_bit_cast(f16x2, x.y), acc, false);
     acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a.z), __builtin_bit_cast(f16x2, x.z), acc, false);
     acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a.w), __builtin_bit_cast(f16x2, x.w), acc, false);
     return acc;
 }
-__device__ __forceinline__ float chunk_dot(TBF16, uint4 a, uint4 x, float acc) {
+__device__ __forceinline__ float chunk_dot2(TBF16, uint4 a, uint4 x, float acc) {
     acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.x), __builtin_bit_cast(bf16x2, x.x), acc, false);
     acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.y), __builtin_bit_cast(bf16x2, x.y), acc, false);
     acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.z), __builtin_bit_cast(bf16x2, x.z), acc, false);
     acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w), __builtin_bit_cast(bf16x2, x.w), acc, false);
     return acc;
+}
+__device__ __forceinline__ float chunk_dot2(TF32, uint4 a, uint4 x, float acc) {
+    return chunk_dot(TF32{}, a, x, acc);
 }
 
 // Chunk = one 16-byte load (VEC) or one element.
@@ -77,6 +113,9 @@ struct Chunk<D, true> {
     __device__ __forceinline__ static float dot(type a, type x, float acc) {
         return chunk_dot(D{}, a, x, acc);
     }
+    __device__ __forceinline__ static float dot2(type a, type x, float acc) {
+        return chunk_dot2(D{}, a, x, acc);
+    }
 };
 template <class D>
 struct Chunk<D, false> {
@@ -88,6 +127,9 @@ struct Chunk<D, false> {
     __device__ __forceinline__ static type zero() { return type(0); }
     __device__ __forceinline__ static float dot(type a, type x, float acc) {
         return __builtin_fmaf(widen(D{}, a), widen(D{}, x), acc);
+    }
+    __device__ __forceinline__ static float dot2(type a, type x, float acc) {
+        return dot(a, x, acc);
     }
 };
 

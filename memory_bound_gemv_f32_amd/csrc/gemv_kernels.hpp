@@ -225,7 +225,7 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
 #pragma unroll
                 for (int r = 0; r < RB; ++r) {
                     const CT ar = ok[i] ? a[r][i] : C::zero();
-                    acc[r][j] = C::dot(ar, xv, acc[r][j]);
+                    acc[r][j] = C::dot2(ar, xv, acc[r][j]);
                 }
             }
         }

@@ -120,7 +120,8 @@ typedef enum {
     GEMV_FAMILY_ROWS_PER_WAVE = 0, /* 64/L rows per wavefront, L lanes per row */
     GEMV_FAMILY_WAVE_PER_ROW = 1,  /* one 64-lane wavefront per row */
     GEMV_FAMILY_GROUP_PER_ROW = 2, /* one workgroup per row, LDS reduction */
-    GEMV_FAMILY_BATCHED = 3        /* several rows × nvec vectors per wave */
+    GEMV_FAMILY_BATCHED = 3,       /* several rows × nvec vectors per wave */
+    GEMV_FAMILY_BATCHED_MFMA = 4   /* 16 rows × 16 vectors on the matrix cores */
 } gemv_family_t;
 
 typedef struct {

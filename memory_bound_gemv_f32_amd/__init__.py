@@ -58,11 +58,13 @@ FAMILY_ROWS_PER_WAVE = 0
 FAMILY_WAVE_PER_ROW = 1
 FAMILY_GROUP_PER_ROW = 2
 FAMILY_BATCHED = 3
+FAMILY_BATCHED_MFMA = 4
 FAMILY_NAMES = {
     FAMILY_ROWS_PER_WAVE: "rows_per_wave",
     FAMILY_WAVE_PER_ROW: "wave_per_row",
     FAMILY_GROUP_PER_ROW: "group_per_row",
     FAMILY_BATCHED: "batched",
+    FAMILY_BATCHED_MFMA: "batched_mfma",
 }
 
 
@@ -154,7 +156,9 @@ def _check_matrix(A):
     M, K = A.shape
     if K > 1 and A.stride(1) != 1:
         raise ValueError("A must have unit column stride")
-    lda = A.stride(0) if M > 1 else max(K, 1)
+    # with one row, or no columns, the row pitch is never used: pass K, the
+    # tightest value (so 16-byte alignment depends only on the pointers)
+    lda = A.stride(0) if (M > 1 and K > 0) else K
     if lda < K:
         raise ValueError("A's row stride is smaller than K")
     return M, K, lda

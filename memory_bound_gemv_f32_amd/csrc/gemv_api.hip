@@ -27,8 +27,11 @@ struct Args {
     float* Y;
     int M;
     int K;
+    int nvec;
 };
 
+// Every kernel takes (A, lda, X, bias, Y, M, K); the matrix-core kernel also
+// takes nvec (the others have it as a template parameter or do not need it).
 hipError_t launch(const void* fn, const Plan& p, hipStream_t stream, const Args& a) {
     const void* A = a.A;
     int64_t lda = a.lda;
@@ -37,7 +40,9 @@ hipError_t launch(const void* fn, const Plan& p, hipStream_t stream, const Args&
     float* Y = a.Y;
     int M = a.M;
     int K = a.K;
-    void* argv[] = {(void*)&A, (void*)&lda, (void*)&X, (void*)&bias, (void*)&Y, (void*)&M, (void*)&K};
+    int nvec = a.nvec;
+    void* argv[] = {(void*)&A, (void*)&lda, (void*)&X, (void*)&bias, (void*)&Y, (void*)&M, (void*)&K,
+                    (void*)&nvec};
     return hipLaunchKernel(fn, dim3((unsigned)p.grid), dim3((unsigned)p.block), argv, 0, stream);
 }
 
@@ -120,6 +125,11 @@ const void* kernel_for(const Plan& p, int nvec) {
     case gemvplan::BATCHED:
         if constexpr (D::bytes == 2) return batched_fn<D, VEC>(nvec);
         return nullptr;
+    case gemvplan::BATCHED_MFMA:
+        if constexpr (D::bytes == 2 && VEC)
+            return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, gemvplan::kMfmaWaves,
+                                                                   gemvplan::kMfmaChunk>;
+        return nullptr;
     default:
         return nullptr;
     }
@@ -149,7 +159,7 @@ gemv_status_t run(int dtype, int family, const void* A, int lda, const void* X,
     default: break;
     }
     if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;
-    const Args args{A, (int64_t)lda, X, bias, Y, M, K};
+    const Args args{A, (int64_t)lda, X, bias, Y, M, K, nvec};
     const hipError_t err = launch(fn, p, stream, args);
     if (err != hipSuccess) {
         g_last_launch_error = err;

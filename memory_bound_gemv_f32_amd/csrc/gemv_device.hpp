@@ -9,6 +9,12 @@ namespace gemvdev {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+// 16 bytes as four 32-bit words: a native vector type (not HIP's uint4
+// struct), so that selects between quads stay in registers
+typedef unsigned int quad __attribute__((ext_vector_type(4)));
 
 // Element types.  `storage` is what sits in memory; products are formed and
 // summed in fp32 (page "GEMM、GEMV、dtype 与算术强度", section "dtype 改变什么":
@@ -51,7 +57,7 @@ __device__ __forceinline__ float hi_f16(uint32_t w) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
-__device__ __forceinline__ float chunk_dot(TF32, uint4 a, uint4 x, float acc) {
+__device__ __forceinline__ float chunk_dot(TF32, quad a, quad x, float acc) {
     acc = __builtin_fmaf(f32_of(a.x), f32_of(x.x), acc);
     acc = __builtin_fmaf(f32_of(a.y), f32_of(x.y), acc);
     acc = __builtin_fmaf(f32_of(a.z), f32_of(x.z), acc);
@@ -67,7 +73,7 @@ __device__ __forceinline__ float pair_dot(TBF16, uint32_t a, uint32_t x, float a
     return __builtin_fmaf(hi_bf16(a), hi_bf16(x), acc);
 }
 template <class D>
-__device__ __forceinline__ float chunk_dot(D, uint4 a, uint4 x, float acc) {
+__device__ __forceinline__ float chunk_dot(D, quad a, quad x, float acc) {
     acc = pair_dot(D{}, a.x, x.x, acc);
     acc = pair_dot(D{}, a.y, x.y, acc);
     acc = pair_dot(D{}, a.z, x.z, acc);
@@ -81,22 +87,38 @@ __device__ __forceinline__ float chunk_dot(D, uint4 a, uint4 x, float acc) {
 // issue, not memory, is the limit.  Their products are exact, but their
 // internal rounding is not IEEE round-to-nearest (measured: negating x does
 // not exactly negate the result), which the tolerance absorbs.
-__device__ __forceinline__ float chunk_dot2(TF16, uint4 a, uint4 x, float acc) {
-    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a.x), __builtin_bit_cast(f16x2, x.x), acc, false);
-    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a.y), __builtin_bit_cast(f16x2, x.y), acc, false);
-    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a.z), __builtin_bit_cast(f16x2, x.z), acc, false);
-    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a.w), __builtin_bit_cast(f16x2, x.w), acc, false);
+// (Each 32-bit word is passed by value before it is reinterpreted: a bit
+// cast applied directly to an element of a native vector read element 0.)
+__device__ __forceinline__ float dot2_word(TF16, uint32_t a, uint32_t x, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, x), acc, false);
+}
+__device__ __forceinline__ float dot2_word(TBF16, uint32_t a, uint32_t x, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, x), acc,
+                                           false);
+}
+template <class D>
+__device__ __forceinline__ float chunk_dot2(D, quad a, quad x, float acc) {
+    acc = dot2_word(D{}, a.x, x.x, acc);
+    acc = dot2_word(D{}, a.y, x.y, acc);
+    acc = dot2_word(D{}, a.z, x.z, acc);
+    acc = dot2_word(D{}, a.w, x.w, acc);
     return acc;
 }
-__device__ __forceinline__ float chunk_dot2(TBF16, uint4 a, uint4 x, float acc) {
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.x), __builtin_bit_cast(bf16x2, x.x), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.y), __builtin_bit_cast(bf16x2, x.y), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.z), __builtin_bit_cast(bf16x2, x.z), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w), __builtin_bit_cast(bf16x2, x.w), acc, false);
-    return acc;
-}
-__device__ __forceinline__ float chunk_dot2(TF32, uint4 a, uint4 x, float acc) {
+__device__ __forceinline__ float chunk_dot2(TF32, quad a, quad x, float acc) {
     return chunk_dot(TF32{}, a, x, acc);
+}
+
+// One 16×16×32 matrix-core step, D = A·B + C with fp32 accumulation:
+// A is 16 rows × 32 k, B is 32 k × 16 columns.  Lane l supplies row (or
+// column) l % 16 and the 8 consecutive k of group l / 16 as one 16-byte
+// register quad; D comes back as rows 4·(l/16) .. 4·(l/16)+3 of column l % 16.
+__device__ __forceinline__ f32x4 mma_16x16x32(TF16, quad a, quad b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_16x16x32(TBF16, quad a, quad b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
 // Chunk = one 16-byte load (VEC) or one element.
@@ -104,12 +126,12 @@ template <class D, bool VEC>
 struct Chunk;
 template <class D>
 struct Chunk<D, true> {
-    using type = uint4;
+    using type = quad;
     static constexpr int elems = 16 / D::bytes;
     __device__ __forceinline__ static type load(const typename D::storage* p, int64_t c) {
-        return *reinterpret_cast<const uint4*>(p + c * elems);
+        return *reinterpret_cast<const quad*>(p + c * elems);
     }
-    __device__ __forceinline__ static type zero() { return make_uint4(0u, 0u, 0u, 0u); }
+    __device__ __forceinline__ static type zero() { return quad{0u, 0u, 0u, 0u}; }
     __device__ __forceinline__ static float dot(type a, type x, float acc) {
         return chunk_dot(D{}, a, x, acc);
     }

@@ -28,6 +28,40 @@
 
 namespace gemvdev {
 
+// One batch of the rows kernels: BATCH chunks per row tile, chunk c + i·L
+// for i < BATCH, all loads issued before any is used.  CHECK: chunks at or
+// past nfull load chunk nfull-1 instead and are replaced by zero.
+template <class C, int L, int U, int BATCH, bool CHECK, class S>
+__device__ __forceinline__ void rows_batch(const S* const (&rp)[U], const S* x, int c, int nfull,
+                                           float (&acc)[U][2]) {
+    using CT = typename C::type;
+    CT a[U][BATCH];
+    CT xv[BATCH];
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+        int cc = c + i * L;
+        if constexpr (CHECK) cc = cc < nfull ? cc : nfull - 1;
+#pragma unroll
+        for (int u = 0; u < U; ++u) a[u][i] = C::load(rp[u], cc);
+        xv[i] = C::load(x, cc);
+    }
+    // keep every load of the batch ahead of the first use: without this
+    // fence the scheduler may interleave each load with its multiply-adds
+    // and leave one load in flight at a time
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+        CT xi = xv[i];
+        if constexpr (CHECK) xi = c + i * L < nfull ? xi : C::zero();
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            CT ai = a[u][i];
+            if constexpr (CHECK) ai = c + i * L < nfull ? ai : C::zero();
+            acc[u][i & 1] = C::dot(ai, xi, acc[u][i & 1]);
+        }
+    }
+}
+
 // Rows-per-wave (L < 64) and wave-per-row (L == 64) kernel.
 // A wavefront covers R = 64/L rows per row tile and takes U consecutive row
 // tiles; lanes sub = lane % L of one row walk its chunks with stride L, BATCH
@@ -40,7 +74,6 @@ gemv_rows_kernel(const typename D::storage* __restrict__ A, int64_t lda,
                  int K) {
     using S = typename D::storage;
     using C = Chunk<D, VEC>;
-    using CT = typename C::type;
     constexpr int R = 64 / L;
     constexpr int E = C::elems;
 
@@ -67,29 +100,12 @@ gemv_rows_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     for (int u = 0; u < U; ++u) acc[u][0] = acc[u][1] = 0.f;
 
     const int nfull = K / E;  // whole chunks per row
-    for (int c0 = 0; c0 < nfull; c0 += BATCH * L) {
-        CT a[U][BATCH];
-        CT xv[BATCH];
-        bool ok[BATCH];
-#pragma unroll
-        for (int i = 0; i < BATCH; ++i) {
-            const int c = c0 + i * L + sub;
-            ok[i] = c < nfull;
-            const int cc = ok[i] ? c : nfull - 1;
-#pragma unroll
-            for (int u = 0; u < U; ++u) a[u][i] = C::load(rp[u], cc);
-            xv[i] = C::load(x, cc);
-        }
-#pragma unroll
-        for (int i = 0; i < BATCH; ++i) {
-            const CT xi = ok[i] ? xv[i] : C::zero();
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const CT ai = ok[i] ? a[u][i] : C::zero();
-                acc[u][i & 1] = C::dot(ai, xi, acc[u][i & 1]);
-            }
-        }
-    }
+    // Batches where every lane's chunks are in range need no checks; at most
+    // one final batch straddles the end of the row.
+    const int nsafe = nfull - nfull % (BATCH * L);
+    int c0 = 0;
+    for (; c0 < nsafe; c0 += BATCH * L) rows_batch<C, L, U, BATCH, false>(rp, x, c0 + sub, nfull, acc);
+    if (c0 < nfull) rows_batch<C, L, U, BATCH, true>(rp, x, c0 + sub, nfull, acc);
     if constexpr (VEC) {
         // elements past the last whole chunk (fewer than E of them)
         for (int k = nfull * E + sub; k < K; k += L) {
@@ -119,7 +135,6 @@ gemv_group_kernel(const typename D::storage* __restrict__ A, int64_t lda,
                   int K) {
     using S = typename D::storage;
     using C = Chunk<D, VEC>;
-    using CT = typename C::type;
     constexpr int L = W * 64;
     constexpr int E = C::elems;
     __shared__ float partial[W];
@@ -131,33 +146,19 @@ gemv_group_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     float b = 0.f;
     if (bias != nullptr && sub == 0) b = bias[row];
 
-    float acc[2] = {0.f, 0.f};
+    float acc[1][2] = {{0.f, 0.f}};
+    const S* const rows[1] = {rp};
     const int nfull = K / E;
-    for (int c0 = 0; c0 < nfull; c0 += BATCH * L) {
-        CT a[BATCH];
-        CT xv[BATCH];
-        bool ok[BATCH];
-#pragma unroll
-        for (int i = 0; i < BATCH; ++i) {
-            const int c = c0 + i * L + sub;
-            ok[i] = c < nfull;
-            const int cc = ok[i] ? c : nfull - 1;
-            a[i] = C::load(rp, cc);
-            xv[i] = C::load(x, cc);
-        }
-#pragma unroll
-        for (int i = 0; i < BATCH; ++i) {
-            const CT ai = ok[i] ? a[i] : C::zero();
-            const CT xi = ok[i] ? xv[i] : C::zero();
-            acc[i & 1] = C::dot(ai, xi, acc[i & 1]);
-        }
-    }
+    const int nsafe = nfull - nfull % (BATCH * L);
+    int c0 = 0;
+    for (; c0 < nsafe; c0 += BATCH * L) rows_batch<C, L, 1, BATCH, false>(rows, x, c0 + sub, nfull, acc);
+    if (c0 < nfull) rows_batch<C, L, 1, BATCH, true>(rows, x, c0 + sub, nfull, acc);
     if constexpr (VEC) {
         for (int k = nfull * E + sub; k < K; k += L)
-            acc[1] = __builtin_fmaf(widen(D{}, rp[k]), widen(D{}, x[k]), acc[1]);
+            acc[0][1] = __builtin_fmaf(widen(D{}, rp[k]), widen(D{}, x[k]), acc[0][1]);
     }
 
-    const float v = segment_sum<64>(acc[0] + acc[1]);
+    const float v = segment_sum<64>(acc[0][0] + acc[0][1]);
     if ((threadIdx.x & 63) == 0) partial[threadIdx.x >> 6] = v;
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -216,6 +217,7 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
 #pragma unroll
             for (int r = 0; r < RB; ++r) a[r][i] = C::load(rp[r], cc[i]);
         }
+        __builtin_amdgcn_sched_barrier(0);  // A loads in flight before X is fetched
 #pragma unroll
         for (int i = 0; i < BATCH; ++i) {
 #pragma unroll
@@ -250,6 +252,125 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
         for (int j = 0; j < NV; ++j) {
             const float v = segment_sum<64>(acc[r][j]);
             if (lane == 0 && m < M) Y[(int64_t)j * M + m] = v + b;
+        }
+    }
+}
+
+// Batched kernel on the matrix cores: Y = A·X (+ bias) for up to 16
+// vectors.  With 16 vectors every A element takes part in 16 multiply-adds,
+// close to the vector ALUs' limit (about 16 FLOP per byte against a ridge of
+// about 20), so the contraction runs as 16×16×32 MFMA steps instead.
+//
+// A workgroup owns 16 consecutive rows; its W wavefronts split the whole
+// 32-wide steps of K into contiguous slices and walk them in chunks of CH
+// steps.  Per chunk a wavefront
+//   1. issues the loads of its 16 rows × CH steps of A (one 16-byte MFMA
+//      operand per lane and step),
+//   2. copies the same K range of every X column into its own LDS region
+//      with coalesced loads (one 1 KiB load per column; X columns are K
+//      elements apart, so reading the operands straight from memory would
+//      send each load to 16 addresses one column pitch apart),
+//   3. runs CH MFMA steps, reading the X operands from LDS.
+// Vectors past nvec are zero operands.  After one barrier wavefront 0 adds
+// the W tiles in wavefront order, adds the bias and writes Y.  Needs 16-byte
+// aligned A, X and row pitch and K % 8 == 0.  A chunk shorter than CH steps
+// at the end of a slice, and the last, partial 32-wide step (K % 32 != 0,
+// done by the last wavefront), read their operands directly.
+template <class D, int W, int CH>
+__global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2)))
+gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
+                         const typename D::storage* __restrict__ X,
+                         const float* __restrict__ bias, float* __restrict__ Y,
+                         int M, int K, int nvec) {
+    using S = typename D::storage;
+    // per wavefront: 16 columns × CH steps × 32 elements, each column
+    // padded by 16 bytes so that 16 lanes reading 16 columns hit distinct banks
+    constexpr int kColBytes = CH * 64 + 16;
+    constexpr int kColQuads = kColBytes / 16;
+    __shared__ quad xs[W][16 * kColQuads];
+    __shared__ f32x4 partial[W][64];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int r = lane & 15;  // A row within the tile / X column of the operand
+    const int g = lane >> 4;  // 8-element group within a 32-wide step
+    const int64_t row0 = (int64_t)blockIdx.x * 16;
+    const int64_t arow = row0 + r < M ? row0 + r : (int64_t)M - 1;
+    const S* ap = A + arow * lda + 8 * g;
+    const bool xcol = r < nvec;
+
+    const int steps = K / 32;
+    const int per = (steps + W - 1) / W;
+    const int s0 = wave * per;
+    const int s1 = s0 + per < steps ? s0 + per : steps;
+    const quad zero = quad{0u, 0u, 0u, 0u};
+    quad* xw = xs[wave];
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    constexpr int kQuads = 16 * 4 * CH;  // X quads (16 bytes) per chunk
+    int c = s0;
+    for (; c + CH <= s1; c += CH) {
+        quad a[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) a[i] = *reinterpret_cast<const quad*>(ap + (int64_t)(c + i) * 32);
+        // X chunk: quad q is column q / (4·CH), elements c·32 + 8·(q % (4·CH)) .. +8;
+        // columns past nvec load column nvec-1 and are stored as zero
+        quad xv[kQuads / 64];
+#pragma unroll
+        for (int t = 0; t < kQuads / 64; ++t) {
+            const int q = t * 64 + lane;
+            const int j = q / (4 * CH) < nvec ? q / (4 * CH) : nvec - 1;
+            xv[t] = *reinterpret_cast<const quad*>(X + (int64_t)j * K + (int64_t)c * 32 + 8 * (q % (4 * CH)));
+        }
+        __builtin_amdgcn_sched_barrier(0);  // all loads of the chunk in flight first
+#pragma unroll
+        for (int t = 0; t < kQuads / 64; ++t) {
+            const int q = t * 64 + lane;
+            xw[(q / (4 * CH)) * kColQuads + q % (4 * CH)] = q / (4 * CH) < nvec ? xv[t] : zero;
+        }
+        // the same wavefront reads back what its lanes wrote
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            // operand of lane (r, g) for step i: column r, elements i·32 + 8g .. +8
+            acc = mma_16x16x32(D{}, a[i], xw[r * kColQuads + 4 * i + g], acc);
+        }
+        // the next chunk overwrites this wavefront's LDS region
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    }
+    // a short last chunk (fewer than CH steps): one step at a time, X read
+    // straight from memory (it only occurs when K/32 does not split evenly)
+    const S* xp = X + (int64_t)(xcol ? r : 0) * K + 8 * g;
+#pragma unroll 1
+    for (; c < s1; ++c) {
+        const quad a = *reinterpret_cast<const quad*>(ap + (int64_t)c * 32);
+        const quad b = *reinterpret_cast<const quad*>(xp + (int64_t)c * 32);
+        acc = mma_16x16x32(D{}, a, xcol ? b : zero, acc);
+    }
+    if (wave == W - 1 && steps * 32 < K) {
+        // last, partial step: groups wholly below K (K % 8 == 0) load, others are zero
+        const bool in = steps * 32 + 8 * g < K;
+        const quad a = in ? *reinterpret_cast<const quad*>(ap + (int64_t)steps * 32) : zero;
+        const quad b = (in && xcol) ? *reinterpret_cast<const quad*>(xp + (int64_t)steps * 32) : zero;
+        acc = mma_16x16x32(D{}, a, b, acc);
+    }
+
+    partial[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        f32x4 t = partial[0][lane];
+#pragma unroll
+        for (int w = 1; w < W; ++w) t += partial[w][lane];
+        // lane holds rows row0 + 4g .. row0 + 4g + 3 of vector r
+        if (xcol) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t m = row0 + 4 * g + i;
+                if (m < M) Y[(int64_t)r * M + m] = t[i] + (bias != nullptr ? bias[m] : 0.f);
+            }
         }
     }
 }

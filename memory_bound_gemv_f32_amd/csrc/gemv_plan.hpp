@@ -27,7 +27,14 @@
 namespace gemvplan {
 
 enum Dtype { F32 = 0, F16 = 1, BF16 = 2 };
-enum Family { AUTO = -1, ROWS_PER_WAVE = 0, WAVE_PER_ROW = 1, GROUP_PER_ROW = 2, BATCHED = 3 };
+enum Family {
+    AUTO = -1,
+    ROWS_PER_WAVE = 0,
+    WAVE_PER_ROW = 1,
+    GROUP_PER_ROW = 2,
+    BATCHED = 3,
+    BATCHED_MFMA = 4
+};
 enum Status { OK = 0, INVALID = 1 };
 
 constexpr int kWave = 64;
@@ -39,7 +46,7 @@ constexpr int kRowsPerWaveMaxLanes = 32;
 // Workgroup-per-row family: wavefronts per workgroup, and when it is chosen
 // automatically (few rows, long rows).
 constexpr int kGroupWaves = 4;
-constexpr int64_t kGroupMaxRows = 2048;
+constexpr int64_t kGroupMaxRows = 256;
 constexpr int64_t kGroupMinLoadsPerRow = 512;
 // Wave-per-row family: loads per lane kept in flight per row.
 constexpr int kWaveBatch = 8;
@@ -49,6 +56,15 @@ constexpr int kGroupBatch = 4;
 // loaded chunks fit the register budget of four wavefronts per SIMD.
 constexpr int kBatchedBatch = 1;
 constexpr int batched_rows(int nvec) { return nvec <= 2 ? 4 : (nvec <= 4 ? 2 : 1); }
+// Matrix-core batched family: 16 rows per workgroup, its wavefronts split K
+// and walk their slice in chunks of this many 32-wide steps (the A loads of a
+// chunk are in flight together; X's chunk is staged in LDS).
+constexpr int kMfmaRows = 16;
+constexpr int kMfmaWaves = 8;
+constexpr int kMfmaChunk = 16;
+constexpr int mfma_lds_bytes() {
+    return kMfmaWaves * 16 * (kMfmaChunk * 64 + 16) + kMfmaWaves * kWave * 16;
+}
 // Threads per workgroup of the rows/wave and batched families.
 constexpr int kBlock = 256;
 // Below this many workgroups the rows-per-wave family stops giving each
@@ -117,10 +133,14 @@ inline int make_plan(int dtype, int M, int K, int lda, int nvec, uintptr_t A,
     const int64_t loads = ceil_div(K, p.chunk_elems);
     const int64_t full = K / p.chunk_elems;
 
+    // the matrix-core kernel reads every 8-element group of a row with one
+    // aligned 16-byte load
+    const bool mfma_ok = dtype != F32 && p.vector_loads && K % 8 == 0;
+
     int fam = family;
     if (fam == AUTO) {
         if (nvec > 1)
-            fam = BATCHED;
+            fam = mfma_ok ? BATCHED_MFMA : BATCHED;
         else if (loads <= kRowsPerWaveMaxLanes)
             fam = ROWS_PER_WAVE;
         else if (M <= kGroupMaxRows && loads >= kGroupMinLoadsPerRow)
@@ -128,8 +148,10 @@ inline int make_plan(int dtype, int M, int K, int lda, int nvec, uintptr_t A,
         else
             fam = WAVE_PER_ROW;
     }
-    if (fam != BATCHED && nvec != 1) return INVALID;
-    if (fam == BATCHED && dtype == F32) return INVALID;
+    const bool batched = fam == BATCHED || fam == BATCHED_MFMA;
+    if (!batched && nvec != 1) return INVALID;
+    if (batched && dtype == F32) return INVALID;
+    if (fam == BATCHED_MFMA && !mfma_ok) return INVALID;
 
     p.family = fam;
     switch (fam) {
@@ -174,16 +196,30 @@ inline int make_plan(int dtype, int M, int K, int lda, int nvec, uintptr_t A,
         p.batch = kBatchedBatch;
         p.row_tiles = 1;
         break;
+    case BATCHED_MFMA:
+        // each wavefront: 4 lanes per row and step, 16 rows; rows span the group
+        p.lanes_per_row = 4 * kMfmaWaves;
+        p.rows_per_wave = kMfmaRows;
+        p.waves_per_group = kMfmaWaves;
+        p.batch = kMfmaChunk;
+        p.row_tiles = 1;
+        p.lds_bytes = mfma_lds_bytes();
+        break;
     default:
         return INVALID;
     }
     p.block = p.waves_per_group * kWave;
     if (fam == GROUP_PER_ROW)
         p.rows_per_group = 1;
+    else if (fam == BATCHED_MFMA)
+        p.rows_per_group = kMfmaRows;
     else
         p.rows_per_group = p.rows_per_wave * p.row_tiles * p.waves_per_group;
     p.grid = ceil_div(M, p.rows_per_group);
-    p.passes = (int)ceil_div(full, (int64_t)p.lanes_per_row);
+    if (fam == BATCHED_MFMA)  // 32-wide steps per wavefront
+        p.passes = (int)ceil_div(K / 32, (int64_t)kMfmaWaves);
+    else
+        p.passes = (int)ceil_div(full, (int64_t)p.lanes_per_row);
     if (p.grid > 0x7fffffff) return INVALID;
     *out = p;
     return OK;

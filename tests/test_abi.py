@@ -142,9 +142,11 @@ def test_mid_rows_get_a_wavefront_each():
 
 
 def test_few_long_rows_get_a_workgroup_each():
-    q = p("bf16", 1024, 4096)
+    q = p("bf16", 256, 4096)
     assert q["family"] == lg.FAMILY_GROUP_PER_ROW
-    assert q["grid"] == 1024 and q["block"] == 256 and q["rows_per_group"] == 1
+    assert q["grid"] == 256 and q["block"] == 256 and q["rows_per_group"] == 1
+    # 1024 rows already give every CU several wavefronts
+    assert p("bf16", 1024, 4096)["family"] == lg.FAMILY_WAVE_PER_ROW
 
 
 def test_worked_example_mapping():
@@ -173,7 +175,17 @@ def test_misaligned_falls_back_to_element_loads(kw):
 
 def test_batched_plans():
     q = p("f16", 4096, 4096, nvec=16)
-    assert q["family"] == lg.FAMILY_BATCHED
+    assert q["family"] == lg.FAMILY_BATCHED_MFMA
+    assert (q["rows_per_group"], q["waves_per_group"], q["grid"]) == (16, 8, 256)
+    assert q["passes"] == 4096 // 32 // 8
+    # the matrix cores need every 8-element group of a row aligned
+    assert p("bf16", 4096, 4104, nvec=3)["family"] == lg.FAMILY_BATCHED_MFMA
+    assert p("bf16", 4096, 4100, lda=4104, nvec=3)["family"] == lg.FAMILY_BATCHED
+    assert p("bf16", 4096, 4096, nvec=3, A=ALIGNED + 2)["family"] == lg.FAMILY_BATCHED
+    with pytest.raises(lg.GemvError):
+        p("bf16", 4096, 4100, lda=4104, nvec=3, family=lg.FAMILY_BATCHED_MFMA)
+    with pytest.raises(lg.GemvError):
+        p("f32", 4096, 4096, nvec=1, family=lg.FAMILY_BATCHED_MFMA)
     q1 = p("f16", 4096, 4096, nvec=1)
     assert q1["family"] != lg.FAMILY_BATCHED   # nvec 1 is plain GEMV
     assert p("f16", 4096, 4095, nvec=4)["vector_loads"] == 0  # X columns misaligned

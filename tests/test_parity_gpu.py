@@ -30,7 +30,7 @@ def families_for(case: gi.Case, misalign: int = 0):
     out = []
     fams = SINGLE_FAMILIES if case.nvec == 1 else [lg.FAMILY_AUTO]
     if case.dtype != "f32":
-        fams = fams + [lg.FAMILY_BATCHED]
+        fams = fams + [lg.FAMILY_BATCHED, lg.FAMILY_BATCHED_MFMA]
     addr = (1 << 20) + misalign * gi.ELEMENT_BYTES[case.dtype]
     for fam in fams:
         try:
@@ -121,6 +121,11 @@ def test_integer_batched(dtype, nvec):
         assert_bit_exact(y, ref, f"{dtype} nvec={nvec} {M}x{K}")
         y1 = run_gpu(case, lg.FAMILY_BATCHED, batched=True, misalign=1)
         assert_bit_exact(y1, ref, f"{dtype} nvec={nvec} {M}x{K} element loads")
+        y2 = run_gpu(case, lg.FAMILY_BATCHED, batched=True)
+        assert_bit_exact(y2, ref, f"{dtype} nvec={nvec} {M}x{K} vector ALU")
+        if K % 8 == 0 and lda % 8 == 0:
+            y3 = run_gpu(case, lg.FAMILY_BATCHED_MFMA, batched=True)
+            assert_bit_exact(y3, ref, f"{dtype} nvec={nvec} {M}x{K} matrix cores")
 
 
 def test_empty_reduction_gives_bias():
@@ -186,8 +191,9 @@ def test_random_batched(dtype, nvec):
         case = gi.make_random(dtype, M, K, seed=nvec + K, nvec=nvec, bias=True,
                               dist="normal", scale=1 / np.sqrt(K))
         ref, absdot = run_oracle(case)
-        y = run_gpu(case, lg.FAMILY_AUTO, batched=True)
-        assert_within_bound(y, ref, absdot, f"{dtype} nvec={nvec} {M}x{K}")
+        for fam in (lg.FAMILY_AUTO, lg.FAMILY_BATCHED, lg.FAMILY_BATCHED_MFMA):
+            y = run_gpu(case, fam, batched=True)
+            assert_within_bound(y, ref, absdot, f"{dtype} nvec={nvec} {M}x{K} family {fam}")
 
 
 # ---------------------------------------------------------------------------

@@ -120,8 +120,13 @@ const void* kernel_for(const Plan& p, int nvec) {
     case gemvplan::WAVE_PER_ROW:
         return rows_fn<D, VEC>(p.lanes_per_row, p.row_tiles);
     case gemvplan::GROUP_PER_ROW:
-        return (const void*)&gemvdev::gemv_group_kernel<D, gemvplan::kGroupWaves,
-                                                        gemvplan::kGroupBatch, VEC>;
+        switch (p.batch) {
+        case 1: return (const void*)&gemvdev::gemv_group_kernel<D, gemvplan::kGroupWaves, 1, VEC>;
+        case 2: return (const void*)&gemvdev::gemv_group_kernel<D, gemvplan::kGroupWaves, 2, VEC>;
+        case 4: return (const void*)&gemvdev::gemv_group_kernel<D, gemvplan::kGroupWaves, 4, VEC>;
+        case 8: return (const void*)&gemvdev::gemv_group_kernel<D, gemvplan::kGroupWaves, 8, VEC>;
+        default: return nullptr;
+        }
     case gemvplan::BATCHED:
         if constexpr (D::bytes == 2) return batched_fn<D, VEC>(nvec);
         return nullptr;

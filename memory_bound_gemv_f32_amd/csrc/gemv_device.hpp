@@ -124,12 +124,18 @@ __device__ __forceinline__ f32x4 mma_16x16x32(TBF16, quad a, quad b, f32x4 c) {
 // Chunk = one 16-byte load (VEC) or one element.
 template <class D, bool VEC>
 struct Chunk;
+// `load` is for data that is re-read (x, X); `stream` is for A, which every
+// call reads exactly once: a nontemporal load, so A streams past the caches
+// instead of evicting the re-read vector.
 template <class D>
 struct Chunk<D, true> {
     using type = quad;
     static constexpr int elems = 16 / D::bytes;
     __device__ __forceinline__ static type load(const typename D::storage* p, int64_t c) {
         return *reinterpret_cast<const quad*>(p + c * elems);
+    }
+    __device__ __forceinline__ static type stream(const typename D::storage* p, int64_t c) {
+        return __builtin_nontemporal_load(reinterpret_cast<const quad*>(p + c * elems));
     }
     __device__ __forceinline__ static type zero() { return quad{0u, 0u, 0u, 0u}; }
     __device__ __forceinline__ static float dot(type a, type x, float acc) {
@@ -145,6 +151,9 @@ struct Chunk<D, false> {
     static constexpr int elems = 1;
     __device__ __forceinline__ static type load(const typename D::storage* p, int64_t c) {
         return p[c];
+    }
+    __device__ __forceinline__ static type stream(const typename D::storage* p, int64_t c) {
+        return __builtin_nontemporal_load(p + c);
     }
     __device__ __forceinline__ static type zero() { return type(0); }
     __device__ __forceinline__ static float dot(type a, type x, float acc) {

@@ -8,7 +8,7 @@
 // one writer.
 //
 // Shared structure:
-//   * A is streamed once with coalesced loads: the lanes that share a row
+//   * A is streamed once with coalesced, nontemporal loads: the lanes that share a row
 //     read consecutive 16-byte chunks, so one wavefront load instruction
 //     covers 1 KiB of A (page "SGEMV CUDA代码学习", section "Kernel 2: k128 +
 //     Vec4", carried to 64 lanes);
@@ -42,7 +42,7 @@ __device__ __forceinline__ void rows_batch(const S* const (&rp)[U], const S* x, 
         int cc = c + i * L;
         if constexpr (CHECK) cc = cc < nfull ? cc : nfull - 1;
 #pragma unroll
-        for (int u = 0; u < U; ++u) a[u][i] = C::load(rp[u], cc);
+        for (int u = 0; u < U; ++u) a[u][i] = C::stream(rp[u], cc);
         xv[i] = C::load(x, cc);
     }
     // keep every load of the batch ahead of the first use: without this
@@ -83,16 +83,24 @@ gemv_rows_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     const int slot = lane / L;
     const int64_t tile0 = ((int64_t)blockIdx.x * (blockDim.x >> 6) + wave) * U;
 
-    int64_t row[U];
     const S* rp[U];
-    float b[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        row[u] = (tile0 + u) * R + slot;
-        const int64_t safe = row[u] < M ? row[u] : (int64_t)M - 1;
-        rp[u] = A + safe * lda;
-        b[u] = 0.f;
-        if (bias != nullptr && sub == 0 && row[u] < M) b[u] = bias[row[u]];
+        const int64_t row = (tile0 + u) * R + slot;
+        rp[u] = A + (row < M ? row : (int64_t)M - 1) * lda;
+    }
+    // Epilogue rows: the wavefront's U·R rows are consecutive, and lane
+    // (slot, sub) adds the bias to and stores the rows of tiles u = sub,
+    // sub + L, ... so that one store covers up to 64 consecutive rows.  The
+    // bias loads are issued now, ahead of the A stream.
+    constexpr int kOut = U < L ? 1 : U / L;  // rows stored per lane
+    float bv[kOut];
+#pragma unroll
+    for (int o = 0; o < kOut; ++o) {
+        const int u = sub + o * L;
+        const int64_t row = (tile0 + u) * R + slot;
+        bv[o] = 0.f;
+        if (bias != nullptr && u < U && row < M) bv[o] = bias[row];
     }
 
     float acc[U][2];
@@ -115,10 +123,18 @@ gemv_rows_kernel(const typename D::storage* __restrict__ A, int64_t lda,
         }
     }
 
+    float v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const float v = segment_sum<L>(acc[u][0] + acc[u][1]);
-        if (sub == 0 && row[u] < M) y[row[u]] = v + b[u];
+    for (int u = 0; u < U; ++u) v[u] = segment_sum<L>(acc[u][0] + acc[u][1]);
+#pragma unroll
+    for (int o = 0; o < kOut; ++o) {
+        const int u = sub + o * L;
+        // every lane of a segment holds the segment's sums: pick tile u
+        float out = v[0];
+#pragma unroll
+        for (int t = 1; t < U; ++t) out = (u == t) ? v[t] : out;
+        const int64_t row = (tile0 + u) * R + slot;
+        if (u < U && row < M) y[row] = out + bv[o];
     }
 }
 
@@ -215,7 +231,7 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
             ok[i] = c < nfull;
             cc[i] = ok[i] ? c : nfull - 1;
 #pragma unroll
-            for (int r = 0; r < RB; ++r) a[r][i] = C::load(rp[r], cc[i]);
+            for (int r = 0; r < RB; ++r) a[r][i] = C::stream(rp[r], cc[i]);
         }
         __builtin_amdgcn_sched_barrier(0);  // A loads in flight before X is fetched
 #pragma unroll
@@ -312,7 +328,8 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     for (; c + CH <= s1; c += CH) {
         quad a[CH];
 #pragma unroll
-        for (int i = 0; i < CH; ++i) a[i] = *reinterpret_cast<const quad*>(ap + (int64_t)(c + i) * 32);
+        for (int i = 0; i < CH; ++i)
+            a[i] = __builtin_nontemporal_load(reinterpret_cast<const quad*>(ap + (int64_t)(c + i) * 32));
         // X chunk: quad q is column q / (4·CH), elements c·32 + 8·(q % (4·CH)) .. +8;
         // columns past nvec load column nvec-1 and are stored as zero
         quad xv[kQuads / 64];

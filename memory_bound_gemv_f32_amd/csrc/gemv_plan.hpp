@@ -44,13 +44,17 @@ constexpr int kMaxVectors = 16;
 // Rows-per-wave family: lanes per row is a power of two up to this.
 constexpr int kRowsPerWaveMaxLanes = 32;
 // Workgroup-per-row family: wavefronts per workgroup, and when it is chosen
-// automatically (few rows, long rows).
+// automatically: few rows (fewer than there are CUs' worth of wavefronts),
+// long rows (a wavefront per row would walk them in several dependent
+// batches), or very many rows.
 constexpr int kGroupWaves = 4;
 constexpr int64_t kGroupMaxRows = 256;
-constexpr int64_t kGroupMinLoadsPerRow = 512;
+constexpr int64_t kGroupLongRowLoads = 1024;
+constexpr int64_t kGroupManyRows = 8192;
+constexpr int64_t kGroupManyRowsMinLoads = 512;
 // Wave-per-row family: loads per lane kept in flight per row.
 constexpr int kWaveBatch = 8;
-constexpr int kGroupBatch = 4;
+constexpr int kGroupBatch = 8;
 // Batched family: loads in flight per row, and rows per wavefront, fewer as
 // the number of vectors grows so that rows × vectors accumulators plus the
 // loaded chunks fit the register budget of four wavefronts per SIMD.
@@ -143,7 +147,8 @@ inline int make_plan(int dtype, int M, int K, int lda, int nvec, uintptr_t A,
             fam = mfma_ok ? BATCHED_MFMA : BATCHED;
         else if (loads <= kRowsPerWaveMaxLanes)
             fam = ROWS_PER_WAVE;
-        else if (M <= kGroupMaxRows && loads >= kGroupMinLoadsPerRow)
+        else if (M <= kGroupMaxRows || loads >= kGroupLongRowLoads ||
+                 (M >= kGroupManyRows && loads >= kGroupManyRowsMinLoads))
             fam = GROUP_PER_ROW;
         else
             fam = WAVE_PER_ROW;
@@ -181,14 +186,17 @@ inline int make_plan(int dtype, int M, int K, int lda, int nvec, uintptr_t A,
         p.batch = kWaveBatch;
         p.row_tiles = 1;
         break;
-    case GROUP_PER_ROW:
+    case GROUP_PER_ROW: {
         p.lanes_per_row = kWave * kGroupWaves;
         p.rows_per_wave = 0;  // a row spans the whole workgroup
         p.waves_per_group = kGroupWaves;
-        p.batch = kGroupBatch;
+        // as many loads per lane in flight as the row gives each lane, up to 8
+        const int64_t per_lane = ceil_div(full, (int64_t)p.lanes_per_row);
+        p.batch = per_lane >= kGroupBatch ? kGroupBatch : next_pow2(per_lane < 1 ? 1 : per_lane);
         p.row_tiles = 1;
         p.lds_bytes = (int)(kGroupWaves * sizeof(float));
         break;
+    }
     case BATCHED:
         p.lanes_per_row = kWave;
         p.rows_per_wave = batched_rows(nvec);

@@ -136,9 +136,18 @@ def test_mid_rows_get_a_wavefront_each():
     q = p("bf16", 4096, 4096)
     assert q["family"] == lg.FAMILY_WAVE_PER_ROW
     assert q["lanes_per_row"] == 64 and q["rows_per_group"] == 4
-    assert q["grid"] == 1024 and q["passes"] == 8
-    q = p("bf16", 4096, 14336)
-    assert q["family"] == lg.FAMILY_WAVE_PER_ROW and q["passes"] == 28
+    assert q["grid"] == 1024 and q["passes"] == 8 and q["batch"] == 8
+    assert p("bf16", 1024, 4096)["family"] == lg.FAMILY_WAVE_PER_ROW
+
+
+def test_long_or_many_rows_get_a_workgroup_each():
+    q = p("bf16", 4096, 14336)  # 1792 loads per row
+    assert q["family"] == lg.FAMILY_GROUP_PER_ROW
+    assert q["lanes_per_row"] == 256 and q["batch"] == 8 and q["passes"] == 7
+    q = p("bf16", 14336, 4096)  # many rows of 512 loads: 2 per lane
+    assert q["family"] == lg.FAMILY_GROUP_PER_ROW and q["batch"] == 2
+    q = p("f32", 100, 1000)     # few rows: 250 loads, one per lane
+    assert q["family"] == lg.FAMILY_GROUP_PER_ROW and q["batch"] == 1
 
 
 def test_few_long_rows_get_a_workgroup_each():

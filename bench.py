@@ -63,7 +63,87 @@ def parse():
                     help="wall-clock budget of the CPU oracle timing (0 = skip)")
     ap.add_argument("--kernel-only", action="store_true",
                     help="only run the timed graph loop of --workload (for profilers)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="CPU only: read the counter CSVs of the two --counters runs and write "
+                         "the traffic summary used for roofline.traffic")
+    ap.add_argument("--counters", action="store_true",
+                    help="for rocprofv3 --pmc runs: a few eager launches of --workload over the "
+                         "rotated buffers, then a plain device copy of COPY_BYTES for scaling")
     return ap.parse_args()
+
+
+COPY_BYTES = 256 << 20   # the calibration copy: reads and writes this many bytes
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    """Hash of every HIP / host source of the library: counter figures taken
+    from one version of the kernels are not reported for another."""
+    import hashlib
+    csrc = os.path.join(ROOT, "memory_bound_gemv_f32_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"traffic_{workload}.json")
+
+
+def summarize_counters(fetch_dir, write_dir, workload):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the GEMV kernel, scaled by
+    the ratio of the calibration copy's known bytes to what the same counter
+    read for it (the copy is the largest copy dispatch of the run)."""
+    import csv
+    out = {"workload": workload, "source_hash": kernel_source_hash(), "copy_bytes": COPY_BYTES}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = list(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))))
+        rows = [r for r in rows if r["Counter_Name"] == counter]
+        gemv = [float(r["Counter_Value"]) for r in rows if "gemvdev::" in r["Kernel_Name"]]
+        copy = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
+        scale = (COPY_BYTES / 1024) / copy
+        key = counter.split("_")[0].lower()
+        out[f"{key}_kib_per_dispatch"] = sum(gemv) / len(gemv)
+        out[f"{key}_dispatches"] = len(gemv)
+        out[f"copy_{key}_kib"] = copy
+        out[f"{key}_scale"] = scale
+        out[f"{key}_bytes_per_launch"] = sum(gemv) / len(gemv) * 1024 * scale
+    out["traffic_bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
+    return out
+
+
+def load_traffic(workload: str):
+    """The stored counter traffic for this workload, or None if there is none
+    or it was measured on other kernel sources."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t
+
+
+def counters_run(case, rot, lg, torch):
+    """Eager launches (one dispatch each) for per-dispatch counters, then a
+    plain copy kernel of known size whose counter readings give the scale."""
+    fns = rot.callers(lg, torch.cuda.current_stream().cuda_stream)
+    for i in range(2 * rot.R):
+        call(fns[i % len(fns)])
+    torch.cuda.synchronize()
+    n = COPY_BYTES // 4
+    src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    # evict src from the caches with an unrelated fill of > 2x the Infinity Cache
+    junk = torch.empty(3 * INFINITY_CACHE_BYTES // 4, dtype=torch.float32, device="cuda").fill_(2.0)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del junk
+    log(f"counters: {2 * rot.R} launches of the workload, then one {COPY_BYTES} B device copy")
 
 
 class Rotation:
@@ -245,6 +325,14 @@ def cpu_baseline(case, seconds):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        t = summarize_counters(*args.summarize_counters, args.workload)
+        os.makedirs(PROFILES, exist_ok=True)
+        with open(traffic_file(args.workload), "w") as f:
+            json.dump(t, f, indent=1)
+            f.write("\n")
+        print(json.dumps(t, indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: every box in this setup has a single MI355X, "
               f"so --gpus {args.gpus} is not supported (the row-sharded multi-GPU layout is "
@@ -272,6 +360,9 @@ def main():
     if args.kernel_only:
         ms = loop.time(args.warmup)
         log(f"kernel-only: {args.steps} launches, {1e3 * ms / args.steps:.3f} us per launch")
+        return
+    if args.counters:
+        counters_run(case, rot, lg, torch)
         return
 
     ok, worst = parity_check(case, rot, torch)
@@ -302,6 +393,16 @@ def main():
                    rot.A[0].data_ptr(), rot.X[0].data_ptr())
     del loop, rot
     torch.cuda.empty_cache()
+
+    t = load_traffic(args.workload)
+    if t is None:
+        traffic_bytes = None
+        traffic_note = "no counter figures for the current kernel sources"
+    else:
+        traffic_bytes = round(t["traffic_bytes_per_launch"])
+        traffic_note = (f"HBM-side bytes per launch from rocprofv3 FETCH_SIZE x {t['fetch_scale']:.3f} "
+                        f"+ WRITE_SIZE x {t['write_scale']:.3f} (scales from a {COPY_BYTES} B copy); "
+                        f"{traffic_bytes / nbytes:.4f} x the algorithmic bytes")
 
     shapes = {}
     names = [] if args.shapes == "none" else (
@@ -351,7 +452,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic_bytes,
+            "traffic_note": traffic_note,
             "kernel_us_mean": round(k_mean, 3),
             "bytes_per_launch": nbytes,
         },

@@ -32,6 +32,9 @@ HIPCC_FLAGS = [
     "-Wall",
     # no packed fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # kernel arguments arrive preloaded in SGPRs (gfx950), so a kernel's
+    # first loads do not wait on scalar loads of its argument block
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 

@@ -145,6 +145,9 @@ const void* kernel_for(const Plan& p, int nvec) {
     return p.vector_loads ? kernel_for<D, true>(p, nvec) : kernel_for<D, false>(p, nvec);
 }
 
+static_assert(gemvplan::kBlock == gemvdev::kRowsWaves * 64,
+              "the planner's workgroup size is the one the rows kernels are compiled for");
+
 gemv_status_t run(int dtype, int family, const void* A, int lda, const void* X,
                   const float* bias, float* Y, int M, int K, int nvec,
                   hipStream_t stream) {

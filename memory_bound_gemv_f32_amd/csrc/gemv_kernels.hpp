@@ -28,6 +28,12 @@
 
 namespace gemvdev {
 
+// Wavefronts per workgroup of the rows and vector-ALU batched kernels: a
+// compile-time constant rather than the launch's block size, so that with
+// the kernel arguments preloaded into SGPRs nothing waits on a scalar load
+// before the first load of A is issued.
+constexpr int kRowsWaves = 4;
+
 // One batch of the rows kernels: BATCH chunks per row tile, chunk c + i·L
 // for i < BATCH, all loads issued before any is used.  CHECK: chunks at or
 // past nfull load chunk nfull-1 instead and are replaced by zero.
@@ -67,7 +73,7 @@ __device__ __forceinline__ void rows_batch(const S* const (&rp)[U], const S* x, 
 // tiles; lanes sub = lane % L of one row walk its chunks with stride L, BATCH
 // chunks in flight per row tile.
 template <class D, int L, int U, int BATCH, bool VEC>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ void __launch_bounds__(kRowsWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
 gemv_rows_kernel(const typename D::storage* __restrict__ A, int64_t lda,
                  const typename D::storage* __restrict__ x,
                  const float* __restrict__ bias, float* __restrict__ y, int M,
@@ -81,7 +87,7 @@ gemv_rows_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     const int wave = threadIdx.x >> 6;
     const int sub = lane & (L - 1);
     const int slot = lane / L;
-    const int64_t tile0 = ((int64_t)blockIdx.x * (blockDim.x >> 6) + wave) * U;
+    const int64_t tile0 = ((int64_t)blockIdx.x * kRowsWaves + wave) * U;
 
     const S* rp[U];
 #pragma unroll
@@ -192,7 +198,7 @@ gemv_group_kernel(const typename D::storage* __restrict__ A, int64_t lda,
 // caches).  RB·NV fp32 accumulators per lane, one 64-lane reduction each, and
 // lane 0 writes the RB·NV outputs.
 template <class D, int NV, int RB, int BATCH, bool VEC>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ void __launch_bounds__(kRowsWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
 gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
                     const typename D::storage* __restrict__ X,
                     const float* __restrict__ bias, float* __restrict__ Y,
@@ -204,7 +210,7 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t row0 = ((int64_t)blockIdx.x * (blockDim.x >> 6) + wave) * RB;
+    const int64_t row0 = ((int64_t)blockIdx.x * kRowsWaves + wave) * RB;
 
     const S* rp[RB];
 #pragma unroll

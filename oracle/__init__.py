@@ -74,6 +74,11 @@ class Oracle:
                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                        ctypes.c_void_p, ctypes.c_void_p]
         self._gemv = fn
+        g = self._lib.oracle_gated_silu
+        g.restype = ctypes.c_int
+        g.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                      ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 5
+        self._gated = g
         self._lib.oracle_num_threads.restype = ctypes.c_int
 
     def num_threads(self) -> int:
@@ -117,6 +122,30 @@ class Oracle:
         return Y, ABS
 
 
+    def gated_silu(self, dtype: str, Ag: np.ndarray, Au: np.ndarray, X: np.ndarray,
+                   M: int, K: int, lda: int | None = None):
+        """h = silu(Ag·x) * (Au·x), with silu(g) = g / (1 + e^-g): the gated
+        FFN projection pair.  Returns (H, G, U, ABS_G, ABS_U), each float64
+        of shape (M,): G and U are the two products, ABS_* their sums of
+        |A·x| (the scale of the GEMV tolerance)."""
+        lda = K if lda is None else lda
+        want = np.float32 if dtype == "f32" else np.uint16
+        Ag = np.ascontiguousarray(Ag, dtype=want).reshape(-1)
+        Au = np.ascontiguousarray(Au, dtype=want).reshape(-1)
+        X = np.ascontiguousarray(X, dtype=want).reshape(-1)
+        if M > 0 and K > 0 and (Ag.size < (M - 1) * lda + K or Au.size < (M - 1) * lda + K
+                                or X.size < K):
+            raise ValueError("an operand is smaller than its shape implies")
+        out = [np.empty(max(M, 0), dtype=np.float64) for _ in range(5)]
+        rc = self._gated(DTYPE_CODES[dtype], Ag.ctypes.data if Ag.size else None,
+                         Au.ctypes.data if Au.size else None, lda,
+                         X.ctypes.data if X.size else None, M, K,
+                         *[o.ctypes.data for o in out])
+        if rc != 0:
+            raise ValueError(f"oracle_gated_silu rejected the arguments (rc={rc})")
+        return tuple(out)
+
+
 _default: Oracle | None = None
 
 
@@ -130,3 +159,7 @@ def default() -> Oracle:
 
 def gemv(*args, **kwargs):
     return default().gemv(*args, **kwargs)
+
+
+def gated_silu(*args, **kwargs):
+    return default().gated_silu(*args, **kwargs)

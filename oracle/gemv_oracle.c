@@ -20,6 +20,12 @@
  *   - reduced-precision inputs are accumulated in a wider type and checked
  *     against a higher-precision recomputation: page "GEMM、GEMV、dtype 与算术
  *     强度", sections "dtype 改变什么" and "可运行 CUDA 实验".
+ *   - the gated pair h = silu(A_gate·x) ⊙ (A_up·x): the FFN of the lqnn.cn
+ *     NPU MatMul essay, sections 1.1 (an up-projection, an activation, a
+ *     down-projection) and 4.2 / 5.1 (fusing the FFN's MatMuls with the
+ *     activation).  The essay names no activation; SiLU,
+ *     silu(g) = g / (1 + e^(-g)), is the gated one of the decode shapes here
+ *     (gate and up projections of equal shape).
  *
  * The oracle is that definition written out: every stored element is decoded
  * exactly to double, products and the running sum are taken in double, in
@@ -122,6 +128,21 @@ int oracle_gemv(int dtype, const void *A, int64_t lda, const void *X,
             Y[j * M + m] = sum;
             ABS[j * M + m] = abs_sum;
         }
+    }
+    return 0;
+}
+
+/* h[m] = silu(g[m]) * u[m] with g = A_gate·x and u = A_up·x (both M×K with
+ * row stride lda, same encoding), in double; G, U, ABS_G, ABS_U receive g, u
+ * and the sums of |A·x| of each product.  Returns 0, or -1 for bad arguments. */
+int oracle_gated_silu(int dtype, const void *Ag, const void *Au, int64_t lda,
+                      const void *X, int64_t M, int64_t K, double *H, double *G,
+                      double *U, double *ABS_G, double *ABS_U) {
+    if (oracle_gemv(dtype, Ag, lda, X, K, NULL, M, K, 1, G, ABS_G) != 0) return -1;
+    if (oracle_gemv(dtype, Au, lda, X, K, NULL, M, K, 1, U, ABS_U) != 0) return -1;
+    for (int64_t m = 0; m < M; ++m) {
+        const double g = G[m];
+        H[m] = g / (1.0 + exp(-g)) * U[m];
     }
     return 0;
 }

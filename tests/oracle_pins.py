@@ -252,6 +252,47 @@ def pin_worked_example_scaling(oracle):
         assert np.array_equal(Y2, 2.0 * Y) and np.array_equal(Yn, -Y)
 
 
+def _torch_silu64(v):
+    return torch.nn.functional.silu(torch.from_numpy(np.asarray(v, dtype=np.float64))).numpy()
+
+
+def pin_gated_silu_against_torch(oracle):
+    """h = silu(A_gate·x) * (A_up·x) checked against torch's float64 SiLU
+    (a library routine) on exactly known products: with A_gate = A_up = I,
+    g = u = x, so h = silu(x)·x; with one-hot rows the products are exact
+    and reach |g| up to 64 (both saturated ends of the sigmoid)."""
+    for dtype in gi.DTYPES:
+        case = gi.make_identity(dtype, 300, seed=3)
+        x = lib_decode(dtype, case.X[0]) / 1000.0 * 9.0   # values in [-9, 9]
+        X = gi.quantise(dtype, x[None, :])
+        xq = lib_decode(dtype, X[0])
+        H, G, U, SG, SU = oracle.gated_silu(dtype, case.A, case.A, X, 300, 300)
+        want = _torch_silu64(xq) * xq
+        assert np.allclose(H, want, rtol=1e-14, atol=1e-300), dtype
+        assert np.array_equal(G, xq) and np.array_equal(U, xq)
+        oh = gi.make_one_hot(dtype, 200, 50, seed=21)
+        oh2 = gi.make_one_hot(dtype, 200, 50, seed=22)
+        X = oh.X
+        H, G, U, _, _ = oracle.gated_silu(dtype, oh.A, oh2.A, X, 200, 50)
+        xv = lib_decode(dtype, X[0])
+        g = oh.coef * xv[oh.cols]
+        u = oh2.coef * xv[oh2.cols]
+        assert np.array_equal(G, g) and np.array_equal(U, u)
+        assert np.allclose(H, _torch_silu64(g) * u, rtol=1e-14, atol=1e-300), dtype
+
+
+def pin_gated_silu_zero_gate(oracle):
+    """A zero gate gives silu(0) = 0 for every row whatever the up product;
+    a zero up product gives h = 0 whatever the gate."""
+    for dtype in gi.DTYPES:
+        case = gi.make_random(dtype, 33, 70, seed=8, dist="normal")
+        zero = gi.quantise(dtype, np.zeros((33, 70)))
+        H, G, U, _, _ = oracle.gated_silu(dtype, zero, case.A, case.X, 33, 70)
+        assert np.all(H == 0) and np.all(G == 0) and np.any(U != 0)
+        H, G, U, _, _ = oracle.gated_silu(dtype, case.A, zero, case.X, 33, 70)
+        assert np.all(H == 0) and np.any(G != 0)
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_identity,
@@ -263,6 +304,8 @@ ALL_PINS = [
     pin_batched_columns,
     pin_rejects_bad_arguments,
     pin_worked_example_scaling,
+    pin_gated_silu_against_torch,
+    pin_gated_silu_zero_gate,
 ]
 
 

@@ -55,6 +55,10 @@ MUTANTS = [
     ("f16_bf16_swapped", r"dtype == ORACLE_F16 \?", "dtype == ORACLE_BF16 ?"),
     ("f32_stride", r"4 \* i", "2 * i"),
     ("accepts_lda_below_K", r"lda < K \|\| ", ""),
+    ("silu_wrong_sign", r"exp\(-g\)", "exp(g)"),
+    ("silu_no_up", r"\)\) \* U\[m\];", "));"),
+    ("silu_as_sigmoid", r"H\[m\] = g / ", "H[m] = 1.0 / "),
+    ("gated_swapped", r"oracle_gemv\(dtype, Au,", "oracle_gemv(dtype, Ag,"),
 ]
 
 

@@ -270,3 +270,37 @@ def make_one_hot(dtype: str, M: int, K: int, *, seed: int, nvec: int = 1,
     case.cols = cols          # the column of each row's non-zero entry
     case.coef = coef          # and its value
     return case
+
+
+# ---------------------------------------------------------------------------
+# fused decode workloads: the sweep's matrices, one shared x
+# ---------------------------------------------------------------------------
+
+def make_fused_qkv() -> list[Case]:
+    """The q, k and v projections of the decode-layer sweep as one problem:
+    their matrices (seeds 640..642) and the q workload's x for all three."""
+    parts = [make_workload(f"sweep_{n}") for n in ("q", "k", "v")]
+    for p in parts[1:]:
+        p.X = parts[0].X
+    return parts
+
+
+def make_fused_gate_up() -> tuple[Case, Case]:
+    """The gate and up projections of the sweep (seeds 644, 645), sharing the
+    gate workload's x."""
+    gate, up = make_workload("sweep_gate"), make_workload("sweep_up")
+    up.X = gate.X
+    return gate, up
+
+
+def fused_qkv_bytes() -> int:
+    """A of q, k, v once, x once, y of all three once."""
+    M = sum(SWEEP_SHAPES[n][0] for n in ("q", "k", "v"))
+    K = SWEEP_SHAPES["q"][1]
+    return M * K * 2 + K * 2 + 4 * M
+
+
+def fused_gate_up_bytes() -> int:
+    """Both matrices once, x once, h once (fp32)."""
+    M, K = SWEEP_SHAPES["gate"]
+    return 2 * M * K * 2 + K * 2 + 4 * M

@@ -104,6 +104,56 @@ gemv_status_t gemv_batched_bf16(const uint16_t *A, int lda, const uint16_t *X,
                                 int nvec, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Fused forms for one decode step.  Page "GEMM、GEMV、dtype 与算术强度",
+ * section "可运行 CUDA 实验", shows a 4096×4096 GEMV taking about the same
+ * time at 1 and 16 vectors: at decode sizes a launch's fixed cost is a large
+ * share of the call.  The lqnn.cn NPU MatMul essay (sections 4.2 and 5.1)
+ * fuses the QKV projections into one operator and the FFN's MatMuls with
+ * their activation; these entry points do that on one GPU launch.
+ * ------------------------------------------------------------------------ */
+
+#define GEMV_MAX_SEGMENTS 8
+
+/* One matrix of a multi-GEMV: y = A·x (+ bias), A M×K with row stride lda. */
+typedef struct {
+    const void *A;      /* device pointer, the call's element type */
+    int lda;            /* >= K */
+    int M;              /* >= 0; 0 = nothing to do for this segment */
+    const float *bias;  /* M values, or NULL */
+    float *y;           /* M values, written */
+} gemv_segment_t;
+
+/* y_i = A_i·x (+ bias_i) for every segment i < count (1..GEMV_MAX_SEGMENTS),
+ * all with the same K and the same x (e.g. the q, k and v projections of one
+ * token), in one launch.  The segment table is read on the host during the
+ * call.  Each segment is validated like a gemv_* call; results are those of
+ * separate calls up to summation order (the same tolerance).  No output may
+ * overlap another output or any input. */
+gemv_status_t gemv_multi_f32(const gemv_segment_t *segments, int count,
+                             const float *x, int K, hipStream_t stream);
+gemv_status_t gemv_multi_f16(const gemv_segment_t *segments, int count,
+                             const uint16_t *x, int K, hipStream_t stream);
+gemv_status_t gemv_multi_bf16(const gemv_segment_t *segments, int count,
+                              const uint16_t *x, int K, hipStream_t stream);
+
+/* h[m] = silu(g[m]) · u[m], g = A_gate·x, u = A_up·x, silu(g) = g/(1+e^-g):
+ * the gated FFN projection pair in one pass over both M×K matrices (same
+ * row stride lda), x read once for both.  h is fp32.  The tolerance follows
+ * from the GEMV one: with t_g, t_u the bounds of g and u,
+ * |h - h_exact| <= 1.1·t_g·(|u| + t_u) + |silu(g)|·t_u + 1e-6·|h| + 1e-6. */
+gemv_status_t gemv_gate_up_silu_f32(const float *A_gate, const float *A_up,
+                                    int lda, const float *x, float *h, int M,
+                                    int K, hipStream_t stream);
+gemv_status_t gemv_gate_up_silu_f16(const uint16_t *A_gate,
+                                    const uint16_t *A_up, int lda,
+                                    const uint16_t *x, float *h, int M, int K,
+                                    hipStream_t stream);
+gemv_status_t gemv_gate_up_silu_bf16(const uint16_t *A_gate,
+                                     const uint16_t *A_up, int lda,
+                                     const uint16_t *x, float *h, int M, int K,
+                                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Introspection and testing.  These do not change what the entry points
  * above compute; they expose how the library maps a problem onto the GPU so
  * that the mapping can be checked without a GPU and every kernel family can
@@ -121,7 +171,8 @@ typedef enum {
     GEMV_FAMILY_WAVE_PER_ROW = 1,  /* one 64-lane wavefront per row */
     GEMV_FAMILY_GROUP_PER_ROW = 2, /* one workgroup per row, LDS reduction */
     GEMV_FAMILY_BATCHED = 3,       /* several rows × nvec vectors per wave */
-    GEMV_FAMILY_BATCHED_MFMA = 4   /* 16 rows × 16 vectors on the matrix cores */
+    GEMV_FAMILY_BATCHED_MFMA = 4,  /* 16 rows × 16 vectors on the matrix cores */
+    GEMV_FAMILY_GATED_SILU = 5     /* a row of A_gate and of A_up per workgroup */
 } gemv_family_t;
 
 typedef struct {

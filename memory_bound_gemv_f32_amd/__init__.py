@@ -59,12 +59,15 @@ FAMILY_WAVE_PER_ROW = 1
 FAMILY_GROUP_PER_ROW = 2
 FAMILY_BATCHED = 3
 FAMILY_BATCHED_MFMA = 4
+FAMILY_GATED_SILU = 5
+MAX_SEGMENTS = 8
 FAMILY_NAMES = {
     FAMILY_ROWS_PER_WAVE: "rows_per_wave",
     FAMILY_WAVE_PER_ROW: "wave_per_row",
     FAMILY_GROUP_PER_ROW: "group_per_row",
     FAMILY_BATCHED: "batched",
     FAMILY_BATCHED_MFMA: "batched_mfma",
+    FAMILY_GATED_SILU: "gated_silu",
 }
 
 
@@ -76,6 +79,12 @@ class GemvPlan(ctypes.Structure):
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class GemvSegment(ctypes.Structure):
+    """gemv_segment_t: one matrix of a multi-GEMV."""
+    _fields_ = [("A", ctypes.c_void_p), ("lda", ctypes.c_int), ("M", ctypes.c_int),
+                ("bias", ctypes.c_void_p), ("y", ctypes.c_void_p)]
 
 
 _vp, _i, _st = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p
@@ -96,12 +105,20 @@ gemv_f16 = _bind("gemv_f16", [_vp, _i, _vp, _vp, _vp, _i, _i, _st])
 gemv_bf16 = _bind("gemv_bf16", [_vp, _i, _vp, _vp, _vp, _i, _i, _st])
 gemv_batched_f16 = _bind("gemv_batched_f16", [_vp, _i, _vp, _vp, _vp, _i, _i, _i, _st])
 gemv_batched_bf16 = _bind("gemv_batched_bf16", [_vp, _i, _vp, _vp, _vp, _i, _i, _i, _st])
+gemv_multi_f32 = _bind("gemv_multi_f32", [ctypes.POINTER(GemvSegment), _i, _vp, _i, _st])
+gemv_multi_f16 = _bind("gemv_multi_f16", [ctypes.POINTER(GemvSegment), _i, _vp, _i, _st])
+gemv_multi_bf16 = _bind("gemv_multi_bf16", [ctypes.POINTER(GemvSegment), _i, _vp, _i, _st])
+gemv_gate_up_silu_f32 = _bind("gemv_gate_up_silu_f32", [_vp, _vp, _i, _vp, _vp, _i, _i, _st])
+gemv_gate_up_silu_f16 = _bind("gemv_gate_up_silu_f16", [_vp, _vp, _i, _vp, _vp, _i, _i, _st])
+gemv_gate_up_silu_bf16 = _bind("gemv_gate_up_silu_bf16", [_vp, _vp, _i, _vp, _vp, _i, _i, _st])
 gemv_plan = _bind("gemv_plan", [_i, _i, _i, _i, _i, _vp, _vp, _i, ctypes.POINTER(GemvPlan)])
 gemv_run_family = _bind("gemv_run_family", [_i, _i, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _st])
 
 EXPORTED = ("gemv_status_string", "gemv_last_hip_error",
             "gemv_last_hip_error_string", "gemv_f32", "gemv_f16", "gemv_bf16",
-            "gemv_batched_f16", "gemv_batched_bf16", "gemv_plan",
+            "gemv_batched_f16", "gemv_batched_bf16", "gemv_multi_f32",
+            "gemv_multi_f16", "gemv_multi_bf16", "gemv_gate_up_silu_f32",
+            "gemv_gate_up_silu_f16", "gemv_gate_up_silu_bf16", "gemv_plan",
             "gemv_run_family")
 
 
@@ -240,3 +257,62 @@ def gemv_batched(A, X, bias=None, out=None, *, family: int = FAMILY_AUTO,
     if rc != GEMV_SUCCESS:
         raise GemvError(rc, where)
     return Y
+
+
+def segment_table(segments) -> "ctypes.Array":
+    """A gemv_segment_t array from (A_addr, lda, M, bias_addr_or_None, y_addr)
+    tuples."""
+    arr = (GemvSegment * len(segments))()
+    for i, (A, lda, M, bias, y) in enumerate(segments):
+        arr[i] = GemvSegment(A, lda, M, bias, y)
+    return arr
+
+
+def gemv_multi(As, x, biases=None, outs=None, *, stream=None):
+    """y_i = A_i @ x (+ bias_i) for up to 8 matrices with the same K and dtype,
+    in one launch; returns the list of y_i (float32)."""
+    if not 1 <= len(As) <= MAX_SEGMENTS:
+        raise ValueError(f"between 1 and {MAX_SEGMENTS} matrices")
+    dt = _dtype_name(As[0])
+    K = As[0].shape[1] if As[0].dim() == 2 else -1
+    if x.dtype != As[0].dtype or x.dim() != 1 or x.shape[0] != K or not x.is_contiguous():
+        raise ValueError("x must be a contiguous (K,) tensor of the matrices' dtype")
+    biases = list(biases) if biases is not None else [None] * len(As)
+    outs = list(outs) if outs is not None else [None] * len(As)
+    segs, ys = [], []
+    for A, b, o in zip(As, biases, outs):
+        M, Ki, lda = _check_matrix(A)
+        if A.dtype != As[0].dtype or Ki != K or A.device != x.device:
+            raise ValueError("every matrix must have x's dtype, K and device")
+        b = _check_bias(b, M, A.device)
+        y = _check_out(o, (M,), A.device)
+        ys.append(y)
+        segs.append((A.data_ptr(), lda, M, b.data_ptr() if b is not None else None, y.data_ptr()))
+    table = segment_table(segs)
+    fn = {"f32": gemv_multi_f32, "f16": gemv_multi_f16, "bf16": gemv_multi_bf16}[dt]
+    rc = fn(table, len(segs), x.data_ptr(), K, _stream_handle(stream))
+    if rc != GEMV_SUCCESS:
+        raise GemvError(rc, fn.__name__)
+    return ys
+
+
+def gemv_gate_up_silu(A_gate, A_up, x, out=None, *, stream=None):
+    """h = silu(A_gate @ x) * (A_up @ x) in one pass over both matrices
+    (same shape, dtype and row stride); returns h (M,) float32."""
+    M, K, lda = _check_matrix(A_gate)
+    M2, K2, lda2 = _check_matrix(A_up)
+    if (M2, K2) != (M, K) or A_up.dtype != A_gate.dtype or A_up.device != A_gate.device:
+        raise ValueError("A_gate and A_up must have the same shape, dtype and device")
+    if lda2 != lda and M > 1:
+        raise ValueError("A_gate and A_up must have the same row stride")
+    dt = _dtype_name(A_gate)
+    if x.dtype != A_gate.dtype or x.dim() != 1 or x.shape[0] != K or not x.is_contiguous():
+        raise ValueError("x must be a contiguous (K,) tensor of the matrices' dtype")
+    h = _check_out(out, (M,), A_gate.device)
+    fn = {"f32": gemv_gate_up_silu_f32, "f16": gemv_gate_up_silu_f16,
+          "bf16": gemv_gate_up_silu_bf16}[dt]
+    rc = fn(A_gate.data_ptr(), A_up.data_ptr(), lda, x.data_ptr(), h.data_ptr(), M, K,
+            _stream_handle(stream))
+    if rc != GEMV_SUCCESS:
+        raise GemvError(rc, fn.__name__)
+    return h

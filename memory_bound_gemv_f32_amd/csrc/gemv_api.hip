@@ -6,6 +6,8 @@
 // chosen by row length and row count (gemv_plan.hpp).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "../../include/gemv.h"
 #include "gemv_kernels.hpp"
 #include "gemv_plan.hpp"
@@ -14,46 +16,53 @@ namespace {
 
 thread_local hipError_t g_last_launch_error = hipSuccess;
 
+using gemvdev::Segments;
 using gemvdev::TBF16;
 using gemvdev::TF16;
 using gemvdev::TF32;
 using gemvplan::Plan;
 
-struct Args {
-    const void* A;
-    int64_t lda;
-    const void* X;
-    const float* bias;
-    float* Y;
-    int M;
-    int K;
-    int nvec;
-};
+static_assert(gemvplan::kBlock == gemvdev::kRowsWaves * 64,
+              "the planner's workgroup size is the one the rows kernels are compiled for");
+static_assert(GEMV_MAX_SEGMENTS == gemvdev::kMaxSegments, "segment table size");
 
-// Every kernel takes (A, lda, X, bias, Y, M, K); the matrix-core kernel also
-// takes nvec (the others have it as a template parameter or do not need it).
-hipError_t launch(const void* fn, const Plan& p, hipStream_t stream, const Args& a) {
-    const void* A = a.A;
-    int64_t lda = a.lda;
-    const void* X = a.X;
-    const float* bias = a.bias;
-    float* Y = a.Y;
-    int M = a.M;
-    int K = a.K;
-    int nvec = a.nvec;
-    void* argv[] = {(void*)&A, (void*)&lda, (void*)&X, (void*)&bias, (void*)&Y, (void*)&M, (void*)&K,
-                    (void*)&nvec};
+template <class D>
+constexpr int dtype_code() {
+    return std::is_same<D, TF32>::value ? gemvplan::F32
+           : std::is_same<D, TF16>::value ? gemvplan::F16 : gemvplan::BF16;
+}
+
+hipError_t launch(const void* fn, const Plan& p, hipStream_t stream, void** argv) {
     return hipLaunchKernel(fn, dim3((unsigned)p.grid), dim3((unsigned)p.block), argv, 0, stream);
 }
 
-// ---- rows-per-wave / wave-per-row ----------------------------------------
+gemv_status_t finish(hipError_t err) {
+    if (err != hipSuccess) {
+        g_last_launch_error = err;
+        return GEMV_ERROR_LAUNCH_FAILURE;
+    }
+    return GEMV_SUCCESS;
+}
 
-template <class D, int L, bool VEC>
+// ---- rows-per-wave / wave-per-row / workgroup-per-row ----------------------
+
+// MULTI selects the segment-table kernels (several matrices sharing x).
+template <class D, int L, bool VEC, bool MULTI>
 const void* rows_fn(int tiles) {
     if constexpr (L == 64) {
         // one wavefront per row: a single row tile, kWaveBatch loads in flight
         if (tiles != 1) return nullptr;
-        return (const void*)&gemvdev::gemv_rows_kernel<D, 64, 1, gemvplan::kWaveBatch, VEC>;
+        if constexpr (MULTI)
+            return (const void*)&gemvdev::gemv_rows_multi_kernel<D, 64, 1, gemvplan::kWaveBatch, VEC>;
+        else
+            return (const void*)&gemvdev::gemv_rows_kernel<D, 64, 1, gemvplan::kWaveBatch, VEC>;
+    } else if constexpr (MULTI) {
+        // per-lane segment lookups cost registers: at most two row tiles
+        switch (tiles) {
+        case 1: return (const void*)&gemvdev::gemv_rows_multi_kernel<D, L, 1, 1, VEC>;
+        case 2: return (const void*)&gemvdev::gemv_rows_multi_kernel<D, L, 2, 1, VEC>;
+        default: return nullptr;
+        }
     } else {
         // several rows per wavefront: one load per row tile, several tiles
         switch (tiles) {
@@ -66,18 +75,53 @@ const void* rows_fn(int tiles) {
     }
 }
 
-template <class D, bool VEC>
+template <class D, bool VEC, bool MULTI>
 const void* rows_fn(int lanes, int tiles) {
     switch (lanes) {
-    case 1: return rows_fn<D, 1, VEC>(tiles);
-    case 2: return rows_fn<D, 2, VEC>(tiles);
-    case 4: return rows_fn<D, 4, VEC>(tiles);
-    case 8: return rows_fn<D, 8, VEC>(tiles);
-    case 16: return rows_fn<D, 16, VEC>(tiles);
-    case 32: return rows_fn<D, 32, VEC>(tiles);
-    case 64: return rows_fn<D, 64, VEC>(tiles);
+    case 1: return rows_fn<D, 1, VEC, MULTI>(tiles);
+    case 2: return rows_fn<D, 2, VEC, MULTI>(tiles);
+    case 4: return rows_fn<D, 4, VEC, MULTI>(tiles);
+    case 8: return rows_fn<D, 8, VEC, MULTI>(tiles);
+    case 16: return rows_fn<D, 16, VEC, MULTI>(tiles);
+    case 32: return rows_fn<D, 32, VEC, MULTI>(tiles);
+    case 64: return rows_fn<D, 64, VEC, MULTI>(tiles);
     default: return nullptr;
     }
+}
+
+template <class D, bool VEC, bool MULTI, int B>
+const void* group_fn_b() {
+    constexpr int W = gemvplan::kGroupWaves;
+    if constexpr (MULTI)
+        return (const void*)&gemvdev::gemv_group_multi_kernel<D, W, B, VEC>;
+    else
+        return (const void*)&gemvdev::gemv_group_kernel<D, W, B, VEC>;
+}
+
+template <class D, bool VEC, bool MULTI>
+const void* group_fn(int batch) {
+    switch (batch) {
+    case 1: return group_fn_b<D, VEC, MULTI, 1>();
+    case 2: return group_fn_b<D, VEC, MULTI, 2>();
+    case 4: return group_fn_b<D, VEC, MULTI, 4>();
+    case 8: return group_fn_b<D, VEC, MULTI, 8>();
+    default: return nullptr;
+    }
+}
+
+template <class D, bool VEC, bool MULTI>
+const void* single_fn(const Plan& p) {
+    switch (p.family) {
+    case gemvplan::ROWS_PER_WAVE:
+    case gemvplan::WAVE_PER_ROW: return rows_fn<D, VEC, MULTI>(p.lanes_per_row, p.row_tiles);
+    case gemvplan::GROUP_PER_ROW: return group_fn<D, VEC, MULTI>(p.batch);
+    default: return nullptr;
+    }
+}
+
+template <class D, bool MULTI>
+const void* single_fn(const Plan& p) {
+    return p.vector_loads ? single_fn<D, true, MULTI>(p) : single_fn<D, false, MULTI>(p);
 }
 
 // ---- batched ----------------------------------------------------------------
@@ -111,46 +155,66 @@ const void* batched_fn(int nvec) {
     }
 }
 
-// ---- family/type dispatch ------------------------------------------------
-
-template <class D, bool VEC>
-const void* kernel_for(const Plan& p, int nvec) {
-    switch (p.family) {
-    case gemvplan::ROWS_PER_WAVE:
-    case gemvplan::WAVE_PER_ROW:
-        return rows_fn<D, VEC>(p.lanes_per_row, p.row_tiles);
-    case gemvplan::GROUP_PER_ROW:
-        switch (p.batch) {
-        case 1: return (const void*)&gemvdev::gemv_group_kernel<D, gemvplan::kGroupWaves, 1, VEC>;
-        case 2: return (const void*)&gemvdev::gemv_group_kernel<D, gemvplan::kGroupWaves, 2, VEC>;
-        case 4: return (const void*)&gemvdev::gemv_group_kernel<D, gemvplan::kGroupWaves, 4, VEC>;
-        case 8: return (const void*)&gemvdev::gemv_group_kernel<D, gemvplan::kGroupWaves, 8, VEC>;
-        default: return nullptr;
-        }
-    case gemvplan::BATCHED:
-        if constexpr (D::bytes == 2) return batched_fn<D, VEC>(nvec);
-        return nullptr;
-    case gemvplan::BATCHED_MFMA:
-        if constexpr (D::bytes == 2 && VEC)
+template <class D>
+const void* batched_kernel(const Plan& p, int nvec) {
+    if constexpr (D::bytes == 2) {
+        if (p.family == gemvplan::BATCHED)
+            return p.vector_loads ? batched_fn<D, true>(nvec) : batched_fn<D, false>(nvec);
+        if (p.family == gemvplan::BATCHED_MFMA && p.vector_loads)
             return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, gemvplan::kMfmaWaves,
                                                                    gemvplan::kMfmaChunk>;
-        return nullptr;
-    default:
-        return nullptr;
+    }
+    return nullptr;
+}
+
+// ---- gated pair ---------------------------------------------------------------
+
+template <class D, int W, bool VEC>
+const void* gated_fn(int batch) {
+    switch (batch) {
+    case 1: return (const void*)&gemvdev::gemv_gated_silu_kernel<D, W, 1, VEC>;
+    case 2: return (const void*)&gemvdev::gemv_gated_silu_kernel<D, W, 2, VEC>;
+    case 4: return (const void*)&gemvdev::gemv_gated_silu_kernel<D, W, 4, VEC>;
+    case 8: return (const void*)&gemvdev::gemv_gated_silu_kernel<D, W, 8, VEC>;
+    default: return nullptr;
     }
 }
 
 template <class D>
-const void* kernel_for(const Plan& p, int nvec) {
-    return p.vector_loads ? kernel_for<D, true>(p, nvec) : kernel_for<D, false>(p, nvec);
+const void* gated_kernel(const Plan& p) {
+    if (p.waves_per_group == 1)
+        return p.vector_loads ? gated_fn<D, 1, true>(p.batch) : gated_fn<D, 1, false>(p.batch);
+    if (p.waves_per_group == gemvplan::kGroupWaves)
+        return p.vector_loads ? gated_fn<D, gemvplan::kGroupWaves, true>(p.batch)
+                              : gated_fn<D, gemvplan::kGroupWaves, false>(p.batch);
+    return nullptr;
 }
 
-static_assert(gemvplan::kBlock == gemvdev::kRowsWaves * 64,
-              "the planner's workgroup size is the one the rows kernels are compiled for");
+// ---- entry points -------------------------------------------------------------
+
+template <class D>
+gemv_status_t run_single(const Plan& p, const void* A, int lda, const void* X, const float* bias,
+                         float* Y, int M, int K, int nvec, hipStream_t stream) {
+    if (p.family == gemvplan::BATCHED || p.family == gemvplan::BATCHED_MFMA) {
+        const void* fn = batched_kernel<D>(p, nvec);
+        if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;
+        int64_t lda64 = lda;
+        void* argv[] = {(void*)&A, (void*)&lda64, (void*)&X, (void*)&bias, (void*)&Y,
+                        (void*)&M, (void*)&K, (void*)&nvec};
+        return finish(launch(fn, p, stream, argv));
+    }
+    const void* fn = single_fn<D, false>(p);
+    if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;
+    int64_t lda64 = lda, M64 = M;
+    void* argv[] = {(void*)&A, (void*)&lda64, (void*)&bias, (void*)&Y, (void*)&M64, (void*)&X,
+                    (void*)&K};
+    return finish(launch(fn, p, stream, argv));
+}
 
 gemv_status_t run(int dtype, int family, const void* A, int lda, const void* X,
                   const float* bias, float* Y, int M, int K, int nvec,
                   hipStream_t stream) {
+    if (family == gemvplan::GATED_SILU) return GEMV_ERROR_INVALID_VALUE;  // own entry points
     if (gemvplan::validate(dtype, M, K, lda, nvec, (uintptr_t)A, (uintptr_t)X,
                            (uintptr_t)bias, (uintptr_t)Y) != gemvplan::OK)
         return GEMV_ERROR_INVALID_VALUE;
@@ -159,21 +223,75 @@ gemv_status_t run(int dtype, int family, const void* A, int lda, const void* X,
     if (gemvplan::make_plan(dtype, M, K, lda, nvec, (uintptr_t)A, (uintptr_t)X, family, &p) !=
         gemvplan::OK)
         return GEMV_ERROR_INVALID_VALUE;
-    const void* fn = nullptr;
     switch (dtype) {
-    case gemvplan::F32: fn = kernel_for<TF32>(p, nvec); break;
-    case gemvplan::F16: fn = kernel_for<TF16>(p, nvec); break;
-    case gemvplan::BF16: fn = kernel_for<TBF16>(p, nvec); break;
-    default: break;
+    case gemvplan::F32: return run_single<TF32>(p, A, lda, X, bias, Y, M, K, nvec, stream);
+    case gemvplan::F16: return run_single<TF16>(p, A, lda, X, bias, Y, M, K, nvec, stream);
+    case gemvplan::BF16: return run_single<TBF16>(p, A, lda, X, bias, Y, M, K, nvec, stream);
+    default: return GEMV_ERROR_INVALID_VALUE;
     }
+}
+
+template <class D>
+gemv_status_t run_multi(const gemv_segment_t* segs, int count, const void* x, int K,
+                        hipStream_t stream) {
+    using S = typename D::storage;
+    constexpr int dtype = dtype_code<D>();
+    if (segs == nullptr || count < 1 || count > GEMV_MAX_SEGMENTS || K < 0)
+        return GEMV_ERROR_INVALID_VALUE;
+    Segments<S> rows{};
+    int64_t total = 0;
+    bool vec = ((uintptr_t)x % gemvplan::kLoadBytes) == 0;
+    for (int i = 0; i < count; ++i) {
+        const gemv_segment_t& s = segs[i];
+        if (gemvplan::validate(dtype, s.M, K, s.lda, 1, (uintptr_t)s.A, (uintptr_t)x,
+                               (uintptr_t)s.bias, (uintptr_t)s.y) != gemvplan::OK)
+            return GEMV_ERROR_INVALID_VALUE;
+        rows.start[i] = total;
+        rows.A[i] = static_cast<const S*>(s.A);
+        rows.lda[i] = s.lda;
+        rows.bias[i] = s.bias;
+        rows.y[i] = s.y;
+        if (s.M > 0)
+            vec = vec && gemvplan::vector_ok(dtype, K, s.lda, 1, (uintptr_t)s.A, (uintptr_t)x);
+        total += s.M;
+    }
+    // unused table entries start past the last row, so no row selects them
+    for (int i = count; i < gemvdev::kMaxSegments; ++i) rows.start[i] = total;
+    if (total > 0x7fffffff) return GEMV_ERROR_INVALID_VALUE;
+    if (total == 0) return GEMV_SUCCESS;
+    rows.M = total;
+    rows.count = count;
+    Plan p;
+    if (gemvplan::make_plan_vec(dtype, (int)total, K, 1, vec, gemvplan::AUTO, &p,
+                                gemvplan::kMultiMaxRowTiles) != gemvplan::OK)
+        return GEMV_ERROR_INVALID_VALUE;
+    const void* fn = single_fn<D, true>(p);
     if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;
-    const Args args{A, (int64_t)lda, X, bias, Y, M, K, nvec};
-    const hipError_t err = launch(fn, p, stream, args);
-    if (err != hipSuccess) {
-        g_last_launch_error = err;
-        return GEMV_ERROR_LAUNCH_FAILURE;
-    }
-    return GEMV_SUCCESS;
+    void* argv[] = {(void*)&rows, (void*)&x, (void*)&K};
+    return finish(launch(fn, p, stream, argv));
+}
+
+template <class D>
+gemv_status_t run_gated(const void* Ag, const void* Au, int lda, const void* x, float* h, int M,
+                        int K, hipStream_t stream) {
+    constexpr int dtype = dtype_code<D>();
+    if (gemvplan::validate(dtype, M, K, lda, 1, (uintptr_t)Ag, (uintptr_t)x, 0, (uintptr_t)h) !=
+            gemvplan::OK ||
+        gemvplan::validate(dtype, M, K, lda, 1, (uintptr_t)Au, (uintptr_t)x, 0, (uintptr_t)h) !=
+            gemvplan::OK)
+        return GEMV_ERROR_INVALID_VALUE;
+    if (M == 0) return GEMV_SUCCESS;
+    const bool vec = gemvplan::vector_ok(dtype, K, lda, 1, (uintptr_t)Ag, (uintptr_t)x) &&
+                     gemvplan::vector_ok(dtype, K, lda, 1, (uintptr_t)Au, (uintptr_t)x);
+    Plan p;
+    if (gemvplan::make_plan_vec(dtype, M, K, 1, vec, gemvplan::GATED_SILU, &p) != gemvplan::OK)
+        return GEMV_ERROR_INVALID_VALUE;
+    const void* fn = gated_kernel<D>(p);
+    if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;
+    int64_t lda64 = lda, M64 = M;
+    void* argv[] = {(void*)&Ag, (void*)&Au, (void*)&lda64, (void*)&h, (void*)&M64, (void*)&x,
+                    (void*)&K};
+    return finish(launch(fn, p, stream, argv));
 }
 
 }  // namespace
@@ -216,6 +334,38 @@ gemv_status_t gemv_batched_f16(const uint16_t* A, int lda, const uint16_t* X, co
 gemv_status_t gemv_batched_bf16(const uint16_t* A, int lda, const uint16_t* X, const float* bias,
                                 float* Y, int M, int K, int nvec, hipStream_t stream) {
     return run(gemvplan::BF16, gemvplan::AUTO, A, lda, X, bias, Y, M, K, nvec, stream);
+}
+
+gemv_status_t gemv_multi_f32(const gemv_segment_t* segments, int count, const float* x, int K,
+                             hipStream_t stream) {
+    return run_multi<TF32>(segments, count, x, K, stream);
+}
+
+gemv_status_t gemv_multi_f16(const gemv_segment_t* segments, int count, const uint16_t* x, int K,
+                             hipStream_t stream) {
+    return run_multi<TF16>(segments, count, x, K, stream);
+}
+
+gemv_status_t gemv_multi_bf16(const gemv_segment_t* segments, int count, const uint16_t* x,
+                              int K, hipStream_t stream) {
+    return run_multi<TBF16>(segments, count, x, K, stream);
+}
+
+gemv_status_t gemv_gate_up_silu_f32(const float* A_gate, const float* A_up, int lda,
+                                    const float* x, float* h, int M, int K, hipStream_t stream) {
+    return run_gated<TF32>(A_gate, A_up, lda, x, h, M, K, stream);
+}
+
+gemv_status_t gemv_gate_up_silu_f16(const uint16_t* A_gate, const uint16_t* A_up, int lda,
+                                    const uint16_t* x, float* h, int M, int K,
+                                    hipStream_t stream) {
+    return run_gated<TF16>(A_gate, A_up, lda, x, h, M, K, stream);
+}
+
+gemv_status_t gemv_gate_up_silu_bf16(const uint16_t* A_gate, const uint16_t* A_up, int lda,
+                                     const uint16_t* x, float* h, int M, int K,
+                                     hipStream_t stream) {
+    return run_gated<TBF16>(A_gate, A_up, lda, x, h, M, K, stream);
 }
 
 gemv_status_t gemv_plan(gemv_dtype_t dtype, int M, int K, int lda, int nvec, const void* A,

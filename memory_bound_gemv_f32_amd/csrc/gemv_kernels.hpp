@@ -34,6 +34,77 @@ namespace gemvdev {
 // before the first load of A is issued.
 constexpr int kRowsWaves = 4;
 
+// Where row m of the (possibly row-concatenated) problem lives and where its
+// result goes.  Passed to the kernels by value, as kernel arguments.
+template <class S>
+struct OneMatrix {
+    const S* A;
+    int64_t lda;
+    const float* bias;  // or nullptr
+    float* y;
+    int64_t M;
+    __device__ __forceinline__ const S* row(int64_t m) const { return A + m * lda; }
+    __device__ __forceinline__ float bias_of(int64_t m) const { return bias != nullptr ? bias[m] : 0.f; }
+    __device__ __forceinline__ void store(int64_t m, float v) const { y[m] = v; }
+};
+
+// Up to kMaxSegments matrices with the same K, stacked row-wise: rows
+// start[i] .. start[i+1]-1 of the stack are rows of segment i.  Every
+// segment multiplies the same x (e.g. the q, k and v projections of one
+// token).  A row's segment is found by a select chain over the (uniform)
+// boundaries, so the fields stay in scalar registers.
+constexpr int kMaxSegments = 8;
+template <class S>
+struct Segments {
+    int64_t M;  // rows in all segments
+    int count;
+    int64_t start[kMaxSegments];
+    const S* A[kMaxSegments];
+    int64_t lda[kMaxSegments];
+    const float* bias[kMaxSegments];
+    float* y[kMaxSegments];
+    __device__ __forceinline__ int find(int64_t m) const {
+        int seg = 0;
+#pragma unroll
+        for (int i = 1; i < kMaxSegments; ++i) seg = (i < count && m >= start[i]) ? i : seg;
+        return seg;
+    }
+    __device__ __forceinline__ const S* row(int64_t m) const {
+        const S* a = A[0];
+        int64_t ld = lda[0], s0 = start[0];
+#pragma unroll
+        for (int i = 1; i < kMaxSegments; ++i) {
+            const bool in = i < count && m >= start[i];
+            a = in ? A[i] : a;
+            ld = in ? lda[i] : ld;
+            s0 = in ? start[i] : s0;
+        }
+        return a + (m - s0) * ld;
+    }
+    __device__ __forceinline__ float bias_of(int64_t m) const {
+        const float* b = bias[0];
+        int64_t s0 = start[0];
+#pragma unroll
+        for (int i = 1; i < kMaxSegments; ++i) {
+            const bool in = i < count && m >= start[i];
+            b = in ? bias[i] : b;
+            s0 = in ? start[i] : s0;
+        }
+        return b != nullptr ? b[m - s0] : 0.f;
+    }
+    __device__ __forceinline__ void store(int64_t m, float v) const {
+        float* o = y[0];
+        int64_t s0 = start[0];
+#pragma unroll
+        for (int i = 1; i < kMaxSegments; ++i) {
+            const bool in = i < count && m >= start[i];
+            o = in ? y[i] : o;
+            s0 = in ? start[i] : s0;
+        }
+        o[m - s0] = v;
+    }
+};
+
 // One batch of the rows kernels: BATCH chunks per row tile, chunk c + i·L
 // for i < BATCH, all loads issued before any is used.  CHECK: chunks at or
 // past nfull load chunk nfull-1 instead and are replaced by zero.
@@ -72,12 +143,9 @@ __device__ __forceinline__ void rows_batch(const S* const (&rp)[U], const S* x, 
 // A wavefront covers R = 64/L rows per row tile and takes U consecutive row
 // tiles; lanes sub = lane % L of one row walk its chunks with stride L, BATCH
 // chunks in flight per row tile.
-template <class D, int L, int U, int BATCH, bool VEC>
-__global__ void __launch_bounds__(kRowsWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
-gemv_rows_kernel(const typename D::storage* __restrict__ A, int64_t lda,
-                 const typename D::storage* __restrict__ x,
-                 const float* __restrict__ bias, float* __restrict__ y, int M,
-                 int K) {
+template <class D, int L, int U, int BATCH, bool VEC, class Rows>
+__device__ __forceinline__ void rows_body(const Rows& rows, const typename D::storage* __restrict__ x,
+                                          int K) {
     using S = typename D::storage;
     using C = Chunk<D, VEC>;
     constexpr int R = 64 / L;
@@ -89,11 +157,12 @@ gemv_rows_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     const int slot = lane / L;
     const int64_t tile0 = ((int64_t)blockIdx.x * kRowsWaves + wave) * U;
 
+    const int64_t M = rows.M;
     const S* rp[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t row = (tile0 + u) * R + slot;
-        rp[u] = A + (row < M ? row : (int64_t)M - 1) * lda;
+        rp[u] = rows.row(row < M ? row : M - 1);
     }
     // Epilogue rows: the wavefront's U·R rows are consecutive, and lane
     // (slot, sub) adds the bias to and stores the rows of tiles u = sub,
@@ -105,8 +174,7 @@ gemv_rows_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     for (int o = 0; o < kOut; ++o) {
         const int u = sub + o * L;
         const int64_t row = (tile0 + u) * R + slot;
-        bv[o] = 0.f;
-        if (bias != nullptr && u < U && row < M) bv[o] = bias[row];
+        bv[o] = (u < U && row < M) ? rows.bias_of(row) : 0.f;
     }
 
     float acc[U][2];
@@ -140,8 +208,25 @@ gemv_rows_kernel(const typename D::storage* __restrict__ A, int64_t lda,
 #pragma unroll
         for (int t = 1; t < U; ++t) out = (u == t) ? v[t] : out;
         const int64_t row = (tile0 + u) * R + slot;
-        if (u < U && row < M) y[row] = out + bv[o];
+        if (u < U && row < M) rows.store(row, out + bv[o]);
     }
+}
+
+// One matrix: the arguments are scalars, so they arrive preloaded in SGPRs.
+template <class D, int L, int U, int BATCH, bool VEC>
+__global__ void __launch_bounds__(kRowsWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
+gemv_rows_kernel(const typename D::storage* A, int64_t lda, const float* bias, float* y, int64_t M,
+                 const typename D::storage* __restrict__ x, int K) {
+    rows_body<D, L, U, BATCH, VEC>(OneMatrix<typename D::storage>{A, lda, bias, y, M}, x, K);
+}
+
+// Several row-stacked matrices sharing x (the segment table is a kernel
+// argument in memory).
+template <class D, int L, int U, int BATCH, bool VEC>
+__global__ void __launch_bounds__(kRowsWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
+gemv_rows_multi_kernel(const Segments<typename D::storage> rows,
+                       const typename D::storage* __restrict__ x, int K) {
+    rows_body<D, L, U, BATCH, VEC>(rows, x, K);
 }
 
 // Workgroup-per-row kernel: W wavefronts (64·W lanes) share one row; each
@@ -149,12 +234,9 @@ gemv_rows_kernel(const typename D::storage* __restrict__ A, int64_t lda,
 // barrier thread 0 adds the W partials in wavefront order, adds the bias and
 // writes y[row] (page "第 3 课", the block-reduction structure of section
 // "C. 点积规约与原子写入解耦" on 64-lane wavefronts).
-template <class D, int W, int BATCH, bool VEC>
-__global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4)))
-gemv_group_kernel(const typename D::storage* __restrict__ A, int64_t lda,
-                  const typename D::storage* __restrict__ x,
-                  const float* __restrict__ bias, float* __restrict__ y, int M,
-                  int K) {
+template <class D, int W, int BATCH, bool VEC, class Rows>
+__device__ __forceinline__ void group_body(const Rows& rows, const typename D::storage* __restrict__ x,
+                                           int K) {
     using S = typename D::storage;
     using C = Chunk<D, VEC>;
     constexpr int L = W * 64;
@@ -162,19 +244,18 @@ gemv_group_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     __shared__ float partial[W];
 
     const int64_t row = blockIdx.x;
-    if (row >= M) return;  // uniform across the workgroup
+    if (row >= rows.M) return;  // uniform across the workgroup
     const int sub = threadIdx.x;
-    const S* rp = A + row * lda;
-    float b = 0.f;
-    if (bias != nullptr && sub == 0) b = bias[row];
+    const S* rp = rows.row(row);
+    const float b = sub == 0 ? rows.bias_of(row) : 0.f;
 
     float acc[1][2] = {{0.f, 0.f}};
-    const S* const rows[1] = {rp};
+    const S* const rps[1] = {rp};
     const int nfull = K / E;
     const int nsafe = nfull - nfull % (BATCH * L);
     int c0 = 0;
-    for (; c0 < nsafe; c0 += BATCH * L) rows_batch<C, L, 1, BATCH, false>(rows, x, c0 + sub, nfull, acc);
-    if (c0 < nfull) rows_batch<C, L, 1, BATCH, true>(rows, x, c0 + sub, nfull, acc);
+    for (; c0 < nsafe; c0 += BATCH * L) rows_batch<C, L, 1, BATCH, false>(rps, x, c0 + sub, nfull, acc);
+    if (c0 < nfull) rows_batch<C, L, 1, BATCH, true>(rps, x, c0 + sub, nfull, acc);
     if constexpr (VEC) {
         for (int k = nfull * E + sub; k < K; k += L)
             acc[0][1] = __builtin_fmaf(widen(D{}, rp[k]), widen(D{}, x[k]), acc[0][1]);
@@ -187,8 +268,22 @@ gemv_group_kernel(const typename D::storage* __restrict__ A, int64_t lda,
         float s = partial[0];
 #pragma unroll
         for (int w = 1; w < W; ++w) s += partial[w];
-        y[row] = s + b;
+        rows.store(row, s + b);
     }
+}
+
+template <class D, int W, int BATCH, bool VEC>
+__global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4)))
+gemv_group_kernel(const typename D::storage* A, int64_t lda, const float* bias, float* y, int64_t M,
+                  const typename D::storage* __restrict__ x, int K) {
+    group_body<D, W, BATCH, VEC>(OneMatrix<typename D::storage>{A, lda, bias, y, M}, x, K);
+}
+
+template <class D, int W, int BATCH, bool VEC>
+__global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4)))
+gemv_group_multi_kernel(const Segments<typename D::storage> rows,
+                        const typename D::storage* __restrict__ x, int K) {
+    group_body<D, W, BATCH, VEC>(rows, x, K);
 }
 
 // Batched kernel: Y = A·X (+ bias) for NV right-hand vectors with one pass
@@ -396,6 +491,63 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
             }
         }
     }
+}
+
+// Gated pair on one pass over two matrices: h[m] = silu(g[m]) · u[m] with
+// g = A_gate·x, u = A_up·x and silu(g) = g / (1 + e^(-g)): the gate and up
+// projections of an FFN fused with their activation (the NPU MatMul essay,
+// sections 4.2 and 5.1, fuses an FFN's MatMuls with the activation; SiLU is
+// the gated activation of the decode shapes here).  W wavefronts share a
+// row pair (W = 1: one wavefront, no LDS); both rows' chunks are loaded
+// together against the same x chunks, so x is read once for the pair.
+template <class D, int W, int BATCH, bool VEC>
+__global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4)))
+gemv_gated_silu_kernel(const typename D::storage* Ag, const typename D::storage* Au, int64_t lda,
+                       float* h, int64_t M, const typename D::storage* __restrict__ x, int K) {
+    using S = typename D::storage;
+    using C = Chunk<D, VEC>;
+    constexpr int L = W * 64;
+    constexpr int E = C::elems;
+    __shared__ float partial[W][2];
+
+    const int64_t row = blockIdx.x;
+    if (row >= M) return;  // uniform across the workgroup
+    const int sub = threadIdx.x;
+    const S* const rps[2] = {Ag + row * lda, Au + row * lda};
+
+    float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+    const int nfull = K / E;
+    const int nsafe = nfull - nfull % (BATCH * L);
+    int c0 = 0;
+    for (; c0 < nsafe; c0 += BATCH * L) rows_batch<C, L, 2, BATCH, false>(rps, x, c0 + sub, nfull, acc);
+    if (c0 < nfull) rows_batch<C, L, 2, BATCH, true>(rps, x, c0 + sub, nfull, acc);
+    if constexpr (VEC) {
+        for (int k = nfull * E + sub; k < K; k += L) {
+            const float xe = widen(D{}, x[k]);
+            acc[0][1] = __builtin_fmaf(widen(D{}, rps[0][k]), xe, acc[0][1]);
+            acc[1][1] = __builtin_fmaf(widen(D{}, rps[1][k]), xe, acc[1][1]);
+        }
+    }
+
+    float g = segment_sum<64>(acc[0][0] + acc[0][1]);
+    float u = segment_sum<64>(acc[1][0] + acc[1][1]);
+    if constexpr (W > 1) {
+        if ((threadIdx.x & 63) == 0) {
+            partial[threadIdx.x >> 6][0] = g;
+            partial[threadIdx.x >> 6][1] = u;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            g = partial[0][0];
+            u = partial[0][1];
+#pragma unroll
+            for (int w = 1; w < W; ++w) {
+                g += partial[w][0];
+                u += partial[w][1];
+            }
+        }
+    }
+    if (threadIdx.x == 0) h[row] = g / (1.f + expf(-g)) * u;
 }
 
 }  // namespace gemvdev

@@ -33,7 +33,8 @@ enum Family {
     WAVE_PER_ROW = 1,
     GROUP_PER_ROW = 2,
     BATCHED = 3,
-    BATCHED_MFMA = 4
+    BATCHED_MFMA = 4,
+    GATED_SILU = 5
 };
 enum Status { OK = 0, INVALID = 1 };
 
@@ -123,15 +124,19 @@ inline bool vector_ok(int dtype, int K, int lda, int nvec, uintptr_t A, uintptr_
     return true;
 }
 
-inline int make_plan(int dtype, int M, int K, int lda, int nvec, uintptr_t A,
-                     uintptr_t X, int family, Plan* out) {
-    // Shape checks only: planning accepts any pointer value, NULL included.
-    if (dtype < F32 || dtype > BF16 || M < 0 || K < 0 || lda < K || nvec < 1 ||
-        nvec > kMaxVectors)
+// Plan for a problem whose 16-byte-load eligibility `vec` the caller has
+// decided (one matrix: vector_ok(); several: all of them).
+// Row tiles per wavefront for several row-stacked matrices: every tile's row
+// looks up its matrix per lane, which costs registers.
+constexpr int kMultiMaxRowTiles = 2;
+
+inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family, Plan* out,
+                         int max_row_tiles = 8) {
+    if (dtype < F32 || dtype > BF16 || M < 0 || K < 0 || nvec < 1 || nvec > kMaxVectors)
         return INVALID;
 
     Plan p;
-    p.vector_loads = vector_ok(dtype, K, lda, nvec, A, X) ? 1 : 0;
+    p.vector_loads = vec ? 1 : 0;
     p.chunk_elems = p.vector_loads ? kLoadBytes / element_bytes(dtype) : 1;
     // loads needed to cover one row (the last may be a partial, element-wise tail)
     const int64_t loads = ceil_div(K, p.chunk_elems);
@@ -142,13 +147,14 @@ inline int make_plan(int dtype, int M, int K, int lda, int nvec, uintptr_t A,
     const bool mfma_ok = dtype != F32 && p.vector_loads && K % 8 == 0;
 
     int fam = family;
+    const bool long_or_many = loads >= kGroupLongRowLoads ||
+                              (M >= kGroupManyRows && loads >= kGroupManyRowsMinLoads);
     if (fam == AUTO) {
         if (nvec > 1)
             fam = mfma_ok ? BATCHED_MFMA : BATCHED;
         else if (loads <= kRowsPerWaveMaxLanes)
             fam = ROWS_PER_WAVE;
-        else if (M <= kGroupMaxRows || loads >= kGroupLongRowLoads ||
-                 (M >= kGroupManyRows && loads >= kGroupManyRowsMinLoads))
+        else if (M <= kGroupMaxRows || long_or_many)
             fam = GROUP_PER_ROW;
         else
             fam = WAVE_PER_ROW;
@@ -169,7 +175,7 @@ inline int make_plan(int dtype, int M, int K, int lda, int nvec, uintptr_t A,
         // as many row tiles per wavefront as keeps >= kTargetGroups groups
         p.row_tiles = 1;
         if (p.vector_loads) {
-            for (int u = 8; u > 1; u >>= 1) {
+            for (int u = max_row_tiles; u > 1; u >>= 1) {
                 const int64_t rows = (int64_t)u * p.rows_per_wave * p.waves_per_group;
                 if (ceil_div(M, rows) >= kTargetGroups) {
                     p.row_tiles = u;
@@ -204,6 +210,19 @@ inline int make_plan(int dtype, int M, int K, int lda, int nvec, uintptr_t A,
         p.batch = kBatchedBatch;
         p.row_tiles = 1;
         break;
+    case GATED_SILU: {
+        // a workgroup per row pair: 4 wavefronts for long rows or tall
+        // matrices, else one wavefront (no LDS, no barrier)
+        const int w = (M <= kGroupMaxRows || long_or_many) ? kGroupWaves : 1;
+        p.lanes_per_row = kWave * w;
+        p.rows_per_wave = 0;
+        p.waves_per_group = w;
+        const int64_t per_lane = ceil_div(full, (int64_t)p.lanes_per_row);
+        p.batch = per_lane >= kGroupBatch ? kGroupBatch : next_pow2(per_lane < 1 ? 1 : per_lane);
+        p.row_tiles = 1;
+        p.lds_bytes = (int)(w * 2 * sizeof(float));
+        break;
+    }
     case BATCHED_MFMA:
         // each wavefront: 4 lanes per row and step, 16 rows; rows span the group
         p.lanes_per_row = 4 * kMfmaWaves;
@@ -217,7 +236,7 @@ inline int make_plan(int dtype, int M, int K, int lda, int nvec, uintptr_t A,
         return INVALID;
     }
     p.block = p.waves_per_group * kWave;
-    if (fam == GROUP_PER_ROW)
+    if (fam == GROUP_PER_ROW || fam == GATED_SILU)
         p.rows_per_group = 1;
     else if (fam == BATCHED_MFMA)
         p.rows_per_group = kMfmaRows;
@@ -231,6 +250,12 @@ inline int make_plan(int dtype, int M, int K, int lda, int nvec, uintptr_t A,
     if (p.grid > 0x7fffffff) return INVALID;
     *out = p;
     return OK;
+}
+
+inline int make_plan(int dtype, int M, int K, int lda, int nvec, uintptr_t A, uintptr_t X,
+                     int family, Plan* out) {
+    if (lda < K) return INVALID;
+    return make_plan_vec(dtype, M, K, nvec, vector_ok(dtype, K, lda, nvec, A, X), family, out);
 }
 
 }  // namespace gemvplan

@@ -200,3 +200,39 @@ def test_batched_plans():
     assert p("f16", 4096, 4095, nvec=4)["vector_loads"] == 0  # X columns misaligned
     with pytest.raises(lg.GemvError):
         p("f16", 4096, 4096, nvec=17)
+
+
+# ---------------------------------------------------------------------------
+# fused entry points: validation without a GPU
+# ---------------------------------------------------------------------------
+
+def test_multi_validation():
+    seg = (GOOD, 8, 4, None, GOOD)
+    ok_table = lg.segment_table([seg, seg])
+    for fn in (lg.gemv_multi_f32, lg.gemv_multi_f16, lg.gemv_multi_bf16):
+        assert fn(ok_table, 0, GOOD, 8, None) == lg.GEMV_ERROR_INVALID_VALUE
+        assert fn(ok_table, lg.MAX_SEGMENTS + 1, GOOD, 8, None) == lg.GEMV_ERROR_INVALID_VALUE
+        assert fn(None, 1, GOOD, 8, None) == lg.GEMV_ERROR_INVALID_VALUE
+        bad = lg.segment_table([seg, (GOOD, 7, 4, None, GOOD)])     # lda < K
+        assert fn(bad, 2, GOOD, 8, None) == lg.GEMV_ERROR_INVALID_VALUE
+        bad = lg.segment_table([seg, (None, 8, 4, None, GOOD)])     # NULL A
+        assert fn(bad, 2, GOOD, 8, None) == lg.GEMV_ERROR_INVALID_VALUE
+        bad = lg.segment_table([seg, (GOOD, 8, -1, None, GOOD)])    # M < 0
+        assert fn(bad, 2, GOOD, 8, None) == lg.GEMV_ERROR_INVALID_VALUE
+        empty = lg.segment_table([(None, 8, 0, None, None)] * 3)   # nothing to do
+        assert fn(empty, 3, GOOD, 8, None) == lg.GEMV_SUCCESS
+
+
+def test_gated_validation():
+    for fn in (lg.gemv_gate_up_silu_f32, lg.gemv_gate_up_silu_f16, lg.gemv_gate_up_silu_bf16):
+        assert fn(GOOD, GOOD, 7, GOOD, GOOD, 4, 8, None) == lg.GEMV_ERROR_INVALID_VALUE
+        assert fn(None, GOOD, 8, GOOD, GOOD, 4, 8, None) == lg.GEMV_ERROR_INVALID_VALUE
+        assert fn(GOOD, None, 8, GOOD, GOOD, 4, 8, None) == lg.GEMV_ERROR_INVALID_VALUE
+        assert fn(GOOD, GOOD, 8, GOOD, None, 4, 8, None) == lg.GEMV_ERROR_INVALID_VALUE
+        assert fn(GOOD, GOOD, 8, GOOD, GOOD, -1, 8, None) == lg.GEMV_ERROR_INVALID_VALUE
+        assert fn(None, None, 8, None, None, 0, 8, None) == lg.GEMV_SUCCESS
+
+
+def test_gated_family_is_not_a_plain_gemv():
+    assert lg.gemv_run_family(lg.DTYPE_BF16, lg.FAMILY_GATED_SILU, GOOD, 8, GOOD, None,
+                              GOOD, 4, 8, 1, None) == lg.GEMV_ERROR_INVALID_VALUE

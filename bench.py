@@ -20,7 +20,10 @@ launch duration over that region (graph replays leave no host gap, so it is
 the kernel's own duration, which rocprofv3's kernel trace confirms).  Also
 measured:
   * eager calls through the C ABI (one ctypes call per step);
-  * µs/call, GB/s and GFLOP/s for every other configured shape;
+  * µs/call, GB/s and GFLOP/s for every other configured shape, including
+    the fused decode calls (q/k/v as one multi-GEMV launch, gate/up with the
+    SiLU product as one launch) and a whole decode layer's projections in
+    four launches;
   * the CPU oracle on the host cores (``cpu_baseline``).
 
 Prints ONE JSON line on stdout; progress goes to stderr.
@@ -190,6 +193,72 @@ class Rotation:
         return fns
 
 
+FUSED = ("fused_qkv", "fused_gate_up")
+
+
+class FusedRotation:
+    """R device sets of a fused decode problem: q/k/v as one multi-GEMV
+    (``fused_qkv``) or the gate/up pair with the SiLU product
+    (``fused_gate_up``); the matrices of one set share one x."""
+
+    def __init__(self, kind, gi, torch, min_bytes=2 * INFINITY_CACHE_BYTES):
+        import numpy as np
+        self.kind = kind
+        self.parts = gi.make_fused_qkv() if kind == "fused_qkv" else list(gi.make_fused_gate_up())
+        p0 = self.parts[0]
+        self.dtype, self.K = p0.dtype, p0.K
+        a_bytes = sum(p.A.nbytes for p in self.parts)
+        self.R = max(2, math.ceil(min_bytes / a_bytes) + 1)
+        tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[p0.dtype]
+        hA = [torch.from_numpy(p.A.view(np.int16)).view(tdt) for p in self.parts]
+        hx = torch.from_numpy(p0.X[0].view(np.int16)).view(tdt)
+        n_out = [p.M for p in self.parts] if kind == "fused_qkv" else [p0.M]
+        self.sets = []
+        for _ in range(self.R):
+            self.sets.append(([a.to("cuda") for a in hA], hx.to("cuda"),
+                              [torch.empty(m, dtype=torch.float32, device="cuda") for m in n_out]))
+        self.bytes = gi.fused_qkv_bytes() if kind == "fused_qkv" else gi.fused_gate_up_bytes()
+        self.M = sum(p.M for p in self.parts)
+
+    def callers(self, lg, stream_handle):
+        fns = []
+        for As, x, ys in self.sets:
+            if self.kind == "fused_qkv":
+                table = lg.segment_table([(a.data_ptr(), p.lda, p.M, None, y.data_ptr())
+                                          for a, p, y in zip(As, self.parts, ys)])
+                f = {"f16": lg.gemv_multi_f16, "bf16": lg.gemv_multi_bf16}[self.dtype]
+                args = (table, len(self.parts), x.data_ptr(), self.K, stream_handle)
+            else:
+                g, u = self.parts
+                f = {"f16": lg.gemv_gate_up_silu_f16, "bf16": lg.gemv_gate_up_silu_bf16}[self.dtype]
+                args = (As[0].data_ptr(), As[1].data_ptr(), g.lda, x.data_ptr(), ys[0].data_ptr(),
+                        g.M, g.K, stream_handle)
+            fns.append((f, args))
+        return fns
+
+    def sanity_check(self, torch):
+        """Set 0 against torch's fp64 products on the device (the GEMV bound
+        per row; for h the bound carried through silu and the product)."""
+        As, x, ys = self.sets[0]
+        xd = x.double()
+        refs, sums = [], []
+        for a, p in zip(As, self.parts):
+            A = a.view(p.M, p.lda)[:, :p.K].double()
+            refs.append(A @ xd)
+            sums.append(A.abs() @ xd.abs())
+        if self.kind == "fused_qkv":
+            errs = [((y.double() - r).abs() / (1e-5 * sm + 1e-6)) for y, r, sm in zip(ys, refs, sums)]
+            worst = max(float(e.max()) for e in errs)
+        else:
+            g, u = refs
+            tg, tu = 1e-5 * sums[0] + 1e-6, 1e-5 * sums[1] + 1e-6
+            sg = g * torch.sigmoid(g)
+            h = sg * u
+            bound = 1.1 * tg * (u.abs() + tu) + sg.abs() * tu + 1e-6 * h.abs() + 1e-6
+            worst = float(((ys[0].double() - h).abs() / bound).max())
+        return worst <= 1.0, worst
+
+
 def call(fn_args):
     f, args = fn_args
     rc = f(*args)
@@ -260,37 +329,66 @@ def time_eager(torch, fns, steps, warmup):
     return e0.elapsed_time(e1)
 
 
-def parity_check(case, rot, torch):
-    """Set 0's output against the CPU oracle (every row)."""
-    import numpy as np
-    import oracle
-    ref, absdot = oracle.gemv(case.dtype, case.A, case.X, case.bias, case.M, case.K,
-                              lda=case.lda, nvec=case.nvec)
-    y = rot.Y[0].cpu().numpy().astype(np.float64)
-    err = np.abs(y - ref)
-    ok = bool(np.all(err <= 1e-5 * absdot + 1e-6))
-    worst = float(np.max(err / (1e-5 * absdot + 1e-6))) if err.size else 0.0
+def sanity_check(case, rot, torch):
+    """Set 0's output (every row) against torch's fp64 matrix product on the
+    device, within 1e-5·Σ|a·x| + 1e-6 per row: a guard that
+    the timed launches compute the right thing.  (Element-by-element parity
+    with the oracle, at this size too, is what the GPU tests check.)"""
+    A = rot.A[0].view(case.M, case.lda)[:, :case.K].double()
+    X = rot.X[0].view(case.nvec, case.K).double()
+    ref = X @ A.T.contiguous()
+    absdot = X.abs() @ A.abs().T.contiguous()
+    if rot.bias is not None:
+        ref += rot.bias.double()
+    err = (rot.Y[0].view(case.nvec, case.M).double() - ref).abs()
+    bound = 1e-5 * absdot + 1e-6
+    ok = bool(torch.all(err <= bound))
+    worst = float((err / bound).max()) if err.numel() else 0.0
     return ok, worst
 
 
 def measure_shape(name, torch, lg, gi, steps):
-    case = gi.make_workload(name)
-    rot = Rotation(case, torch)
+    fused = name in FUSED
+    if fused:
+        rot = FusedRotation(name, gi, torch)
+        nbytes, dtype, M, K, nvec, has_bias = rot.bytes, rot.dtype, rot.M, rot.K, 1, False
+    else:
+        case = gi.make_workload(name)
+        rot = Rotation(case, torch)
+        nbytes, dtype, M, K = case.algorithmic_bytes(), case.dtype, case.M, case.K
+        nvec, has_bias = case.nvec, case.bias is not None
     loop = GraphLoop(torch, rot, lg, steps, per=rot.R * max(1, 64 // rot.R))
     ms, n = loop.time(warmup=loop.per), steps
     fns = rot.callers(lg, torch.cuda.current_stream().cuda_stream)
     eager_ms = time_eager(torch, fns, steps, warmup=rot.R)
-    nbytes = case.algorithmic_bytes()
-    flops = gi.workload_flops(case.M, case.K, case.nvec, case.bias is not None)
+    if fused:
+        call(fns[0])
+        torch.cuda.synchronize()
+        ok, worst = rot.sanity_check(torch)
+        if name == "fused_qkv":  # the planner sees the concatenated rows
+            p0 = rot.parts[0]
+            plan = lg.plan(dtype, M, K, p0.lda, 1, rot.sets[0][0][0].data_ptr(),
+                           rot.sets[0][1].data_ptr())
+            family = lg.FAMILY_NAMES[plan["family"]] + " (multi)"
+        else:
+            family = "gated_silu"
+    else:
+        call(fns[0])
+        torch.cuda.synchronize()
+        ok, worst = sanity_check(case, rot, torch)
+        plan = lg.plan(case.dtype, case.M, case.K, case.lda, case.nvec,
+                       rot.A[0].data_ptr(), rot.X[0].data_ptr())
+        family = lg.FAMILY_NAMES[plan["family"]]
+    if not ok:
+        raise RuntimeError(f"{name}: output outside the bound (worst error/bound {worst:.3g})")
+    flops = gi.workload_flops(M, K, nvec, has_bias)
     us = 1e3 * ms / n
-    plan = lg.plan(case.dtype, case.M, case.K, case.lda, case.nvec,
-                   rot.A[0].data_ptr(), rot.X[0].data_ptr())
     del loop, rot
     torch.cuda.empty_cache()
     return {
-        "dtype": case.dtype, "M": case.M, "K": case.K, "nvec": case.nvec,
-        "bias": case.bias is not None, "bytes": nbytes,
-        "family": lg.FAMILY_NAMES[plan["family"]],
+        "dtype": dtype, "M": M, "K": K, "nvec": nvec,
+        "bias": has_bias, "bytes": nbytes,
+        "family": family,
         "us_per_call_graph": round(us, 3),
         "us_per_call_eager": round(1e3 * eager_ms / steps, 3),
         "GBps": round(nbytes / us / 1e3, 1),
@@ -365,8 +463,10 @@ def main():
         counters_run(case, rot, lg, torch)
         return
 
-    ok, worst = parity_check(case, rot, torch)
-    log(f"parity vs oracle (set 0, every row): {'ok' if ok else 'FAILED'}; "
+    call(rot.callers(lg, torch.cuda.current_stream().cuda_stream)[0])
+    torch.cuda.synchronize()
+    ok, worst = sanity_check(case, rot, torch)
+    log(f"check vs torch fp64 on the device (set 0, every row): {'ok' if ok else 'FAILED'}; "
         f"worst error / bound = {worst:.3g}")
     if not ok:
         sys.exit(1)
@@ -406,7 +506,7 @@ def main():
 
     shapes = {}
     names = [] if args.shapes == "none" else (
-        list(gi.WORKLOADS) if args.shapes == "all" else args.shapes.split(","))
+        list(gi.WORKLOADS) + list(FUSED) if args.shapes == "all" else args.shapes.split(","))
     for name in names:
         shapes[name] = measure_shape(name, torch, lg, gi, args.shape_steps)
         log(f"  {name}: {shapes[name]}")
@@ -417,6 +517,18 @@ def main():
         tus = sum(shapes[n]["us_per_call_graph"] for n in sweep)
         sweep_agg = {"bytes": tb, "us": round(tus, 3), "GBps": round(tb / tus / 1e3, 1),
                      "frac_of_8TBps": round(tb / tus / 1e3 / HBM_PEAK_GBS, 4)}
+
+    # one decode layer's projections: q/k/v fused, o, gate/up fused with the
+    # SiLU product, down; against the same matrices as seven plain GEMVs
+    layer = None
+    if all(n in shapes for n in ("fused_qkv", "sweep_o", "fused_gate_up", "sweep_down")):
+        parts = ("fused_qkv", "sweep_o", "fused_gate_up", "sweep_down")
+        tb = sum(shapes[n]["bytes"] for n in parts)
+        tus = sum(shapes[n]["us_per_call_graph"] for n in parts)
+        layer = {"launches": 4, "bytes": tb, "us": round(tus, 3), "GBps": round(tb / tus / 1e3, 1),
+                 "frac_of_8TBps": round(tb / tus / 1e3 / HBM_PEAK_GBS, 4)}
+        if sweep_agg is not None:
+            layer["speedup_vs_7_plain_gemvs"] = round(sweep_agg["us"] / tus, 3)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -460,6 +572,7 @@ def main():
         "cpu_baseline": cpu,
         "per_shape": shapes,
         "sweep_aggregate": sweep_agg,
+        "decode_layer_fused": layer,
     }
     print(json.dumps(out), flush=True)
 

@@ -153,9 +153,10 @@ class Rotation:
     """R device copies of one case's inputs/outputs, R chosen so that the
     copies of A together exceed 2× the Infinity Cache."""
 
-    def __init__(self, case, torch, min_bytes=2 * INFINITY_CACHE_BYTES):
+    def __init__(self, case, torch, min_bytes=2 * INFINITY_CACHE_BYTES, splitk=False):
         import numpy as np
         self.case = case
+        self.splitk = splitk  # run through gemv_splitk_* (one shared workspace)
         a_bytes = case.A.nbytes
         self.R = max(2, math.ceil(min_bytes / max(a_bytes, 1)) + 1)
         tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[case.dtype]
@@ -174,6 +175,11 @@ class Rotation:
         if case.bias is not None:
             self.bias = torch.from_numpy(case.bias).to("cuda")
         self.bytes_resident = self.R * (a_bytes + case.X.nbytes + 4 * case.M * case.nvec)
+        self.ws = None
+        if splitk:
+            import memory_bound_gemv_f32_amd as lg
+            n = lg.splitk_workspace_size(case.dtype, case.M, case.K)
+            self.ws = torch.empty(max(n // 4, 1), dtype=torch.float32, device="cuda")
 
     def callers(self, lg, stream_handle):
         """One zero-argument callable per set that enqueues one call through
@@ -183,7 +189,13 @@ class Rotation:
         bias = self.bias.data_ptr() if self.bias is not None else None
         for i in range(self.R):
             A, X, Y = self.A[i].data_ptr(), self.X[i].data_ptr(), self.Y[i].data_ptr()
-            if c.nvec > 1:
+            if self.splitk:
+                f = {"f32": lg.gemv_splitk_f32, "f16": lg.gemv_splitk_f16,
+                     "bf16": lg.gemv_splitk_bf16}[c.dtype]
+                ws = self.ws
+                args = (A, c.lda, X, bias, Y, c.M, c.K, 0, ws.data_ptr(),
+                        ws.numel() * 4, stream_handle)
+            elif c.nvec > 1:
                 f = {"f16": lg.gemv_batched_f16, "bf16": lg.gemv_batched_bf16}[c.dtype]
                 args = (A, c.lda, X, bias, Y, c.M, c.K, c.nvec, stream_handle)
             else:
@@ -354,7 +366,7 @@ def measure_shape(name, torch, lg, gi, steps):
         nbytes, dtype, M, K, nvec, has_bias = rot.bytes, rot.dtype, rot.M, rot.K, 1, False
     else:
         case = gi.make_workload(name)
-        rot = Rotation(case, torch)
+        rot = Rotation(case, torch, splitk=name in gi.SPLITK_WORKLOADS)
         nbytes, dtype, M, K = case.algorithmic_bytes(), case.dtype, case.M, case.K
         nvec, has_bias = case.nvec, case.bias is not None
     loop = GraphLoop(torch, rot, lg, steps, per=rot.R * max(1, 64 // rot.R))
@@ -376,9 +388,20 @@ def measure_shape(name, torch, lg, gi, steps):
         call(fns[0])
         torch.cuda.synchronize()
         ok, worst = sanity_check(case, rot, torch)
-        plan = lg.plan(case.dtype, case.M, case.K, case.lda, case.nvec,
-                       rot.A[0].data_ptr(), rot.X[0].data_ptr())
-        family = lg.FAMILY_NAMES[plan["family"]]
+        if rot.splitk:
+            plan = lg.plan_splitk(case.dtype, case.M, case.K, case.lda, 0,
+                                  rot.A[0].data_ptr(), rot.X[0].data_ptr())
+            family = f"{lg.FAMILY_NAMES[plan['family']]} ({plan['splits']} slices) + reduce"
+        else:
+            plan = lg.plan(case.dtype, case.M, case.K, case.lda, case.nvec,
+                           rot.A[0].data_ptr(), rot.X[0].data_ptr())
+            family = lg.FAMILY_NAMES[plan["family"]]
+    single_us = None
+    if not fused and rot.splitk:  # the same problem in one pass, for comparison
+        rot.splitk = False
+        single = GraphLoop(torch, rot, lg, steps, per=rot.R * max(1, 64 // rot.R))
+        single_us = round(1e3 * single.time(warmup=single.per) / steps, 3)
+        del single
     if not ok:
         raise RuntimeError(f"{name}: output outside the bound (worst error/bound {worst:.3g})")
     flops = gi.workload_flops(M, K, nvec, has_bias)
@@ -394,6 +417,7 @@ def measure_shape(name, torch, lg, gi, steps):
         "GBps": round(nbytes / us / 1e3, 1),
         "frac_of_8TBps": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
         "GFLOPps": round(flops / us / 1e3, 1),
+        **({"us_per_call_single_pass": single_us} if single_us is not None else {}),
     }
 
 

@@ -187,6 +187,11 @@ WORKLOADS = {
 }
 for _i, (_n, (_m, _k)) in enumerate(SWEEP_SHAPES.items()):
     WORKLOADS[f"sweep_{_n}"] = ("bf16", _m, _k, 1, False, "normal", 0.02, 640 + _i)
+# few, long rows (the split-K case): the small-M example of the SGEMV page
+# (M = 8) with 2^21-element fp32 rows, and 64 bf16 rows of 2^18 elements
+WORKLOADS["splitk_f32_8x2M"] = ("f32", 8, 1 << 21, 1, False, "uniform", None, 66)
+WORKLOADS["splitk_bf16_64x256k"] = ("bf16", 64, 1 << 18, 1, False, "normal", 0.02, 67)
+SPLITK_WORKLOADS = ("splitk_f32_8x2M", "splitk_bf16_64x256k")
 
 
 def workload_shape(name: str):

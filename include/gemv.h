@@ -3,6 +3,9 @@
  *
  *   y = A·x (+ bias)                 gemv_f32 / gemv_f16 / gemv_bf16
  *   Y = A·X (+ bias), 1..16 vectors   gemv_batched_f16 / gemv_batched_bf16
+ *   several y_i = A_i·x in one launch gemv_multi_*
+ *   h = silu(A_gate·x) ⊙ (A_up·x)     gemv_gate_up_silu_*
+ *   y = A·x for few, long rows        gemv_splitk_* (caller's workspace)
  *
  * The operation.  Output m is the dot product of row m of A with x (page
  * "SGEMV CUDA代码学习", section "问题定义: 一行一个点积": A is M×K, x is K×1,
@@ -38,8 +41,8 @@
  * Pointers and ownership.  A, x/X, bias and y/Y are device pointers (memory
  * from hipMalloc or a device allocator such as PyTorch's), owned by the
  * caller.  The library never allocates, frees, retains or synchronises: a
- * call only enqueues one kernel on `stream` (NULL = the null stream) and
- * returns.  y/Y must not overlap A, x/X or bias.  Pointers must be aligned
+ * call only enqueues its kernel on `stream` (NULL = the null stream; split-K
+ * enqueues two) and returns.  y/Y must not overlap A, x/X or bias.  Pointers must be aligned
  * to their element size; any further alignment is optional (16-byte aligned
  * A, x and row pitch lda·element_size select the widest loads).
  *
@@ -54,6 +57,7 @@
 #ifndef LIBGEMV_GEMV_H
 #define LIBGEMV_GEMV_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include <hip/hip_runtime_api.h>
@@ -153,14 +157,57 @@ gemv_status_t gemv_gate_up_silu_bf16(const uint16_t *A_gate,
                                      const uint16_t *x, float *h, int M, int K,
                                      hipStream_t stream);
 
+typedef enum { GEMV_DTYPE_F32 = 0, GEMV_DTYPE_F16 = 1, GEMV_DTYPE_BF16 = 2 } gemv_dtype_t;
+
+/* ------------------------------------------------------------------------
+ * Split-K, for few rows of many elements.  Page "SGEMV CUDA代码学习",
+ * section "Kernel 1: k32", points out that with one row per warp a small M
+ * (its example: M = 8) starts only a handful of blocks and leaves the rest
+ * of the GPU idle.  Here each row is cut into `splits` slices of K; one
+ * workgroup per (row, slice) writes a partial sum into a caller-provided
+ * workspace, and a second kernel adds each row's partials in a fixed order
+ * and the bias (two kernels on `stream`, no atomics).  The result is
+ * y = A·x (+ bias) with the same tolerance as gemv_*, and identical bits on
+ * every call with the same `splits`.
+ *
+ * splits: 0 = let the library choose (1 when M already fills the GPU or the
+ * rows are short; then the call is exactly a gemv_* call and needs no
+ * workspace); >= 1 = that many slices, rounded so that each slice is a whole
+ * number of 16-byte loads (at most 1024; the effective count may be lower).
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of workspace gemv_splitk_* needs for these arguments: 4·M·(effective
+ * splits), or 0 when a single slice is used.  GEMV_ERROR_INVALID_VALUE for
+ * M < 0, K < 0, splits < 0, a bad dtype or a NULL `bytes`. */
+gemv_status_t gemv_splitk_workspace_size(gemv_dtype_t dtype, int M, int K,
+                                         int splits, size_t *bytes);
+
+/* y = A·x (+ bias) by split-K.  workspace: device memory of at least the
+ * size above, 4-byte aligned, owned by the caller, not overlapping any
+ * argument; it is overwritten (no initial contents are needed) and may be
+ * reused once the call's kernels have finished on `stream`; two calls in
+ * flight at the same time need separate workspaces.  Errors as for gemv_*,
+ * plus GEMV_ERROR_INVALID_VALUE for splits < 0 or a NULL, misaligned or too
+ * small workspace when one is needed. */
+gemv_status_t gemv_splitk_f32(const float *A, int lda, const float *x,
+                              const float *bias, float *y, int M, int K,
+                              int splits, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+gemv_status_t gemv_splitk_f16(const uint16_t *A, int lda, const uint16_t *x,
+                              const float *bias, float *y, int M, int K,
+                              int splits, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+gemv_status_t gemv_splitk_bf16(const uint16_t *A, int lda, const uint16_t *x,
+                               const float *bias, float *y, int M, int K,
+                               int splits, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Introspection and testing.  These do not change what the entry points
  * above compute; they expose how the library maps a problem onto the GPU so
  * that the mapping can be checked without a GPU and every kernel family can
  * be exercised at every shape it supports.
  * ------------------------------------------------------------------------ */
-
-typedef enum { GEMV_DTYPE_F32 = 0, GEMV_DTYPE_F16 = 1, GEMV_DTYPE_BF16 = 2 } gemv_dtype_t;
 
 /* Kernel families.  Page "SGEMV CUDA代码学习", section "三 kernel 的设计空间
  * 总结", frames GEMV's only design choice as how many lanes share one row;
@@ -172,7 +219,8 @@ typedef enum {
     GEMV_FAMILY_GROUP_PER_ROW = 2, /* one workgroup per row, LDS reduction */
     GEMV_FAMILY_BATCHED = 3,       /* several rows × nvec vectors per wave */
     GEMV_FAMILY_BATCHED_MFMA = 4,  /* 16 rows × 16 vectors on the matrix cores */
-    GEMV_FAMILY_GATED_SILU = 5     /* a row of A_gate and of A_up per workgroup */
+    GEMV_FAMILY_GATED_SILU = 5,    /* a row of A_gate and of A_up per workgroup */
+    GEMV_FAMILY_SPLIT_K = 6        /* a workgroup per row and K-slice, then a reduce */
 } gemv_family_t;
 
 typedef struct {
@@ -188,7 +236,9 @@ typedef struct {
     int passes;          /* loop trips per lane over one row's full chunks */
     int block;           /* threads per workgroup */
     int lds_bytes;       /* static + dynamic LDS per workgroup */
-    int64_t grid;        /* workgroups */
+    int splits;          /* K-slices per row (split-K), else 1 */
+    int slice_elems;     /* elements per K-slice (the last may be shorter), else K */
+    int64_t grid;        /* workgroups (split-K: per slice) */
 } gemv_plan_t;
 
 /* Compute, on the host only, the mapping a call with these arguments would
@@ -197,10 +247,16 @@ typedef struct {
  * value, including host addresses or NULL).  Returns GEMV_ERROR_INVALID_VALUE
  * for arguments the entry points would reject or a family that cannot run
  * this shape (e.g. GEMV_FAMILY_BATCHED for fp32, or a single-vector family
- * with nvec > 1). */
+ * with nvec > 1; the gated and split-K families have their own calls). */
 gemv_status_t gemv_plan(gemv_dtype_t dtype, int M, int K, int lda, int nvec,
                         const void *A, const void *X, int family,
                         gemv_plan_t *plan);
+
+/* The mapping gemv_splitk_* would launch: family GEMV_FAMILY_SPLIT_K with
+ * its splits and slice length, or (one slice) the gemv_* mapping. */
+gemv_status_t gemv_plan_splitk(gemv_dtype_t dtype, int M, int K, int lda,
+                               int splits, const void *A, const void *x,
+                               gemv_plan_t *plan);
 
 /* Run with a forced family (GEMV_FAMILY_AUTO = what the entry points do).
  * Same arguments, validation and results contract as the entry points;

@@ -8,10 +8,11 @@ without a built ``libgemv.so`` raises ``ImportError``.
 Two levels:
 
 * the C ABI under the same names (``gemv_f32``, ``gemv_f16``, ``gemv_bf16``,
-  ``gemv_batched_f16``, ``gemv_batched_bf16``, ``gemv_plan``,
-  ``gemv_run_family``, ``gemv_status_string``), taking integer addresses and
-  returning the ``gemv_status_t`` code;
-* tensor helpers ``gemv`` and ``gemv_batched`` that check dtype, shape,
+  ``gemv_batched_*``, ``gemv_multi_*``, ``gemv_gate_up_silu_*``,
+  ``gemv_splitk_*``, ``gemv_plan``, ``gemv_run_family``, ...), taking integer
+  addresses and returning the ``gemv_status_t`` code;
+* tensor helpers ``gemv``, ``gemv_batched``, ``gemv_multi``,
+  ``gemv_gate_up_silu`` and ``gemv_splitk`` that check dtype, shape,
   strides and device, call the matching entry point on
   ``torch.cuda.current_stream()`` and raise ``GemvError`` on a failure code.
 
@@ -60,6 +61,7 @@ FAMILY_GROUP_PER_ROW = 2
 FAMILY_BATCHED = 3
 FAMILY_BATCHED_MFMA = 4
 FAMILY_GATED_SILU = 5
+FAMILY_SPLIT_K = 6
 MAX_SEGMENTS = 8
 FAMILY_NAMES = {
     FAMILY_ROWS_PER_WAVE: "rows_per_wave",
@@ -68,6 +70,7 @@ FAMILY_NAMES = {
     FAMILY_BATCHED: "batched",
     FAMILY_BATCHED_MFMA: "batched_mfma",
     FAMILY_GATED_SILU: "gated_silu",
+    FAMILY_SPLIT_K: "split_k",
 }
 
 
@@ -75,7 +78,8 @@ class GemvPlan(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int) for name in (
         "family", "vector_loads", "chunk_elems", "lanes_per_row",
         "rows_per_wave", "row_tiles", "waves_per_group", "rows_per_group",
-        "batch", "passes", "block", "lds_bytes")] + [("grid", ctypes.c_int64)]
+        "batch", "passes", "block", "lds_bytes", "splits", "slice_elems")] + [
+        ("grid", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -111,15 +115,22 @@ gemv_multi_bf16 = _bind("gemv_multi_bf16", [ctypes.POINTER(GemvSegment), _i, _vp
 gemv_gate_up_silu_f32 = _bind("gemv_gate_up_silu_f32", [_vp, _vp, _i, _vp, _vp, _i, _i, _st])
 gemv_gate_up_silu_f16 = _bind("gemv_gate_up_silu_f16", [_vp, _vp, _i, _vp, _vp, _i, _i, _st])
 gemv_gate_up_silu_bf16 = _bind("gemv_gate_up_silu_bf16", [_vp, _vp, _i, _vp, _vp, _i, _i, _st])
+_sz = ctypes.c_size_t
+gemv_splitk_workspace_size = _bind("gemv_splitk_workspace_size", [_i, _i, _i, _i, ctypes.POINTER(_sz)])
+gemv_splitk_f32 = _bind("gemv_splitk_f32", [_vp, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _st])
+gemv_splitk_f16 = _bind("gemv_splitk_f16", [_vp, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _st])
+gemv_splitk_bf16 = _bind("gemv_splitk_bf16", [_vp, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _st])
 gemv_plan = _bind("gemv_plan", [_i, _i, _i, _i, _i, _vp, _vp, _i, ctypes.POINTER(GemvPlan)])
+gemv_plan_splitk = _bind("gemv_plan_splitk", [_i, _i, _i, _i, _i, _vp, _vp, ctypes.POINTER(GemvPlan)])
 gemv_run_family = _bind("gemv_run_family", [_i, _i, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _st])
 
 EXPORTED = ("gemv_status_string", "gemv_last_hip_error",
             "gemv_last_hip_error_string", "gemv_f32", "gemv_f16", "gemv_bf16",
             "gemv_batched_f16", "gemv_batched_bf16", "gemv_multi_f32",
             "gemv_multi_f16", "gemv_multi_bf16", "gemv_gate_up_silu_f32",
-            "gemv_gate_up_silu_f16", "gemv_gate_up_silu_bf16", "gemv_plan",
-            "gemv_run_family")
+            "gemv_gate_up_silu_f16", "gemv_gate_up_silu_bf16",
+            "gemv_splitk_workspace_size", "gemv_splitk_f32", "gemv_splitk_f16",
+            "gemv_splitk_bf16", "gemv_plan", "gemv_plan_splitk", "gemv_run_family")
 
 
 class GemvError(RuntimeError):
@@ -140,6 +151,26 @@ def plan(dtype: str, M: int, K: int, lda: int | None = None, nvec: int = 1,
     if rc != GEMV_SUCCESS:
         raise GemvError(rc, "gemv_plan")
     return out.as_dict()
+
+
+def plan_splitk(dtype: str, M: int, K: int, lda: int | None = None, splits: int = 0,
+                A_addr: int = 0, x_addr: int = 0) -> dict:
+    """The mapping gemv_splitk_* would launch (host-only)."""
+    out = GemvPlan()
+    rc = gemv_plan_splitk(DTYPE_CODES[dtype], M, K, K if lda is None else lda, splits,
+                          A_addr, x_addr, ctypes.byref(out))
+    if rc != GEMV_SUCCESS:
+        raise GemvError(rc, "gemv_plan_splitk")
+    return out.as_dict()
+
+
+def splitk_workspace_size(dtype: str, M: int, K: int, splits: int = 0) -> int:
+    """Workspace bytes gemv_splitk_* needs (0: a single slice, none needed)."""
+    n = ctypes.c_size_t(0)
+    rc = gemv_splitk_workspace_size(DTYPE_CODES[dtype], M, K, splits, ctypes.byref(n))
+    if rc != GEMV_SUCCESS:
+        raise GemvError(rc, "gemv_splitk_workspace_size")
+    return n.value
 
 
 # ---------------------------------------------------------------------------
@@ -257,6 +288,34 @@ def gemv_batched(A, X, bias=None, out=None, *, family: int = FAMILY_AUTO,
     if rc != GEMV_SUCCESS:
         raise GemvError(rc, where)
     return Y
+
+
+def gemv_splitk(A, x, bias=None, out=None, *, splits: int = 0, workspace=None, stream=None):
+    """y = A @ x (+ bias) by split-K (for few, long rows); returns y (M,)
+    float32.  ``workspace``: a device tensor of at least
+    ``splitk_workspace_size(...)`` bytes, allocated here through torch when
+    not given."""
+    torch = _torch()
+    M, K, lda = _check_matrix(A)
+    dt = _dtype_name(A)
+    if x.dtype != A.dtype or x.dim() != 1 or x.shape[0] != K or not x.is_contiguous():
+        raise ValueError("x must be a contiguous (K,) tensor of A's dtype")
+    if x.device != A.device:
+        raise ValueError("x is on another device")
+    bias = _check_bias(bias, M, A.device)
+    y = _check_out(out, (M,), A.device)
+    need = splitk_workspace_size(dt, M, K, splits)
+    if workspace is None:
+        workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=A.device)
+    if workspace.device != A.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on A's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    fn = {"f32": gemv_splitk_f32, "f16": gemv_splitk_f16, "bf16": gemv_splitk_bf16}[dt]
+    rc = fn(A.data_ptr(), lda, x.data_ptr(), bias.data_ptr() if bias is not None else None,
+            y.data_ptr(), M, K, splits, workspace.data_ptr(), ws_bytes, _stream_handle(stream))
+    if rc != GEMV_SUCCESS:
+        raise GemvError(rc, fn.__name__)
+    return y
 
 
 def segment_table(segments) -> "ctypes.Array":

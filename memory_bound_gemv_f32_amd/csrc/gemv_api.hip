@@ -190,6 +190,22 @@ const void* gated_kernel(const Plan& p) {
     return nullptr;
 }
 
+// ---- split-K ------------------------------------------------------------------
+
+template <class D, bool VEC>
+const void* splitk_fn(int batch) {
+    switch (batch) {
+    case 1: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, 1, VEC>;
+    case 2: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, 2, VEC>;
+    case 4: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, 4, VEC>;
+    case 8: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, 8, VEC>;
+    default: return nullptr;
+    }
+}
+
+static_assert(gemvplan::kGroupWaves == gemvdev::kGroupWavesDev,
+              "the planner's split-K workgroup is the one the kernel is compiled for");
+
 // ---- entry points -------------------------------------------------------------
 
 template <class D>
@@ -214,7 +230,9 @@ gemv_status_t run_single(const Plan& p, const void* A, int lda, const void* X, c
 gemv_status_t run(int dtype, int family, const void* A, int lda, const void* X,
                   const float* bias, float* Y, int M, int K, int nvec,
                   hipStream_t stream) {
-    if (family == gemvplan::GATED_SILU) return GEMV_ERROR_INVALID_VALUE;  // own entry points
+    // the gated and split-K families have entry points of their own
+    if (family == gemvplan::GATED_SILU || family == gemvplan::SPLIT_K)
+        return GEMV_ERROR_INVALID_VALUE;
     if (gemvplan::validate(dtype, M, K, lda, nvec, (uintptr_t)A, (uintptr_t)X,
                            (uintptr_t)bias, (uintptr_t)Y) != gemvplan::OK)
         return GEMV_ERROR_INVALID_VALUE;
@@ -292,6 +310,62 @@ gemv_status_t run_gated(const void* Ag, const void* Au, int lda, const void* x, 
     void* argv[] = {(void*)&Ag, (void*)&Au, (void*)&lda64, (void*)&h, (void*)&M64, (void*)&x,
                     (void*)&K};
     return finish(launch(fn, p, stream, argv));
+}
+
+template <class D>
+gemv_status_t run_splitk(const void* A, int lda, const void* x, const float* bias, float* y, int M,
+                         int K, int splits, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+    constexpr int dtype = dtype_code<D>();
+    if (splits < 0 ||
+        gemvplan::validate(dtype, M, K, lda, 1, (uintptr_t)A, (uintptr_t)x, (uintptr_t)bias,
+                           (uintptr_t)y) != gemvplan::OK)
+        return GEMV_ERROR_INVALID_VALUE;
+    if (M == 0) return GEMV_SUCCESS;
+    const bool vec = gemvplan::vector_ok(dtype, K, lda, 1, (uintptr_t)A, (uintptr_t)x);
+    Plan p;
+    if (gemvplan::make_split_plan(dtype, M, K, vec, splits, &p) != gemvplan::OK)
+        return GEMV_ERROR_INVALID_VALUE;
+    if (p.splits == 1) return run_single<D>(p, A, lda, x, bias, y, M, K, 1, stream);
+
+    const int64_t need = gemvplan::split_workspace_bytes(M, p.splits);
+    if (workspace == nullptr || (uintptr_t)workspace % sizeof(float) != 0 ||
+        workspace_bytes < (size_t)need)
+        return GEMV_ERROR_INVALID_VALUE;
+    const void* fn = p.vector_loads ? splitk_fn<D, true>(p.batch) : splitk_fn<D, false>(p.batch);
+    if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;
+
+    float* ws = static_cast<float*>(workspace);
+    int64_t lda64 = lda, M64 = M;
+    int slice = p.slice_elems, nsplit = p.splits;
+    void* argv1[] = {(void*)&A, (void*)&lda64, (void*)&ws, (void*)&M64, (void*)&x, (void*)&K,
+                     (void*)&slice};
+    hipError_t err = hipLaunchKernel(fn, dim3((unsigned)M, (unsigned)nsplit), dim3((unsigned)p.block),
+                                     argv1, 0, stream);
+    if (err != hipSuccess) return finish(err);
+    const float* wsc = ws;
+    void* argv2[] = {(void*)&wsc, (void*)&nsplit, (void*)&bias, (void*)&y, (void*)&M64};
+    const unsigned groups = (unsigned)gemvplan::ceil_div(M, gemvdev::kRowsWaves);
+    return finish(hipLaunchKernel((const void*)&gemvdev::gemv_splitk_reduce_kernel, dim3(groups),
+                                  dim3(gemvdev::kRowsWaves * 64), argv2, 0, stream));
+}
+
+void export_plan(const Plan& p, gemv_plan_t* plan) {
+    plan->family = p.family;
+    plan->vector_loads = p.vector_loads;
+    plan->chunk_elems = p.chunk_elems;
+    plan->lanes_per_row = p.lanes_per_row;
+    plan->rows_per_wave = p.rows_per_wave;
+    plan->row_tiles = p.row_tiles;
+    plan->waves_per_group = p.waves_per_group;
+    plan->rows_per_group = p.rows_per_group;
+    plan->batch = p.batch;
+    plan->passes = p.passes;
+    plan->block = p.block;
+    plan->lds_bytes = p.lds_bytes;
+    plan->splits = p.splits;
+    plan->slice_elems = p.slice_elems;
+    plan->grid = p.grid;
 }
 
 }  // namespace
@@ -375,20 +449,47 @@ gemv_status_t gemv_plan(gemv_dtype_t dtype, int M, int K, int lda, int nvec, con
     if (gemvplan::make_plan((int)dtype, M, K, lda, nvec, (uintptr_t)A, (uintptr_t)X, family,
                             &p) != gemvplan::OK)
         return GEMV_ERROR_INVALID_VALUE;
-    plan->family = p.family;
-    plan->vector_loads = p.vector_loads;
-    plan->chunk_elems = p.chunk_elems;
-    plan->lanes_per_row = p.lanes_per_row;
-    plan->rows_per_wave = p.rows_per_wave;
-    plan->row_tiles = p.row_tiles;
-    plan->waves_per_group = p.waves_per_group;
-    plan->rows_per_group = p.rows_per_group;
-    plan->batch = p.batch;
-    plan->passes = p.passes;
-    plan->block = p.block;
-    plan->lds_bytes = p.lds_bytes;
-    plan->grid = p.grid;
+    export_plan(p, plan);
     return GEMV_SUCCESS;
+}
+
+gemv_status_t gemv_plan_splitk(gemv_dtype_t dtype, int M, int K, int lda, int splits,
+                               const void* A, const void* x, gemv_plan_t* plan) {
+    if (plan == nullptr || lda < K) return GEMV_ERROR_INVALID_VALUE;
+    Plan p;
+    const bool vec = gemvplan::vector_ok((int)dtype, K, lda, 1, (uintptr_t)A, (uintptr_t)x);
+    if (gemvplan::make_split_plan((int)dtype, M, K, vec, splits, &p) != gemvplan::OK)
+        return GEMV_ERROR_INVALID_VALUE;
+    export_plan(p, plan);
+    return GEMV_SUCCESS;
+}
+
+gemv_status_t gemv_splitk_workspace_size(gemv_dtype_t dtype, int M, int K, int splits,
+                                         size_t* bytes) {
+    int n = 1, slice = 0;
+    if (bytes == nullptr ||
+        gemvplan::split_geometry((int)dtype, M, K, splits, &n, &slice) != gemvplan::OK)
+        return GEMV_ERROR_INVALID_VALUE;
+    *bytes = (size_t)gemvplan::split_workspace_bytes(M, n);
+    return GEMV_SUCCESS;
+}
+
+gemv_status_t gemv_splitk_f32(const float* A, int lda, const float* x, const float* bias,
+                              float* y, int M, int K, int splits, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+    return run_splitk<TF32>(A, lda, x, bias, y, M, K, splits, workspace, workspace_bytes, stream);
+}
+
+gemv_status_t gemv_splitk_f16(const uint16_t* A, int lda, const uint16_t* x, const float* bias,
+                              float* y, int M, int K, int splits, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+    return run_splitk<TF16>(A, lda, x, bias, y, M, K, splits, workspace, workspace_bytes, stream);
+}
+
+gemv_status_t gemv_splitk_bf16(const uint16_t* A, int lda, const uint16_t* x, const float* bias,
+                               float* y, int M, int K, int splits, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+    return run_splitk<TBF16>(A, lda, x, bias, y, M, K, splits, workspace, workspace_bytes, stream);
 }
 
 gemv_status_t gemv_run_family(gemv_dtype_t dtype, int family, const void* A, int lda,

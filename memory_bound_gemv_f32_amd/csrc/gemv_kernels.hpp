@@ -33,6 +33,8 @@ namespace gemvdev {
 // the kernel arguments preloaded into SGPRs nothing waits on a scalar load
 // before the first load of A is issued.
 constexpr int kRowsWaves = 4;
+// Wavefronts per workgroup of the workgroup-per-row and split-K kernels.
+constexpr int kGroupWavesDev = 4;
 
 // Where row m of the (possibly row-concatenated) problem lives and where its
 // result goes.  Passed to the kernels by value, as kernel arguments.
@@ -284,6 +286,55 @@ __global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4))
 gemv_group_multi_kernel(const Segments<typename D::storage> rows,
                         const typename D::storage* __restrict__ x, int K) {
     group_body<D, W, BATCH, VEC>(rows, x, K);
+}
+
+// Split-K, pass 1: workgroup (m, s) of a grid of M × splits forms the dot
+// product of row m's slice s (elements s·slice .. s·slice + slice - 1, the
+// last slice shorter) with the same slice of x, in the workgroup-per-row
+// body, and writes it to ws[m·splits + s].  The A and x pointers of a slice
+// are offset by a whole number of 16-byte loads, so the vector path's
+// alignment holds in every slice.
+template <class S>
+struct SliceOfRows {
+    const S* A;  // first element of the slice in row 0
+    int64_t lda;
+    float* ws;   // ws + s: the row-major M × splits partials, column s
+    int splits;
+    int64_t M;
+    __device__ __forceinline__ const S* row(int64_t m) const { return A + m * lda; }
+    __device__ __forceinline__ float bias_of(int64_t) const { return 0.f; }
+    __device__ __forceinline__ void store(int64_t m, float v) const { ws[m * splits] = v; }
+};
+
+template <class D, int BATCH, bool VEC>
+__global__ void __launch_bounds__(kGroupWavesDev * 64) __attribute__((amdgpu_waves_per_eu(4)))
+gemv_splitk_partial_kernel(const typename D::storage* A, int64_t lda, float* ws, int64_t M,
+                           const typename D::storage* __restrict__ x, int K, int slice) {
+    const int s = blockIdx.y;
+    const int64_t k0 = (int64_t)s * slice;
+    const int64_t rest = (int64_t)K - k0;
+    const int ks = rest < slice ? (int)rest : slice;
+    group_body<D, kGroupWavesDev, BATCH, VEC>(
+        SliceOfRows<typename D::storage>{A + k0, lda, ws + s, (int)gridDim.y, M}, x + k0, ks);
+}
+
+// Split-K, pass 2: one wavefront per row adds the row's `splits` partials in
+// a fixed order (lane l takes partials l, l + 64, ... in turn, then the
+// 64-lane tree of segment_sum), adds the bias, and writes y[m].  The order
+// depends on nothing but `splits`, so repeated calls give identical results
+// (the two-stage reduction of page "第 3 课" with its second stage in a
+// kernel of its own, so that no atomics are needed).
+__global__ void __launch_bounds__(kRowsWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
+gemv_splitk_reduce_kernel(const float* __restrict__ ws, int splits, const float* __restrict__ bias,
+                          float* __restrict__ y, int64_t M) {
+    const int lane = threadIdx.x & 63;
+    const int64_t m = (int64_t)blockIdx.x * kRowsWaves + (threadIdx.x >> 6);
+    if (m >= M) return;  // uniform across the wavefront
+    const float* p = ws + m * splits;
+    float acc = 0.f;
+    for (int s = lane; s < splits; s += 64) acc += p[s];
+    acc = segment_sum<64>(acc);
+    if (lane == 0) y[m] = acc + (bias != nullptr ? bias[m] : 0.f);
 }
 
 // Batched kernel: Y = A·X (+ bias) for NV right-hand vectors with one pass

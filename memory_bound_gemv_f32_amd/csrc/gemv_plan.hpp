@@ -34,7 +34,8 @@ enum Family {
     GROUP_PER_ROW = 2,
     BATCHED = 3,
     BATCHED_MFMA = 4,
-    GATED_SILU = 5
+    GATED_SILU = 5,
+    SPLIT_K = 6
 };
 enum Status { OK = 0, INVALID = 1 };
 
@@ -70,6 +71,22 @@ constexpr int kMfmaChunk = 16;
 constexpr int mfma_lds_bytes() {
     return kMfmaWaves * 16 * (kMfmaChunk * 64 + 16) + kMfmaWaves * kWave * 16;
 }
+// Split-K: when there are too few rows to fill the chip and each row holds
+// much more than a workgroup keeps in flight (page "SGEMV CUDA代码学习",
+// section "Kernel 1: k32": with M = 8 only two blocks run and the rest of the
+// machine idles), every row is cut into `splits` slices; a workgroup per
+// (row, slice) writes a partial sum, and a second kernel adds each row's
+// partials in slice order (a fixed order, so results are reproducible).
+// Chosen automatically for fewer than kSplitMaxRows rows of at least
+// kSplitMinRowLoads 16-byte loads (4 batches of the workgroup-per-row
+// family); below that the second launch (~2 µs) costs more than it saves.
+// Slices are at least kSplitMinSliceLoads loads and a whole number of loads
+// per lane.  Measured on MI355X: fp32 8×2^21 265 -> 22.6 µs, bf16 64×2^18
+// 20.7 -> 10.6 µs, while bf16 256×2^16 and 512×2^15 are faster unsplit.
+constexpr int64_t kSplitMaxRows = 256;
+constexpr int64_t kSplitMinRowLoads = 4 * kGroupWaves * kWave * kGroupBatch;
+constexpr int64_t kSplitMinSliceLoads = 512;
+constexpr int kSplitMaxSplits = 1024;
 // Threads per workgroup of the rows/wave and batched families.
 constexpr int kBlock = 256;
 // Below this many workgroups the rows-per-wave family stops giving each
@@ -89,7 +106,9 @@ struct Plan {
     int passes = 0;
     int block = 0;
     int lds_bytes = 0;
-    int64_t grid = 0;
+    int splits = 1;       // K-slices per row (split-K), else 1
+    int slice_elems = 0;  // elements per slice (split-K), else K
+    int64_t grid = 0;     // workgroups (split-K: per slice)
 };
 
 inline int element_bytes(int dtype) { return dtype == F32 ? 4 : 2; }
@@ -243,11 +262,86 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
     else
         p.rows_per_group = p.rows_per_wave * p.row_tiles * p.waves_per_group;
     p.grid = ceil_div(M, p.rows_per_group);
+    p.slice_elems = K;
     if (fam == BATCHED_MFMA)  // 32-wide steps per wavefront
         p.passes = (int)ceil_div(K / 32, (int64_t)kMfmaWaves);
     else
         p.passes = (int)ceil_div(full, (int64_t)p.lanes_per_row);
     if (p.grid > 0x7fffffff) return INVALID;
+    *out = p;
+    return OK;
+}
+
+// Slices for split-K.  `requested` = 0 chooses: 1 unless the rows are few
+// and long (above), else as many slices as keep M × splits within
+// kTargetGroups workgroups, each at least kSplitMinSliceLoads loads long.  `requested` >= 1 asks for that many (used as
+// given, after rounding the slice up to whole 16-byte loads and capping at
+// kSplitMaxSplits).  The slice is a whole number of 16-byte loads of every
+// dtype, so 16-byte alignment of A and x carries over to every slice.
+inline int split_geometry(int dtype, int M, int K, int requested, int* splits, int* slice) {
+    if (dtype < F32 || dtype > BF16 || M < 0 || K < 0 || requested < 0) return INVALID;
+    const int64_t granule = kLoadBytes / element_bytes(dtype);  // elements per load
+    const int64_t loads = ceil_div(K, granule);
+    int64_t want = requested;
+    if (requested == 0) {
+        want = 1;
+        if (M > 0 && M < kSplitMaxRows && loads >= kSplitMinRowLoads) {
+            const int64_t by_rows = kTargetGroups / M;
+            const int64_t by_len = loads / kSplitMinSliceLoads;
+            want = by_rows < by_len ? by_rows : by_len;
+            if (want < 2) want = 1;
+        }
+    }
+    if (want > kSplitMaxSplits) want = kSplitMaxSplits;
+    if (want < 1 || loads <= 1) want = 1;
+    int64_t slice_loads = ceil_div(loads, want);
+    if (requested == 0 && want > 1) {  // the same number of loads for every lane
+        const int64_t lanes = (int64_t)kGroupWaves * kWave;
+        slice_loads = ceil_div(slice_loads, lanes) * lanes;
+    }
+    int64_t n = ceil_div(loads, slice_loads < 1 ? 1 : slice_loads);
+    if (n < 1) n = 1;
+    *splits = (int)n;
+    *slice = n == 1 ? K : (int)(slice_loads * granule);
+    return OK;
+}
+
+// Workspace bytes split-K needs: one fp32 partial per row and slice (none
+// when one slice is chosen, which runs the single-pass families).
+inline int64_t split_workspace_bytes(int M, int splits) {
+    return splits > 1 ? (int64_t)M * splits * (int64_t)sizeof(float) : 0;
+}
+
+// Plan of a split-K call: pass 1 of family SPLIT_K (a workgroup of 4
+// wavefronts per row and slice, grid = M × splits), or, with one slice, the
+// automatic single-pass plan.
+inline int make_split_plan(int dtype, int M, int K, bool vec, int requested, Plan* out) {
+    int splits = 1, slice = K;
+    if (split_geometry(dtype, M, K, requested, &splits, &slice) != OK) return INVALID;
+    if (splits == 1) {
+        if (make_plan_vec(dtype, M, K, 1, vec, AUTO, out) != OK) return INVALID;
+        out->splits = 1;
+        out->slice_elems = K;
+        return OK;
+    }
+    Plan p;
+    p.family = SPLIT_K;
+    p.vector_loads = vec ? 1 : 0;
+    p.chunk_elems = p.vector_loads ? kLoadBytes / element_bytes(dtype) : 1;
+    const int64_t full = slice / p.chunk_elems;  // whole chunks of a full slice
+    p.lanes_per_row = kWave * kGroupWaves;
+    p.rows_per_wave = 0;
+    p.waves_per_group = kGroupWaves;
+    const int64_t per_lane = ceil_div(full, (int64_t)p.lanes_per_row);
+    p.batch = per_lane >= kGroupBatch ? kGroupBatch : next_pow2(per_lane < 1 ? 1 : per_lane);
+    p.row_tiles = 1;
+    p.rows_per_group = 1;
+    p.block = p.waves_per_group * kWave;
+    p.lds_bytes = (int)(kGroupWaves * sizeof(float));
+    p.splits = splits;
+    p.slice_elems = slice;
+    p.grid = M;
+    p.passes = (int)per_lane;
     *out = p;
     return OK;
 }

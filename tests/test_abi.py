@@ -236,3 +236,90 @@ def test_gated_validation():
 def test_gated_family_is_not_a_plain_gemv():
     assert lg.gemv_run_family(lg.DTYPE_BF16, lg.FAMILY_GATED_SILU, GOOD, 8, GOOD, None,
                               GOOD, 4, 8, 1, None) == lg.GEMV_ERROR_INVALID_VALUE
+
+
+# ---------------------------------------------------------------------------
+# split-K: validation, workspace size and slice geometry, without a GPU
+# ---------------------------------------------------------------------------
+
+SPLITK = (lg.gemv_splitk_f32, lg.gemv_splitk_f16, lg.gemv_splitk_bf16)
+
+
+def test_splitk_validation():
+    big_K = 1 << 20            # 4 rows of 2^20: the automatic plan splits
+    for fn in SPLITK:
+        def call(M=4, K=big_K, lda=big_K, splits=0, ws=GOOD, ws_bytes=1 << 20, y=GOOD):
+            return fn(GOOD, lda, GOOD, None, y, M, K, splits, ws, ws_bytes, None)
+        assert call(splits=-1) == lg.GEMV_ERROR_INVALID_VALUE
+        assert call(lda=big_K - 1) == lg.GEMV_ERROR_INVALID_VALUE
+        assert call(M=-1) == lg.GEMV_ERROR_INVALID_VALUE
+        assert call(y=None) == lg.GEMV_ERROR_INVALID_VALUE
+        assert call(ws=None) == lg.GEMV_ERROR_INVALID_VALUE          # needed, missing
+        assert call(ws=GOOD + 2) == lg.GEMV_ERROR_INVALID_VALUE      # misaligned
+        assert call(ws_bytes=16) == lg.GEMV_ERROR_INVALID_VALUE      # too small
+        assert call(M=0, ws=None, ws_bytes=0) == lg.GEMV_SUCCESS     # nothing to do
+
+
+def test_splitk_family_is_not_a_plain_gemv():
+    assert lg.gemv_run_family(lg.DTYPE_F32, lg.FAMILY_SPLIT_K, GOOD, 8, GOOD, None,
+                              GOOD, 4, 8, 1, None) == lg.GEMV_ERROR_INVALID_VALUE
+    with pytest.raises(lg.GemvError):
+        lg.plan("f32", 4, 8, family=lg.FAMILY_SPLIT_K)
+
+
+def test_splitk_workspace_size():
+    n = ctypes.c_size_t(7)
+    assert lg.gemv_splitk_workspace_size(0, 4, 8, -1, ctypes.byref(n)) == lg.GEMV_ERROR_INVALID_VALUE
+    assert lg.gemv_splitk_workspace_size(0, -1, 8, 0, ctypes.byref(n)) == lg.GEMV_ERROR_INVALID_VALUE
+    assert lg.gemv_splitk_workspace_size(3, 4, 8, 0, ctypes.byref(n)) == lg.GEMV_ERROR_INVALID_VALUE
+    assert lg.gemv_splitk_workspace_size(0, 4, 8, 0, None) == lg.GEMV_ERROR_INVALID_VALUE
+    # rows too short or numerous enough: no split, no workspace
+    assert lg.splitk_workspace_size("bf16", 4096, 4096) == 0
+    assert lg.splitk_workspace_size("f32", 16, 1000) == 0
+    p = lg.plan_splitk("f32", 16, 1 << 20)
+    assert lg.splitk_workspace_size("f32", 16, 1 << 20) == 4 * 16 * p["splits"]
+
+
+def test_splitk_for_few_long_rows():
+    """The small-M case: fewer than 256 rows of at least 8192 16-byte loads
+    are cut into slices so that rows × slices approaches 1024 workgroups, each
+    slice at least 512 loads and a whole number of loads per lane."""
+    for dtype, M, K in (("f32", 16, 1 << 20), ("f32", 8, 1 << 21), ("bf16", 64, 1 << 18),
+                        ("f16", 1, 1 << 24), ("bf16", 100, 100000), ("f32", 255, 1 << 15),
+                        ("bf16", 32, 65536)):
+        p = lg.plan_splitk(dtype, M, K, A_addr=ALIGNED, x_addr=ALIGNED)
+        s = 4 if dtype == "f32" else 2
+        assert p["family"] == lg.FAMILY_SPLIT_K, (dtype, M, K)
+        assert p["splits"] >= 2 and M * p["splits"] <= 1024
+        assert (p["slice_elems"] * s) % 16 == 0
+        assert p["slice_elems"] * s >= 512 * 16 and (p["slice_elems"] * s // 16) % 256 == 0
+        assert (p["splits"] - 1) * p["slice_elems"] < K <= p["splits"] * p["slice_elems"]
+        assert p["grid"] == M and p["block"] == 256
+        per_lane = p["slice_elems"] * s // 16 // 256
+        assert p["batch"] == min(8, 1 << (per_lane - 1).bit_length())
+
+
+def test_splitk_keeps_the_plain_plan_when_it_fills_the_gpu():
+    for dtype, M, K in (("bf16", 4096, 4096), ("bf16", 1024, 4096), ("bf16", 1000, 40000),
+                        ("f32", 16, 1000), ("f32", 1 << 20, 16), ("bf16", 5, 0),
+                        ("bf16", 256, 1 << 16), ("bf16", 512, 1 << 15), ("bf16", 64, 14336),
+                        ("f32", 100, 32764)):           # 8191 loads per row
+        p = lg.plan_splitk(dtype, M, K, A_addr=ALIGNED, x_addr=ALIGNED)
+        assert p["splits"] == 1 and p["slice_elems"] == K
+        assert p == {**lg.plan(dtype, M, K, A_addr=ALIGNED, X_addr=ALIGNED),
+                     "splits": 1, "slice_elems": K}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_splitk_requested_slices(dtype):
+    s = 4 if dtype == "f32" else 2
+    g = 16 // s
+    for M, K, want in ((7, 1000, 3), (3, 10, 100), (2, 1 << 20, 5000), (1, 8, 2), (4, 129, 2),
+                       (9, 4097, 7), (1, 1, 3)):
+        p = lg.plan_splitk(dtype, M, K, splits=want, A_addr=ALIGNED, x_addr=ALIGNED)
+        S, sl = p["splits"], p["slice_elems"]
+        assert 1 <= S <= min(want, 1024)
+        assert (S - 1) * sl < K <= S * sl or (K == 0 and S == 1)
+        if S > 1:
+            assert sl % g == 0 and p["family"] == lg.FAMILY_SPLIT_K
+    assert lg.plan_splitk(dtype, 7, 1000, splits=3)["slice_elems"] == -(-(-(-1000 // 3)) // g) * g

@@ -238,7 +238,7 @@ typedef struct {
     int lds_bytes;       /* static + dynamic LDS per workgroup */
     int splits;          /* K-slices per row (split-K), else 1 */
     int slice_elems;     /* elements per K-slice (the last may be shorter), else K */
-    int64_t grid;        /* workgroups (split-K: per slice) */
+    int64_t grid;        /* workgroups (split-K: rows × slices) */
 } gemv_plan_t;
 
 /* Compute, on the host only, the mapping a call with these arguments would

@@ -339,9 +339,9 @@ gemv_status_t run_splitk(const void* A, int lda, const void* x, const float* bia
     int64_t lda64 = lda, M64 = M;
     int slice = p.slice_elems, nsplit = p.splits;
     void* argv1[] = {(void*)&A, (void*)&lda64, (void*)&ws, (void*)&M64, (void*)&x, (void*)&K,
-                     (void*)&slice};
-    hipError_t err = hipLaunchKernel(fn, dim3((unsigned)M, (unsigned)nsplit), dim3((unsigned)p.block),
-                                     argv1, 0, stream);
+                     (void*)&slice, (void*)&nsplit};
+    hipError_t err = hipLaunchKernel(fn, dim3((unsigned)p.grid), dim3((unsigned)p.block), argv1, 0,
+                                     stream);
     if (err != hipSuccess) return finish(err);
     const float* wsc = ws;
     void* argv2[] = {(void*)&wsc, (void*)&nsplit, (void*)&bias, (void*)&y, (void*)&M64};

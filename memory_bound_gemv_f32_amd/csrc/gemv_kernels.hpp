@@ -238,14 +238,13 @@ gemv_rows_multi_kernel(const Segments<typename D::storage> rows,
 // "C. 点积规约与原子写入解耦" on 64-lane wavefronts).
 template <class D, int W, int BATCH, bool VEC, class Rows>
 __device__ __forceinline__ void group_body(const Rows& rows, const typename D::storage* __restrict__ x,
-                                           int K) {
+                                           int K, int64_t row) {
     using S = typename D::storage;
     using C = Chunk<D, VEC>;
     constexpr int L = W * 64;
     constexpr int E = C::elems;
     __shared__ float partial[W];
 
-    const int64_t row = blockIdx.x;
     if (row >= rows.M) return;  // uniform across the workgroup
     const int sub = threadIdx.x;
     const S* rp = rows.row(row);
@@ -278,22 +277,25 @@ template <class D, int W, int BATCH, bool VEC>
 __global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4)))
 gemv_group_kernel(const typename D::storage* A, int64_t lda, const float* bias, float* y, int64_t M,
                   const typename D::storage* __restrict__ x, int K) {
-    group_body<D, W, BATCH, VEC>(OneMatrix<typename D::storage>{A, lda, bias, y, M}, x, K);
+    group_body<D, W, BATCH, VEC>(OneMatrix<typename D::storage>{A, lda, bias, y, M}, x, K, blockIdx.x);
 }
 
 template <class D, int W, int BATCH, bool VEC>
 __global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4)))
 gemv_group_multi_kernel(const Segments<typename D::storage> rows,
                         const typename D::storage* __restrict__ x, int K) {
-    group_body<D, W, BATCH, VEC>(rows, x, K);
+    group_body<D, W, BATCH, VEC>(rows, x, K, blockIdx.x);
 }
 
-// Split-K, pass 1: workgroup (m, s) of a grid of M × splits forms the dot
-// product of row m's slice s (elements s·slice .. s·slice + slice - 1, the
-// last slice shorter) with the same slice of x, in the workgroup-per-row
-// body, and writes it to ws[m·splits + s].  The A and x pointers of a slice
-// are offset by a whole number of 16-byte loads, so the vector path's
-// alignment holds in every slice.
+// Split-K, pass 1: workgroup (m, s) forms the dot product of row m's slice s
+// (elements s·slice .. s·slice + slice - 1, the last slice shorter) with the
+// same slice of x, in the workgroup-per-row body, and writes it to
+// ws[m·splits + s].  The A and x pointers of a slice are offset by a whole
+// number of 16-byte loads, so the vector path's alignment holds in every
+// slice.  Workgroup id = m·splits + s: consecutive ids, which the dispatcher
+// deals round-robin to the 8 XCDs, walk the slices of one row, so with
+// splits a multiple of 8 every row's slice s runs on the same XCD and its x
+// slice is fetched into that XCD's L2 once, not once per row.
 template <class S>
 struct SliceOfRows {
     const S* A;  // first element of the slice in row 0
@@ -309,13 +311,16 @@ struct SliceOfRows {
 template <class D, int BATCH, bool VEC>
 __global__ void __launch_bounds__(kGroupWavesDev * 64) __attribute__((amdgpu_waves_per_eu(4)))
 gemv_splitk_partial_kernel(const typename D::storage* A, int64_t lda, float* ws, int64_t M,
-                           const typename D::storage* __restrict__ x, int K, int slice) {
-    const int s = blockIdx.y;
+                           const typename D::storage* __restrict__ x, int K, int slice,
+                           int splits) {
+    const uint32_t id = blockIdx.x;
+    const int s = (int)(id % (uint32_t)splits);
+    const int64_t m = id / (uint32_t)splits;
     const int64_t k0 = (int64_t)s * slice;
     const int64_t rest = (int64_t)K - k0;
     const int ks = rest < slice ? (int)rest : slice;
     group_body<D, kGroupWavesDev, BATCH, VEC>(
-        SliceOfRows<typename D::storage>{A + k0, lda, ws + s, (int)gridDim.y, M}, x + k0, ks);
+        SliceOfRows<typename D::storage>{A + k0, lda, ws + s, splits, M}, x + k0, ks, m);
 }
 
 // Split-K, pass 2: one wavefront per row adds the row's `splits` partials in

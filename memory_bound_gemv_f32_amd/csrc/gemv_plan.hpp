@@ -80,9 +80,12 @@ constexpr int mfma_lds_bytes() {
 // Chosen automatically for fewer than kSplitMaxRows rows of at least
 // kSplitMinRowLoads 16-byte loads (4 batches of the workgroup-per-row
 // family); below that the second launch (~2 µs) costs more than it saves.
-// Slices are at least kSplitMinSliceLoads loads and a whole number of loads
-// per lane.  Measured on MI355X: fp32 8×2^21 265 -> 22.6 µs, bf16 64×2^18
-// 20.7 -> 10.6 µs, while bf16 256×2^16 and 512×2^15 are faster unsplit.
+// Slices are at least kSplitMinSliceLoads loads, a whole number of 64-lane
+// loads, and their count a multiple of 8 when it is 8 or more (see the
+// pass-1 kernel: then every XCD serves whole slices of x).  Measured on
+// MI355X, the reduce launch included: fp32 8×2^21 265 -> 15.6 µs, fp32
+// 1×2^24 2147 -> 24.4 µs, bf16 64×2^18 20.7 -> 9.3 µs; bf16 256×2^16 and
+// 512×2^15 are faster unsplit.
 constexpr int64_t kSplitMaxRows = 256;
 constexpr int64_t kSplitMinRowLoads = 4 * kGroupWaves * kWave * kGroupBatch;
 constexpr int64_t kSplitMinSliceLoads = 512;
@@ -108,7 +111,7 @@ struct Plan {
     int lds_bytes = 0;
     int splits = 1;       // K-slices per row (split-K), else 1
     int slice_elems = 0;  // elements per slice (split-K), else K
-    int64_t grid = 0;     // workgroups (split-K: per slice)
+    int64_t grid = 0;     // workgroups (split-K: rows × slices)
 };
 
 inline int element_bytes(int dtype) { return dtype == F32 ? 4 : 2; }
@@ -286,21 +289,30 @@ inline int split_geometry(int dtype, int M, int K, int requested, int* splits, i
     if (requested == 0) {
         want = 1;
         if (M > 0 && M < kSplitMaxRows && loads >= kSplitMinRowLoads) {
-            const int64_t by_rows = kTargetGroups / M;
+            // below 8 rows x is not shared between rows, so each workgroup
+            // streams as many x bytes as A bytes: half as many workgroups
+            const int64_t by_rows = (M < 8 ? kTargetGroups / 2 : kTargetGroups) / M;
             const int64_t by_len = loads / kSplitMinSliceLoads;
             want = by_rows < by_len ? by_rows : by_len;
+            if (want >= 8) want -= want % 8;  // whole rounds of the 8 XCDs
             if (want < 2) want = 1;
         }
     }
     if (want > kSplitMaxSplits) want = kSplitMaxSplits;
     if (want < 1 || loads <= 1) want = 1;
-    int64_t slice_loads = ceil_div(loads, want);
-    if (requested == 0 && want > 1) {  // the same number of loads for every lane
-        const int64_t lanes = (int64_t)kGroupWaves * kWave;
-        slice_loads = ceil_div(slice_loads, lanes) * lanes;
+    int64_t slice_loads = 1, n = 1;
+    for (;;) {
+        slice_loads = ceil_div(loads, want);
+        if (requested == 0 && want > 1)  // whole wavefront-wide loads
+            slice_loads = ceil_div(slice_loads, (int64_t)kWave) * kWave;
+        if (slice_loads < 1) slice_loads = 1;
+        n = ceil_div(loads, slice_loads);
+        if (n < 1) n = 1;
+        // an automatic count of 8 or more stays a multiple of 8 (rounding
+        // the slice up can leave fewer slices than asked for)
+        if (requested != 0 || n < 8 || n % 8 == 0 || want <= 8) break;
+        want -= 8;
     }
-    int64_t n = ceil_div(loads, slice_loads < 1 ? 1 : slice_loads);
-    if (n < 1) n = 1;
     *splits = (int)n;
     *slice = n == 1 ? K : (int)(slice_loads * granule);
     return OK;
@@ -340,7 +352,8 @@ inline int make_split_plan(int dtype, int M, int K, bool vec, int requested, Pla
     p.lds_bytes = (int)(kGroupWaves * sizeof(float));
     p.splits = splits;
     p.slice_elems = slice;
-    p.grid = M;
+    p.grid = (int64_t)M * splits;  // one workgroup per (row, slice)
+    if (p.grid * p.block > 0xffffffffLL) return INVALID;  // HIP's 32-bit grid size
     p.passes = (int)per_lane;
     *out = p;
     return OK;

@@ -283,7 +283,8 @@ def test_splitk_workspace_size():
 def test_splitk_for_few_long_rows():
     """The small-M case: fewer than 256 rows of at least 8192 16-byte loads
     are cut into slices so that rows × slices approaches 1024 workgroups, each
-    slice at least 512 loads and a whole number of loads per lane."""
+    slice at least 512 loads and a whole number of 64-lane loads, and the
+    slice count a multiple of the 8 XCDs once it reaches 8."""
     for dtype, M, K in (("f32", 16, 1 << 20), ("f32", 8, 1 << 21), ("bf16", 64, 1 << 18),
                         ("f16", 1, 1 << 24), ("bf16", 100, 100000), ("f32", 255, 1 << 15),
                         ("bf16", 32, 65536)):
@@ -292,10 +293,11 @@ def test_splitk_for_few_long_rows():
         assert p["family"] == lg.FAMILY_SPLIT_K, (dtype, M, K)
         assert p["splits"] >= 2 and M * p["splits"] <= 1024
         assert (p["slice_elems"] * s) % 16 == 0
-        assert p["slice_elems"] * s >= 512 * 16 and (p["slice_elems"] * s // 16) % 256 == 0
+        assert p["slice_elems"] * s >= 512 * 16 and (p["slice_elems"] * s // 16) % 64 == 0
         assert (p["splits"] - 1) * p["slice_elems"] < K <= p["splits"] * p["slice_elems"]
-        assert p["grid"] == M and p["block"] == 256
-        per_lane = p["slice_elems"] * s // 16 // 256
+        assert p["splits"] < 8 or p["splits"] % 8 == 0
+        assert p["grid"] == M * p["splits"] and p["block"] == 256
+        per_lane = -(-p["slice_elems"] * s // 16 // 256)
         assert p["batch"] == min(8, 1 << (per_lane - 1).bit_length())
 
 
@@ -323,3 +325,30 @@ def test_splitk_requested_slices(dtype):
         if S > 1:
             assert sl % g == 0 and p["family"] == lg.FAMILY_SPLIT_K
     assert lg.plan_splitk(dtype, 7, 1000, splits=3)["slice_elems"] == -(-(-(-1000 // 3)) // g) * g
+
+
+def test_splitk_geometry_properties():
+    """Over many shapes: slices cover K exactly once, automatic counts of 8 or
+    more are multiples of 8, and the workspace matches rows × slices."""
+    import random
+    rnd = random.Random(7)
+    for _ in range(3000):
+        dtype = rnd.choice(["f32", "f16", "bf16"])
+        M = rnd.choice([0, 1, 2, 3, 7, 8, 31, 64, 100, 255, 256, 1000, rnd.randint(1, 300)])
+        K = rnd.choice([0, 1, 15, 4096, 8192 * 8, rnd.randint(1, 1 << 22), rnd.randint(1 << 16, 1 << 24)])
+        splits = rnd.choice([0, 0, 0, 1, 2, 3, 8, 100, 5000])
+        p = lg.plan_splitk(dtype, M, K, splits=splits, A_addr=ALIGNED, x_addr=ALIGNED)
+        S, sl = p["splits"], p["slice_elems"]
+        assert S >= 1 and S <= 1024
+        if S == 1:
+            assert sl == K and p["family"] != lg.FAMILY_SPLIT_K
+            assert lg.splitk_workspace_size(dtype, M, K, splits) == 0
+            continue
+        assert p["family"] == lg.FAMILY_SPLIT_K
+        assert (S - 1) * sl < K <= S * sl
+        assert (sl * (4 if dtype == "f32" else 2)) % 16 == 0
+        if splits == 0:
+            assert M < 256 and (S < 8 or S % 8 == 0) and M * S <= 1024
+        else:
+            assert S <= splits
+        assert lg.splitk_workspace_size(dtype, M, K, splits) == 4 * M * S

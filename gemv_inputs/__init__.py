@@ -298,6 +298,108 @@ def make_fused_gate_up() -> tuple[Case, Case]:
     return gate, up
 
 
+# ---------------------------------------------------------------------------
+# weight-only int8 problems: int8 weights, one fp32 scale per row, float x
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class Q8Case:
+    """Q is (M, ldq) int8 row-major (columns K..ldq-1 are padding, filled
+    with -128 so that a stray read changes a result), scale is float32 (M,),
+    X is (nvec, K) in the stored encoding of ``xdtype``, bias float32 (M,)
+    or None."""
+
+    name: str
+    xdtype: str
+    M: int
+    K: int
+    Q: np.ndarray
+    scale: np.ndarray
+    X: np.ndarray
+    bias: np.ndarray | None
+    ldq: int
+    nvec: int = 1
+    seed: int | None = None
+
+    def algorithmic_bytes(self) -> int:
+        return q8_bytes(self.xdtype, self.M, self.K, self.nvec, self.bias is not None)
+
+
+def q8_bytes(xdtype: str, M: int, K: int, nvec: int = 1, has_bias: bool = False) -> int:
+    """Q once (1 byte per weight), the scales, x once, y once (fp32)."""
+    s = ELEMENT_BYTES[xdtype]
+    return M * K + 4 * M + nvec * K * s + 4 * M * nvec + (4 * M if has_bias else 0)
+
+
+def _pad_q(q: np.ndarray, ldq: int) -> np.ndarray:
+    M, K = q.shape
+    out = np.full((M, ldq), -128, dtype=np.int8)
+    out[:, :K] = q
+    return out
+
+
+def make_q8_random(xdtype: str, M: int, K: int, *, seed: int, nvec: int = 1,
+                   ldq: int | None = None, bias: bool = False, q_std: float = 32.0,
+                   w_std: float = 0.02, name: str | None = None) -> Q8Case:
+    """Bell-shaped int8 weights (normal with standard deviation ``q_std``,
+    rounded and clipped to [-127, 127], as weights of standard deviation
+    ``w_std`` look after a per-row absmax scaling), per-row scales near
+    4·w_std/127, x ~ N(0, 1) in ``xdtype``."""
+    rng = np.random.default_rng(seed)
+    ldq = K if ldq is None else ldq
+    q = np.clip(np.rint(rng.standard_normal((M, K)) * q_std), -127, 127).astype(np.int8)
+    scale = to_f32(4.0 * w_std / 127.0 * rng.uniform(0.8, 1.2, size=M))
+    x = rng.standard_normal((nvec, K))
+    b = rng.standard_normal(M) if bias else None
+    return Q8Case(name or f"q8_{xdtype}_{M}x{K}", xdtype, M, K, _pad_q(q, ldq), scale,
+                  np.ascontiguousarray(quantise(xdtype, x)), None if b is None else to_f32(b),
+                  ldq, nvec, seed)
+
+
+def make_q8_integer(xdtype: str, M: int, K: int, *, seed: int, nvec: int = 1,
+                    ldq: int | None = None, bias: bool = False, lo: int = -8,
+                    hi: int = 8) -> Q8Case:
+    """Every int8 value in Q, integer x in [lo, hi], power-of-two scales
+    2^-e (e in 0..6) and integer bias: for K·128·max(|lo|, |hi|) < 2^24
+    every partial sum is exact in fp32, and so is the scaled result."""
+    rng = np.random.default_rng(seed)
+    ldq = K if ldq is None else ldq
+    q = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+    scale = to_f32(2.0 ** -rng.integers(0, 7, size=M))
+    x = rng.integers(lo, hi + 1, size=(nvec, K)).astype(np.float64)
+    b = rng.integers(lo, hi + 1, size=M).astype(np.float64) if bias else None
+    return Q8Case(f"q8int_{xdtype}_{M}x{K}", xdtype, M, K, _pad_q(q, ldq), scale,
+                  np.ascontiguousarray(quantise(xdtype, x)), None if b is None else to_f32(b),
+                  ldq, nvec, seed)
+
+
+def make_q8_worked_example(xdtype: str, bias: bool = False) -> Q8Case:
+    """The M=3, K=1024 walk-through with int8 weights Q[m,k] = (m+1)(-1)^k,
+    x[k] = k mod 8 and scales 2^-(m+1)."""
+    M, K = 3, 1024
+    k = np.arange(K)
+    q = np.array([(m + 1) * (-1.0) ** k for m in range(M)]).astype(np.int8)
+    x = (k % 8).astype(np.float64)[None, :]
+    scale = to_f32([2.0 ** -(m + 1) for m in range(M)])
+    b = to_f32([0.5, -0.25, 1.0]) if bias else None
+    return Q8Case(f"q8_worked_{xdtype}", xdtype, M, K, _pad_q(q, K), scale,
+                  np.ascontiguousarray(quantise(xdtype, x)), b, K)
+
+
+# the int8 forms of the decode sweep's q/o and gate/up shapes: int8 weights,
+# fp16 (q/o) or bf16 (gate/up) activations
+Q8_WORKLOADS = {
+    # name: (xdtype, M, K, seed)
+    "q8_f16_4096": ("f16", 4096, 4096, 68),
+    "q8_bf16_14336x4096": ("bf16", 14336, 4096, 69),
+}
+
+
+def make_q8_workload(name: str) -> Q8Case:
+    xdtype, M, K, seed = Q8_WORKLOADS[name]
+    return make_q8_random(xdtype, M, K, seed=seed, name=name)
+
+
 def fused_qkv_bytes() -> int:
     """A of q, k, v once, x once, y of all three once."""
     M = sum(SWEEP_SHAPES[n][0] for n in ("q", "k", "v"))

@@ -12,7 +12,9 @@ row m of A with x (page "SGEMV CUDAä»£ç å­¦ä¹ ", section "é—®é¢˜å®šä¹‰: ä¸€è¡Œä
 plus an optional per-row bias that may be absent (page "ç¬¬ 3 è¯¾ï¼šGEMV ä¸Žè¡Œçº§
 å¹¶è¡Œ", sections "æ ¸å¿ƒå¿ƒæ™ºæ¨¡åž‹" item 1 and "3. æ­£ç¡®æ€§è¾¹ç•Œä¸ŽæŒ‡é’ˆå®‰å…¨æ€§"), for one
 or several right-hand vectors (page "GEMMã€GEMVã€dtype ä¸Žç®—æœ¯å¼ºåº¦", section
-"å¯è¿è¡Œ CUDA å®žéªŒ", the m = 16 small-batch run).
+"å¯è¿è¡Œ CUDA å®žéªŒ", the m = 16 small-batch run); the gated SiLU pair and the
+weight-only int8 form with a per-row scale (the lqnn.cn NPU MatMul essay,
+sections 1.1, 1.2, 4.2, 5.1, 5.2).
 
 Pins: every function here is pinned by tests under ``tests/`` that do not
 re-derive it from this code (closed forms, exact integer arithmetic with
@@ -79,6 +81,12 @@ class Oracle:
         g.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                       ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 5
         self._gated = g
+        q = self._lib.oracle_gemv_q8
+        q.restype = ctypes.c_int
+        q.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                      ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                      ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+        self._q8 = q
         self._lib.oracle_num_threads.restype = ctypes.c_int
 
     def num_threads(self) -> int:
@@ -146,6 +154,41 @@ class Oracle:
         return tuple(out)
 
 
+    def gemv_q8(self, xdtype: str, Q: np.ndarray, scale, X: np.ndarray, bias, M: int,
+                K: int, ldq: int | None = None, nvec: int = 1, ldx: int | None = None):
+        """Weight-only int8 GEMV: Y[j, m] = scale[m]Â·sum_k Q[m,k]Â·X[j,k]
+        (+ bias[m]), ABS[j, m] = |scale[m]|Â·sum_k |Q[m,k]Â·X[j,k]|, both
+        float64 of shape (nvec, M).  ``Q`` is int8 (row stride ``ldq``),
+        ``scale`` float32 (M,), X in the stored encoding of ``xdtype``."""
+        ldq = K if ldq is None else ldq
+        ldx = K if ldx is None else ldx
+        want = np.float32 if xdtype == "f32" else np.uint16
+        Q = np.ascontiguousarray(Q, dtype=np.int8).reshape(-1).view(np.uint8)
+        X = np.ascontiguousarray(X, dtype=want).reshape(-1)
+        scale = np.ascontiguousarray(scale, dtype=np.float32).reshape(-1)
+        if M > 0 and K > 0:
+            if Q.size < (M - 1) * ldq + K:
+                raise ValueError("Q is smaller than its shape implies")
+            if X.size < (nvec - 1) * ldx + K:
+                raise ValueError("X is smaller than its shape implies")
+        if scale.size < M:
+            raise ValueError("scale is shorter than M")
+        if bias is not None:
+            bias = np.ascontiguousarray(bias, dtype=np.float32).reshape(-1)
+            if bias.size < M:
+                raise ValueError("bias is shorter than M")
+        Y = np.empty((nvec, max(M, 0)), dtype=np.float64)
+        ABS = np.empty_like(Y)
+        rc = self._q8(DTYPE_CODES[xdtype], Q.ctypes.data if Q.size else None, ldq,
+                      scale.ctypes.data if scale.size else None,
+                      X.ctypes.data if X.size else None, ldx,
+                      bias.ctypes.data if bias is not None else None,
+                      M, K, nvec, Y.ctypes.data, ABS.ctypes.data)
+        if rc != 0:
+            raise ValueError(f"oracle_gemv_q8 rejected the arguments (rc={rc})")
+        return Y, ABS
+
+
 _default: Oracle | None = None
 
 
@@ -163,3 +206,7 @@ def gemv(*args, **kwargs):
 
 def gated_silu(*args, **kwargs):
     return default().gated_silu(*args, **kwargs)
+
+
+def gemv_q8(*args, **kwargs):
+    return default().gemv_q8(*args, **kwargs)

@@ -26,6 +26,14 @@
  *     activation).  The essay names no activation; SiLU,
  *     silu(g) = g / (1 + e^(-g)), is the gated one of the decode shapes here
  *     (gate and up projections of equal shape).
+ *   - weight-only int8: y[m] = scale[m] · Σ_k q[m,k]·x[k] (+ bias[m]), the
+ *     weights stored as int8 with one fp32 scale per output row
+ *     ("per-channel"), the activations still in a float encoding and the
+ *     accumulation wide: the lqnn.cn NPU MatMul essay, sections 1.2
+ *     (quantised MatMul: int8 weights, fp16 activations, fp32 accumulator),
+ *     4.2 (int8 weights with a per-channel scale) and 5.2 (bytes halve,
+ *     fp32 accumulation).  No zero point: the scale alone is the
+ *     per-channel compensation the essay applies.
  *
  * The oracle is that definition written out: every stored element is decoded
  * exactly to double, products and the running sum are taken in double, in
@@ -127,6 +135,47 @@ int oracle_gemv(int dtype, const void *A, int64_t lda, const void *X,
             if (bias != NULL) sum += (double)bias[m];
             Y[j * M + m] = sum;
             ABS[j * M + m] = abs_sum;
+        }
+    }
+    return 0;
+}
+
+/* A two's-complement byte as a double: bytes 0..127 are themselves, bytes
+ * 128..255 are byte - 256. */
+static double decode_i8(uint8_t b) {
+    return b < 128 ? (double)b : (double)b - 256.0;
+}
+
+/* Y[j*M+m] = scale[m] · Σ_k q[m,k]·x_j[k] (+ bias[m]) and
+ * ABS[j*M+m] = |scale[m]| · Σ_k |q[m,k]·x_j[k]|, in double: the sum over k
+ * first, in k order, then the scale, then the bias.  Q is row-major int8
+ * with row stride ldq (bytes K..ldq-1 of a row never read); x_j is column j
+ * of X (stride ldx) in encoding xdtype; scale has M fp32 values.  Returns 0,
+ * or -1 for bad arguments. */
+int oracle_gemv_q8(int xdtype, const uint8_t *Q, int64_t ldq, const float *scale,
+                   const void *X, int64_t ldx, const float *bias, int64_t M,
+                   int64_t K, int64_t nvec, double *Y, double *ABS) {
+    if (xdtype < ORACLE_F32 || xdtype > ORACLE_BF16) return -1;
+    if (M < 0 || K < 0 || nvec < 1 || ldq < K || ldx < K) return -1;
+    if (M > 0 && (Y == NULL || ABS == NULL || scale == NULL)) return -1;
+    if (M > 0 && K > 0 && (Q == NULL || X == NULL)) return -1;
+
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const double s = (double)scale[m];
+        for (int64_t j = 0; j < nvec; ++j) {
+            double sum = 0.0;
+            double abs_sum = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double q = decode_i8(Q[m * ldq + k]);
+                const double x = load_elem(xdtype, X, j * ldx + k);
+                sum += q * x;
+                abs_sum += fabs(q * x);
+            }
+            double y = s * sum;
+            if (bias != NULL) y += (double)bias[m];
+            Y[j * M + m] = y;
+            ABS[j * M + m] = fabs(s) * abs_sum;
         }
     }
     return 0;

@@ -11,6 +11,7 @@ the real oracle, and against copies with planted mistakes that must fail.
 
 from __future__ import annotations
 
+import dataclasses
 import json
 import math
 from fractions import Fraction
@@ -293,6 +294,124 @@ def pin_gated_silu_zero_gate(oracle):
         assert np.all(H == 0) and np.any(G != 0)
 
 
+# ---------------------------------------------------------------------------
+# weight-only int8 (int8 weights, per-row fp32 scale, float activations)
+# ---------------------------------------------------------------------------
+
+def _run_q8(oracle, c, **kw):
+    return oracle.gemv_q8(c.xdtype, c.Q, c.scale, c.X, c.bias, c.M, c.K, ldq=c.ldq,
+                          nvec=c.nvec, **kw)
+
+
+def pin_q8_worked_example(oracle):
+    """The M=3, K=1024 walk-through with int8 weights (m+1)(-1)^k: the sum
+    is -512 (m+1) as for the float case, scaled by 2^-(m+1), so
+    y = [-256, -256, -192] (plus the bias); sum|q·x| = 3584 (m+1) scaled
+    likewise."""
+    for xdtype in gi.DTYPES:
+        for with_bias in (False, True):
+            c = gi.make_q8_worked_example(xdtype, bias=with_bias)
+            Y, S = _run_q8(oracle, c)
+            want = [-256.0, -256.0, -192.0]
+            if with_bias:
+                want = [w + b for w, b in zip(want, (0.5, -0.25, 1.0))]
+            assert list(Y[0]) == want, (xdtype, with_bias, Y[0])
+            assert list(S[0]) == [3584 * (m + 1) / 2 ** (m + 1) for m in range(3)]
+
+
+def pin_q8_every_byte(oracle):
+    """All 256 int8 bit patterns, one per row at a random column (the rest
+    of the row zero), with power-of-two scales: y[m] = scale[m]·q·x[col]
+    exactly, q taken from numpy's int8 view of the byte."""
+    rng = np.random.default_rng(3)
+    M, K = 256, 37
+    Q = np.zeros((M, K + 3), dtype=np.int8)
+    cols = rng.integers(0, K, size=M)
+    Q[np.arange(M), cols] = np.arange(256, dtype=np.uint8).view(np.int8)
+    Q[:, K:] = 127                                   # padding, never read
+    scale = (2.0 ** rng.integers(-4, 5, size=M)).astype(np.float32)
+    for xdtype in gi.DTYPES:
+        X = gi.quantise(xdtype, rng.integers(-64, 65, size=(1, K)).astype(np.float64))
+        Y, S = oracle.gemv_q8(xdtype, Q, scale, X, None, M, K, ldq=K + 3)
+        xv = lib_decode(xdtype, X)[0]
+        qv = np.arange(256, dtype=np.uint8).view(np.int8).astype(np.float64)
+        want = scale.astype(np.float64) * qv * xv[cols]
+        assert np.array_equal(Y[0], want), xdtype
+        assert np.array_equal(S[0], np.abs(want)), xdtype
+
+
+def pin_q8_numpy_float64(oracle):
+    """numpy's float64 product of the int8 matrix (as float64) with x, times
+    the scale, plus the bias, on random shapes with ldq > K and several
+    vectors: agreement to 1e-12 of |scale|·sum|q·x|."""
+    for xdtype, (M, K, nvec) in (("f32", (99, 1000, 1)), ("f16", (70, 777, 4)),
+                                 ("bf16", (33, 4100, 2))):
+        c = gi.make_q8_random(xdtype, M, K, seed=9, nvec=nvec, ldq=K + 5, bias=True)
+        Y, S = _run_q8(oracle, c)
+        Qf = c.Q[:, :K].astype(np.float64)
+        X = lib_decode(xdtype, c.X)
+        s = c.scale.astype(np.float64)
+        want = (Qf @ X.T).T * s[None, :] + c.bias.astype(np.float64)[None, :]
+        wantS = (np.abs(Qf) @ np.abs(X).T).T * np.abs(s)[None, :]
+        assert Y.shape == (nvec, M)
+        assert np.all(np.abs(Y - want) <= 1e-12 * wantS + 1e-300), xdtype
+        assert np.allclose(S, wantS, rtol=1e-12, atol=0), xdtype
+
+
+def pin_q8_brute_force_exact(oracle):
+    """Tiny shapes against exact rational arithmetic: the double result lies
+    within (K+3)·2^-53 of |scale|·sum|terms| (+ 2^-53 |y|) of the exact value."""
+    u = 2.0 ** -53
+    seed = 400
+    for xdtype in gi.DTYPES:
+        for M, K in ((1, 0), (1, 1), (2, 3), (3, 9), (4, 16), (2, 31)):
+            for with_bias, nvec, extra in ((False, 1, 0), (True, 2, 4)):
+                seed += 1
+                c = gi.make_q8_random(xdtype, M, K, seed=seed, nvec=nvec, ldq=K + extra,
+                                      bias=with_bias, q_std=80.0)
+                Y, S = _run_q8(oracle, c)
+                X = lib_decode(xdtype, c.X)
+                for j in range(nvec):
+                    for m in range(M):
+                        terms = [Fraction(int(c.Q[m, k])) * Fraction(float(X[j, k]))
+                                 for k in range(K)]
+                        sc = Fraction(float(c.scale[m]))
+                        exact = sc * sum(terms, Fraction(0))
+                        if with_bias:
+                            exact += Fraction(float(c.bias[m]))
+                        eS = abs(sc) * sum((abs(t) for t in terms), Fraction(0))
+                        bound = (K + 3) * u * float(eS) + u * abs(float(exact))
+                        assert float(abs(Fraction(float(Y[j, m])) - exact)) <= bound, (xdtype, M, K)
+                        assert float(abs(Fraction(float(S[j, m])) - eS)) <= (K + 3) * u * float(eS)
+
+
+def pin_q8_scale_and_bias(oracle):
+    """Scale 0 gives y = bias exactly; negating the scales negates y exactly
+    (no bias); sum|q·x| carries |scale|."""
+    for xdtype in gi.DTYPES:
+        c = gi.make_q8_random(xdtype, 20, 300, seed=12, bias=True)
+        zero = dataclasses.replace(c, scale=np.zeros(20, dtype=np.float32))
+        Y, S = _run_q8(oracle, zero)
+        assert np.array_equal(Y[0], c.bias.astype(np.float64)) and not S.any()
+        nb = dataclasses.replace(c, bias=None)
+        neg = dataclasses.replace(nb, scale=-c.scale)
+        Yp, Sp = _run_q8(oracle, nb)
+        Yn, Sn = _run_q8(oracle, neg)
+        assert np.array_equal(Yn, -Yp) and np.array_equal(Sn, Sp)
+
+
+def pin_q8_rejects_bad_arguments(oracle):
+    c = gi.make_q8_random("f16", 4, 8, seed=1)
+    for kw in (dict(M=-1), dict(K=-1), dict(ldq=7)):
+        args = dict(M=4, K=8, ldq=8)
+        args.update(kw)
+        try:
+            oracle.gemv_q8("f16", c.Q, c.scale, c.X, None, args["M"], args["K"], ldq=args["ldq"])
+        except ValueError:
+            continue
+        raise AssertionError(f"accepted {kw}")
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_identity,
@@ -306,6 +425,12 @@ ALL_PINS = [
     pin_worked_example_scaling,
     pin_gated_silu_against_torch,
     pin_gated_silu_zero_gate,
+    pin_q8_worked_example,
+    pin_q8_every_byte,
+    pin_q8_numpy_float64,
+    pin_q8_brute_force_exact,
+    pin_q8_scale_and_bias,
+    pin_q8_rejects_bad_arguments,
 ]
 
 

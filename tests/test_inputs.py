@@ -75,3 +75,18 @@ def test_byte_model_matches_pages():
     # x@W with m rows and fp32 output instead of s-byte output
     m, k, n, s = 16, 4096, 4096, 2
     assert gi.workload_bytes("f16", n, k, m) == (m * k + k * n) * s + 4 * m * n
+
+
+def test_q8_generators():
+    c = gi.make_q8_random("bf16", 10, 100, seed=1, ldq=104, bias=True, nvec=2)
+    assert c.Q.dtype == np.int8 and c.Q.shape == (10, 104)
+    assert np.all(c.Q[:, 100:] == -128) and np.abs(c.Q[:, :100].astype(int)).max() <= 127
+    assert c.scale.dtype == np.float32 and np.all(c.scale > 0)
+    assert c.X.shape == (2, 100) and c.X.dtype == np.uint16
+    assert c.algorithmic_bytes() == 10 * 100 + 4 * 10 + 2 * 100 * 2 + 4 * 10 * 2 + 4 * 10
+    i = gi.make_q8_integer("f16", 300, 50, seed=2)
+    assert set(np.unique(i.Q)) <= set(range(-128, 128)) and i.Q.min() == -128 and i.Q.max() == 127
+    assert np.all(np.log2(i.scale) == np.round(np.log2(i.scale)))
+    w = gi.make_q8_workload("q8_f16_4096")
+    assert (w.M, w.K, w.xdtype) == (4096, 4096, "f16")
+    assert w.algorithmic_bytes() == 4096 * 4096 + 4 * 4096 + 2 * 4096 + 4 * 4096

@@ -59,6 +59,14 @@ MUTANTS = [
     ("silu_no_up", r"\)\) \* U\[m\];", "));"),
     ("silu_as_sigmoid", r"H\[m\] = g / ", "H[m] = 1.0 / "),
     ("gated_swapped", r"oracle_gemv\(dtype, Au,", "oracle_gemv(dtype, Ag,"),
+    ("q8_unsigned", r"\(double\)b - 256\.0", "(double)b"),
+    ("q8_scale_dropped", r"double y = s \* sum;", "double y = sum;"),
+    ("q8_scale_first_row", r"\(double\)scale\[m\]", "(double)scale[0]"),
+    ("q8_bias_scaled", r"double y = s \* sum;\n            if \(bias != NULL\) y \+= \(double\)bias\[m\];",
+     "double y = sum;\n            if (bias != NULL) y += (double)bias[m];\n            y *= s;"),
+    ("q8_abs_unscaled", r"fabs\(s\) \* abs_sum", "abs_sum"),
+    ("q8_ldq_ignored", r"Q\[m \* ldq \+ k\]", "Q[m * K + k]"),
+    ("q8_accepts_ldq_below_K", r"ldq < K \|\| ", ""),
 ]
 
 

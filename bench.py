@@ -271,6 +271,42 @@ class FusedRotation:
         return worst <= 1.0, worst
 
 
+class Q8Rotation:
+    """R device sets of a weight-only int8 problem (int8 Q, fp32 scales, x of
+    a float type): y = scale ⊙ (Q·x) through gemv_q8_*."""
+
+    def __init__(self, name, gi, torch, min_bytes=2 * INFINITY_CACHE_BYTES):
+        import numpy as np
+        self.case = c = gi.make_q8_workload(name)
+        self.R = max(2, math.ceil(min_bytes / c.Q.nbytes) + 1)
+        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[c.xdtype]
+        hQ = torch.from_numpy(np.ascontiguousarray(c.Q))
+        hx = (torch.from_numpy(c.X[0].astype(np.float32)) if c.xdtype == "f32"
+              else torch.from_numpy(c.X[0].view(np.int16)).view(tdt))
+        self.scale = torch.from_numpy(c.scale).to("cuda")
+        self.sets = [(hQ.to("cuda"), hx.to("cuda"),
+                      torch.empty(c.M, dtype=torch.float32, device="cuda")) for _ in range(self.R)]
+
+    def callers(self, lg, stream_handle):
+        c = self.case
+        f = {"f32": lg.gemv_q8_f32, "f16": lg.gemv_q8_f16, "bf16": lg.gemv_q8_bf16}[c.xdtype]
+        return [(f, (Q.data_ptr(), c.ldq, self.scale.data_ptr(), x.data_ptr(), None,
+                     y.data_ptr(), c.M, c.K, stream_handle)) for Q, x, y in self.sets]
+
+    def sanity_check(self, torch):
+        """Set 0 against torch's fp64 product on the device, within
+        1e-5·|scale|·Σ|q·x| + 1e-6 per row."""
+        c = self.case
+        Q, x, y = self.sets[0]
+        Qd = Q.view(c.M, c.ldq)[:, :c.K].double()
+        xd = x.double()
+        s = self.scale.double()
+        ref = s * (Qd @ xd)
+        bound = 1e-5 * s.abs() * (Qd.abs() @ xd.abs()) + 1e-6
+        worst = float(((y.double() - ref).abs() / bound).max())
+        return worst <= 1.0, worst
+
+
 def call(fn_args):
     f, args = fn_args
     rc = f(*args)
@@ -361,9 +397,15 @@ def sanity_check(case, rot, torch):
 
 def measure_shape(name, torch, lg, gi, steps):
     fused = name in FUSED
+    q8 = name in gi.Q8_WORKLOADS
     if fused:
         rot = FusedRotation(name, gi, torch)
         nbytes, dtype, M, K, nvec, has_bias = rot.bytes, rot.dtype, rot.M, rot.K, 1, False
+    elif q8:
+        rot = Q8Rotation(name, gi, torch)
+        c = rot.case
+        nbytes, dtype, M, K, nvec, has_bias = c.algorithmic_bytes(), f"int8 x {c.xdtype}", \
+            c.M, c.K, 1, False
     else:
         case = gi.make_workload(name)
         rot = Rotation(case, torch, splitk=name in gi.SPLITK_WORKLOADS)
@@ -373,7 +415,14 @@ def measure_shape(name, torch, lg, gi, steps):
     ms, n = loop.time(warmup=loop.per), steps
     fns = rot.callers(lg, torch.cuda.current_stream().cuda_stream)
     eager_ms = time_eager(torch, fns, steps, warmup=rot.R)
-    if fused:
+    if q8:
+        call(fns[0])
+        torch.cuda.synchronize()
+        ok, worst = rot.sanity_check(torch)
+        Q0, x0, _ = rot.sets[0]
+        plan = lg.plan_q8(c.xdtype, M, K, c.ldq, Q0.data_ptr(), x0.data_ptr())
+        family = lg.FAMILY_NAMES[plan["family"]] + " (int8 weights)"
+    elif fused:
         call(fns[0])
         torch.cuda.synchronize()
         ok, worst = rot.sanity_check(torch)
@@ -397,7 +446,7 @@ def measure_shape(name, torch, lg, gi, steps):
                            rot.A[0].data_ptr(), rot.X[0].data_ptr())
             family = lg.FAMILY_NAMES[plan["family"]]
     single_us = None
-    if not fused and rot.splitk:  # the same problem in one pass, for comparison
+    if not fused and not q8 and rot.splitk:  # the same problem in one pass, for comparison
         rot.splitk = False
         single = GraphLoop(torch, rot, lg, steps, per=rot.R * max(1, 64 // rot.R))
         single_us = round(1e3 * single.time(warmup=single.per) / steps, 3)
@@ -530,7 +579,8 @@ def main():
 
     shapes = {}
     names = [] if args.shapes == "none" else (
-        list(gi.WORKLOADS) + list(FUSED) if args.shapes == "all" else args.shapes.split(","))
+        list(gi.WORKLOADS) + list(FUSED) + list(gi.Q8_WORKLOADS) if args.shapes == "all"
+        else args.shapes.split(","))
     for name in names:
         shapes[name] = measure_shape(name, torch, lg, gi, args.shape_steps)
         log(f"  {name}: {shapes[name]}")

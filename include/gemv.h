@@ -6,6 +6,7 @@
  *   several y_i = A_i·x in one launch gemv_multi_*
  *   h = silu(A_gate·x) ⊙ (A_up·x)     gemv_gate_up_silu_*
  *   y = A·x for few, long rows        gemv_splitk_* (caller's workspace)
+ *   y = scale ⊙ (Q·x), int8 Q         gemv_q8_f32 / gemv_q8_f16 / gemv_q8_bf16
  *
  * The operation.  Output m is the dot product of row m of A with x (page
  * "SGEMV CUDA代码学习", section "问题定义: 一行一个点积": A is M×K, x is K×1,
@@ -203,6 +204,34 @@ gemv_status_t gemv_splitk_bf16(const uint16_t *A, int lda, const uint16_t *x,
                                size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Weight-only int8.  The lqnn.cn NPU MatMul essay (sections 1.2, 4.2 and
+ * 5.2) stores weights as int8 with a per-channel scale while activations
+ * stay in floating point and the accumulator is fp32: at decode the weight
+ * bytes halve against fp16/bf16, and the GEMV is bound by those bytes.
+ *
+ *   y[m] = scale[m] · Σ_k Q[m,k]·x[k] (+ bias[m])
+ *
+ * Q     row-major int8 (two's complement), element (m, k) at Q[m·ldq + k],
+ *       ldq >= K (bytes K..ldq-1 of a row never read).  No zero point.
+ * scale M fp32 values, one per row, applied after the row's sum.
+ * x     K elements of the float type in the name (fp32 words, binary16 or
+ *       bfloat16 bit patterns).
+ * Products q·x are exact in fp32 and summed in fp32 in the library's own
+ * order; |y - exact| <= 1e-5·|scale[m]|·Σ_k|Q[m,k]·x[k]| + 1e-6.
+ * Errors as for gemv_*, plus a NULL scale when M > 0.  16-byte aligned Q,
+ * x and ldq select the widest loads; any other alignment works.
+ * ------------------------------------------------------------------------ */
+gemv_status_t gemv_q8_f32(const int8_t *Q, int ldq, const float *scale,
+                          const float *x, const float *bias, float *y, int M,
+                          int K, hipStream_t stream);
+gemv_status_t gemv_q8_f16(const int8_t *Q, int ldq, const float *scale,
+                          const uint16_t *x, const float *bias, float *y,
+                          int M, int K, hipStream_t stream);
+gemv_status_t gemv_q8_bf16(const int8_t *Q, int ldq, const float *scale,
+                           const uint16_t *x, const float *bias, float *y,
+                           int M, int K, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Introspection and testing.  These do not change what the entry points
  * above compute; they expose how the library maps a problem onto the GPU so
  * that the mapping can be checked without a GPU and every kernel family can
@@ -257,6 +286,17 @@ gemv_status_t gemv_plan(gemv_dtype_t dtype, int M, int K, int lda, int nvec,
 gemv_status_t gemv_plan_splitk(gemv_dtype_t dtype, int M, int K, int lda,
                                int splits, const void *A, const void *x,
                                gemv_plan_t *plan);
+
+/* The mapping gemv_q8_* would launch for x of type xdtype (or a forced
+ * family: rows per wavefront, wave per row or workgroup per row), and a run
+ * with a forced family; same contracts as the entry points. */
+gemv_status_t gemv_plan_q8(gemv_dtype_t xdtype, int M, int K, int ldq,
+                           const void *Q, const void *x, int family,
+                           gemv_plan_t *plan);
+gemv_status_t gemv_q8_run_family(gemv_dtype_t xdtype, int family,
+                                 const int8_t *Q, int ldq, const float *scale,
+                                 const void *x, const float *bias, float *y,
+                                 int M, int K, hipStream_t stream);
 
 /* Run with a forced family (GEMV_FAMILY_AUTO = what the entry points do).
  * Same arguments, validation and results contract as the entry points;

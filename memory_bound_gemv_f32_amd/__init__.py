@@ -9,10 +9,10 @@ Two levels:
 
 * the C ABI under the same names (``gemv_f32``, ``gemv_f16``, ``gemv_bf16``,
   ``gemv_batched_*``, ``gemv_multi_*``, ``gemv_gate_up_silu_*``,
-  ``gemv_splitk_*``, ``gemv_plan``, ``gemv_run_family``, ...), taking integer
+  ``gemv_splitk_*``, ``gemv_q8_*``, ``gemv_plan``, ``gemv_run_family``, ...), taking integer
   addresses and returning the ``gemv_status_t`` code;
 * tensor helpers ``gemv``, ``gemv_batched``, ``gemv_multi``,
-  ``gemv_gate_up_silu`` and ``gemv_splitk`` that check dtype, shape,
+  ``gemv_gate_up_silu``, ``gemv_splitk`` and ``gemv_q8`` that check dtype, shape,
   strides and device, call the matching entry point on
   ``torch.cuda.current_stream()`` and raise ``GemvError`` on a failure code.
 
@@ -120,6 +120,11 @@ gemv_splitk_workspace_size = _bind("gemv_splitk_workspace_size", [_i, _i, _i, _i
 gemv_splitk_f32 = _bind("gemv_splitk_f32", [_vp, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _st])
 gemv_splitk_f16 = _bind("gemv_splitk_f16", [_vp, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _st])
 gemv_splitk_bf16 = _bind("gemv_splitk_bf16", [_vp, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _st])
+gemv_q8_f32 = _bind("gemv_q8_f32", [_vp, _i, _vp, _vp, _vp, _vp, _i, _i, _st])
+gemv_q8_f16 = _bind("gemv_q8_f16", [_vp, _i, _vp, _vp, _vp, _vp, _i, _i, _st])
+gemv_q8_bf16 = _bind("gemv_q8_bf16", [_vp, _i, _vp, _vp, _vp, _vp, _i, _i, _st])
+gemv_q8_run_family = _bind("gemv_q8_run_family", [_i, _i, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _st])
+gemv_plan_q8 = _bind("gemv_plan_q8", [_i, _i, _i, _i, _vp, _vp, _i, ctypes.POINTER(GemvPlan)])
 gemv_plan = _bind("gemv_plan", [_i, _i, _i, _i, _i, _vp, _vp, _i, ctypes.POINTER(GemvPlan)])
 gemv_plan_splitk = _bind("gemv_plan_splitk", [_i, _i, _i, _i, _i, _vp, _vp, ctypes.POINTER(GemvPlan)])
 gemv_run_family = _bind("gemv_run_family", [_i, _i, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _st])
@@ -130,7 +135,9 @@ EXPORTED = ("gemv_status_string", "gemv_last_hip_error",
             "gemv_multi_f16", "gemv_multi_bf16", "gemv_gate_up_silu_f32",
             "gemv_gate_up_silu_f16", "gemv_gate_up_silu_bf16",
             "gemv_splitk_workspace_size", "gemv_splitk_f32", "gemv_splitk_f16",
-            "gemv_splitk_bf16", "gemv_plan", "gemv_plan_splitk", "gemv_run_family")
+            "gemv_splitk_bf16", "gemv_q8_f32", "gemv_q8_f16", "gemv_q8_bf16",
+            "gemv_q8_run_family", "gemv_plan_q8", "gemv_plan", "gemv_plan_splitk",
+            "gemv_run_family")
 
 
 class GemvError(RuntimeError):
@@ -161,6 +168,18 @@ def plan_splitk(dtype: str, M: int, K: int, lda: int | None = None, splits: int 
                           A_addr, x_addr, ctypes.byref(out))
     if rc != GEMV_SUCCESS:
         raise GemvError(rc, "gemv_plan_splitk")
+    return out.as_dict()
+
+
+def plan_q8(xdtype: str, M: int, K: int, ldq: int | None = None, Q_addr: int = 0,
+            x_addr: int = 0, family: int = FAMILY_AUTO) -> dict:
+    """The mapping gemv_q8_* would launch for int8 weights and x of type
+    ``xdtype`` (host-only)."""
+    out = GemvPlan()
+    rc = gemv_plan_q8(DTYPE_CODES[xdtype], M, K, K if ldq is None else ldq, Q_addr, x_addr,
+                      family, ctypes.byref(out))
+    if rc != GEMV_SUCCESS:
+        raise GemvError(rc, "gemv_plan_q8")
     return out.as_dict()
 
 
@@ -315,6 +334,37 @@ def gemv_splitk(A, x, bias=None, out=None, *, splits: int = 0, workspace=None, s
             y.data_ptr(), M, K, splits, workspace.data_ptr(), ws_bytes, _stream_handle(stream))
     if rc != GEMV_SUCCESS:
         raise GemvError(rc, fn.__name__)
+    return y
+
+
+def gemv_q8(Q, scale, x, bias=None, out=None, *, family: int = FAMILY_AUTO, stream=None):
+    """Weight-only int8: y = scale * (Q @ x) (+ bias) with Q int8 (M, K)
+    (unit column stride, row stride ldq), scale float32 (M,), x (K,) float32,
+    float16 or bfloat16; returns y (M,) float32."""
+    torch = _torch()
+    if Q.dtype != torch.int8:
+        raise TypeError("Q must be int8")
+    M, K, ldq = _check_matrix(Q)
+    if x.dim() != 1 or x.shape[0] != K or not x.is_contiguous() or x.device != Q.device:
+        raise ValueError("x must be a contiguous (K,) tensor on Q's device")
+    dt = _dtype_name(x)
+    if (scale.dtype != torch.float32 or scale.dim() != 1 or scale.shape[0] != M
+            or not scale.is_contiguous() or scale.device != Q.device):
+        raise ValueError("scale must be a contiguous float32 (M,) tensor on Q's device")
+    bias = _check_bias(bias, M, Q.device)
+    y = _check_out(out, (M,), Q.device)
+    bptr = bias.data_ptr() if bias is not None else None
+    if family == FAMILY_AUTO:
+        fn = {"f32": gemv_q8_f32, "f16": gemv_q8_f16, "bf16": gemv_q8_bf16}[dt]
+        rc = fn(Q.data_ptr(), ldq, scale.data_ptr(), x.data_ptr(), bptr, y.data_ptr(), M, K,
+                _stream_handle(stream))
+        where = fn.__name__
+    else:
+        rc = gemv_q8_run_family(DTYPE_CODES[dt], family, Q.data_ptr(), ldq, scale.data_ptr(),
+                                x.data_ptr(), bptr, y.data_ptr(), M, K, _stream_handle(stream))
+        where = "gemv_q8_run_family"
+    if rc != GEMV_SUCCESS:
+        raise GemvError(rc, where)
     return y
 
 

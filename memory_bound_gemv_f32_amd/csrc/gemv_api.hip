@@ -190,6 +190,57 @@ const void* gated_kernel(const Plan& p) {
     return nullptr;
 }
 
+// ---- int8 weights ------------------------------------------------------------
+
+template <class X, int L, bool VEC>
+const void* q8_rows_fn(int tiles, int batch) {
+    if constexpr (L == 64) {
+        if (tiles != 1 && tiles != 2) return nullptr;
+        switch (batch * 4 + tiles) {
+        case 1 * 4 + 1: return (const void*)&gemvdev::gemv_rows_q8_kernel<X, 64, 1, 1, VEC>;
+        case 2 * 4 + 1: return (const void*)&gemvdev::gemv_rows_q8_kernel<X, 64, 1, 2, VEC>;
+        case 4 * 4 + 1: return (const void*)&gemvdev::gemv_rows_q8_kernel<X, 64, 1, 4, VEC>;
+        case 1 * 4 + 2: return (const void*)&gemvdev::gemv_rows_q8_kernel<X, 64, 2, 1, VEC>;
+        case 2 * 4 + 2: return (const void*)&gemvdev::gemv_rows_q8_kernel<X, 64, 2, 2, VEC>;
+        case 4 * 4 + 2: return (const void*)&gemvdev::gemv_rows_q8_kernel<X, 64, 2, 4, VEC>;
+        default: return nullptr;
+        }
+    } else {
+        if (batch != 1) return nullptr;
+        switch (tiles) {
+        case 1: return (const void*)&gemvdev::gemv_rows_q8_kernel<X, L, 1, 1, VEC>;
+        case 2: return (const void*)&gemvdev::gemv_rows_q8_kernel<X, L, 2, 1, VEC>;
+        case 4: return (const void*)&gemvdev::gemv_rows_q8_kernel<X, L, 4, 1, VEC>;
+        case 8: return (const void*)&gemvdev::gemv_rows_q8_kernel<X, L, 8, 1, VEC>;
+        default: return nullptr;
+        }
+    }
+}
+
+template <class X, bool VEC>
+const void* q8_fn(const Plan& p) {
+    if (p.family == gemvplan::GROUP_PER_ROW) {
+        constexpr int W = gemvplan::kGroupWaves;
+        switch (p.batch) {
+        case 1: return (const void*)&gemvdev::gemv_group_q8_kernel<X, W, 1, VEC>;
+        case 2: return (const void*)&gemvdev::gemv_group_q8_kernel<X, W, 2, VEC>;
+        case 4: return (const void*)&gemvdev::gemv_group_q8_kernel<X, W, 4, VEC>;
+        default: return nullptr;
+        }
+    }
+    if (p.family != gemvplan::ROWS_PER_WAVE && p.family != gemvplan::WAVE_PER_ROW) return nullptr;
+    switch (p.lanes_per_row) {
+    case 1: return q8_rows_fn<X, 1, VEC>(p.row_tiles, p.batch);
+    case 2: return q8_rows_fn<X, 2, VEC>(p.row_tiles, p.batch);
+    case 4: return q8_rows_fn<X, 4, VEC>(p.row_tiles, p.batch);
+    case 8: return q8_rows_fn<X, 8, VEC>(p.row_tiles, p.batch);
+    case 16: return q8_rows_fn<X, 16, VEC>(p.row_tiles, p.batch);
+    case 32: return q8_rows_fn<X, 32, VEC>(p.row_tiles, p.batch);
+    case 64: return q8_rows_fn<X, 64, VEC>(p.row_tiles, p.batch);
+    default: return nullptr;
+    }
+}
+
 // ---- split-K ------------------------------------------------------------------
 
 template <class D, bool VEC>
@@ -203,6 +254,7 @@ const void* splitk_fn(int batch) {
     }
 }
 
+static_assert(gemvplan::kQ8Batch == 4, "the int8 kernels are instantiated for batches 1, 2, 4");
 static_assert(gemvplan::kGroupWaves == gemvdev::kGroupWavesDev,
               "the planner's split-K workgroup is the one the kernel is compiled for");
 
@@ -350,6 +402,30 @@ gemv_status_t run_splitk(const void* A, int lda, const void* x, const float* bia
                                   dim3(gemvdev::kRowsWaves * 64), argv2, 0, stream));
 }
 
+int q8_plan(int xdtype, int M, int K, int ldq, const void* Q, const void* x, int family, Plan* p) {
+    if (xdtype < gemvplan::F32 || xdtype > gemvplan::BF16 || ldq < K) return gemvplan::INVALID;
+    const bool vec = gemvplan::vector_ok_q8(ldq, (uintptr_t)Q, (uintptr_t)x);
+    return gemvplan::make_plan_vec(gemvplan::Q8, M, K, 1, vec, family, p);
+}
+
+template <class X>
+gemv_status_t run_q8(int family, const int8_t* Q, int ldq, const float* scale, const void* x,
+                     const float* bias, float* y, int M, int K, hipStream_t stream) {
+    constexpr int xdtype = dtype_code<X>();
+    if (gemvplan::validate_q8(xdtype, M, K, ldq, (uintptr_t)Q, (uintptr_t)scale, (uintptr_t)x,
+                              (uintptr_t)bias, (uintptr_t)y) != gemvplan::OK)
+        return GEMV_ERROR_INVALID_VALUE;
+    if (M == 0) return GEMV_SUCCESS;
+    Plan p;
+    if (q8_plan(xdtype, M, K, ldq, Q, x, family, &p) != gemvplan::OK) return GEMV_ERROR_INVALID_VALUE;
+    const void* fn = p.vector_loads ? q8_fn<X, true>(p) : q8_fn<X, false>(p);
+    if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;
+    int64_t ldq64 = ldq, M64 = M;
+    void* argv[] = {(void*)&Q, (void*)&ldq64, (void*)&scale, (void*)&bias, (void*)&y, (void*)&M64,
+                    (void*)&x, (void*)&K};
+    return finish(launch(fn, p, stream, argv));
+}
+
 void export_plan(const Plan& p, gemv_plan_t* plan) {
     plan->family = p.family;
     plan->vector_loads = p.vector_loads;
@@ -442,9 +518,45 @@ gemv_status_t gemv_gate_up_silu_bf16(const uint16_t* A_gate, const uint16_t* A_u
     return run_gated<TBF16>(A_gate, A_up, lda, x, h, M, K, stream);
 }
 
+gemv_status_t gemv_q8_f32(const int8_t* Q, int ldq, const float* scale, const float* x,
+                          const float* bias, float* y, int M, int K, hipStream_t stream) {
+    return run_q8<TF32>(gemvplan::AUTO, Q, ldq, scale, x, bias, y, M, K, stream);
+}
+
+gemv_status_t gemv_q8_f16(const int8_t* Q, int ldq, const float* scale, const uint16_t* x,
+                          const float* bias, float* y, int M, int K, hipStream_t stream) {
+    return run_q8<TF16>(gemvplan::AUTO, Q, ldq, scale, x, bias, y, M, K, stream);
+}
+
+gemv_status_t gemv_q8_bf16(const int8_t* Q, int ldq, const float* scale, const uint16_t* x,
+                           const float* bias, float* y, int M, int K, hipStream_t stream) {
+    return run_q8<TBF16>(gemvplan::AUTO, Q, ldq, scale, x, bias, y, M, K, stream);
+}
+
+gemv_status_t gemv_q8_run_family(gemv_dtype_t xdtype, int family, const int8_t* Q, int ldq,
+                                 const float* scale, const void* x, const float* bias, float* y,
+                                 int M, int K, hipStream_t stream) {
+    switch ((int)xdtype) {
+    case gemvplan::F32: return run_q8<TF32>(family, Q, ldq, scale, x, bias, y, M, K, stream);
+    case gemvplan::F16: return run_q8<TF16>(family, Q, ldq, scale, x, bias, y, M, K, stream);
+    case gemvplan::BF16: return run_q8<TBF16>(family, Q, ldq, scale, x, bias, y, M, K, stream);
+    default: return GEMV_ERROR_INVALID_VALUE;
+    }
+}
+
+gemv_status_t gemv_plan_q8(gemv_dtype_t xdtype, int M, int K, int ldq, const void* Q,
+                           const void* x, int family, gemv_plan_t* plan) {
+    Plan p;
+    if (plan == nullptr || M < 0 ||
+        q8_plan((int)xdtype, M, K, ldq, Q, x, family, &p) != gemvplan::OK)
+        return GEMV_ERROR_INVALID_VALUE;
+    export_plan(p, plan);
+    return GEMV_SUCCESS;
+}
+
 gemv_status_t gemv_plan(gemv_dtype_t dtype, int M, int K, int lda, int nvec, const void* A,
                         const void* X, int family, gemv_plan_t* plan) {
-    if (plan == nullptr) return GEMV_ERROR_INVALID_VALUE;
+    if (plan == nullptr || (int)dtype > gemvplan::BF16) return GEMV_ERROR_INVALID_VALUE;
     Plan p;
     if (gemvplan::make_plan((int)dtype, M, K, lda, nvec, (uintptr_t)A, (uintptr_t)X, family,
                             &p) != gemvplan::OK)

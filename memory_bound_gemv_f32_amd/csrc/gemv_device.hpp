@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace gemvdev {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -21,15 +23,29 @@ typedef unsigned int quad __attribute__((ext_vector_type(4)));
 // half-precision inputs with a wider accumulator).
 struct TF32 {
     using storage = float;
+    using xstorage = float;  // x has the matrix's type
     static constexpr int bytes = 4;
 };
 struct TF16 {
     using storage = uint16_t;
+    using xstorage = uint16_t;
     static constexpr int bytes = 2;
 };
 struct TBF16 {
     using storage = uint16_t;
+    using xstorage = uint16_t;
     static constexpr int bytes = 2;
+};
+// Weight-only int8: the matrix holds int8 weights (one fp32 scale per row is
+// applied after the row's sum), x stays in the float type X (the lqnn.cn NPU
+// MatMul essay, section 1.2: int8 weights, fp16 activations, an fp32
+// accumulator).  One 16-byte load carries 16 weights.
+template <class X>
+struct TQ8 {
+    using storage = int8_t;
+    using xstorage = typename X::storage;
+    using xtype = X;
+    static constexpr int bytes = 1;
 };
 
 // One stored element widened to fp32 (exact for all three types).
@@ -42,6 +58,17 @@ __device__ __forceinline__ float widen(TBF16, uint16_t h) {
 }
 
 __device__ __forceinline__ float f32_of(uint32_t w) { return __builtin_bit_cast(float, w); }
+
+// The tail loops read A and x element by element; for the float types both
+// are widened alike, for int8 weights the weight is an integer.
+template <class D>
+__device__ __forceinline__ float widen_a(D, typename D::storage v) { return widen(D{}, v); }
+template <class D>
+__device__ __forceinline__ float widen_x(D, typename D::xstorage v) { return widen(D{}, v); }
+template <class X>
+__device__ __forceinline__ float widen_a(TQ8<X>, int8_t q) { return (float)q; }
+template <class X>
+__device__ __forceinline__ float widen_x(TQ8<X>, typename X::storage v) { return widen(X{}, v); }
 
 // acc + Σ a_i·x_i over one 16-byte chunk (4 fp32 or 8 half-width elements),
 // as a chain of IEEE fp32 fused multiply-adds in element order.  Half-width
@@ -138,6 +165,9 @@ struct Chunk<D, true> {
         return __builtin_nontemporal_load(reinterpret_cast<const quad*>(p + c * elems));
     }
     __device__ __forceinline__ static type zero() { return quad{0u, 0u, 0u, 0u}; }
+    using xtype = type;  // x chunks are A chunks
+    __device__ __forceinline__ static type keep_a(bool ok, type v) { return ok ? v : zero(); }
+    __device__ __forceinline__ static type keep_x(bool ok, type v) { return ok ? v : zero(); }
     __device__ __forceinline__ static float dot(type a, type x, float acc) {
         return chunk_dot(D{}, a, x, acc);
     }
@@ -156,11 +186,75 @@ struct Chunk<D, false> {
         return __builtin_nontemporal_load(p + c);
     }
     __device__ __forceinline__ static type zero() { return type(0); }
+    using xtype = type;
+    __device__ __forceinline__ static type keep_a(bool ok, type v) { return ok ? v : zero(); }
+    __device__ __forceinline__ static type keep_x(bool ok, type v) { return ok ? v : zero(); }
     __device__ __forceinline__ static float dot(type a, type x, float acc) {
         return __builtin_fmaf(widen(D{}, a), widen(D{}, x), acc);
     }
     __device__ __forceinline__ static float dot2(type a, type x, float acc) {
         return dot(a, x, acc);
+    }
+};
+
+// int8 weights: a chunk is 16 weights (one 16-byte quad, nontemporal) and
+// the 16 matching x elements (32 bytes of fp16/bf16 or 64 of fp32, cached),
+// held as native vectors so that selects stay in registers.
+typedef unsigned int u32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x16 __attribute__((ext_vector_type(16)));
+
+// weight i (0..3) of a 32-bit word, sign-extended and converted exactly
+__device__ __forceinline__ float q8_at(uint32_t w, int i) {
+    return (float)(int)(int8_t)(uint8_t)(w >> (8 * i));
+}
+// x element e of a chunk: one word holds two half-width or one fp32 element
+__device__ __forceinline__ float x_at(TF16, u32x8 x, int e) {
+    const uint32_t w = x[e >> 1];
+    return (e & 1) ? hi_f16(w) : lo_f16(w);
+}
+__device__ __forceinline__ float x_at(TBF16, u32x8 x, int e) {
+    const uint32_t w = x[e >> 1];
+    return (e & 1) ? hi_bf16(w) : lo_bf16(w);
+}
+__device__ __forceinline__ float x_at(TF32, u32x16 x, int e) { return f32_of(x[e]); }
+
+template <class X>
+struct Chunk<TQ8<X>, true> {
+    using type = quad;
+    using xtype = typename std::conditional<X::bytes == 4, u32x16, u32x8>::type;
+    static constexpr int elems = 16;
+    __device__ __forceinline__ static xtype load(const typename X::storage* p, int64_t c) {
+        return *reinterpret_cast<const xtype*>(p + c * elems);
+    }
+    __device__ __forceinline__ static type stream(const int8_t* p, int64_t c) {
+        return __builtin_nontemporal_load(reinterpret_cast<const quad*>(p + c * elems));
+    }
+    __device__ __forceinline__ static type zero() { return quad{0u, 0u, 0u, 0u}; }
+    __device__ __forceinline__ static type keep_a(bool ok, type v) { return ok ? v : zero(); }
+    __device__ __forceinline__ static xtype keep_x(bool ok, xtype v) { return ok ? v : xtype(0u); }
+    // acc + Σ q_e·x_e over the 16 weights, in weight order, IEEE fp32 FMA
+    __device__ __forceinline__ static float dot(type a, xtype x, float acc) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(q8_at(a[w], i), x_at(X{}, x, 4 * w + i), acc);
+        return acc;
+    }
+};
+template <class X>
+struct Chunk<TQ8<X>, false> {
+    using type = int8_t;
+    using xtype = typename X::storage;
+    static constexpr int elems = 1;
+    __device__ __forceinline__ static xtype load(const xtype* p, int64_t c) { return p[c]; }
+    __device__ __forceinline__ static type stream(const int8_t* p, int64_t c) {
+        return __builtin_nontemporal_load(p + c);
+    }
+    __device__ __forceinline__ static type zero() { return type(0); }
+    __device__ __forceinline__ static type keep_a(bool ok, type v) { return ok ? v : type(0); }
+    __device__ __forceinline__ static xtype keep_x(bool ok, xtype v) { return ok ? v : xtype(0); }
+    __device__ __forceinline__ static float dot(type a, xtype x, float acc) {
+        return __builtin_fmaf((float)a, widen(X{}, x), acc);
     }
 };
 

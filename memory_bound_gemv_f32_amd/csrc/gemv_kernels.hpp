@@ -40,6 +40,7 @@ constexpr int kGroupWavesDev = 4;
 // result goes.  Passed to the kernels by value, as kernel arguments.
 template <class S>
 struct OneMatrix {
+    static constexpr bool kScaled = false;  // no per-row scale
     const S* A;
     int64_t lda;
     const float* bias;  // or nullptr
@@ -50,6 +51,41 @@ struct OneMatrix {
     __device__ __forceinline__ void store(int64_t m, float v) const { y[m] = v; }
 };
 
+// One int8 weight matrix with a fp32 scale per row: y[m] = scale[m]·(row
+// m · x) + bias[m] (the lqnn.cn NPU MatMul essay, section 4.2: int8
+// weights with a per-channel scale).
+template <class S>
+struct ScaledMatrix {
+    static constexpr bool kScaled = true;
+    const S* A;
+    int64_t lda;
+    const float* scale;
+    const float* bias;  // or nullptr
+    float* y;
+    int64_t M;
+    __device__ __forceinline__ const S* row(int64_t m) const { return A + m * lda; }
+    __device__ __forceinline__ float scale_of(int64_t m) const { return scale[m]; }
+    __device__ __forceinline__ float bias_of(int64_t m) const { return bias != nullptr ? bias[m] : 0.f; }
+    __device__ __forceinline__ void store(int64_t m, float v) const { y[m] = v; }
+};
+
+// The epilogue of one row: sum·scale + bias (one rounding) for a scaled
+// matrix, sum + bias otherwise.
+template <class Rows>
+__device__ __forceinline__ float row_result(float sum, float scale, float bias) {
+    if constexpr (Rows::kScaled)
+        return __builtin_fmaf(sum, scale, bias);
+    else
+        return sum + bias;
+}
+template <class Rows>
+__device__ __forceinline__ float scale_of(const Rows& rows, int64_t m) {
+    if constexpr (Rows::kScaled)
+        return rows.scale_of(m);
+    else
+        return 1.f;
+}
+
 // Up to kMaxSegments matrices with the same K, stacked row-wise: rows
 // start[i] .. start[i+1]-1 of the stack are rows of segment i.  Every
 // segment multiplies the same x (e.g. the q, k and v projections of one
@@ -58,6 +94,7 @@ struct OneMatrix {
 constexpr int kMaxSegments = 8;
 template <class S>
 struct Segments {
+    static constexpr bool kScaled = false;
     int64_t M;  // rows in all segments
     int count;
     int64_t start[kMaxSegments];
@@ -110,12 +147,13 @@ struct Segments {
 // One batch of the rows kernels: BATCH chunks per row tile, chunk c + i·L
 // for i < BATCH, all loads issued before any is used.  CHECK: chunks at or
 // past nfull load chunk nfull-1 instead and are replaced by zero.
-template <class C, int L, int U, int BATCH, bool CHECK, class S>
-__device__ __forceinline__ void rows_batch(const S* const (&rp)[U], const S* x, int c, int nfull,
+template <class C, int L, int U, int BATCH, bool CHECK, class S, class XS>
+__device__ __forceinline__ void rows_batch(const S* const (&rp)[U], const XS* x, int c, int nfull,
                                            float (&acc)[U][2]) {
     using CT = typename C::type;
+    using XT = typename C::xtype;
     CT a[U][BATCH];
-    CT xv[BATCH];
+    XT xv[BATCH];
 #pragma unroll
     for (int i = 0; i < BATCH; ++i) {
         int cc = c + i * L;
@@ -130,12 +168,12 @@ __device__ __forceinline__ void rows_batch(const S* const (&rp)[U], const S* x, 
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < BATCH; ++i) {
-        CT xi = xv[i];
-        if constexpr (CHECK) xi = c + i * L < nfull ? xi : C::zero();
+        XT xi = xv[i];
+        if constexpr (CHECK) xi = C::keep_x(c + i * L < nfull, xi);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             CT ai = a[u][i];
-            if constexpr (CHECK) ai = c + i * L < nfull ? ai : C::zero();
+            if constexpr (CHECK) ai = C::keep_a(c + i * L < nfull, ai);
             acc[u][i & 1] = C::dot(ai, xi, acc[u][i & 1]);
         }
     }
@@ -146,7 +184,7 @@ __device__ __forceinline__ void rows_batch(const S* const (&rp)[U], const S* x, 
 // tiles; lanes sub = lane % L of one row walk its chunks with stride L, BATCH
 // chunks in flight per row tile.
 template <class D, int L, int U, int BATCH, bool VEC, class Rows>
-__device__ __forceinline__ void rows_body(const Rows& rows, const typename D::storage* __restrict__ x,
+__device__ __forceinline__ void rows_body(const Rows& rows, const typename D::xstorage* __restrict__ x,
                                           int K) {
     using S = typename D::storage;
     using C = Chunk<D, VEC>;
@@ -171,12 +209,14 @@ __device__ __forceinline__ void rows_body(const Rows& rows, const typename D::st
     // sub + L, ... so that one store covers up to 64 consecutive rows.  The
     // bias loads are issued now, ahead of the A stream.
     constexpr int kOut = U < L ? 1 : U / L;  // rows stored per lane
-    float bv[kOut];
+    float bv[kOut], sv[kOut];
 #pragma unroll
     for (int o = 0; o < kOut; ++o) {
         const int u = sub + o * L;
         const int64_t row = (tile0 + u) * R + slot;
-        bv[o] = (u < U && row < M) ? rows.bias_of(row) : 0.f;
+        const bool in = u < U && row < M;
+        bv[o] = in ? rows.bias_of(row) : 0.f;
+        sv[o] = in ? scale_of(rows, row) : 0.f;
     }
 
     float acc[U][2];
@@ -193,9 +233,9 @@ __device__ __forceinline__ void rows_body(const Rows& rows, const typename D::st
     if constexpr (VEC) {
         // elements past the last whole chunk (fewer than E of them)
         for (int k = nfull * E + sub; k < K; k += L) {
-            const float xe = widen(D{}, x[k]);
+            const float xe = widen_x(D{}, x[k]);
 #pragma unroll
-            for (int u = 0; u < U; ++u) acc[u][1] = __builtin_fmaf(widen(D{}, rp[u][k]), xe, acc[u][1]);
+            for (int u = 0; u < U; ++u) acc[u][1] = __builtin_fmaf(widen_a(D{}, rp[u][k]), xe, acc[u][1]);
         }
     }
 
@@ -210,7 +250,7 @@ __device__ __forceinline__ void rows_body(const Rows& rows, const typename D::st
 #pragma unroll
         for (int t = 1; t < U; ++t) out = (u == t) ? v[t] : out;
         const int64_t row = (tile0 + u) * R + slot;
-        if (u < U && row < M) rows.store(row, out + bv[o]);
+        if (u < U && row < M) rows.store(row, row_result<Rows>(out, sv[o], bv[o]));
     }
 }
 
@@ -237,7 +277,7 @@ gemv_rows_multi_kernel(const Segments<typename D::storage> rows,
 // writes y[row] (page "第 3 课", the block-reduction structure of section
 // "C. 点积规约与原子写入解耦" on 64-lane wavefronts).
 template <class D, int W, int BATCH, bool VEC, class Rows>
-__device__ __forceinline__ void group_body(const Rows& rows, const typename D::storage* __restrict__ x,
+__device__ __forceinline__ void group_body(const Rows& rows, const typename D::xstorage* __restrict__ x,
                                            int K, int64_t row) {
     using S = typename D::storage;
     using C = Chunk<D, VEC>;
@@ -249,6 +289,7 @@ __device__ __forceinline__ void group_body(const Rows& rows, const typename D::s
     const int sub = threadIdx.x;
     const S* rp = rows.row(row);
     const float b = sub == 0 ? rows.bias_of(row) : 0.f;
+    const float sc = sub == 0 ? scale_of(rows, row) : 0.f;
 
     float acc[1][2] = {{0.f, 0.f}};
     const S* const rps[1] = {rp};
@@ -259,7 +300,7 @@ __device__ __forceinline__ void group_body(const Rows& rows, const typename D::s
     if (c0 < nfull) rows_batch<C, L, 1, BATCH, true>(rps, x, c0 + sub, nfull, acc);
     if constexpr (VEC) {
         for (int k = nfull * E + sub; k < K; k += L)
-            acc[0][1] = __builtin_fmaf(widen(D{}, rp[k]), widen(D{}, x[k]), acc[0][1]);
+            acc[0][1] = __builtin_fmaf(widen_a(D{}, rp[k]), widen_x(D{}, x[k]), acc[0][1]);
     }
 
     const float v = segment_sum<64>(acc[0][0] + acc[0][1]);
@@ -269,7 +310,7 @@ __device__ __forceinline__ void group_body(const Rows& rows, const typename D::s
         float s = partial[0];
 #pragma unroll
         for (int w = 1; w < W; ++w) s += partial[w];
-        rows.store(row, s + b);
+        rows.store(row, row_result<Rows>(s, sc, b));
     }
 }
 
@@ -287,6 +328,23 @@ gemv_group_multi_kernel(const Segments<typename D::storage> rows,
     group_body<D, W, BATCH, VEC>(rows, x, K, blockIdx.x);
 }
 
+// Weight-only int8: the rows and workgroup-per-row bodies on int8 weights,
+// x of type X, and the per-row scale applied after each row's sum.
+template <class X, int L, int U, int BATCH, bool VEC>
+__global__ void __launch_bounds__(kRowsWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
+gemv_rows_q8_kernel(const int8_t* Q, int64_t ldq, const float* scale, const float* bias, float* y,
+                    int64_t M, const typename X::storage* __restrict__ x, int K) {
+    rows_body<TQ8<X>, L, U, BATCH, VEC>(ScaledMatrix<int8_t>{Q, ldq, scale, bias, y, M}, x, K);
+}
+
+template <class X, int W, int BATCH, bool VEC>
+__global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4)))
+gemv_group_q8_kernel(const int8_t* Q, int64_t ldq, const float* scale, const float* bias, float* y,
+                     int64_t M, const typename X::storage* __restrict__ x, int K) {
+    group_body<TQ8<X>, W, BATCH, VEC>(ScaledMatrix<int8_t>{Q, ldq, scale, bias, y, M}, x, K,
+                                      blockIdx.x);
+}
+
 // Split-K, pass 1: workgroup (m, s) forms the dot product of row m's slice s
 // (elements s·slice .. s·slice + slice - 1, the last slice shorter) with the
 // same slice of x, in the workgroup-per-row body, and writes it to
@@ -298,6 +356,7 @@ gemv_group_multi_kernel(const Segments<typename D::storage> rows,
 // slice is fetched into that XCD's L2 once, not once per row.
 template <class S>
 struct SliceOfRows {
+    static constexpr bool kScaled = false;
     const S* A;  // first element of the slice in row 0
     int64_t lda;
     float* ws;   // ws + s: the row-major M × splits partials, column s

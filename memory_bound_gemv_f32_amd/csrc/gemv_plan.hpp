@@ -27,6 +27,9 @@
 namespace gemvplan {
 
 enum Dtype { F32 = 0, F16 = 1, BF16 = 2 };
+// Int8 weights: planned by their own 1-byte rows (16 weights per load); x
+// keeps its float type (validate_q8).
+constexpr int Q8 = 3;
 enum Family {
     AUTO = -1,
     ROWS_PER_WAVE = 0,
@@ -90,6 +93,11 @@ constexpr int64_t kSplitMaxRows = 256;
 constexpr int64_t kSplitMinRowLoads = 4 * kGroupWaves * kWave * kGroupBatch;
 constexpr int64_t kSplitMinSliceLoads = 512;
 constexpr int kSplitMaxSplits = 1024;
+// Int8 weights: loads per lane per batch (each weight chunk brings a 32- or
+// 64-byte x chunk), and the workgroups below which a wavefront keeps one
+// row instead of two.
+constexpr int kQ8Batch = 4;
+constexpr int64_t kQ8PairRowsMinGroups = 256;
 // Threads per workgroup of the rows/wave and batched families.
 constexpr int kBlock = 256;
 // Below this many workgroups the rows-per-wave family stops giving each
@@ -114,7 +122,7 @@ struct Plan {
     int64_t grid = 0;     // workgroups (split-K: rows × slices)
 };
 
-inline int element_bytes(int dtype) { return dtype == F32 ? 4 : 2; }
+inline int element_bytes(int dtype) { return dtype == F32 ? 4 : (dtype == Q8 ? 1 : 2); }
 
 inline int next_pow2(int64_t v) {
     int p = 1;
@@ -137,6 +145,25 @@ inline int validate(int dtype, int M, int K, int lda, int nvec, uintptr_t A,
     return OK;
 }
 
+// Argument checks of the int8-weight entry points: Q int8 with row pitch
+// ldq >= K, x in float type xdtype, one fp32 scale per row.
+inline int validate_q8(int xdtype, int M, int K, int ldq, uintptr_t Q, uintptr_t scale,
+                       uintptr_t x, uintptr_t bias, uintptr_t y) {
+    if (xdtype < F32 || xdtype > BF16) return INVALID;
+    if (M < 0 || K < 0 || ldq < K) return INVALID;
+    if (M > 0 && K > 0 && (Q == 0 || x == 0)) return INVALID;
+    if (M > 0 && (y == 0 || scale == 0)) return INVALID;
+    if (x % (uintptr_t)element_bytes(xdtype) != 0 || scale % 4 != 0 || bias % 4 != 0 ||
+        y % 4 != 0)
+        return INVALID;
+    return OK;
+}
+
+// 16-byte loads of int8 rows: Q, its row pitch and x 16-byte aligned.
+inline bool vector_ok_q8(int ldq, uintptr_t Q, uintptr_t x) {
+    return Q % kLoadBytes == 0 && x % kLoadBytes == 0 && ldq % kLoadBytes == 0;
+}
+
 // 16-byte loads need 16-byte aligned A, x (and every X column) and row pitch.
 inline bool vector_ok(int dtype, int K, int lda, int nvec, uintptr_t A, uintptr_t X) {
     const int64_t s = element_bytes(dtype);
@@ -154,7 +181,7 @@ constexpr int kMultiMaxRowTiles = 2;
 
 inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family, Plan* out,
                          int max_row_tiles = 8) {
-    if (dtype < F32 || dtype > BF16 || M < 0 || K < 0 || nvec < 1 || nvec > kMaxVectors)
+    if (dtype < F32 || dtype > Q8 || M < 0 || K < 0 || nvec < 1 || nvec > kMaxVectors)
         return INVALID;
 
     Plan p;
@@ -183,6 +210,9 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
     }
     const bool batched = fam == BATCHED || fam == BATCHED_MFMA;
     if (!batched && nvec != 1) return INVALID;
+    // int8 weights run the three single-vector row families only
+    if (dtype == Q8 && fam != ROWS_PER_WAVE && fam != WAVE_PER_ROW && fam != GROUP_PER_ROW)
+        return INVALID;
     if (batched && dtype == F32) return INVALID;
     if (fam == BATCHED_MFMA && !mfma_ok) return INVALID;
 
@@ -213,6 +243,14 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         p.waves_per_group = kBlock / kWave;
         p.batch = kWaveBatch;
         p.row_tiles = 1;
+        if (dtype == Q8) {
+            // int8 rows: x chunks are 2-4 times the weight chunk, so batches
+            // stop at kQ8Batch and two rows share every x chunk when there
+            // are rows enough
+            const int64_t per_lane = ceil_div(full, (int64_t)kWave);
+            p.batch = per_lane >= kQ8Batch ? kQ8Batch : next_pow2(per_lane < 1 ? 1 : per_lane);
+            if (ceil_div(M, 2 * (kBlock / kWave)) >= kQ8PairRowsMinGroups) p.row_tiles = 2;
+        }
         break;
     case GROUP_PER_ROW: {
         p.lanes_per_row = kWave * kGroupWaves;
@@ -220,7 +258,8 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         p.waves_per_group = kGroupWaves;
         // as many loads per lane in flight as the row gives each lane, up to 8
         const int64_t per_lane = ceil_div(full, (int64_t)p.lanes_per_row);
-        p.batch = per_lane >= kGroupBatch ? kGroupBatch : next_pow2(per_lane < 1 ? 1 : per_lane);
+        const int cap = dtype == Q8 ? kQ8Batch : kGroupBatch;
+        p.batch = per_lane >= cap ? cap : next_pow2(per_lane < 1 ? 1 : per_lane);
         p.row_tiles = 1;
         p.lds_bytes = (int)(kGroupWaves * sizeof(float));
         break;

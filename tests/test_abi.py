@@ -352,3 +352,57 @@ def test_splitk_geometry_properties():
         else:
             assert S <= splits
         assert lg.splitk_workspace_size(dtype, M, K, splits) == 4 * M * S
+
+
+# ---------------------------------------------------------------------------
+# weight-only int8: validation and mapping, without a GPU
+# ---------------------------------------------------------------------------
+
+Q8 = (lg.gemv_q8_f32, lg.gemv_q8_f16, lg.gemv_q8_bf16)
+
+
+def test_q8_validation():
+    for fn, s in zip(Q8, (4, 2, 2)):
+        def call(Q=GOOD, ldq=64, scale=GOOD, x=GOOD, bias=None, y=GOOD, M=4, K=64):
+            return fn(Q, ldq, scale, x, bias, y, M, K, None)
+        assert call(M=-1) == lg.GEMV_ERROR_INVALID_VALUE
+        assert call(K=-1) == lg.GEMV_ERROR_INVALID_VALUE
+        assert call(ldq=63) == lg.GEMV_ERROR_INVALID_VALUE
+        assert call(Q=None) == lg.GEMV_ERROR_INVALID_VALUE
+        assert call(x=None) == lg.GEMV_ERROR_INVALID_VALUE
+        assert call(y=None) == lg.GEMV_ERROR_INVALID_VALUE
+        assert call(scale=None) == lg.GEMV_ERROR_INVALID_VALUE
+        assert call(scale=GOOD + 2) == lg.GEMV_ERROR_INVALID_VALUE
+        assert call(bias=GOOD + 1) == lg.GEMV_ERROR_INVALID_VALUE
+        assert call(y=GOOD + 2) == lg.GEMV_ERROR_INVALID_VALUE
+        assert call(x=GOOD + s - 1) == lg.GEMV_ERROR_INVALID_VALUE   # x not element-aligned
+        assert call(M=0, Q=None, x=None, y=None, scale=None) == lg.GEMV_SUCCESS
+    # the x type code must be a float type
+    assert lg.gemv_q8_run_family(3, lg.FAMILY_AUTO, GOOD, 64, GOOD, GOOD, None, GOOD, 4, 64,
+                                 None) == lg.GEMV_ERROR_INVALID_VALUE
+
+
+def test_q8_families():
+    """int8 weights run the three single-vector row families only, planned by
+    their 1-byte rows: 16 weights per 16-byte load."""
+    for fam in (lg.FAMILY_BATCHED, lg.FAMILY_BATCHED_MFMA, lg.FAMILY_SPLIT_K):
+        with pytest.raises(lg.GemvError):
+            lg.plan_q8("f16", 64, 4096, family=fam, Q_addr=ALIGNED, x_addr=ALIGNED)
+    # K = 16 int8 weights are one load: one lane per row, 64 rows per wavefront
+    p = lg.plan_q8("f16", 1000, 16, Q_addr=ALIGNED, x_addr=ALIGNED)
+    assert (p["family"], p["lanes_per_row"], p["rows_per_wave"]) == (lg.FAMILY_ROWS_PER_WAVE, 1, 64)
+    assert p["chunk_elems"] == 16
+    # 4096 weights are 256 loads: a wavefront per row, 4 loads per lane in
+    # flight, two rows per wavefront once there are workgroups enough
+    p = lg.plan_q8("bf16", 4096, 4096, Q_addr=ALIGNED, x_addr=ALIGNED)
+    assert (p["family"], p["batch"], p["row_tiles"]) == (lg.FAMILY_WAVE_PER_ROW, 4, 2)
+    assert p["grid"] == 4096 // 8
+    p = lg.plan_q8("bf16", 300, 4096, family=lg.FAMILY_WAVE_PER_ROW, Q_addr=ALIGNED,
+                   x_addr=ALIGNED)
+    assert p["row_tiles"] == 1 and p["grid"] == 75
+    # few, long rows: a workgroup per row, batches capped at 4
+    p = lg.plan_q8("bf16", 100, 100000, Q_addr=ALIGNED, x_addr=ALIGNED)
+    assert (p["family"], p["batch"], p["grid"]) == (lg.FAMILY_GROUP_PER_ROW, 4, 100)
+    # byte-aligned Q or an odd row pitch fall back to element loads
+    assert lg.plan_q8("f16", 64, 4096, Q_addr=ALIGNED + 1, x_addr=ALIGNED)["vector_loads"] == 0
+    assert lg.plan_q8("f16", 64, 4096, ldq=4100, Q_addr=ALIGNED, x_addr=ALIGNED)["vector_loads"] == 0

@@ -26,6 +26,10 @@ from a seeded ``numpy.random.default_rng`` in the order A, then x, then bias):
 * ``batched_f16_4096x16``: fp16 W 4096x4096 ~ N(0,1)/sqrt(K), X with 16
   columns (K x 16, column-major) ~ N(0,1), no bias; the m = 16
   small_batch_decode run of the same section, seed 65.
+* ``batched_f16_4096x{32,64}``: the same W and X drawn with 32 and 64
+  columns, the batch sizes of 16 to 32 and beyond at which page "第 3 课：
+  GEMV 与行级并行", section "4. 性能与工程权舍", moves to matrix-core GEMM;
+  seeds 70 and 71.
 """
 
 from __future__ import annotations
@@ -184,6 +188,8 @@ WORKLOADS = {
     "skinny_k128": ("f32", 1 << 20, 128, 1, True, "uniform", None, 62),
     "decode_f16_4096": ("f16", 4096, 4096, 1, False, "normal", "1/sqrtK", 63),
     "batched_f16_4096x16": ("f16", 4096, 4096, 16, False, "normal", "1/sqrtK", 65),
+    "batched_f16_4096x32": ("f16", 4096, 4096, 32, False, "normal", "1/sqrtK", 70),
+    "batched_f16_4096x64": ("f16", 4096, 4096, 64, False, "normal", "1/sqrtK", 71),
 }
 for _i, (_n, (_m, _k)) in enumerate(SWEEP_SHAPES.items()):
     WORKLOADS[f"sweep_{_n}"] = ("bf16", _m, _k, 1, False, "normal", 0.02, 640 + _i)

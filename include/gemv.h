@@ -2,7 +2,7 @@
  * libgemv — dense matrix-vector products on AMD Instinct MI355X (gfx950).
  *
  *   y = A·x (+ bias)                 gemv_f32 / gemv_f16 / gemv_bf16
- *   Y = A·X (+ bias), 1..16 vectors   gemv_batched_f16 / gemv_batched_bf16
+ *   Y = A·X (+ bias), 1..64 vectors   gemv_batched_f16 / gemv_batched_bf16
  *   several y_i = A_i·x in one launch gemv_multi_*
  *   h = silu(A_gate·x) ⊙ (A_up·x)     gemv_gate_up_silu_*
  *   y = A·x for few, long rows        gemv_splitk_* (caller's workspace)
@@ -13,10 +13,12 @@
  * y is M×1), plus bias[m] when a bias is given; the bias may be absent, in
  * which case nothing is added (page "第 3 课：GEMV 与行级并行", section
  * "核心心智模型" item 1 for y = A x + bias, section "3. 正确性边界与指针安全性"
- * for the absent bias).  The batched form applies one pass over A to up to 16
- * right-hand vectors, the small-batch decode case measured on page "GEMM、
- * GEMV、dtype 与算术强度", section "可运行 CUDA 实验" (m = 16), below the batch
- * size at which page "第 3 课" section "4. 性能与工程权舍" moves to GEMM.
+ * for the absent bias).  The batched form applies one pass over A to up to 64
+ * right-hand vectors: the small-batch decode case measured on page "GEMM、
+ * GEMV、dtype 与算术强度", section "可运行 CUDA 实验" (m = 16), and beyond it
+ * the batches of 16 to 32 at which page "第 3 课" section "4. 性能与工程权舍"
+ * moves to a matrix-core GEMM (here: the matrix-core kernel, still one
+ * pass over A).
  *
  * Arithmetic.  fp16 and bf16 elements are multiplied and summed in fp32, the
  * wider accumulator that page "GEMM、GEMV、dtype 与算术强度", section "dtype
@@ -49,7 +51,7 @@
  *
  * Errors.  Every entry point validates its arguments before touching the
  * GPU.  GEMV_ERROR_INVALID_VALUE (nothing enqueued, y untouched) for:
- * M < 0, K < 0, lda < K, nvec outside [1, 16], a NULL A or x when
+ * M < 0, K < 0, lda < K, nvec outside [1, 64], a NULL A or x when
  * M > 0 and K > 0, a NULL y when M > 0, or a pointer not aligned to its
  * element size.  M == 0 succeeds without enqueuing anything.  K == 0 writes
  * y = bias (or 0): the empty sum.  GEMV_ERROR_LAUNCH_FAILURE if the HIP
@@ -97,8 +99,11 @@ gemv_status_t gemv_bf16(const uint16_t *A, int lda, const uint16_t *x,
                         const float *bias, float *y, int M, int K,
                         hipStream_t stream);
 
-/* Y = A·X (+ bias added to every column); 1 <= nvec <= 16; A is read from
- * memory once for all nvec vectors.  nvec == 1 computes what gemv_f16 does. */
+/* Y = A·X (+ bias added to every column); 1 <= nvec <= 64.  With 16-byte
+ * aligned A and X, a row pitch of whole 16-byte units and K % 8 == 0, A is
+ * read from memory once for all nvec vectors (matrix cores); otherwise the
+ * vectors run in blocks of 16, one pass over A per block.  nvec == 1
+ * computes what gemv_f16 does. */
 gemv_status_t gemv_batched_f16(const uint16_t *A, int lda, const uint16_t *X,
                                const float *bias, float *Y, int M, int K,
                                int nvec, hipStream_t stream);

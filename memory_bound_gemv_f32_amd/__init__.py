@@ -280,7 +280,7 @@ def gemv(A, x, bias=None, out=None, *, family: int = FAMILY_AUTO, stream=None):
 
 def gemv_batched(A, X, bias=None, out=None, *, family: int = FAMILY_AUTO,
                  stream=None):
-    """Y = A @ X (+ bias) for X of shape (nvec, K), 1 <= nvec <= 16, fp16 or
+    """Y = A @ X (+ bias) for X of shape (nvec, K), 1 <= nvec <= 64, fp16 or
     bf16; returns Y of shape (nvec, M) float32 (column j = output for X[j])."""
     M, K, lda = _check_matrix(A)
     dt = _dtype_name(A)

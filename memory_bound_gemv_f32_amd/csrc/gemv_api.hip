@@ -160,9 +160,15 @@ const void* batched_kernel(const Plan& p, int nvec) {
     if constexpr (D::bytes == 2) {
         if (p.family == gemvplan::BATCHED)
             return p.vector_loads ? batched_fn<D, true>(nvec) : batched_fn<D, false>(nvec);
-        if (p.family == gemvplan::BATCHED_MFMA && p.vector_loads)
-            return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, gemvplan::kMfmaWaves,
-                                                                   gemvplan::kMfmaChunk>;
+        if (p.family == gemvplan::BATCHED_MFMA && p.vector_loads) {
+            constexpr int W = gemvplan::kMfmaWaves;
+            switch (gemvplan::mfma_tiles(nvec)) {
+            case 1: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 1, gemvplan::mfma_chunk(16)>;
+            case 2: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 2, gemvplan::mfma_chunk(32)>;
+            case 4: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 4, gemvplan::mfma_chunk(64)>;
+            default: return nullptr;
+            }
+        }
     }
     return nullptr;
 }
@@ -263,13 +269,35 @@ static_assert(gemvplan::kGroupWaves == gemvdev::kGroupWavesDev,
 template <class D>
 gemv_status_t run_single(const Plan& p, const void* A, int lda, const void* X, const float* bias,
                          float* Y, int M, int K, int nvec, hipStream_t stream) {
-    if (p.family == gemvplan::BATCHED || p.family == gemvplan::BATCHED_MFMA) {
+    if (p.family == gemvplan::BATCHED_MFMA) {
         const void* fn = batched_kernel<D>(p, nvec);
         if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;
         int64_t lda64 = lda;
         void* argv[] = {(void*)&A, (void*)&lda64, (void*)&X, (void*)&bias, (void*)&Y,
                         (void*)&M, (void*)&K, (void*)&nvec};
         return finish(launch(fn, p, stream, argv));
+    }
+    if (p.family == gemvplan::BATCHED) {
+        // column blocks of at most kValuVectors vectors, one launch each
+        // (X and Y columns j0 .. j0 + nv - 1 start at X + j0·K and Y + j0·M)
+        using S = typename D::storage;
+        for (int j0 = 0; j0 < nvec; j0 += gemvplan::kValuVectors) {
+            int nv = nvec - j0 < gemvplan::kValuVectors ? nvec - j0 : gemvplan::kValuVectors;
+            Plan pb;
+            if (gemvplan::make_plan_vec(dtype_code<D>(), M, K, nv,
+                                        p.vector_loads != 0, gemvplan::BATCHED, &pb) != gemvplan::OK)
+                return GEMV_ERROR_INVALID_VALUE;
+            const void* fn = batched_kernel<D>(pb, nv);
+            if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;
+            int64_t lda64 = lda;
+            const S* Xb = static_cast<const S*>(X) + (int64_t)j0 * K;
+            float* Yb = Y + (int64_t)j0 * M;
+            void* argv[] = {(void*)&A, (void*)&lda64, (void*)&Xb, (void*)&bias, (void*)&Yb,
+                            (void*)&M, (void*)&K, (void*)&nv};
+            const gemv_status_t st = finish(launch(fn, pb, stream, argv));
+            if (st != GEMV_SUCCESS) return st;
+        }
+        return GEMV_SUCCESS;
     }
     const void* fn = single_fn<D, false>(p);
     if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;

@@ -488,10 +488,15 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     }
 }
 
-// Batched kernel on the matrix cores: Y = A·X (+ bias) for up to 16
+// Batched kernel on the matrix cores: Y = A·X (+ bias) for up to 16·NT
 // vectors.  With 16 vectors every A element takes part in 16 multiply-adds,
 // close to the vector ALUs' limit (about 16 FLOP per byte against a ridge of
-// about 20), so the contraction runs as 16×16×32 MFMA steps instead.
+// about 20), so the contraction runs as 16×16×32 MFMA steps instead.  Past
+// 16 vectors (page "第 3 课：GEMV 与行级并行", section "4. 性能与工程权舍" puts
+// the switch to matrix-core GEMM at a batch of 16 to 32) each A operand
+// meets NT tiles of 16 vectors: A is still read once, and at 64 vectors
+// (about 64 FLOP per byte against a matrix-core ridge of about 300) the
+// path stays bound by HBM.
 //
 // A workgroup owns 16 consecutive rows; its W wavefronts split the whole
 // 32-wide steps of K into contiguous slices and walk them in chunks of CH
@@ -502,34 +507,35 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
 //      with coalesced loads (one 1 KiB load per column; X columns are K
 //      elements apart, so reading the operands straight from memory would
 //      send each load to 16 addresses one column pitch apart),
-//   3. runs CH MFMA steps, reading the X operands from LDS.
+//   3. runs CH·NT MFMA steps, reading the X operands from LDS.
 // Vectors past nvec are zero operands.  After one barrier wavefront 0 adds
 // the W tiles in wavefront order, adds the bias and writes Y.  Needs 16-byte
 // aligned A, X and row pitch and K % 8 == 0.  A chunk shorter than CH steps
 // at the end of a slice, and the last, partial 32-wide step (K % 32 != 0,
 // done by the last wavefront), read their operands directly.
-template <class D, int W, int CH>
+template <class D, int W, int NT, int CH>
 __global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2)))
 gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
                          const typename D::storage* __restrict__ X,
                          const float* __restrict__ bias, float* __restrict__ Y,
                          int M, int K, int nvec) {
     using S = typename D::storage;
-    // per wavefront: 16 columns × CH steps × 32 elements, each column
+    constexpr int kCols = 16 * NT;
+    // per wavefront: kCols columns × CH steps × 32 elements, each column
     // padded by 16 bytes so that 16 lanes reading 16 columns hit distinct banks
     constexpr int kColBytes = CH * 64 + 16;
     constexpr int kColQuads = kColBytes / 16;
-    __shared__ quad xs[W][16 * kColQuads];
-    __shared__ f32x4 partial[W][64];
+    // the wavefront's W partial tiles reuse its own X region once it is done
+    static_assert(kCols * kColQuads >= NT * 64, "partials fit in the X region");
+    __shared__ quad xs[W][kCols * kColQuads];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int r = lane & 15;  // A row within the tile / X column of the operand
+    const int r = lane & 15;  // A row within the tile / X column within a tile
     const int g = lane >> 4;  // 8-element group within a 32-wide step
     const int64_t row0 = (int64_t)blockIdx.x * 16;
     const int64_t arow = row0 + r < M ? row0 + r : (int64_t)M - 1;
     const S* ap = A + arow * lda + 8 * g;
-    const bool xcol = r < nvec;
 
     const int steps = K / 32;
     const int per = (steps + W - 1) / W;
@@ -538,8 +544,10 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     const quad zero = quad{0u, 0u, 0u, 0u};
     quad* xw = xs[wave];
 
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    constexpr int kQuads = 16 * 4 * CH;  // X quads (16 bytes) per chunk
+    f32x4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int kQuads = kCols * 4 * CH;  // X quads (16 bytes) per chunk
     int c = s0;
     for (; c + CH <= s1; c += CH) {
         quad a[CH];
@@ -567,8 +575,11 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            // operand of lane (r, g) for step i: column r, elements i·32 + 8g .. +8
-            acc = mma_16x16x32(D{}, a[i], xw[r * kColQuads + 4 * i + g], acc);
+            // operand of lane (r, g) for step i and tile t: column 16t + r,
+            // elements i·32 + 8g .. +8
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                acc[t] = mma_16x16x32(D{}, a[i], xw[(16 * t + r) * kColQuads + 4 * i + g], acc[t]);
         }
         // the next chunk overwrites this wavefront's LDS region
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -576,33 +587,49 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     }
     // a short last chunk (fewer than CH steps): one step at a time, X read
     // straight from memory (it only occurs when K/32 does not split evenly)
-    const S* xp = X + (int64_t)(xcol ? r : 0) * K + 8 * g;
+    const S* xp[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        xp[t] = X + (int64_t)(16 * t + r < nvec ? 16 * t + r : 0) * K + 8 * g;
 #pragma unroll 1
     for (; c < s1; ++c) {
         const quad a = *reinterpret_cast<const quad*>(ap + (int64_t)c * 32);
-        const quad b = *reinterpret_cast<const quad*>(xp + (int64_t)c * 32);
-        acc = mma_16x16x32(D{}, a, xcol ? b : zero, acc);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const quad b = *reinterpret_cast<const quad*>(xp[t] + (int64_t)c * 32);
+            acc[t] = mma_16x16x32(D{}, a, 16 * t + r < nvec ? b : zero, acc[t]);
+        }
     }
     if (wave == W - 1 && steps * 32 < K) {
         // last, partial step: groups wholly below K (K % 8 == 0) load, others are zero
         const bool in = steps * 32 + 8 * g < K;
         const quad a = in ? *reinterpret_cast<const quad*>(ap + (int64_t)steps * 32) : zero;
-        const quad b = (in && xcol) ? *reinterpret_cast<const quad*>(xp + (int64_t)steps * 32) : zero;
-        acc = mma_16x16x32(D{}, a, b, acc);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const bool col = 16 * t + r < nvec;
+            const quad b = (in && col) ? *reinterpret_cast<const quad*>(xp[t] + (int64_t)steps * 32) : zero;
+            acc[t] = mma_16x16x32(D{}, a, b, acc[t]);
+        }
     }
 
-    partial[wave][lane] = acc;
+    f32x4* partial = reinterpret_cast<f32x4*>(xw);  // this wavefront's region, now free
+#pragma unroll
+    for (int t = 0; t < NT; ++t) partial[t * 64 + lane] = acc[t];
     __syncthreads();
     if (wave == 0) {
-        f32x4 t = partial[0][lane];
 #pragma unroll
-        for (int w = 1; w < W; ++w) t += partial[w][lane];
-        // lane holds rows row0 + 4g .. row0 + 4g + 3 of vector r
-        if (xcol) {
+        for (int t = 0; t < NT; ++t) {
+            f32x4 v = acc[t];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t m = row0 + 4 * g + i;
-                if (m < M) Y[(int64_t)r * M + m] = t[i] + (bias != nullptr ? bias[m] : 0.f);
+            for (int w = 1; w < W; ++w) v += reinterpret_cast<const f32x4*>(xs[w])[t * 64 + lane];
+            // lane holds rows row0 + 4g .. row0 + 4g + 3 of vector 16t + r
+            const int j = 16 * t + r;
+            if (j < nvec) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t m = row0 + 4 * g + i;
+                    if (m < M) Y[(int64_t)j * M + m] = v[i] + (bias != nullptr ? bias[m] : 0.f);
+                }
             }
         }
     }

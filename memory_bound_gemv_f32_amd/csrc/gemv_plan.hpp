@@ -44,7 +44,12 @@ enum Status { OK = 0, INVALID = 1 };
 
 constexpr int kWave = 64;
 constexpr int kLoadBytes = 16;
-constexpr int kMaxVectors = 16;
+// Right-hand vectors of the batched entry points.  The vector-ALU batched
+// kernel keeps one accumulator per (row, vector) in registers and takes at
+// most kValuVectors per launch; the matrix-core kernel takes up to
+// kMaxVectors in one pass over A (tiles of 16 vectors).
+constexpr int kMaxVectors = 64;
+constexpr int kValuVectors = 16;
 
 // Rows-per-wave family: lanes per row is a power of two up to this.
 constexpr int kRowsPerWaveMaxLanes = 32;
@@ -71,8 +76,12 @@ constexpr int batched_rows(int nvec) { return nvec <= 2 ? 4 : (nvec <= 4 ? 2 : 1
 constexpr int kMfmaRows = 16;
 constexpr int kMfmaWaves = 8;
 constexpr int kMfmaChunk = 16;
-constexpr int mfma_lds_bytes() {
-    return kMfmaWaves * 16 * (kMfmaChunk * 64 + 16) + kMfmaWaves * kWave * 16;
+// 16-vector tiles for nvec vectors (1, 2 or 4); the chunk shrinks as the
+// tiles grow so that the X staged per chunk stays 16 KiB per wavefront.
+constexpr int mfma_tiles(int nvec) { return nvec <= 16 ? 1 : (nvec <= 32 ? 2 : 4); }
+constexpr int mfma_chunk(int nvec) { return kMfmaChunk / mfma_tiles(nvec); }
+constexpr int mfma_lds_bytes(int nvec) {
+    return kMfmaWaves * 16 * mfma_tiles(nvec) * (mfma_chunk(nvec) * 64 + 16);
 }
 // Split-K: when there are too few rows to fill the chip and each row holds
 // much more than a workgroup keeps in flight (page "SGEMV CUDA代码学习",
@@ -265,6 +274,10 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         break;
     }
     case BATCHED:
+        // more than kValuVectors vectors run as column blocks of at most
+        // kValuVectors (one launch and one pass over A each); the plan is
+        // the first block's
+        if (nvec > kValuVectors) nvec = kValuVectors;
         p.lanes_per_row = kWave;
         p.rows_per_wave = batched_rows(nvec);
         p.waves_per_group = kBlock / kWave;
@@ -289,9 +302,9 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         p.lanes_per_row = 4 * kMfmaWaves;
         p.rows_per_wave = kMfmaRows;
         p.waves_per_group = kMfmaWaves;
-        p.batch = kMfmaChunk;
+        p.batch = mfma_chunk(nvec);
         p.row_tiles = 1;
-        p.lds_bytes = mfma_lds_bytes();
+        p.lds_bytes = mfma_lds_bytes(nvec);
         break;
     default:
         return INVALID;

@@ -67,7 +67,7 @@ def test_half_validation(fn):
 
 
 @pytest.mark.parametrize("fn", [lg.gemv_batched_f16, lg.gemv_batched_bf16])
-@pytest.mark.parametrize("nvec", [0, 17, -3])
+@pytest.mark.parametrize("nvec", [0, 65, -3])
 def test_batched_rejects_nvec(fn, nvec):
     assert fn(GOOD, 8, GOOD, None, GOOD, 4, 8, nvec, None) == lg.GEMV_ERROR_INVALID_VALUE
 
@@ -199,7 +199,22 @@ def test_batched_plans():
     assert q1["family"] != lg.FAMILY_BATCHED   # nvec 1 is plain GEMV
     assert p("f16", 4096, 4095, nvec=4)["vector_loads"] == 0  # X columns misaligned
     with pytest.raises(lg.GemvError):
-        p("f16", 4096, 4096, nvec=17)
+        p("f16", 4096, 4096, nvec=65)
+
+
+def test_wide_batched_plans():
+    """17-64 vectors: the matrix-core kernel takes 2 or 4 tiles of 16
+    vectors per A operand, in chunks of 8 or 4 steps, so the X staged per
+    chunk stays 16 KiB per wavefront and the LDS within 160 KiB; the
+    vector-ALU family plans its first block of 16 vectors."""
+    for nvec, chunk, tiles in ((16, 16, 1), (17, 8, 2), (32, 8, 2), (33, 4, 4), (64, 4, 4)):
+        q = p("bf16", 4096, 4096, nvec=nvec)
+        assert q["family"] == lg.FAMILY_BATCHED_MFMA and q["batch"] == chunk
+        assert q["grid"] == 256 and q["block"] == 512
+        assert q["lds_bytes"] == 8 * 16 * tiles * (chunk * 64 + 16) <= 160 * 1024
+    for nvec in (17, 40, 64):
+        assert p("f16", 999, 1000, nvec=nvec, A=ALIGNED + 2) == p("f16", 999, 1000, nvec=16,
+                                                                  A=ALIGNED + 2)
 
 
 # ---------------------------------------------------------------------------

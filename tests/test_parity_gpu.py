@@ -185,7 +185,28 @@ def test_random_every_family(dtype, M, K):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("nvec", [2, 3, 8, 13, 16])
+@pytest.mark.parametrize("nvec", [17, 24, 31, 32, 33, 47, 64])
+def test_integer_wide_batched(dtype, nvec):
+    """17-64 vectors: one pass over A on the matrix cores (2 or 4 vector
+    tiles), or blocks of 16 vectors on the vector ALUs; all bit-exact."""
+    for M, K, lda in ((67, 512, 512), (130, 1000, 1000), (9, 4104, 4104), (33, 77, 80),
+                      (300, 2048, 2056)):
+        case = gi.make_integer(dtype, M, K, seed=nvec * 100 + K, nvec=nvec, lda=lda,
+                               bias=nvec % 2 == 1)
+        ref, _ = run_oracle(case)
+        assert_bit_exact(run_gpu(case, lg.FAMILY_AUTO, batched=True), ref,
+                         f"{dtype} nvec={nvec} {M}x{K}")
+        assert_bit_exact(run_gpu(case, lg.FAMILY_BATCHED, batched=True, misalign=1), ref,
+                         f"{dtype} nvec={nvec} {M}x{K} element loads")
+        assert_bit_exact(run_gpu(case, lg.FAMILY_BATCHED, batched=True), ref,
+                         f"{dtype} nvec={nvec} {M}x{K} vector ALU blocks")
+        if K % 8 == 0 and lda % 8 == 0:
+            assert_bit_exact(run_gpu(case, lg.FAMILY_BATCHED_MFMA, batched=True), ref,
+                             f"{dtype} nvec={nvec} {M}x{K} matrix cores")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("nvec", [2, 3, 8, 13, 16, 20, 32, 64])
 def test_random_batched(dtype, nvec):
     for M, K in ((4096, 4096), (1000, 1000), (64, 14336)):
         case = gi.make_random(dtype, M, K, seed=nvec + K, nvec=nvec, bias=True,
@@ -227,6 +248,15 @@ def test_batched_columns_and_single_vector_agree():
         cp = gi.Case(case.name, dtype, case.M, case.K, case.A, case.X[perm], case.bias,
                      case.lda, case.nvec)
         assert_bit_exact(run_gpu(cp, lg.FAMILY_AUTO, batched=True), Y[perm], "column permutation")
+        # 40 vectors span three matrix-core tiles: columns moved between tiles
+        # (and into the zero-padded last tile) give the same bits
+        wide = gi.make_random(dtype, 500, 1024, seed=5, nvec=40, bias=True, dist="normal")
+        W = run_gpu(wide, lg.FAMILY_AUTO, batched=True)
+        perm = np.random.default_rng(3).permutation(wide.nvec)
+        cw = gi.Case(wide.name, dtype, wide.M, wide.K, wide.A, wide.X[perm], wide.bias,
+                     wide.lda, wide.nvec)
+        assert_bit_exact(run_gpu(cw, lg.FAMILY_AUTO, batched=True), W[perm],
+                         "column permutation across tiles")
         for j in (0, 5, 10):
             c1 = gi.Case(case.name, dtype, case.M, case.K, case.A, case.X[j:j + 1], case.bias,
                          case.lda)

@@ -90,21 +90,30 @@ const void* rows_fn(int lanes, int tiles) {
 }
 
 template <class D, bool VEC, bool MULTI, int B>
-const void* group_fn_b() {
+const void* group_fn_b(int rows) {
     constexpr int W = gemvplan::kGroupWaves;
-    if constexpr (MULTI)
-        return (const void*)&gemvdev::gemv_group_multi_kernel<D, W, B, VEC>;
-    else
-        return (const void*)&gemvdev::gemv_group_kernel<D, W, B, VEC>;
+    if constexpr (MULTI) {
+        return rows == 1 ? (const void*)&gemvdev::gemv_group_multi_kernel<D, W, B, VEC> : nullptr;
+    } else {
+        switch (rows) {
+        case 1: return (const void*)&gemvdev::gemv_group_kernel<D, W, 1, B, VEC>;
+        case 2:
+            static_assert(gemvplan::kGroupMaxTileRows == 2, "group kernels are built for 1 or 2 rows");
+            if constexpr (2 * B <= gemvplan::kGroupTileLoads)
+                return (const void*)&gemvdev::gemv_group_kernel<D, W, 2, B, VEC>;
+            return nullptr;
+        default: return nullptr;
+        }
+    }
 }
 
 template <class D, bool VEC, bool MULTI>
-const void* group_fn(int batch) {
+const void* group_fn(int batch, int rows) {
     switch (batch) {
-    case 1: return group_fn_b<D, VEC, MULTI, 1>();
-    case 2: return group_fn_b<D, VEC, MULTI, 2>();
-    case 4: return group_fn_b<D, VEC, MULTI, 4>();
-    case 8: return group_fn_b<D, VEC, MULTI, 8>();
+    case 1: return group_fn_b<D, VEC, MULTI, 1>(rows);
+    case 2: return group_fn_b<D, VEC, MULTI, 2>(rows);
+    case 4: return group_fn_b<D, VEC, MULTI, 4>(rows);
+    case 8: return group_fn_b<D, VEC, MULTI, 8>(rows);
     default: return nullptr;
     }
 }
@@ -114,7 +123,7 @@ const void* single_fn(const Plan& p) {
     switch (p.family) {
     case gemvplan::ROWS_PER_WAVE:
     case gemvplan::WAVE_PER_ROW: return rows_fn<D, VEC, MULTI>(p.lanes_per_row, p.row_tiles);
-    case gemvplan::GROUP_PER_ROW: return group_fn<D, VEC, MULTI>(p.batch);
+    case gemvplan::GROUP_PER_ROW: return group_fn<D, VEC, MULTI>(p.batch, p.row_tiles);
     default: return nullptr;
     }
 }
@@ -361,7 +370,7 @@ gemv_status_t run_multi(const gemv_segment_t* segs, int count, const void* x, in
     rows.count = count;
     Plan p;
     if (gemvplan::make_plan_vec(dtype, (int)total, K, 1, vec, gemvplan::AUTO, &p,
-                                gemvplan::kMultiMaxRowTiles) != gemvplan::OK)
+                                gemvplan::kMultiMaxRowTiles, 1) != gemvplan::OK)
         return GEMV_ERROR_INVALID_VALUE;
     const void* fn = single_fn<D, true>(p);
     if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;

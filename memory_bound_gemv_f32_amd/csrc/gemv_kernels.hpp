@@ -271,61 +271,78 @@ gemv_rows_multi_kernel(const Segments<typename D::storage> rows,
     rows_body<D, L, U, BATCH, VEC>(rows, x, K);
 }
 
-// Workgroup-per-row kernel: W wavefronts (64·W lanes) share one row; each
-// wavefront reduces its lanes, writes one partial to LDS, and after one
-// barrier thread 0 adds the W partials in wavefront order, adds the bias and
-// writes y[row] (page "第 3 课", the block-reduction structure of section
-// "C. 点积规约与原子写入解耦" on 64-lane wavefronts).
-template <class D, int W, int BATCH, bool VEC, class Rows>
+// Workgroup-per-row kernel: W wavefronts (64·W lanes) share U consecutive
+// rows, rows tile·U .. tile·U + U - 1; lane `sub` walks chunks sub, sub + 64·W,
+// ... of every one of the U rows against the same x chunk, so a workgroup
+// fetches x once for its U rows.  Each wavefront reduces its lanes, writes one
+// partial per row to LDS, and after one barrier thread u adds row u's W
+// partials in wavefront order, adds the bias and writes y (page "第 3 课", the
+// block-reduction structure of section "C. 点积规约与原子写入解耦" on 64-lane
+// wavefronts).  A row's sum does not depend on U.
+template <class D, int W, int U, int BATCH, bool VEC, class Rows>
 __device__ __forceinline__ void group_body(const Rows& rows, const typename D::xstorage* __restrict__ x,
-                                           int K, int64_t row) {
+                                           int K, int64_t tile) {
     using S = typename D::storage;
     using C = Chunk<D, VEC>;
     constexpr int L = W * 64;
     constexpr int E = C::elems;
-    __shared__ float partial[W];
+    __shared__ float partial[W][U];
 
-    if (row >= rows.M) return;  // uniform across the workgroup
+    const int64_t M = rows.M;
+    const int64_t row0 = tile * U;
+    if (row0 >= M) return;  // uniform across the workgroup
     const int sub = threadIdx.x;
-    const S* rp = rows.row(row);
-    const float b = sub == 0 ? rows.bias_of(row) : 0.f;
-    const float sc = sub == 0 ? scale_of(rows, row) : 0.f;
+    const S* rp[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) rp[u] = rows.row(row0 + u < M ? row0 + u : M - 1);
+    // thread u < U finishes row row0 + u; its bias and scale are read now
+    const bool writer = sub < U && row0 + sub < M;
+    const float b = writer ? rows.bias_of(row0 + sub) : 0.f;
+    const float sc = writer ? scale_of(rows, row0 + sub) : 0.f;
 
-    float acc[1][2] = {{0.f, 0.f}};
-    const S* const rps[1] = {rp};
+    float acc[U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u][0] = acc[u][1] = 0.f;
     const int nfull = K / E;
     const int nsafe = nfull - nfull % (BATCH * L);
     int c0 = 0;
-    for (; c0 < nsafe; c0 += BATCH * L) rows_batch<C, L, 1, BATCH, false>(rps, x, c0 + sub, nfull, acc);
-    if (c0 < nfull) rows_batch<C, L, 1, BATCH, true>(rps, x, c0 + sub, nfull, acc);
+    for (; c0 < nsafe; c0 += BATCH * L) rows_batch<C, L, U, BATCH, false>(rp, x, c0 + sub, nfull, acc);
+    if (c0 < nfull) rows_batch<C, L, U, BATCH, true>(rp, x, c0 + sub, nfull, acc);
     if constexpr (VEC) {
-        for (int k = nfull * E + sub; k < K; k += L)
-            acc[0][1] = __builtin_fmaf(widen_a(D{}, rp[k]), widen_x(D{}, x[k]), acc[0][1]);
+        for (int k = nfull * E + sub; k < K; k += L) {
+            const float xe = widen_x(D{}, x[k]);
+#pragma unroll
+            for (int u = 0; u < U; ++u) acc[u][1] = __builtin_fmaf(widen_a(D{}, rp[u][k]), xe, acc[u][1]);
+        }
     }
 
-    const float v = segment_sum<64>(acc[0][0] + acc[0][1]);
-    if ((threadIdx.x & 63) == 0) partial[threadIdx.x >> 6] = v;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        float s = partial[0];
 #pragma unroll
-        for (int w = 1; w < W; ++w) s += partial[w];
-        rows.store(row, row_result<Rows>(s, sc, b));
+    for (int u = 0; u < U; ++u) {
+        const float v = segment_sum<64>(acc[u][0] + acc[u][1]);
+        if ((threadIdx.x & 63) == 0) partial[threadIdx.x >> 6][u] = v;
+    }
+    __syncthreads();
+    if (writer) {
+        float s = partial[0][sub];
+#pragma unroll
+        for (int w = 1; w < W; ++w) s += partial[w][sub];
+        rows.store(row0 + sub, row_result<Rows>(s, sc, b));
     }
 }
 
-template <class D, int W, int BATCH, bool VEC>
+template <class D, int W, int U, int BATCH, bool VEC>
 __global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4)))
 gemv_group_kernel(const typename D::storage* A, int64_t lda, const float* bias, float* y, int64_t M,
                   const typename D::storage* __restrict__ x, int K) {
-    group_body<D, W, BATCH, VEC>(OneMatrix<typename D::storage>{A, lda, bias, y, M}, x, K, blockIdx.x);
+    group_body<D, W, U, BATCH, VEC>(OneMatrix<typename D::storage>{A, lda, bias, y, M}, x, K,
+                                    blockIdx.x);
 }
 
 template <class D, int W, int BATCH, bool VEC>
 __global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4)))
 gemv_group_multi_kernel(const Segments<typename D::storage> rows,
                         const typename D::storage* __restrict__ x, int K) {
-    group_body<D, W, BATCH, VEC>(rows, x, K, blockIdx.x);
+    group_body<D, W, 1, BATCH, VEC>(rows, x, K, blockIdx.x);
 }
 
 // Weight-only int8: the rows and workgroup-per-row bodies on int8 weights,
@@ -341,8 +358,8 @@ template <class X, int W, int BATCH, bool VEC>
 __global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4)))
 gemv_group_q8_kernel(const int8_t* Q, int64_t ldq, const float* scale, const float* bias, float* y,
                      int64_t M, const typename X::storage* __restrict__ x, int K) {
-    group_body<TQ8<X>, W, BATCH, VEC>(ScaledMatrix<int8_t>{Q, ldq, scale, bias, y, M}, x, K,
-                                      blockIdx.x);
+    group_body<TQ8<X>, W, 1, BATCH, VEC>(ScaledMatrix<int8_t>{Q, ldq, scale, bias, y, M}, x, K,
+                                         blockIdx.x);
 }
 
 // Split-K, pass 1: workgroup (m, s) forms the dot product of row m's slice s
@@ -378,7 +395,7 @@ gemv_splitk_partial_kernel(const typename D::storage* A, int64_t lda, float* ws,
     const int64_t k0 = (int64_t)s * slice;
     const int64_t rest = (int64_t)K - k0;
     const int ks = rest < slice ? (int)rest : slice;
-    group_body<D, kGroupWavesDev, BATCH, VEC>(
+    group_body<D, kGroupWavesDev, 1, BATCH, VEC>(
         SliceOfRows<typename D::storage>{A + k0, lda, ws + s, splits, M}, x + k0, ks, m);
 }
 

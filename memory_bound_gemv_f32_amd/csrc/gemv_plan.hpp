@@ -65,6 +65,18 @@ constexpr int64_t kGroupManyRowsMinLoads = 512;
 // Wave-per-row family: loads per lane kept in flight per row.
 constexpr int kWaveBatch = 8;
 constexpr int kGroupBatch = 8;
+// Workgroup-per-row family: when x is longer than kGroupShareMinXBytes (it
+// no longer stays in a CU's vector L1 next to the A stream, and a workgroup
+// per row would fetch all of x from L2 once per row), up to
+// kGroupMaxTileRows rows per workgroup share each x chunk, as long as rows ×
+// loads per lane stays within kGroupTileLoads per batch and at least
+// kGroupTileMinGroups workgroups remain.  Measured on MI355X, bf16
+// 4096 × 14336: 21.7 -> 20.1 µs with two rows per workgroup; with an 8 KiB x
+// (4096 × 4096, 14336 × 4096) sharing it was 1-9 % slower.
+constexpr int64_t kGroupShareMinXBytes = 16 * 1024;
+constexpr int kGroupMaxTileRows = 2;
+constexpr int kGroupTileLoads = 16;
+constexpr int64_t kGroupTileMinGroups = 256;
 // Batched family: loads in flight per row, and rows per wavefront, fewer as
 // the number of vectors grows so that rows × vectors accumulators plus the
 // loaded chunks fit the register budget of four wavefronts per SIMD.
@@ -189,7 +201,7 @@ inline bool vector_ok(int dtype, int K, int lda, int nvec, uintptr_t A, uintptr_
 constexpr int kMultiMaxRowTiles = 2;
 
 inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family, Plan* out,
-                         int max_row_tiles = 8) {
+                         int max_row_tiles = 8, int max_group_rows = kGroupMaxTileRows) {
     if (dtype < F32 || dtype > Q8 || M < 0 || K < 0 || nvec < 1 || nvec > kMaxVectors)
         return INVALID;
 
@@ -269,8 +281,16 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         const int64_t per_lane = ceil_div(full, (int64_t)p.lanes_per_row);
         const int cap = dtype == Q8 ? kQ8Batch : kGroupBatch;
         p.batch = per_lane >= cap ? cap : next_pow2(per_lane < 1 ? 1 : per_lane);
-        p.row_tiles = 1;
-        p.lds_bytes = (int)(kGroupWaves * sizeof(float));
+        // rows per workgroup (one x chunk serves all of them)
+        int u = 1;
+        const int umax = dtype == Q8 ? 1 : max_group_rows;
+        if ((int64_t)K * element_bytes(dtype) > kGroupShareMinXBytes) {
+            while (2 * u <= umax && 2 * u * p.batch <= kGroupTileLoads &&
+                   ceil_div(M, 2 * u) >= kGroupTileMinGroups)
+                u *= 2;
+        }
+        p.row_tiles = u;
+        p.lds_bytes = (int)(kGroupWaves * u * sizeof(float));
         break;
     }
     case BATCHED:
@@ -310,7 +330,9 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         return INVALID;
     }
     p.block = p.waves_per_group * kWave;
-    if (fam == GROUP_PER_ROW || fam == GATED_SILU)
+    if (fam == GROUP_PER_ROW)
+        p.rows_per_group = p.row_tiles;
+    else if (fam == GATED_SILU)
         p.rows_per_group = 1;
     else if (fam == BATCHED_MFMA)
         p.rows_per_group = kMfmaRows;

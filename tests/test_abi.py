@@ -421,3 +421,21 @@ def test_q8_families():
     # byte-aligned Q or an odd row pitch fall back to element loads
     assert lg.plan_q8("f16", 64, 4096, Q_addr=ALIGNED + 1, x_addr=ALIGNED)["vector_loads"] == 0
     assert lg.plan_q8("f16", 64, 4096, ldq=4100, Q_addr=ALIGNED, x_addr=ALIGNED)["vector_loads"] == 0
+
+
+def test_long_x_rows_share_a_workgroup():
+    """Rows whose x is longer than 16 KiB run two to a workgroup (each x chunk
+    serves both), when that still leaves 256 workgroups; shorter x keeps one
+    row per workgroup."""
+    q = p("bf16", 4096, 14336)
+    assert (q["family"], q["row_tiles"], q["rows_per_group"], q["grid"]) == \
+        (lg.FAMILY_GROUP_PER_ROW, 2, 2, 2048)
+    assert p("f32", 515, 8300, family=lg.FAMILY_GROUP_PER_ROW)["grid"] == 258
+    for dtype, M, K in (("bf16", 14336, 4096), ("bf16", 4096, 8192), ("bf16", 100, 100000),
+                        ("bf16", 510, 50000)):
+        q = p(dtype, M, K, family=lg.FAMILY_GROUP_PER_ROW)
+        assert q["row_tiles"] == 1 and q["grid"] == M
+    # the loads of both rows' batch stay within 16 per lane
+    for K in (8200, 14336, 30000, 1 << 20):
+        q = p("bf16", 4096, K, family=lg.FAMILY_GROUP_PER_ROW)
+        assert q["row_tiles"] * q["batch"] <= 16

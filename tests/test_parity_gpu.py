@@ -94,7 +94,8 @@ def test_one_hot(dtype, M, K, extra):
 
 INT_SHAPES = [(1, 1), (5, 3), (63, 8), (64, 15), (65, 16), (130, 17), (257, 31),
               (33, 32), (17, 33), (9, 127), (300, 128), (31, 129), (7, 255),
-              (129, 256), (3, 257), (70, 1000), (40, 1024), (5, 4097), (3, 14337)]
+              (129, 256), (3, 257), (70, 1000), (40, 1024), (5, 4097), (3, 14337),
+              (513, 4200), (515, 8300)]  # last two: two rows per workgroup share x
 
 
 @pytest.mark.parametrize("dtype", gi.DTYPES)

@@ -46,21 +46,31 @@ gemv_status_t finish(hipError_t err) {
 
 // ---- rows-per-wave / wave-per-row / workgroup-per-row ----------------------
 
-// MULTI selects the segment-table kernels (several matrices sharing x).
-template <class D, int L, bool VEC, bool MULTI>
+// NSEG > 0 selects the segment-table kernels (several matrices sharing x;
+// the select chains cover NSEG segments), NSEG == 0 the one-matrix kernels.
+template <class D, int L, bool VEC, int NSEG>
 const void* rows_fn(int tiles) {
     if constexpr (L == 64) {
         // one wavefront per row: a single row tile, kWaveBatch loads in flight
         if (tiles != 1) return nullptr;
-        if constexpr (MULTI)
-            return (const void*)&gemvdev::gemv_rows_multi_kernel<D, 64, 1, gemvplan::kWaveBatch, VEC>;
+        if constexpr (NSEG == gemvdev::kFewSegments)
+            return (const void*)&gemvdev::gemv_rows_multi3_kernel<D, 64, 1, gemvplan::kWaveBatch, VEC>;
+        else if constexpr (NSEG > 0)
+            return (const void*)&gemvdev::gemv_rows_multi_kernel<D, 64, 1, gemvplan::kWaveBatch, VEC, NSEG>;
         else
             return (const void*)&gemvdev::gemv_rows_kernel<D, 64, 1, gemvplan::kWaveBatch, VEC>;
-    } else if constexpr (MULTI) {
+    } else if constexpr (NSEG > 0) {
         // per-lane segment lookups cost registers: at most two row tiles
+        if constexpr (NSEG == gemvdev::kFewSegments) {
+            switch (tiles) {
+            case 1: return (const void*)&gemvdev::gemv_rows_multi3_kernel<D, L, 1, 1, VEC>;
+            case 2: return (const void*)&gemvdev::gemv_rows_multi3_kernel<D, L, 2, 1, VEC>;
+            default: return nullptr;
+            }
+        }
         switch (tiles) {
-        case 1: return (const void*)&gemvdev::gemv_rows_multi_kernel<D, L, 1, 1, VEC>;
-        case 2: return (const void*)&gemvdev::gemv_rows_multi_kernel<D, L, 2, 1, VEC>;
+        case 1: return (const void*)&gemvdev::gemv_rows_multi_kernel<D, L, 1, 1, VEC, NSEG>;
+        case 2: return (const void*)&gemvdev::gemv_rows_multi_kernel<D, L, 2, 1, VEC, NSEG>;
         default: return nullptr;
         }
     } else {
@@ -75,25 +85,27 @@ const void* rows_fn(int tiles) {
     }
 }
 
-template <class D, bool VEC, bool MULTI>
+template <class D, bool VEC, int NSEG>
 const void* rows_fn(int lanes, int tiles) {
     switch (lanes) {
-    case 1: return rows_fn<D, 1, VEC, MULTI>(tiles);
-    case 2: return rows_fn<D, 2, VEC, MULTI>(tiles);
-    case 4: return rows_fn<D, 4, VEC, MULTI>(tiles);
-    case 8: return rows_fn<D, 8, VEC, MULTI>(tiles);
-    case 16: return rows_fn<D, 16, VEC, MULTI>(tiles);
-    case 32: return rows_fn<D, 32, VEC, MULTI>(tiles);
-    case 64: return rows_fn<D, 64, VEC, MULTI>(tiles);
+    case 1: return rows_fn<D, 1, VEC, NSEG>(tiles);
+    case 2: return rows_fn<D, 2, VEC, NSEG>(tiles);
+    case 4: return rows_fn<D, 4, VEC, NSEG>(tiles);
+    case 8: return rows_fn<D, 8, VEC, NSEG>(tiles);
+    case 16: return rows_fn<D, 16, VEC, NSEG>(tiles);
+    case 32: return rows_fn<D, 32, VEC, NSEG>(tiles);
+    case 64: return rows_fn<D, 64, VEC, NSEG>(tiles);
     default: return nullptr;
     }
 }
 
-template <class D, bool VEC, bool MULTI, int B>
+template <class D, bool VEC, int NSEG, int B>
 const void* group_fn_b(int rows) {
     constexpr int W = gemvplan::kGroupWaves;
-    if constexpr (MULTI) {
-        return rows == 1 ? (const void*)&gemvdev::gemv_group_multi_kernel<D, W, B, VEC> : nullptr;
+    if constexpr (NSEG == gemvdev::kFewSegments) {
+        return rows == 1 ? (const void*)&gemvdev::gemv_group_multi3_kernel<D, W, B, VEC> : nullptr;
+    } else if constexpr (NSEG > 0) {
+        return rows == 1 ? (const void*)&gemvdev::gemv_group_multi_kernel<D, W, B, VEC, NSEG> : nullptr;
     } else {
         switch (rows) {
         case 1: return (const void*)&gemvdev::gemv_group_kernel<D, W, 1, B, VEC>;
@@ -107,30 +119,30 @@ const void* group_fn_b(int rows) {
     }
 }
 
-template <class D, bool VEC, bool MULTI>
+template <class D, bool VEC, int NSEG>
 const void* group_fn(int batch, int rows) {
     switch (batch) {
-    case 1: return group_fn_b<D, VEC, MULTI, 1>(rows);
-    case 2: return group_fn_b<D, VEC, MULTI, 2>(rows);
-    case 4: return group_fn_b<D, VEC, MULTI, 4>(rows);
-    case 8: return group_fn_b<D, VEC, MULTI, 8>(rows);
+    case 1: return group_fn_b<D, VEC, NSEG, 1>(rows);
+    case 2: return group_fn_b<D, VEC, NSEG, 2>(rows);
+    case 4: return group_fn_b<D, VEC, NSEG, 4>(rows);
+    case 8: return group_fn_b<D, VEC, NSEG, 8>(rows);
     default: return nullptr;
     }
 }
 
-template <class D, bool VEC, bool MULTI>
+template <class D, bool VEC, int NSEG>
 const void* single_fn(const Plan& p) {
     switch (p.family) {
     case gemvplan::ROWS_PER_WAVE:
-    case gemvplan::WAVE_PER_ROW: return rows_fn<D, VEC, MULTI>(p.lanes_per_row, p.row_tiles);
-    case gemvplan::GROUP_PER_ROW: return group_fn<D, VEC, MULTI>(p.batch, p.row_tiles);
+    case gemvplan::WAVE_PER_ROW: return rows_fn<D, VEC, NSEG>(p.lanes_per_row, p.row_tiles);
+    case gemvplan::GROUP_PER_ROW: return group_fn<D, VEC, NSEG>(p.batch, p.row_tiles);
     default: return nullptr;
     }
 }
 
-template <class D, bool MULTI>
+template <class D, int NSEG>
 const void* single_fn(const Plan& p) {
-    return p.vector_loads ? single_fn<D, true, MULTI>(p) : single_fn<D, false, MULTI>(p);
+    return p.vector_loads ? single_fn<D, true, NSEG>(p) : single_fn<D, false, NSEG>(p);
 }
 
 // ---- batched ----------------------------------------------------------------
@@ -308,7 +320,7 @@ gemv_status_t run_single(const Plan& p, const void* A, int lda, const void* X, c
         }
         return GEMV_SUCCESS;
     }
-    const void* fn = single_fn<D, false>(p);
+    const void* fn = single_fn<D, 0>(p);
     if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;
     int64_t lda64 = lda, M64 = M;
     void* argv[] = {(void*)&A, (void*)&lda64, (void*)&bias, (void*)&Y, (void*)&M64, (void*)&X,
@@ -338,14 +350,72 @@ gemv_status_t run(int dtype, int family, const void* A, int lda, const void* X,
     }
 }
 
+template <class D, int NSEG>
+gemv_status_t launch_multi(const gemv_segment_t* segs, int count, const void* x, int K, int total,
+                           bool vec, hipStream_t stream) {
+    using S = typename D::storage;
+    Segments<S, NSEG> rows{};
+    rows.x = static_cast<const S*>(x);
+    rows.K = K;
+    rows.M = total;
+    int end = 0;
+    for (int i = 0; i < count; ++i) {
+        end += segs[i].M;
+        rows.seg[i] = gemvdev::SegEntry<S>{static_cast<const S*>(segs[i].A), end, segs[i].lda};
+        rows.bias[i] = segs[i].bias;
+        rows.y[i] = segs[i].y;
+    }
+    // unused entries end at the last row, so no row selects the entry after them
+    for (int i = count; i < gemvdev::kMaxSegments; ++i) rows.seg[i] = gemvdev::SegEntry<S>{nullptr, total, 0};
+    Plan p;
+    if (gemvplan::make_plan_vec(dtype_code<D>(), total, K, 1, vec, gemvplan::AUTO, &p,
+                                gemvplan::kMultiMaxRowTiles, 1) != gemvplan::OK)
+        return GEMV_ERROR_INVALID_VALUE;
+    const void* fn = single_fn<D, NSEG>(p);
+    if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;
+    void* argv[] = {(void*)&rows};
+    return finish(launch(fn, p, stream, argv));
+}
+
+template <class D>
+gemv_status_t launch_multi3(const gemv_segment_t* segs, int count, const void* x, int K, int total,
+                            int lda, bool vec, hipStream_t stream) {
+    using S = typename D::storage;
+    // absent segments (count < 3) are empty: they end at the last row and are
+    // never selected
+    const S* A[3] = {nullptr, nullptr, nullptr};
+    int end[3] = {total, total, total};
+    const float* b[3] = {nullptr, nullptr, nullptr};
+    float* y[3] = {nullptr, nullptr, nullptr};
+    int e = 0;
+    for (int i = 0; i < count; ++i) {
+        e += segs[i].M;
+        A[i] = static_cast<const S*>(segs[i].A);
+        end[i] = e;
+        b[i] = segs[i].bias;
+        y[i] = segs[i].y;
+    }
+    Plan p;
+    if (gemvplan::make_plan_vec(dtype_code<D>(), total, K, 1, vec, gemvplan::AUTO, &p,
+                                gemvplan::kMultiMaxRowTiles, 1) != gemvplan::OK)
+        return GEMV_ERROR_INVALID_VALUE;
+    const void* fn = single_fn<D, gemvdev::kFewSegments>(p);
+    if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;
+    const S* xs = static_cast<const S*>(x);
+    int has_bias = b[0] != nullptr || b[1] != nullptr || b[2] != nullptr;
+    void* argv[] = {(void*)&xs,   (void*)&A[0], (void*)&A[1],     (void*)&A[2], (void*)&end[0],
+                    (void*)&end[1], (void*)&lda, (void*)&K,      (void*)&total, (void*)&has_bias,
+                    (void*)&b[0], (void*)&b[1], (void*)&b[2],     (void*)&y[0], (void*)&y[1],
+                    (void*)&y[2]};
+    return finish(launch(fn, p, stream, argv));
+}
+
 template <class D>
 gemv_status_t run_multi(const gemv_segment_t* segs, int count, const void* x, int K,
                         hipStream_t stream) {
-    using S = typename D::storage;
     constexpr int dtype = dtype_code<D>();
     if (segs == nullptr || count < 1 || count > GEMV_MAX_SEGMENTS || K < 0)
         return GEMV_ERROR_INVALID_VALUE;
-    Segments<S> rows{};
     int64_t total = 0;
     bool vec = ((uintptr_t)x % gemvplan::kLoadBytes) == 0;
     for (int i = 0; i < count; ++i) {
@@ -353,29 +423,28 @@ gemv_status_t run_multi(const gemv_segment_t* segs, int count, const void* x, in
         if (gemvplan::validate(dtype, s.M, K, s.lda, 1, (uintptr_t)s.A, (uintptr_t)x,
                                (uintptr_t)s.bias, (uintptr_t)s.y) != gemvplan::OK)
             return GEMV_ERROR_INVALID_VALUE;
-        rows.start[i] = total;
-        rows.A[i] = static_cast<const S*>(s.A);
-        rows.lda[i] = s.lda;
-        rows.bias[i] = s.bias;
-        rows.y[i] = s.y;
-        if (s.M > 0)
+        // a segment of one row never steps by its pitch: only its A pointer
+        // must be aligned for 16-byte loads
+        if (s.M > 1)
             vec = vec && gemvplan::vector_ok(dtype, K, s.lda, 1, (uintptr_t)s.A, (uintptr_t)x);
+        else if (s.M == 1)
+            vec = vec && ((uintptr_t)s.A % gemvplan::kLoadBytes) == 0;
         total += s.M;
     }
-    // unused table entries start past the last row, so no row selects them
-    for (int i = count; i < gemvdev::kMaxSegments; ++i) rows.start[i] = total;
     if (total > 0x7fffffff) return GEMV_ERROR_INVALID_VALUE;
     if (total == 0) return GEMV_SUCCESS;
-    rows.M = total;
-    rows.count = count;
-    Plan p;
-    if (gemvplan::make_plan_vec(dtype, (int)total, K, 1, vec, gemvplan::AUTO, &p,
-                                gemvplan::kMultiMaxRowTiles, 1) != gemvplan::OK)
-        return GEMV_ERROR_INVALID_VALUE;
-    const void* fn = single_fn<D, true>(p);
-    if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;
-    void* argv[] = {(void*)&rows, (void*)&x, (void*)&K};
-    return finish(launch(fn, p, stream, argv));
+    // up to three segments with one row pitch (segments of at most one row
+    // never step by theirs): the scalar-argument kernels
+    int pitch = -1;
+    bool one_pitch = true;
+    for (int i = 0; i < count; ++i) {
+        if (segs[i].M <= 1) continue;
+        if (pitch < 0) pitch = segs[i].lda;
+        one_pitch = one_pitch && segs[i].lda == pitch;
+    }
+    if (count <= gemvdev::kFewSegments && one_pitch)
+        return launch_multi3<D>(segs, count, x, K, (int)total, pitch < 0 ? K : pitch, vec, stream);
+    return launch_multi<D, gemvdev::kMaxSegments>(segs, count, x, K, (int)total, vec, stream);
 }
 
 template <class D>

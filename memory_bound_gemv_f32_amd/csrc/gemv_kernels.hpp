@@ -47,7 +47,8 @@ struct OneMatrix {
     float* y;
     int64_t M;
     __device__ __forceinline__ const S* row(int64_t m) const { return A + m * lda; }
-    __device__ __forceinline__ float bias_of(int64_t m) const { return bias != nullptr ? bias[m] : 0.f; }
+    __device__ __forceinline__ bool any_bias() const { return bias != nullptr; }
+    __device__ __forceinline__ float bias_of(int64_t m) const { return bias[m]; }
     __device__ __forceinline__ void store(int64_t m, float v) const { y[m] = v; }
 };
 
@@ -65,7 +66,8 @@ struct ScaledMatrix {
     int64_t M;
     __device__ __forceinline__ const S* row(int64_t m) const { return A + m * lda; }
     __device__ __forceinline__ float scale_of(int64_t m) const { return scale[m]; }
-    __device__ __forceinline__ float bias_of(int64_t m) const { return bias != nullptr ? bias[m] : 0.f; }
+    __device__ __forceinline__ bool any_bias() const { return bias != nullptr; }
+    __device__ __forceinline__ float bias_of(int64_t m) const { return bias[m]; }
     __device__ __forceinline__ void store(int64_t m, float v) const { y[m] = v; }
 };
 
@@ -87,59 +89,134 @@ __device__ __forceinline__ float scale_of(const Rows& rows, int64_t m) {
 }
 
 // Up to kMaxSegments matrices with the same K, stacked row-wise: rows
-// start[i] .. start[i+1]-1 of the stack are rows of segment i.  Every
-// segment multiplies the same x (e.g. the q, k and v projections of one
-// token).  A row's segment is found by a select chain over the (uniform)
-// boundaries, so the fields stay in scalar registers.
+// seg[i-1].end .. seg[i].end - 1 of the stack are rows of segment i (segment
+// 0 starts at row 0).  Every segment multiplies the same x (e.g. the q, k
+// and v projections of one token).  A row's segment is found by a select
+// chain over the boundaries of the first NSEG entries.  The table is the
+// kernel's only argument, read from memory; calls with at most three
+// segments of one row pitch use ThreeSegments below instead.
 constexpr int kMaxSegments = 8;
+constexpr int kFewSegments = 3;
+
+// A wave-uniform value (a kernel argument) passed through readfirstlane.  The
+// segment choosers select between such values: a select between two fields
+// read from the argument structure would otherwise be turned into one read
+// from a selected address, which leaves the structure in scratch memory (or
+// makes an indexed memory load of the argument table) ahead of the first
+// A load.
+template <class T>
+__device__ __forceinline__ T uniform(T v) {
+    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+    } else {
+        const uint64_t u = __builtin_bit_cast(uint64_t, v);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+        return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+    }
+}
 template <class S>
+struct SegEntry {
+    const S* A;
+    int end;  // one past the segment's last row in the stack
+    int lda;
+};
+static_assert(sizeof(SegEntry<float>) == 16, "four argument dwords per segment");
+template <class S, int NSEG>
 struct Segments {
     static constexpr bool kScaled = false;
-    int64_t M;  // rows in all segments
-    int count;
-    int64_t start[kMaxSegments];
-    const S* A[kMaxSegments];
-    int64_t lda[kMaxSegments];
+    __device__ __forceinline__ bool any_bias() const { return true; }  // decided per row
+    const S* x;
+    int K;
+    int M;  // rows in all segments
+    SegEntry<S> seg[kMaxSegments];
     const float* bias[kMaxSegments];
     float* y[kMaxSegments];
-    __device__ __forceinline__ int find(int64_t m) const {
-        int seg = 0;
-#pragma unroll
-        for (int i = 1; i < kMaxSegments; ++i) seg = (i < count && m >= start[i]) ? i : seg;
-        return seg;
-    }
     __device__ __forceinline__ const S* row(int64_t m) const {
-        const S* a = A[0];
-        int64_t ld = lda[0], s0 = start[0];
+        const S* a = seg[0].A;
+        int ld = seg[0].lda;
+        int64_t s0 = 0;
 #pragma unroll
-        for (int i = 1; i < kMaxSegments; ++i) {
-            const bool in = i < count && m >= start[i];
-            a = in ? A[i] : a;
-            ld = in ? lda[i] : ld;
-            s0 = in ? start[i] : s0;
+        for (int i = 1; i < NSEG; ++i) {
+            const int e = seg[i - 1].end;
+            const bool in = m >= e;
+            a = in ? seg[i].A : a;
+            ld = in ? seg[i].lda : ld;
+            s0 = in ? e : s0;
         }
-        return a + (m - s0) * ld;
+        return a + (m - s0) * (int64_t)ld;
     }
     __device__ __forceinline__ float bias_of(int64_t m) const {
         const float* b = bias[0];
-        int64_t s0 = start[0];
+        int64_t s0 = 0;
 #pragma unroll
-        for (int i = 1; i < kMaxSegments; ++i) {
-            const bool in = i < count && m >= start[i];
+        for (int i = 1; i < NSEG; ++i) {
+            const int e = seg[i - 1].end;
+            const bool in = m >= e;
             b = in ? bias[i] : b;
-            s0 = in ? start[i] : s0;
+            s0 = in ? e : s0;
         }
         return b != nullptr ? b[m - s0] : 0.f;
     }
     __device__ __forceinline__ void store(int64_t m, float v) const {
         float* o = y[0];
-        int64_t s0 = start[0];
+        int64_t s0 = 0;
 #pragma unroll
-        for (int i = 1; i < kMaxSegments; ++i) {
-            const bool in = i < count && m >= start[i];
+        for (int i = 1; i < NSEG; ++i) {
+            const int e = seg[i - 1].end;
+            const bool in = m >= e;
             o = in ? y[i] : o;
-            s0 = in ? start[i] : s0;
+            s0 = in ? e : s0;
         }
+        o[m - s0] = v;
+    }
+};
+
+// Up to three segments with one row pitch, passed as scalar kernel
+// arguments: x, the three A pointers, two boundaries, the row pitch, K, the
+// row count and whether any segment has a bias are the first 14 argument
+// dwords, the ones that arrive preloaded in SGPRs, so the first loads wait on
+// no argument load (an aggregate argument is read from memory instead, and
+// the select chain over a table in memory became an indexed load ahead of
+// the first A load).  Rows below end0 are segment 0, below end1 segment 1,
+// the rest segment 2.
+template <class S>
+struct ThreeSegments {
+    static constexpr bool kScaled = false;
+    const S* A0;
+    const S* A1;
+    const S* A2;
+    int end0, end1;
+    int lda;
+    int M;
+    int has_bias;  // 0: no segment has a bias (b0..b2 are never read)
+    const float* b0;
+    const float* b1;
+    const float* b2;
+    float* y0;
+    float* y1;
+    float* y2;
+    __device__ __forceinline__ const S* row(int64_t m) const {
+        const int e0 = uniform(end0), e1 = uniform(end1);
+        const bool in1 = m >= e0, in2 = m >= e1;
+        const S* a = in2 ? uniform(A2) : (in1 ? uniform(A1) : uniform(A0));
+        const int64_t s0 = in2 ? e1 : (in1 ? e0 : 0);
+        return a + (m - s0) * (int64_t)lda;
+    }
+    __device__ __forceinline__ bool any_bias() const { return has_bias != 0; }
+    __device__ __forceinline__ float bias_of(int64_t m) const {
+        const int e0 = uniform(end0), e1 = uniform(end1);
+        const bool in1 = m >= e0, in2 = m >= e1;
+        const float* b = in2 ? uniform(b2) : (in1 ? uniform(b1) : uniform(b0));
+        const int64_t s0 = in2 ? e1 : (in1 ? e0 : 0);
+        return b != nullptr ? b[m - s0] : 0.f;
+    }
+    __device__ __forceinline__ void store(int64_t m, float v) const {
+        const int e0 = uniform(end0), e1 = uniform(end1);
+        const bool in1 = m >= e0, in2 = m >= e1;
+        float* o = in2 ? uniform(y2) : (in1 ? uniform(y1) : uniform(y0));
+        const int64_t s0 = in2 ? e1 : (in1 ? e0 : 0);
         o[m - s0] = v;
     }
 };
@@ -215,7 +292,9 @@ __device__ __forceinline__ void rows_body(const Rows& rows, const typename D::xs
         const int u = sub + o * L;
         const int64_t row = (tile0 + u) * R + slot;
         const bool in = u < U && row < M;
-        bv[o] = in ? rows.bias_of(row) : 0.f;
+        bv[o] = 0.f;
+        // a uniform test first, so that a call without a bias reads no bias pointer
+        if (rows.any_bias() && in) bv[o] = rows.bias_of(row);
         sv[o] = in ? scale_of(rows, row) : 0.f;
     }
 
@@ -264,11 +343,26 @@ gemv_rows_kernel(const typename D::storage* A, int64_t lda, const float* bias, f
 
 // Several row-stacked matrices sharing x (the segment table is a kernel
 // argument in memory).
+template <class D, int L, int U, int BATCH, bool VEC, int NSEG>
+__global__ void __launch_bounds__(kRowsWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
+gemv_rows_multi_kernel(const Segments<typename D::storage, NSEG> rows) {
+    rows_body<D, L, U, BATCH, VEC>(rows, rows.x, rows.K);
+}
+
+// Up to three matrices: scalar arguments (see ThreeSegments).
+#define GEMV_THREE_SEGMENT_PARAMS                                                              \
+    const typename D::storage *__restrict__ x, const typename D::storage *A0,                   \
+        const typename D::storage *A1, const typename D::storage *A2, int end0, int end1,      \
+        int lda, int K, int M, int has_bias, const float *b0, const float *b1,                 \
+        const float *b2, float *y0, float *y1, float *y2
+#define GEMV_THREE_SEGMENT_ROWS                                                                \
+    ThreeSegments<typename D::storage> {                                                       \
+        A0, A1, A2, end0, end1, lda, M, has_bias, b0, b1, b2, y0, y1, y2                      \
+    }
 template <class D, int L, int U, int BATCH, bool VEC>
 __global__ void __launch_bounds__(kRowsWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
-gemv_rows_multi_kernel(const Segments<typename D::storage> rows,
-                       const typename D::storage* __restrict__ x, int K) {
-    rows_body<D, L, U, BATCH, VEC>(rows, x, K);
+gemv_rows_multi3_kernel(GEMV_THREE_SEGMENT_PARAMS) {
+    rows_body<D, L, U, BATCH, VEC>(GEMV_THREE_SEGMENT_ROWS, x, K);
 }
 
 // Workgroup-per-row kernel: W wavefronts (64·W lanes) share U consecutive
@@ -297,7 +391,7 @@ __device__ __forceinline__ void group_body(const Rows& rows, const typename D::x
     for (int u = 0; u < U; ++u) rp[u] = rows.row(row0 + u < M ? row0 + u : M - 1);
     // thread u < U finishes row row0 + u; its bias and scale are read now
     const bool writer = sub < U && row0 + sub < M;
-    const float b = writer ? rows.bias_of(row0 + sub) : 0.f;
+    const float b = (rows.any_bias() && writer) ? rows.bias_of(row0 + sub) : 0.f;
     const float sc = writer ? scale_of(rows, row0 + sub) : 0.f;
 
     float acc[U][2];
@@ -338,11 +432,16 @@ gemv_group_kernel(const typename D::storage* A, int64_t lda, const float* bias, 
                                     blockIdx.x);
 }
 
+template <class D, int W, int BATCH, bool VEC, int NSEG>
+__global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4)))
+gemv_group_multi_kernel(const Segments<typename D::storage, NSEG> rows) {
+    group_body<D, W, 1, BATCH, VEC>(rows, rows.x, rows.K, blockIdx.x);
+}
+
 template <class D, int W, int BATCH, bool VEC>
 __global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4)))
-gemv_group_multi_kernel(const Segments<typename D::storage> rows,
-                        const typename D::storage* __restrict__ x, int K) {
-    group_body<D, W, 1, BATCH, VEC>(rows, x, K, blockIdx.x);
+gemv_group_multi3_kernel(GEMV_THREE_SEGMENT_PARAMS) {
+    group_body<D, W, 1, BATCH, VEC>(GEMV_THREE_SEGMENT_ROWS, x, K, blockIdx.x);
 }
 
 // Weight-only int8: the rows and workgroup-per-row bodies on int8 weights,
@@ -380,6 +479,7 @@ struct SliceOfRows {
     int splits;
     int64_t M;
     __device__ __forceinline__ const S* row(int64_t m) const { return A + m * lda; }
+    __device__ __forceinline__ bool any_bias() const { return false; }
     __device__ __forceinline__ float bias_of(int64_t) const { return 0.f; }
     __device__ __forceinline__ void store(int64_t m, float v) const { ws[m * splits] = v; }
 };

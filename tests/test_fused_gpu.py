@@ -66,6 +66,25 @@ def test_multi_integer_bit_exact(dtype, Ms, K):
 
 
 @pytest.mark.parametrize("dtype", gi.DTYPES)
+@pytest.mark.parametrize("Ms,K", [([4096, 1024, 1024], 4096), ([5, 0, 300], 1000),
+                                  ([1000, 1000], 16), ([64], 14336), ([0, 17, 9000], 100),
+                                  ([3000, 1, 6000], 600), ([200, 56], 5000)])
+@pytest.mark.parametrize("bias", ["none", "middle", "all"])
+def test_multi_three_segments_one_pitch(dtype, Ms, K, bias):
+    """At most three matrices of one row pitch run the kernels that take the
+    segment table as scalar arguments: every family, empty segments, a bias
+    on some segments only; bit-exact."""
+    lda = K + (3 if K % 2 else 0)
+    def has_bias(i):
+        return bias == "all" or (bias == "middle" and i == 1)
+    cases = [gi.make_integer(dtype, M, K, seed=M + 5 * i, bias=has_bias(i), lda=lda)
+             for i, M in enumerate(Ms)]
+    got = run_multi(cases)
+    for c, g, (ref, _) in zip(cases, got, oracle_multi(cases)):
+        assert_bit_exact(g[None, :], ref[None, :], f"{dtype} segment M={c.M} bias={bias}")
+
+
+@pytest.mark.parametrize("dtype", gi.DTYPES)
 @pytest.mark.parametrize("misalign", [0, 1])
 def test_multi_random_within_bound(dtype, misalign):
     K = 2048

@@ -527,8 +527,8 @@ gemv_status_t run_q8(int family, const int8_t* Q, int ldq, const float* scale, c
     const void* fn = p.vector_loads ? q8_fn<X, true>(p) : q8_fn<X, false>(p);
     if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;
     int64_t ldq64 = ldq, M64 = M;
-    void* argv[] = {(void*)&Q, (void*)&ldq64, (void*)&scale, (void*)&bias, (void*)&y, (void*)&M64,
-                    (void*)&x, (void*)&K};
+    void* argv[] = {(void*)&Q, (void*)&ldq64, (void*)&x, (void*)&M64, (void*)&K, (void*)&scale,
+                    (void*)&bias, (void*)&y};
     return finish(launch(fn, p, stream, argv));
 }
 

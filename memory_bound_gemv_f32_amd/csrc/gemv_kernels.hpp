@@ -36,6 +36,17 @@ constexpr int kRowsWaves = 4;
 // Wavefronts per workgroup of the workgroup-per-row and split-K kernels.
 constexpr int kGroupWavesDev = 4;
 
+// A load that stays a vector-memory load even at a wave-uniform address: the
+// offset is a zero the compiler cannot see through.  (At a uniform row, as
+// in the workgroup-per-row kernel, a plain load of the bias became a scalar
+// load that the wavefront waited on before issuing its first A load; a
+// vector load is waited on only where its value is used, after the A stream.)
+__device__ __forceinline__ float vector_load(const float* p) {
+    int zero;
+    asm("v_mov_b32 %0, 0" : "=v"(zero));
+    return p[zero];
+}
+
 // Where row m of the (possibly row-concatenated) problem lives and where its
 // result goes.  Passed to the kernels by value, as kernel arguments.
 template <class S>
@@ -48,7 +59,7 @@ struct OneMatrix {
     int64_t M;
     __device__ __forceinline__ const S* row(int64_t m) const { return A + m * lda; }
     __device__ __forceinline__ bool any_bias() const { return bias != nullptr; }
-    __device__ __forceinline__ float bias_of(int64_t m) const { return bias[m]; }
+    __device__ __forceinline__ float bias_of(int64_t m) const { return vector_load(bias + m); }
     __device__ __forceinline__ void store(int64_t m, float v) const { y[m] = v; }
 };
 
@@ -65,9 +76,9 @@ struct ScaledMatrix {
     float* y;
     int64_t M;
     __device__ __forceinline__ const S* row(int64_t m) const { return A + m * lda; }
-    __device__ __forceinline__ float scale_of(int64_t m) const { return scale[m]; }
+    __device__ __forceinline__ float scale_of(int64_t m) const { return vector_load(scale + m); }
     __device__ __forceinline__ bool any_bias() const { return bias != nullptr; }
-    __device__ __forceinline__ float bias_of(int64_t m) const { return bias[m]; }
+    __device__ __forceinline__ float bias_of(int64_t m) const { return vector_load(bias + m); }
     __device__ __forceinline__ void store(int64_t m, float v) const { y[m] = v; }
 };
 
@@ -445,18 +456,20 @@ gemv_group_multi3_kernel(GEMV_THREE_SEGMENT_PARAMS) {
 }
 
 // Weight-only int8: the rows and workgroup-per-row bodies on int8 weights,
-// x of type X, and the per-row scale applied after each row's sum.
+// x of type X, and the per-row scale applied after each row's sum.  What the
+// first loads need (Q, its pitch, x, M, K, then scale and bias) comes first:
+// the first 14 argument dwords arrive preloaded in SGPRs.
 template <class X, int L, int U, int BATCH, bool VEC>
 __global__ void __launch_bounds__(kRowsWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
-gemv_rows_q8_kernel(const int8_t* Q, int64_t ldq, const float* scale, const float* bias, float* y,
-                    int64_t M, const typename X::storage* __restrict__ x, int K) {
+gemv_rows_q8_kernel(const int8_t* Q, int64_t ldq, const typename X::storage* __restrict__ x,
+                    int64_t M, int K, const float* scale, const float* bias, float* y) {
     rows_body<TQ8<X>, L, U, BATCH, VEC>(ScaledMatrix<int8_t>{Q, ldq, scale, bias, y, M}, x, K);
 }
 
 template <class X, int W, int BATCH, bool VEC>
 __global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4)))
-gemv_group_q8_kernel(const int8_t* Q, int64_t ldq, const float* scale, const float* bias, float* y,
-                     int64_t M, const typename X::storage* __restrict__ x, int K) {
+gemv_group_q8_kernel(const int8_t* Q, int64_t ldq, const typename X::storage* __restrict__ x,
+                     int64_t M, int K, const float* scale, const float* bias, float* y) {
     group_body<TQ8<X>, W, 1, BATCH, VEC>(ScaledMatrix<int8_t>{Q, ldq, scale, bias, y, M}, x, K,
                                          blockIdx.x);
 }

@@ -307,6 +307,21 @@ class Q8Rotation:
         return worst <= 1.0, worst
 
 
+class ProbeRotation:
+    """The read probe over the A buffers of a Rotation: every step streams
+    one copy of A (no x, no output) with the GEMV kernels' access pattern."""
+
+    def __init__(self, rot, torch):
+        self.rot = rot
+        self.R = rot.R
+        self.sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def callers(self, lg, stream_handle):
+        nbytes = self.rot.case.A.nbytes
+        return [(lg.gemv_read_probe, (A.data_ptr(), nbytes, self.sink.data_ptr(), stream_handle))
+                for A in self.rot.A]
+
+
 def call(fn_args):
     f, args = fn_args
     rc = f(*args)
@@ -564,7 +579,22 @@ def main():
 
     plan = lg.plan(case.dtype, case.M, case.K, case.lda, case.nvec,
                    rot.A[0].data_ptr(), rot.X[0].data_ptr())
-    del loop, rot
+    # the practical ceiling: the same A buffers streamed by the read probe
+    probe = ProbeRotation(rot, torch)
+    ploop = GraphLoop(torch, probe, lg, args.steps, per=rot.R * max(1, 256 // rot.R))
+    probe_us = 1e3 * ploop.time(args.warmup) / args.steps
+    a_bytes = case.A.nbytes
+    read_probe = {
+        "bytes": a_bytes, "us": round(probe_us, 3),
+        "GBps": round(a_bytes / probe_us / 1e3, 1),
+        "frac_of_8TBps": round(a_bytes / probe_us / 1e3 / HBM_PEAK_GBS, 4),
+        "gemv_us_over_probe_us": round(us_step / probe_us, 3),
+        "what": "gemv_read_probe over the same rotated A buffers: A streamed once with the "
+                "GEMV access pattern, no x, no output",
+    }
+    log(f"read probe: {probe_us:.3f} us for the {a_bytes} A bytes; GEMV/probe time "
+        f"{us_step / probe_us:.3f}")
+    del loop, ploop, probe, rot
     torch.cuda.empty_cache()
 
     t = load_traffic(args.workload)
@@ -644,6 +674,7 @@ def main():
             "bytes_per_launch": nbytes,
         },
         "cpu_baseline": cpu,
+        "read_probe": read_probe,
         "per_shape": shapes,
         "sweep_aggregate": sweep_agg,
         "decode_layer_fused": layer,

@@ -303,6 +303,20 @@ gemv_status_t gemv_q8_run_family(gemv_dtype_t xdtype, int family,
                                  const void *x, const float *bias, float *y,
                                  int M, int K, hipStream_t stream);
 
+/* Read probe (measurement only): stream `bytes` of device memory from
+ * `buffer` once, in the access pattern of the GEMV kernels (64-lane
+ * wavefronts with eight 1 KiB nontemporal loads in flight each), and write
+ * nothing; `sink` (4 device bytes) is written only if the folded data equal
+ * one fixed 32-bit value.  Timed beside a GEMV of the same bytes it separates
+ * what streaming those bytes costs on this GPU from what the GEMV adds
+ * (page "GEMM、GEMV、dtype 与算术强度", section "FLOPs、最低字节数与算术强度":
+ * the minimum byte count is an algorithmic bound, not what a kernel
+ * achieves).  bytes == 0 enqueues nothing; a NULL buffer or sink, bytes not
+ * a multiple of 16, or a buffer not 16-byte aligned gives
+ * GEMV_ERROR_INVALID_VALUE. */
+gemv_status_t gemv_read_probe(const void *buffer, size_t bytes, unsigned *sink,
+                              hipStream_t stream);
+
 /* Run with a forced family (GEMV_FAMILY_AUTO = what the entry points do).
  * Same arguments, validation and results contract as the entry points;
  * for tests and benchmarks. */

@@ -125,6 +125,7 @@ gemv_q8_f16 = _bind("gemv_q8_f16", [_vp, _i, _vp, _vp, _vp, _vp, _i, _i, _st])
 gemv_q8_bf16 = _bind("gemv_q8_bf16", [_vp, _i, _vp, _vp, _vp, _vp, _i, _i, _st])
 gemv_q8_run_family = _bind("gemv_q8_run_family", [_i, _i, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _st])
 gemv_plan_q8 = _bind("gemv_plan_q8", [_i, _i, _i, _i, _vp, _vp, _i, ctypes.POINTER(GemvPlan)])
+gemv_read_probe = _bind("gemv_read_probe", [_vp, _sz, _vp, _st])
 gemv_plan = _bind("gemv_plan", [_i, _i, _i, _i, _i, _vp, _vp, _i, ctypes.POINTER(GemvPlan)])
 gemv_plan_splitk = _bind("gemv_plan_splitk", [_i, _i, _i, _i, _i, _vp, _vp, ctypes.POINTER(GemvPlan)])
 gemv_run_family = _bind("gemv_run_family", [_i, _i, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _st])
@@ -136,8 +137,8 @@ EXPORTED = ("gemv_status_string", "gemv_last_hip_error",
             "gemv_gate_up_silu_f16", "gemv_gate_up_silu_bf16",
             "gemv_splitk_workspace_size", "gemv_splitk_f32", "gemv_splitk_f16",
             "gemv_splitk_bf16", "gemv_q8_f32", "gemv_q8_f16", "gemv_q8_bf16",
-            "gemv_q8_run_family", "gemv_plan_q8", "gemv_plan", "gemv_plan_splitk",
-            "gemv_run_family")
+            "gemv_q8_run_family", "gemv_plan_q8", "gemv_read_probe", "gemv_plan",
+            "gemv_plan_splitk", "gemv_run_family")
 
 
 class GemvError(RuntimeError):

@@ -660,6 +660,23 @@ gemv_status_t gemv_plan_q8(gemv_dtype_t xdtype, int M, int K, int ldq, const voi
     return GEMV_SUCCESS;
 }
 
+gemv_status_t gemv_read_probe(const void* buffer, size_t bytes, unsigned* sink,
+                              hipStream_t stream) {
+    if (bytes == 0) return GEMV_SUCCESS;
+    if (buffer == nullptr || sink == nullptr || bytes % 16 != 0 ||
+        (uintptr_t)buffer % 16 != 0 || (uintptr_t)sink % 4 != 0)
+        return GEMV_ERROR_INVALID_VALUE;
+    const int64_t n16 = (int64_t)(bytes / 16);
+    const int64_t per_group = (int64_t)gemvdev::kRowsWaves * 8 * 64;  // 16-byte units
+    Plan p;
+    p.grid = (n16 + per_group - 1) / per_group;
+    p.block = gemvdev::kRowsWaves * 64;
+    if (p.grid > 0x7fffffff) return GEMV_ERROR_INVALID_VALUE;
+    const gemvdev::quad* q = static_cast<const gemvdev::quad*>(buffer);
+    void* argv[] = {(void*)&q, (void*)&n16, (void*)&sink};
+    return finish(launch((const void*)&gemvdev::gemv_read_probe_kernel, p, stream, argv));
+}
+
 gemv_status_t gemv_plan(gemv_dtype_t dtype, int M, int K, int lda, int nvec, const void* A,
                         const void* X, int family, gemv_plan_t* plan) {
     if (plan == nullptr || (int)dtype > gemvplan::BF16) return GEMV_ERROR_INVALID_VALUE;

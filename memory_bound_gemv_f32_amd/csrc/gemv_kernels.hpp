@@ -822,4 +822,30 @@ gemv_gated_silu_kernel(const typename D::storage* Ag, const typename D::storage*
     if (threadIdx.x == 0) h[row] = g / (1.f + expf(-g)) * u;
 }
 
+// Read probe: streams `n16` 16-byte units once, the way the GEMV kernels
+// stream A (64-lane wavefronts, 8 nontemporal 1 KiB loads in flight each,
+// 4 wavefronts per workgroup, consecutive blocks to consecutive workgroups),
+// and writes nothing: the loaded words are folded into one value that is
+// stored only if it equals a constant the data cannot be expected to
+// produce, so the loads stay live.  It measures what streaming the bytes
+// alone costs on this GPU, the practical ceiling for a GEMV of those bytes.
+__global__ void __launch_bounds__(kRowsWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
+gemv_read_probe_kernel(const quad* __restrict__ p, int64_t n16, unsigned* sink) {
+    constexpr int kLoads = 8;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * kRowsWaves + (threadIdx.x >> 6);
+    const int64_t base = wave * kLoads * 64 + lane;
+    quad v[kLoads];
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+        const int64_t q = base + (int64_t)i * 64;
+        v[i] = __builtin_nontemporal_load(p + (q < n16 ? q : n16 - 1));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    unsigned acc = 0;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+    if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
 }  // namespace gemvdev

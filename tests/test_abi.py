@@ -439,3 +439,11 @@ def test_long_x_rows_share_a_workgroup():
     for K in (8200, 14336, 30000, 1 << 20):
         q = p("bf16", 4096, K, family=lg.FAMILY_GROUP_PER_ROW)
         assert q["row_tiles"] * q["batch"] <= 16
+
+
+def test_read_probe_validation():
+    sink = GOOD
+    assert lg.gemv_read_probe(GOOD, 0, None, None) == lg.GEMV_SUCCESS  # nothing to read
+    for buf, n, snk in ((None, 1024, sink), (GOOD, 1024, None), (GOOD, 1000, sink),
+                        (GOOD + 8, 1024, sink), (GOOD, 1024, sink + 2)):
+        assert lg.gemv_read_probe(buf, n, snk, None) == lg.GEMV_ERROR_INVALID_VALUE

@@ -276,3 +276,16 @@ def test_full_size_workload(name):
     ref, absdot = run_oracle(case)
     y = run_gpu(case, lg.FAMILY_AUTO, batched=case.nvec > 1)
     assert_within_bound(y, ref, absdot, name)
+
+
+def test_read_probe_reads_and_writes_nothing():
+    """The measurement probe streams a buffer (whole and ragged sizes) and
+    leaves the sink word alone."""
+    buf = torch.full(((3 << 20) // 4 + 64,), 0x01010101, dtype=torch.int32, device="cuda")
+    sink = torch.full((4,), 7, dtype=torch.int32, device="cuda")
+    for nbytes in (16, 1040, 1 << 20, (3 << 20) + 16):
+        rc = lg.gemv_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(),
+                                torch.cuda.current_stream().cuda_stream)
+        assert rc == lg.GEMV_SUCCESS
+    torch.cuda.synchronize()
+    assert sink.cpu().tolist() == [7, 7, 7, 7]

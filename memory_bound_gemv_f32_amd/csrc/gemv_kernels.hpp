@@ -19,7 +19,8 @@
 //     is read element by element.  Nothing beyond column K-1 of a row is
 //     read, so padding between rows (lda > K) never enters a sum;
 //   * x is small and read by every row; it stays in the L1/L2 caches (page
-//     "第 3 课", section "B. 向量 x 的高速片上缓存复用");
+//     "第 3 课", section "B. 向量 x 的高速片上缓存复用"); an x too long to stay
+//     in a CU's L1 beside the A stream is shared by two rows per workgroup;
 //   * rows past M in the last wavefront clamp their loads to row M-1, take
 //     part in the reduction, and do not write.
 #pragma once

@@ -629,21 +629,33 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
 // (about 64 FLOP per byte against a matrix-core ridge of about 300) the
 // path stays bound by HBM.
 //
-// A workgroup owns 16 consecutive rows; its W wavefronts split the whole
-// 32-wide steps of K into contiguous slices and walk them in chunks of CH
-// steps.  Per chunk a wavefront
-//   1. issues the loads of its 16 rows × CH steps of A (one 16-byte MFMA
-//      operand per lane and step),
+// Full-line A loads.  A 16×16×32 step takes 16 operand rows with 4 lanes of
+// 16 bytes each, so a load in the plain operand layout reads 64 bytes of
+// each of 16 rows (half of every 128-byte line; reading A that way took 1 µs
+// longer for 32 MiB).  Here each operand row is half of a real row: operand
+// row v is real row v/2, elements 64·i + 32·(v % 2) + 8·g of step i, so one
+// load reads whole 128-byte lines of 8 real rows.  The contraction index
+// must be the same for the two operands, so each A operand meets two X
+// operands, one per half (elements 64·i + 8·g and 64·i + 32 + 8·g), in two
+// MFMA steps; each step's outputs are right for the operand rows of its half
+// and the others are dropped.  Real row R's sum is the even row of the first
+// step's tile plus the odd row of the second's.
+//
+// A workgroup owns 16 real rows (two groups of 8); its W wavefronts split
+// the 64-element steps of K into contiguous slices and walk them in chunks
+// of CH steps.  Per chunk a wavefront
+//   1. issues the loads of its 16 rows × CH steps of A,
 //   2. copies the same K range of every X column into its own LDS region
 //      with coalesced loads (one 1 KiB load per column; X columns are K
 //      elements apart, so reading the operands straight from memory would
-//      send each load to 16 addresses one column pitch apart),
-//   3. runs CH·NT MFMA steps, reading the X operands from LDS.
+//      send each load to 16 addresses one column pitch apart, measured
+//      15-20 % slower),
+//   3. runs 2·CH·NT·2 MFMA steps, reading the X operands from LDS.
 // Vectors past nvec are zero operands.  After one barrier wavefront 0 adds
-// the W tiles in wavefront order, adds the bias and writes Y.  Needs 16-byte
-// aligned A, X and row pitch and K % 8 == 0.  A chunk shorter than CH steps
-// at the end of a slice, and the last, partial 32-wide step (K % 32 != 0,
-// done by the last wavefront), read their operands directly.
+// the W partial tiles in wavefront order, adds the bias and writes Y.  Needs
+// 16-byte aligned A, X and row pitch and K % 8 == 0.  A chunk shorter than
+// CH steps at the end of a slice, and the last, partial 64-wide step
+// (K % 64 != 0, done by the last wavefront), read their operands directly.
 template <class D, int W, int NT, int CH>
 __global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2)))
 gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
@@ -652,53 +664,60 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
                          int M, int K, int nvec) {
     using S = typename D::storage;
     constexpr int kCols = 16 * NT;
-    // per wavefront: kCols columns × CH steps × 32 elements, each column
+    // per wavefront: kCols columns × CH steps × 64 elements, each column
     // padded by 16 bytes so that 16 lanes reading 16 columns hit distinct banks
-    constexpr int kColBytes = CH * 64 + 16;
-    constexpr int kColQuads = kColBytes / 16;
-    // the wavefront's W partial tiles reuse its own X region once it is done
+    constexpr int kColQuads = CH * 8 + 1;
     static_assert(kCols * kColQuads >= NT * 64, "partials fit in the X region");
     __shared__ quad xs[W][kCols * kColQuads];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int r = lane & 15;  // A row within the tile / X column within a tile
-    const int g = lane >> 4;  // 8-element group within a 32-wide step
+    const int r = lane & 15;  // operand row (A) / column within a tile (X)
+    const int g = lane >> 4;  // 8-element group within a 32-element half-step
+    const int half = r & 1;
     const int64_t row0 = (int64_t)blockIdx.x * 16;
-    const int64_t arow = row0 + r < M ? row0 + r : (int64_t)M - 1;
-    const S* ap = A + arow * lda + 8 * g;
+    const S* ap[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int64_t row = row0 + 8 * q + (r >> 1);
+        ap[q] = A + (row < M ? row : (int64_t)M - 1) * lda + 32 * half + 8 * g;
+    }
 
-    const int steps = K / 32;
+    const int steps = K / 64;
     const int per = (steps + W - 1) / W;
     const int s0 = wave * per;
     const int s1 = s0 + per < steps ? s0 + per : steps;
     const quad zero = quad{0u, 0u, 0u, 0u};
     quad* xw = xs[wave];
 
-    f32x4 acc[NT];
+    f32x4 acc[2][NT][2];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    constexpr int kQuads = kCols * 4 * CH;  // X quads (16 bytes) per chunk
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[q][t][0] = acc[q][t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int kQuads = kCols * 8 * CH;  // X quads (16 bytes) per chunk
     int c = s0;
     for (; c + CH <= s1; c += CH) {
-        quad a[CH];
+        quad a[2][CH];
 #pragma unroll
         for (int i = 0; i < CH; ++i)
-            a[i] = __builtin_nontemporal_load(reinterpret_cast<const quad*>(ap + (int64_t)(c + i) * 32));
-        // X chunk: quad q is column q / (4·CH), elements c·32 + 8·(q % (4·CH)) .. +8;
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                a[q][i] = __builtin_nontemporal_load(reinterpret_cast<const quad*>(ap[q] + (int64_t)(c + i) * 64));
+        // X chunk: quad qd is column qd / (8·CH), elements c·64 + 8·(qd % (8·CH)) .. +8;
         // columns past nvec load column nvec-1 and are stored as zero
         quad xv[kQuads / 64];
 #pragma unroll
         for (int t = 0; t < kQuads / 64; ++t) {
-            const int q = t * 64 + lane;
-            const int j = q / (4 * CH) < nvec ? q / (4 * CH) : nvec - 1;
-            xv[t] = *reinterpret_cast<const quad*>(X + (int64_t)j * K + (int64_t)c * 32 + 8 * (q % (4 * CH)));
+            const int qd = t * 64 + lane;
+            const int j = qd / (8 * CH) < nvec ? qd / (8 * CH) : nvec - 1;
+            xv[t] = *reinterpret_cast<const quad*>(X + (int64_t)j * K + (int64_t)c * 64 + 8 * (qd % (8 * CH)));
         }
         __builtin_amdgcn_sched_barrier(0);  // all loads of the chunk in flight first
 #pragma unroll
         for (int t = 0; t < kQuads / 64; ++t) {
-            const int q = t * 64 + lane;
-            xw[(q / (4 * CH)) * kColQuads + q % (4 * CH)] = q / (4 * CH) < nvec ? xv[t] : zero;
+            const int qd = t * 64 + lane;
+            xw[(qd / (8 * CH)) * kColQuads + qd % (8 * CH)] = qd / (8 * CH) < nvec ? xv[t] : zero;
         }
         // the same wavefront reads back what its lanes wrote
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -706,59 +725,74 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            // operand of lane (r, g) for step i and tile t: column 16t + r,
-            // elements i·32 + 8g .. +8
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-                acc[t] = mma_16x16x32(D{}, a[i], xw[(16 * t + r) * kColQuads + 4 * i + g], acc[t]);
+            for (int t = 0; t < NT; ++t) {
+                // X operands of lane (column 16t + r, group g): the two halves of step i
+                const quad b0 = xw[(16 * t + r) * kColQuads + 8 * i + g];
+                const quad b1 = xw[(16 * t + r) * kColQuads + 8 * i + 4 + g];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    acc[q][t][0] = mma_16x16x32(D{}, a[q][i], b0, acc[q][t][0]);
+                    acc[q][t][1] = mma_16x16x32(D{}, a[q][i], b1, acc[q][t][1]);
+                }
+            }
         }
         // the next chunk overwrites this wavefront's LDS region
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
     }
-    // a short last chunk (fewer than CH steps): one step at a time, X read
-    // straight from memory (it only occurs when K/32 does not split evenly)
-    const S* xp[NT];
+    // a short last chunk (fewer than CH steps) one step at a time, and the
+    // last, partial step (K % 64 != 0, done by the last wavefront), with X
+    // read straight from memory; groups of 8 wholly past K are zero (K % 8 == 0)
+    const S* xq[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-        xp[t] = X + (int64_t)(16 * t + r < nvec ? 16 * t + r : 0) * K + 8 * g;
+    for (int t = 0; t < NT; ++t) xq[t] = X + (int64_t)(16 * t + r < nvec ? 16 * t + r : 0) * K + 8 * g;
+    const int last = (wave == W - 1 && steps * 64 < K) ? steps + 1 : s1;
 #pragma unroll 1
-    for (; c < s1; ++c) {
-        const quad a = *reinterpret_cast<const quad*>(ap + (int64_t)c * 32);
+    for (; c < last; ++c) {
+        const int e = c * 64;
+        const bool ina = e + 32 * half + 8 * g < K;
+        quad a[2];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const quad b = *reinterpret_cast<const quad*>(xp[t] + (int64_t)c * 32);
-            acc[t] = mma_16x16x32(D{}, a, 16 * t + r < nvec ? b : zero, acc[t]);
-        }
-    }
-    if (wave == W - 1 && steps * 32 < K) {
-        // last, partial step: groups wholly below K (K % 8 == 0) load, others are zero
-        const bool in = steps * 32 + 8 * g < K;
-        const quad a = in ? *reinterpret_cast<const quad*>(ap + (int64_t)steps * 32) : zero;
+        for (int q = 0; q < 2; ++q)
+            a[q] = ina ? *reinterpret_cast<const quad*>(ap[q] + (int64_t)e) : zero;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const bool col = 16 * t + r < nvec;
-            const quad b = (in && col) ? *reinterpret_cast<const quad*>(xp[t] + (int64_t)steps * 32) : zero;
-            acc[t] = mma_16x16x32(D{}, a, b, acc[t]);
+            const quad b0 = (col && e + 8 * g < K) ? *reinterpret_cast<const quad*>(xq[t] + e) : zero;
+            const quad b1 = (col && e + 32 + 8 * g < K) ? *reinterpret_cast<const quad*>(xq[t] + e + 32) : zero;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                acc[q][t][0] = mma_16x16x32(D{}, a[q], b0, acc[q][t][0]);
+                acc[q][t][1] = mma_16x16x32(D{}, a[q], b1, acc[q][t][1]);
+            }
         }
     }
 
+    // lane (column j, group g) holds operand rows 4g .. 4g+3, i.e. real rows
+    // 2g (halves 0, 1) and 2g+1 of each row group: pair them up
     f32x4* partial = reinterpret_cast<f32x4*>(xw);  // this wavefront's region, now free
 #pragma unroll
-    for (int t = 0; t < NT; ++t) partial[t * 64 + lane] = acc[t];
+    for (int t = 0; t < NT; ++t) {
+        f32x4 v;
+        v[0] = acc[0][t][0][0] + acc[0][t][1][1];
+        v[1] = acc[0][t][0][2] + acc[0][t][1][3];
+        v[2] = acc[1][t][0][0] + acc[1][t][1][1];
+        v[3] = acc[1][t][0][2] + acc[1][t][1][3];
+        partial[t * 64 + lane] = v;
+    }
     __syncthreads();
     if (wave == 0) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            f32x4 v = acc[t];
+            f32x4 v = partial[t * 64 + lane];
 #pragma unroll
             for (int w = 1; w < W; ++w) v += reinterpret_cast<const f32x4*>(xs[w])[t * 64 + lane];
-            // lane holds rows row0 + 4g .. row0 + 4g + 3 of vector 16t + r
             const int j = 16 * t + r;
             if (j < nvec) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int64_t m = row0 + 4 * g + i;
+                    const int64_t m = row0 + 8 * (i >> 1) + 2 * g + (i & 1);
                     if (m < M) Y[(int64_t)j * M + m] = v[i] + (bias != nullptr ? bias[m] : 0.f);
                 }
             }

@@ -83,17 +83,17 @@ constexpr int64_t kGroupTileMinGroups = 256;
 constexpr int kBatchedBatch = 1;
 constexpr int batched_rows(int nvec) { return nvec <= 2 ? 4 : (nvec <= 4 ? 2 : 1); }
 // Matrix-core batched family: 16 rows per workgroup, its wavefronts split K
-// and walk their slice in chunks of this many 32-wide steps (the A loads of a
+// and walk their slice in chunks of this many 64-wide steps (the A loads of a
 // chunk are in flight together; X's chunk is staged in LDS).
 constexpr int kMfmaRows = 16;
 constexpr int kMfmaWaves = 8;
-constexpr int kMfmaChunk = 16;
+constexpr int kMfmaChunk = 8;
 // 16-vector tiles for nvec vectors (1, 2 or 4); the chunk shrinks as the
 // tiles grow so that the X staged per chunk stays 16 KiB per wavefront.
 constexpr int mfma_tiles(int nvec) { return nvec <= 16 ? 1 : (nvec <= 32 ? 2 : 4); }
 constexpr int mfma_chunk(int nvec) { return kMfmaChunk / mfma_tiles(nvec); }
 constexpr int mfma_lds_bytes(int nvec) {
-    return kMfmaWaves * 16 * mfma_tiles(nvec) * (mfma_chunk(nvec) * 64 + 16);
+    return kMfmaWaves * 16 * mfma_tiles(nvec) * (mfma_chunk(nvec) * 128 + 16);
 }
 // Split-K: when there are too few rows to fill the chip and each row holds
 // much more than a workgroup keeps in flight (page "SGEMV CUDA代码学习",
@@ -340,8 +340,8 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         p.rows_per_group = p.rows_per_wave * p.row_tiles * p.waves_per_group;
     p.grid = ceil_div(M, p.rows_per_group);
     p.slice_elems = K;
-    if (fam == BATCHED_MFMA)  // 32-wide steps per wavefront
-        p.passes = (int)ceil_div(K / 32, (int64_t)kMfmaWaves);
+    if (fam == BATCHED_MFMA)  // 64-wide steps per wavefront
+        p.passes = (int)ceil_div(K / 64, (int64_t)kMfmaWaves);
     else
         p.passes = (int)ceil_div(full, (int64_t)p.lanes_per_row);
     if (p.grid > 0x7fffffff) return INVALID;

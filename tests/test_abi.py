@@ -186,7 +186,7 @@ def test_batched_plans():
     q = p("f16", 4096, 4096, nvec=16)
     assert q["family"] == lg.FAMILY_BATCHED_MFMA
     assert (q["rows_per_group"], q["waves_per_group"], q["grid"]) == (16, 8, 256)
-    assert q["passes"] == 4096 // 32 // 8
+    assert q["passes"] == 4096 // 64 // 8
     # the matrix cores need every 8-element group of a row aligned
     assert p("bf16", 4096, 4104, nvec=3)["family"] == lg.FAMILY_BATCHED_MFMA
     assert p("bf16", 4096, 4100, lda=4104, nvec=3)["family"] == lg.FAMILY_BATCHED
@@ -204,14 +204,14 @@ def test_batched_plans():
 
 def test_wide_batched_plans():
     """17-64 vectors: the matrix-core kernel takes 2 or 4 tiles of 16
-    vectors per A operand, in chunks of 8 or 4 steps, so the X staged per
-    chunk stays 16 KiB per wavefront and the LDS within 160 KiB; the
-    vector-ALU family plans its first block of 16 vectors."""
-    for nvec, chunk, tiles in ((16, 16, 1), (17, 8, 2), (32, 8, 2), (33, 4, 4), (64, 4, 4)):
+    vectors per A operand, in chunks of 4 or 2 64-wide steps, so the X
+    staged per chunk stays 16 KiB per wavefront and the LDS within 160 KiB;
+    the vector-ALU family plans its first block of 16 vectors."""
+    for nvec, chunk, tiles in ((16, 8, 1), (17, 4, 2), (32, 4, 2), (33, 2, 4), (64, 2, 4)):
         q = p("bf16", 4096, 4096, nvec=nvec)
         assert q["family"] == lg.FAMILY_BATCHED_MFMA and q["batch"] == chunk
         assert q["grid"] == 256 and q["block"] == 512
-        assert q["lds_bytes"] == 8 * 16 * tiles * (chunk * 64 + 16) <= 160 * 1024
+        assert q["lds_bytes"] == 8 * 16 * tiles * (chunk * 128 + 16) <= 160 * 1024
     for nvec in (17, 40, 64):
         assert p("f16", 999, 1000, nvec=nvec, A=ALIGNED + 2) == p("f16", 999, 1000, nvec=16,
                                                                   A=ALIGNED + 2)

@@ -46,8 +46,10 @@ gemv_status_t finish(hipError_t err) {
 
 // ---- rows-per-wave / wave-per-row / workgroup-per-row ----------------------
 
-// NSEG > 0 selects the segment-table kernels (several matrices sharing x;
-// the select chains cover NSEG segments), NSEG == 0 the one-matrix kernels.
+// NSEG selects the kernels for several matrices sharing x: 0 the one-matrix
+// kernels, kFewSegments the kernels that take up to three segments as scalar
+// arguments, any other value the segment-table kernels whose select chains
+// cover NSEG entries.
 template <class D, int L, bool VEC, int NSEG>
 const void* rows_fn(int tiles) {
     if constexpr (L == 64) {

@@ -289,3 +289,26 @@ def test_read_probe_reads_and_writes_nothing():
         assert rc == lg.GEMV_SUCCESS
     torch.cuda.synchronize()
     assert sink.cpu().tolist() == [7, 7, 7, 7]
+
+
+def test_seeded_random_shapes_integer():
+    """Sixty shapes drawn from a fixed seed (M, K, row pitch, pointer
+    offset, bias, dtype, family, batch size), all in the exact-integer
+    regime: every result bit-exact."""
+    rng = np.random.default_rng(2024)
+    for trial in range(60):
+        dtype = str(rng.choice(gi.DTYPES))
+        M = int(rng.choice([1, 2, 3, 7, 63, 64, 65, 255, 256, 257, 1000, 3000, 9000]))
+        K = int(rng.choice([1, 5, 8, 16, 31, 64, 100, 129, 512, 1000, 2049, 4096, 7000, 16384]))
+        per = 16 // gi.ELEMENT_BYTES[dtype]
+        lda = K + int(rng.choice([0, 0, 1, per, 3 * per + 1]))
+        misalign = int(rng.choice([0, 0, 1]))
+        nvec = 1 if dtype == "f32" else int(rng.choice([1, 1, 2, 5, 16, 24]))
+        case = gi.make_integer(dtype, M, K, seed=trial, nvec=nvec, lda=lda,
+                               bias=bool(rng.integers(2)))
+        ref, _ = run_oracle(case)
+        fams = families_for(case, misalign)
+        fam = fams[int(rng.integers(len(fams)))]
+        y = run_gpu(case, fam, misalign=misalign, batched=nvec > 1)
+        assert_bit_exact(y, ref, f"trial {trial}: {dtype} {M}x{K} lda={lda} nvec={nvec} "
+                                 f"misalign={misalign} family {fam}")

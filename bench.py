@@ -410,6 +410,16 @@ def sanity_check(case, rot, torch):
     return ok, worst
 
 
+def rotation_for(name, gi, torch):
+    """The rotation sets of any named shape: a plain, split-K, fused or
+    int8 workload."""
+    if name in FUSED:
+        return FusedRotation(name, gi, torch)
+    if name in gi.Q8_WORKLOADS:
+        return Q8Rotation(name, gi, torch)
+    return Rotation(gi.make_workload(name), torch, splitk=name in gi.SPLITK_WORKLOADS)
+
+
 def measure_shape(name, torch, lg, gi, steps):
     fused = name in FUSED
     q8 = name in gi.Q8_WORKLOADS
@@ -537,16 +547,20 @@ def main():
     torch.cuda.set_device(0)
     log(f"device {torch.cuda.get_device_name(0)} ({torch.cuda.get_device_properties(0).gcnArchName})")
 
+    if args.kernel_only:
+        # only the timed graph loop of one named shape (for profilers)
+        krot = rotation_for(args.workload, gi, torch)
+        kloop = GraphLoop(torch, krot, lg, args.steps, per=krot.R * max(1, 256 // krot.R))
+        ms = kloop.time(args.warmup)
+        log(f"kernel-only {args.workload}: {args.steps} launches, {1e3 * ms / args.steps:.3f} us "
+            f"per launch")
+        return
+
     case = gi.make_workload(args.workload)
     rot = Rotation(case, torch)
     log(f"workload {args.workload}: {case.dtype} M={case.M} K={case.K} nvec={case.nvec} "
         f"rotation sets {rot.R} ({rot.bytes_resident / 2**20:.0f} MiB resident)")
     loop = GraphLoop(torch, rot, lg, args.steps, per=rot.R * max(1, 256 // rot.R))
-
-    if args.kernel_only:
-        ms = loop.time(args.warmup)
-        log(f"kernel-only: {args.steps} launches, {1e3 * ms / args.steps:.3f} us per launch")
-        return
     if args.counters:
         counters_run(case, rot, lg, torch)
         return

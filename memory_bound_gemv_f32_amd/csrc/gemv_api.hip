@@ -185,10 +185,12 @@ const void* batched_kernel(const Plan& p, int nvec) {
             return p.vector_loads ? batched_fn<D, true>(nvec) : batched_fn<D, false>(nvec);
         if (p.family == gemvplan::BATCHED_MFMA && p.vector_loads) {
             constexpr int W = gemvplan::kMfmaWaves;
+            if (nvec <= gemvplan::kMfmaFewVectors)
+                return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 1, gemvplan::mfma_chunk(16), true>;
             switch (gemvplan::mfma_tiles(nvec)) {
-            case 1: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 1, gemvplan::mfma_chunk(16)>;
-            case 2: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 2, gemvplan::mfma_chunk(32)>;
-            case 4: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 4, gemvplan::mfma_chunk(64)>;
+            case 1: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 1, gemvplan::mfma_chunk(16), false>;
+            case 2: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 2, gemvplan::mfma_chunk(32), false>;
+            case 4: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 4, gemvplan::mfma_chunk(64), false>;
             default: return nullptr;
             }
         }

@@ -88,6 +88,9 @@ constexpr int batched_rows(int nvec) { return nvec <= 2 ? 4 : (nvec <= 4 ? 2 : 1
 constexpr int kMfmaRows = 16;
 constexpr int kMfmaWaves = 8;
 constexpr int kMfmaChunk = 8;
+// Up to this many vectors the matrix-core kernel loads and stages only the
+// X columns in use.
+constexpr int kMfmaFewVectors = 8;
 // 16-vector tiles for nvec vectors (1, 2 or 4); the chunk shrinks as the
 // tiles grow so that the X staged per chunk stays 16 KiB per wavefront.
 constexpr int mfma_tiles(int nvec) { return nvec <= 16 ? 1 : (nvec <= 32 ? 2 : 4); }

@@ -269,20 +269,38 @@ constexpr int kDppSwapPairs = 0x4E;      // quad_perm [2,3,0,1]: lane ^ 2
 constexpr int kDppHalfRowMirror = 0x141; // lane i <- 7 - i within 8 lanes
 constexpr int kDppRowMirror = 0x140;     // lane i <- 15 - i within 16 lanes
 
+// Sums across 16-lane rows with the gfx950 row-swap instructions: swapping
+// the odd rows of one copy of v with the even rows of another leaves the
+// even row's values in the first copy and the odd row's in the second, in
+// both rows of each pair, so their sum is the xor-16 butterfly step (and
+// likewise with the two 32-lane halves for xor-32).  Both lanes of a pair add
+// the same two values in the same order.
+__device__ __forceinline__ float row_pair_sum16(float v) {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ __forceinline__ float half_pair_sum32(float v) {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
 // Sum over each aligned segment of L lanes (L a power of two, 1..64); every
 // lane of the segment receives the same, bit-identical total.  Every lane of
 // the wavefront must execute this (no lane may be inactive).  After the two
 // quad steps all four lanes of a quad hold the quad sum, so the mirrors act
-// as the xor-4 and xor-8 butterfly steps; the 32- and 64-lane steps cross DPP
-// rows through the LDS crossbar (ds_bpermute), which uses no LDS storage.
+// as the xor-4 and xor-8 butterfly steps; the 32- and 64-lane steps swap
+// 16-lane rows and 32-lane halves between registers (v_permlane16_swap,
+// v_permlane32_swap), without a round trip through the LDS crossbar.
 template <int L>
 __device__ __forceinline__ float segment_sum(float v) {
     if constexpr (L >= 2) v += dpp<kDppSwapAdjacent>(v);
     if constexpr (L >= 4) v += dpp<kDppSwapPairs>(v);
     if constexpr (L >= 8) v += dpp<kDppHalfRowMirror>(v);
     if constexpr (L >= 16) v += dpp<kDppRowMirror>(v);
-    if constexpr (L >= 32) v += __shfl_xor(v, 16, 64);
-    if constexpr (L >= 64) v += __shfl_xor(v, 32, 64);
+    if constexpr (L >= 32) v = row_pair_sum16(v);
+    if constexpr (L >= 64) v = half_pair_sum32(v);
     return v;
 }
 

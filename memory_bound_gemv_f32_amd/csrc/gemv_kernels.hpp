@@ -28,6 +28,17 @@
 #include "gemv_device.hpp"
 
 namespace gemvdev {
+// 16 bytes per lane from global memory straight into LDS at lds + 16·lane
+// (global_load_lds_dwordx4; the device pass only: the host pass never
+// emits kernel bodies).
+__device__ __forceinline__ void load_to_lds16(const void* src, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+#endif
+}
+}  // namespace gemvdev
+
+namespace gemvdev {
 
 // Wavefronts per workgroup of the rows and vector-ALU batched kernels: a
 // compile-time constant rather than the launch's block size, so that with
@@ -649,16 +660,18 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
 //      with coalesced loads (one 1 KiB load per column; X columns are K
 //      elements apart, so reading the operands straight from memory would
 //      send each load to 16 addresses one column pitch apart, measured
-//      15-20 % slower),
+//      15-20 % slower); with one tile of vectors the loads go straight to
+//      LDS (global_load_lds), otherwise through registers,
 //   3. runs 2·CH·NT·2 MFMA steps, reading the X operands from LDS.
-// Vectors past nvec are zero operands.  After one barrier wavefront 0 adds
-// the W partial tiles in wavefront order, adds the bias and writes Y.  Needs
+// An MFMA output column depends on its own X column only, so the operand
+// columns of vectors past nvec are left as they are (their outputs are never
+// stored).  After one barrier wavefront 0 adds the W partial tiles in
+// wavefront order, adds the bias and writes Y.  Needs
 // 16-byte aligned A, X and row pitch and K % 8 == 0.  A chunk shorter than
 // CH steps at the end of a slice, and the last, partial 64-wide step
 // (K % 64 != 0, done by the last wavefront), read their operands directly.
 // FEW (at most kMfmaFewVectors vectors, one tile): only the X columns in use
-// are loaded and staged (2 vectors: 9.2 -> 8.6 µs at 4096 × 4096; with more
-// vectors the skipping cost more than it saved).
+// are loaded and staged (2 vectors: 9.2 -> 8.6 µs at 4096 × 4096).
 template <class D, int W, int NT, int CH, bool FEW>
 __global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2)))
 gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
@@ -709,25 +722,43 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
                 a[q][i] = __builtin_nontemporal_load(reinterpret_cast<const quad*>(ap[q] + (int64_t)(c + i) * 64));
         // X chunk: quad qd is column qd / (8·CH), elements c·64 + 8·(qd % (8·CH)) .. +8.
         // Load instruction t covers columns t·kLoadCols .. (t+1)·kLoadCols - 1.
-        // FEW: one whose columns are all past nvec is skipped (those columns are
-        // never read: their operands are zero).  Columns past nvec in a used
-        // load load column nvec-1 and are stored as zero.
+        // Columns past nvec hold anything finite or not: an MFMA output column
+        // depends on its own X column only, and those outputs are dropped.  So
+        // a load whose columns are all past nvec is skipped (FEW), and in a
+        // used one the columns past nvec repeat column nvec-1.
         constexpr int kLoadCols = 64 / (8 * CH);
-        quad xv[kQuads / 64];
+        if constexpr (NT == 1) {
+            // one column per load, straight into the wavefront's LDS region
+            // (global_load_lds: no register round trip, no LDS write instructions)
+            static_assert(kLoadCols == 1, "one 1 KiB column per load");
 #pragma unroll
-        for (int t = 0; t < kQuads / 64; ++t) {
-            if (!FEW || t * kLoadCols < nvec) {
-                const int qd = t * 64 + lane;
-                const int j = qd / (8 * CH) < nvec ? qd / (8 * CH) : nvec - 1;
-                xv[t] = *reinterpret_cast<const quad*>(X + (int64_t)j * K + (int64_t)c * 64 + 8 * (qd % (8 * CH)));
+            for (int t = 0; t < kQuads / 64; ++t) {
+                if (!FEW || t < nvec) {
+                    const int j = t < nvec ? t : nvec - 1;
+                    load_to_lds16(X + (int64_t)j * K + (int64_t)c * 64 + 8 * lane, xw + t * kColQuads);
+                }
             }
-        }
-        __builtin_amdgcn_sched_barrier(0);  // all loads of the chunk in flight first
+            __builtin_amdgcn_sched_barrier(0);
+            // the loads into LDS (and the A loads) have landed
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        } else {
+            quad xv[kQuads / 64];
 #pragma unroll
-        for (int t = 0; t < kQuads / 64; ++t) {
-            if (!FEW || t * kLoadCols < nvec) {
-                const int qd = t * 64 + lane;
-                xw[(qd / (8 * CH)) * kColQuads + qd % (8 * CH)] = qd / (8 * CH) < nvec ? xv[t] : zero;
+            for (int t = 0; t < kQuads / 64; ++t) {
+                if (!FEW || t * kLoadCols < nvec) {
+                    const int qd = t * 64 + lane;
+                    const int j = qd / (8 * CH) < nvec ? qd / (8 * CH) : nvec - 1;
+                    xv[t] = *reinterpret_cast<const quad*>(X + (int64_t)j * K + (int64_t)c * 64 +
+                                                           8 * (qd % (8 * CH)));
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);  // all loads of the chunk in flight first
+#pragma unroll
+            for (int t = 0; t < kQuads / 64; ++t) {
+                if (!FEW || t * kLoadCols < nvec) {
+                    const int qd = t * 64 + lane;
+                    xw[(qd / (8 * CH)) * kColQuads + qd % (8 * CH)] = xv[t];
+                }
             }
         }
         // the same wavefront reads back what its lanes wrote
@@ -738,12 +769,9 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
         for (int i = 0; i < CH; ++i) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                // X operands of lane (column 16t + r, group g): the two halves of
-                // step i (FEW: zero for columns past nvec, whose LDS rows were not
-                // written; otherwise those rows hold zeros)
-                const bool col = !FEW || 16 * t + r < nvec;
-                const quad b0 = col ? xw[(16 * t + r) * kColQuads + 8 * i + g] : zero;
-                const quad b1 = col ? xw[(16 * t + r) * kColQuads + 8 * i + 4 + g] : zero;
+                // X operands of lane (column 16t + r, group g): the two halves of step i
+                const quad b0 = xw[(16 * t + r) * kColQuads + 8 * i + g];
+                const quad b1 = xw[(16 * t + r) * kColQuads + 8 * i + 4 + g];
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
                     acc[q][t][0] = mma_16x16x32(D{}, a[q][i], b0, acc[q][t][0]);

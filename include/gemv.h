@@ -272,6 +272,8 @@ typedef struct {
     int lds_bytes;       /* static + dynamic LDS per workgroup */
     int splits;          /* K-slices per row (split-K), else 1 */
     int slice_elems;     /* elements per K-slice (the last may be shorter), else K */
+    int x_in_registers;  /* workgroup per row: 1 if each lane keeps its x chunks in
+                            registers while the workgroup walks its rows */
     int64_t grid;        /* workgroups (split-K: rows × slices) */
 } gemv_plan_t;
 

@@ -78,7 +78,8 @@ class GemvPlan(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int) for name in (
         "family", "vector_loads", "chunk_elems", "lanes_per_row",
         "rows_per_wave", "row_tiles", "waves_per_group", "rows_per_group",
-        "batch", "passes", "block", "lds_bytes", "splits", "slice_elems")] + [
+        "batch", "passes", "block", "lds_bytes", "splits", "slice_elems",
+        "x_in_registers")] + [
         ("grid", ctypes.c_int64)]
 
     def as_dict(self) -> dict:

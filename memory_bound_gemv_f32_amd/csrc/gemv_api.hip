@@ -132,12 +132,44 @@ const void* group_fn(int batch, int rows) {
     }
 }
 
+// workgroup per row with x in registers: NX chunks of x per lane, R rows
+template <class D, int NX>
+const void* group_stream_fn_nx(int rows) {
+    constexpr int W = gemvplan::kGroupStreamWaves;
+    static_assert(gemvplan::kGroupStreamRows == 4, "streaming kernels are built for 2 or 4 rows");
+    switch (rows) {
+    case 2: return (const void*)&gemvdev::gemv_group_stream_kernel<D, W, NX, 2>;
+    case 4: return (const void*)&gemvdev::gemv_group_stream_kernel<D, W, NX, 4>;
+    default: return nullptr;
+    }
+}
+
+template <class D>
+const void* group_stream_fn(int chunks, int rows) {
+    static_assert(gemvplan::kGroupStreamMaxChunks == 7, "streaming kernels hold up to 7 x chunks");
+    switch (chunks) {
+    case 1: return group_stream_fn_nx<D, 1>(rows);
+    case 2: return group_stream_fn_nx<D, 2>(rows);
+    case 3: return group_stream_fn_nx<D, 3>(rows);
+    case 4: return group_stream_fn_nx<D, 4>(rows);
+    case 5: return group_stream_fn_nx<D, 5>(rows);
+    case 6: return group_stream_fn_nx<D, 6>(rows);
+    case 7: return group_stream_fn_nx<D, 7>(rows);
+    default: return nullptr;
+    }
+}
+
 template <class D, bool VEC, int NSEG>
 const void* single_fn(const Plan& p) {
     switch (p.family) {
     case gemvplan::ROWS_PER_WAVE:
     case gemvplan::WAVE_PER_ROW: return rows_fn<D, VEC, NSEG>(p.lanes_per_row, p.row_tiles);
-    case gemvplan::GROUP_PER_ROW: return group_fn<D, VEC, NSEG>(p.batch, p.row_tiles);
+    case gemvplan::GROUP_PER_ROW:
+        if (p.x_in_registers) {
+            if constexpr (NSEG == 0 && VEC) return group_stream_fn<D>(p.batch, p.row_tiles);
+            return nullptr;
+        }
+        return group_fn<D, VEC, NSEG>(p.batch, p.row_tiles);
     default: return nullptr;
     }
 }
@@ -551,6 +583,7 @@ void export_plan(const Plan& p, gemv_plan_t* plan) {
     plan->lds_bytes = p.lds_bytes;
     plan->splits = p.splits;
     plan->slice_elems = p.slice_elems;
+    plan->x_in_registers = p.x_in_registers;
     plan->grid = p.grid;
 }
 

@@ -20,7 +20,8 @@
 //     read, so padding between rows (lda > K) never enters a sum;
 //   * x is small and read by every row; it stays in the L1/L2 caches (page
 //     "第 3 课", section "B. 向量 x 的高速片上缓存复用"); an x too long to stay
-//     in a CU's L1 beside the A stream is shared by two rows per workgroup;
+//     in a CU's L1 beside the A stream is kept in registers while a workgroup
+//     walks several rows, or (longer still) shared by two rows per workgroup;
 //   * rows past M in the last wavefront clamp their loads to row M-1, take
 //     part in the reduction, and do not write.
 #pragma once
@@ -453,6 +454,81 @@ gemv_group_kernel(const typename D::storage* A, int64_t lda, const float* bias, 
                   const typename D::storage* __restrict__ x, int K) {
     group_body<D, W, U, BATCH, VEC>(OneMatrix<typename D::storage>{A, lda, bias, y, M}, x, K,
                                     blockIdx.x);
+}
+
+// Workgroup-per-row family, x held in registers: for rows whose x is at most
+// NX chunks per lane of the W·64 lanes, each lane loads its NX chunks of x
+// once and the workgroup walks the R consecutive rows tile·R .. tile·R + R - 1,
+// issuing row j+1's loads before row j's multiply-adds.  A workgroup fetches
+// x from L2 once for R rows instead of once per row (the block-per-row
+// mapping of page "第 3 课" with the x reuse of its section "B. 向量 x 的高速片
+// 上缓存复用" moved into registers).  Needs K a whole number of chunks and
+// (NX - 1)·64·W < K/E ≤ NX·64·W; the last chunk of a lane may lie past the
+// row, and is then a clamped load whose products are dropped.  The per-row
+// sums follow the workgroup-per-row body's order for the same W.
+template <class D, int W, int NX, int R, class Rows>
+__device__ __forceinline__ void group_stream_body(const Rows& rows,
+                                                  const typename D::xstorage* __restrict__ x, int K,
+                                                  int64_t tile) {
+    using S = typename D::storage;
+    using C = Chunk<D, true>;
+    using CT = typename C::type;
+    constexpr int L = W * 64;
+    __shared__ float partial[W][R];
+
+    const int64_t M = rows.M;
+    const int64_t row0 = tile * R;
+    if (row0 >= M) return;  // uniform across the workgroup
+    const int sub = threadIdx.x;
+    const int nfull = K / C::elems;
+    // lane `sub` owns chunks sub + i·L; only the last can lie past the row
+    const bool last_ok = sub + (NX - 1) * L < nfull;
+    const int clast = last_ok ? sub + (NX - 1) * L : nfull - 1;
+    const bool writer = sub < R && row0 + sub < M;
+    const float b = (rows.any_bias() && writer) ? rows.bias_of(row0 + sub) : 0.f;
+    const float sc = writer ? scale_of(rows, row0 + sub) : 0.f;
+
+    CT xv[NX];
+#pragma unroll
+    for (int i = 0; i < NX; ++i) xv[i] = C::load(x, i + 1 < NX ? sub + i * L : clast);
+
+    CT a[2][NX];
+    auto fetch = [&](CT (&dst)[NX], int64_t m) {
+        const S* p = rows.row(m < M ? m : M - 1);
+#pragma unroll
+        for (int i = 0; i < NX; ++i) dst[i] = C::stream(p, i + 1 < NX ? sub + i * L : clast);
+    };
+    fetch(a[0], row0);
+    // x and row 0 are the first loads, so that row 0 waits for nothing else
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        if (j + 1 < R) fetch(a[(j + 1) & 1], row0 + j + 1);
+        // row j+1's loads stay ahead of row j's multiply-adds
+        __builtin_amdgcn_sched_barrier(0);
+        // a clamped last chunk contributes nothing (zeroed once x has arrived)
+        if (j == 0) xv[NX - 1] = C::keep_x(last_ok, xv[NX - 1]);
+        float acc[2] = {0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NX; ++i) acc[i & 1] = C::dot(a[j & 1][i], xv[i], acc[i & 1]);
+        const float v = segment_sum<64>(acc[0] + acc[1]);
+        if ((threadIdx.x & 63) == 0) partial[threadIdx.x >> 6][j] = v;
+    }
+    __syncthreads();
+    if (writer) {
+        float s = partial[0][sub];
+#pragma unroll
+        for (int w = 1; w < W; ++w) s += partial[w][sub];
+        rows.store(row0 + sub, row_result<Rows>(s, sc, b));
+    }
+}
+
+template <class D, int W, int NX, int R>
+__global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4)))
+gemv_group_stream_kernel(const typename D::storage* A, int64_t lda, const float* bias, float* y,
+                         int64_t M, const typename D::storage* __restrict__ x, int K) {
+    group_stream_body<D, W, NX, R>(OneMatrix<typename D::storage>{A, lda, bias, y, M}, x, K,
+                                   blockIdx.x);
 }
 
 template <class D, int W, int BATCH, bool VEC, int NSEG>

@@ -77,6 +77,14 @@ constexpr int64_t kGroupShareMinXBytes = 16 * 1024;
 constexpr int kGroupMaxTileRows = 2;
 constexpr int kGroupTileLoads = 16;
 constexpr int64_t kGroupTileMinGroups = 256;
+// When such an x is at most kGroupStreamMaxChunks 16-byte chunks per lane
+// (bf16 K <= 14336, fp32 K <= 7168) and K is whole chunks, each lane keeps
+// its x chunks in registers and the workgroup walks up to kGroupStreamRows
+// rows (halved while fewer than kGroupTileMinGroups workgroups would remain),
+// each row's loads issued before the previous row's multiply-adds.
+constexpr int kGroupStreamWaves = 4;
+constexpr int kGroupStreamMaxChunks = 7;
+constexpr int kGroupStreamRows = 4;
 // Batched family: loads in flight per row, and rows per wavefront, fewer as
 // the number of vectors grows so that rows × vectors accumulators plus the
 // loaded chunks fit the register budget of four wavefronts per SIMD.
@@ -143,6 +151,7 @@ struct Plan {
     int lds_bytes = 0;
     int splits = 1;       // K-slices per row (split-K), else 1
     int slice_elems = 0;  // elements per slice (split-K), else K
+    int x_in_registers = 0;  // workgroup per row: x kept in registers across its rows
     int64_t grid = 0;     // workgroups (split-K: rows × slices)
 };
 
@@ -204,7 +213,7 @@ inline bool vector_ok(int dtype, int K, int lda, int nvec, uintptr_t A, uintptr_
 constexpr int kMultiMaxRowTiles = 2;
 
 inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family, Plan* out,
-                         int max_row_tiles = 8, int max_group_rows = kGroupMaxTileRows) {
+                         int max_row_tiles = 8, int max_group_rows = kGroupStreamRows) {
     if (dtype < F32 || dtype > Q8 || M < 0 || K < 0 || nvec < 1 || nvec > kMaxVectors)
         return INVALID;
 
@@ -288,12 +297,26 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         int u = 1;
         const int umax = dtype == Q8 ? 1 : max_group_rows;
         if ((int64_t)K * element_bytes(dtype) > kGroupShareMinXBytes) {
-            while (2 * u <= umax && 2 * u * p.batch <= kGroupTileLoads &&
+            const int64_t lanes = (int64_t)kWave * kGroupStreamWaves;
+            const int64_t chunks = ceil_div(full, lanes);
+            if (p.vector_loads && full * p.chunk_elems == K && chunks <= kGroupStreamMaxChunks) {
+                int r = kGroupStreamRows < umax ? kGroupStreamRows : umax;
+                while (r > 1 && ceil_div(M, r) < kGroupTileMinGroups) r /= 2;
+                if (r > 1) {
+                    p.x_in_registers = 1;
+                    p.waves_per_group = kGroupStreamWaves;
+                    p.lanes_per_row = (int)lanes;
+                    p.batch = (int)chunks;  // every chunk of a row in flight
+                    u = r;
+                }
+            }
+            const int ushare = umax < kGroupMaxTileRows ? umax : kGroupMaxTileRows;
+            while (!p.x_in_registers && 2 * u <= ushare && 2 * u * p.batch <= kGroupTileLoads &&
                    ceil_div(M, 2 * u) >= kGroupTileMinGroups)
                 u *= 2;
         }
         p.row_tiles = u;
-        p.lds_bytes = (int)(kGroupWaves * u * sizeof(float));
+        p.lds_bytes = (int)(p.waves_per_group * u * sizeof(float));
         break;
     }
     case BATCHED:

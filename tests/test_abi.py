@@ -143,7 +143,7 @@ def test_mid_rows_get_a_wavefront_each():
 def test_long_or_many_rows_get_a_workgroup_each():
     q = p("bf16", 4096, 14336)  # 1792 loads per row
     assert q["family"] == lg.FAMILY_GROUP_PER_ROW
-    assert q["lanes_per_row"] == 256 and q["batch"] == 8 and q["passes"] == 7
+    assert q["lanes_per_row"] == 256 and q["batch"] == 7 and q["passes"] == 7
     q = p("bf16", 14336, 4096)  # many rows of 512 loads: 2 per lane
     assert q["family"] == lg.FAMILY_GROUP_PER_ROW and q["batch"] == 2
     q = p("f32", 100, 1000)     # few rows: 250 loads, one per lane
@@ -424,21 +424,37 @@ def test_q8_families():
 
 
 def test_long_x_rows_share_a_workgroup():
-    """Rows whose x is longer than 16 KiB run two to a workgroup (each x chunk
-    serves both), when that still leaves 256 workgroups; shorter x keeps one
-    row per workgroup."""
+    """Rows whose x is longer than 16 KiB share a workgroup, as long as 256
+    workgroups remain.  Up to 7 x chunks per lane (bf16 K <= 14336, fp32 K <=
+    7168, K whole chunks) stay in registers while the workgroup walks 4 rows
+    (2 when 4 would leave too few workgroups); longer x, or K not whole
+    chunks, runs two rows per workgroup sharing each x chunk.  Shorter x
+    keeps one row per workgroup."""
     q = p("bf16", 4096, 14336)
-    assert (q["family"], q["row_tiles"], q["rows_per_group"], q["grid"]) == \
-        (lg.FAMILY_GROUP_PER_ROW, 2, 2, 2048)
+    assert (q["family"], q["row_tiles"], q["rows_per_group"], q["grid"], q["x_in_registers"]) == \
+        (lg.FAMILY_GROUP_PER_ROW, 4, 4, 1024, 1)
+    assert (q["batch"], q["block"], q["lds_bytes"]) == (7, 256, 64)
+    q = p("bf16", 1000, 14336)
+    assert (q["row_tiles"], q["grid"], q["x_in_registers"]) == (2, 500, 1)
+    assert p("bf16", 300, 14336)["grid"] == 300
+    assert p("f32", 2051, 7168)["batch"] == 7 and p("f32", 1025, 4100)["batch"] == 5
+    for dtype, M, K in (("bf16", 4096, 14344), ("bf16", 4096, 14340), ("f32", 4096, 8192)):
+        q = p(dtype, M, K)
+        assert (q["row_tiles"], q["batch"], q["x_in_registers"]) == (2, 8, 0), (dtype, K)
+    # element loads never keep x in registers
+    q = p("bf16", 4096, 14336, A=ALIGNED + 2)
+    assert q["vector_loads"] == 0 and q["x_in_registers"] == 0
     assert p("f32", 515, 8300, family=lg.FAMILY_GROUP_PER_ROW)["grid"] == 258
     for dtype, M, K in (("bf16", 14336, 4096), ("bf16", 4096, 8192), ("bf16", 100, 100000),
                         ("bf16", 510, 50000)):
         q = p(dtype, M, K, family=lg.FAMILY_GROUP_PER_ROW)
         assert q["row_tiles"] == 1 and q["grid"] == M
     # the loads of both rows' batch stay within 16 per lane
-    for K in (8200, 14336, 30000, 1 << 20):
+    for K in (8200, 14336, 14344, 30000, 1 << 20):
         q = p("bf16", 4096, K, family=lg.FAMILY_GROUP_PER_ROW)
-        assert q["row_tiles"] * q["batch"] <= 16
+        assert q["x_in_registers"] or q["row_tiles"] * q["batch"] <= 16
+        # with x in registers: the row's chunks and the next row's in flight
+        assert not q["x_in_registers"] or q["batch"] <= 7
 
 
 def test_read_probe_validation():

@@ -111,6 +111,26 @@ def test_integer_every_family(dtype, M, K):
             assert_bit_exact(y, ref, f"{dtype} {M}x{K} lda={lda} misalign={misalign} family {fam}")
 
 
+# x of 16-28 KiB held in registers while a workgroup walks 2 or 4 rows: 5 to 7
+# chunks per lane, the last one whole or partial; the last workgroup short
+STREAM_SHAPES = [("bf16", 1025, 8200), ("f16", 513, 12288), ("bf16", 4099, 14336),
+                 ("f16", 1030, 12296), ("bf16", 600, 10248), ("f32", 1025, 4100),
+                 ("f32", 517, 6144), ("f32", 2051, 7168), ("f32", 1026, 6148)]
+
+
+@pytest.mark.parametrize("dtype,M,K", STREAM_SHAPES)
+def test_integer_x_in_registers(dtype, M, K):
+    per = 16 // gi.ELEMENT_BYTES[dtype]
+    for lda in (K, K + per):
+        q = lg.plan(dtype, M, K, lda, 1, 1 << 20, 1 << 20)
+        assert q["family"] == lg.FAMILY_GROUP_PER_ROW and q["x_in_registers"] == 1
+        case = gi.make_integer(dtype, M, K, seed=M + K, lda=lda, bias=lda == K)
+        ref, _ = run_oracle(case)
+        print(f"{dtype} {M}x{K} lda={lda}: {q['row_tiles']} rows per workgroup, "
+              f"{q['batch']} x chunks per lane", flush=True)
+        assert_bit_exact(run_gpu(case, lg.FAMILY_AUTO), ref, f"{dtype} {M}x{K} lda={lda}")
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("nvec", list(range(1, 17)))
 def test_integer_batched(dtype, nvec):

@@ -140,6 +140,17 @@ __device__ __forceinline__ T uniform(T v) {
         return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
     }
 }
+// A wave-uniform pointer to global memory, passed through readfirstlane like
+// uniform() and rebuilt as a pointer into the global address space: rebuilt
+// as a generic pointer, every load and store through it was a flat
+// instruction (fused q/k/v, 6144 rows: 9.30 -> 9.09 µs).
+template <class T>
+__device__ __forceinline__ T* uniform_global(T* p) {
+    const uint64_t u = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+    return (T*)(__attribute__((address_space(1))) T*)(((uint64_t)hi << 32) | lo);
+}
 template <class S>
 struct SegEntry {
     const S* A;
@@ -224,7 +235,7 @@ struct ThreeSegments {
     __device__ __forceinline__ const S* row(int64_t m) const {
         const int e0 = uniform(end0), e1 = uniform(end1);
         const bool in1 = m >= e0, in2 = m >= e1;
-        const S* a = in2 ? uniform(A2) : (in1 ? uniform(A1) : uniform(A0));
+        const S* a = in2 ? uniform_global(A2) : (in1 ? uniform_global(A1) : uniform_global(A0));
         const int64_t s0 = in2 ? e1 : (in1 ? e0 : 0);
         return a + (m - s0) * (int64_t)lda;
     }
@@ -232,14 +243,14 @@ struct ThreeSegments {
     __device__ __forceinline__ float bias_of(int64_t m) const {
         const int e0 = uniform(end0), e1 = uniform(end1);
         const bool in1 = m >= e0, in2 = m >= e1;
-        const float* b = in2 ? uniform(b2) : (in1 ? uniform(b1) : uniform(b0));
+        const float* b = in2 ? uniform_global(b2) : (in1 ? uniform_global(b1) : uniform_global(b0));
         const int64_t s0 = in2 ? e1 : (in1 ? e0 : 0);
         return b != nullptr ? b[m - s0] : 0.f;
     }
     __device__ __forceinline__ void store(int64_t m, float v) const {
         const int e0 = uniform(end0), e1 = uniform(end1);
         const bool in1 = m >= e0, in2 = m >= e1;
-        float* o = in2 ? uniform(y2) : (in1 ? uniform(y1) : uniform(y0));
+        float* o = in2 ? uniform_global(y2) : (in1 ? uniform_global(y1) : uniform_global(y0));
         const int64_t s0 = in2 ? e1 : (in1 ? e0 : 0);
         o[m - s0] = v;
     }
@@ -293,7 +304,9 @@ __device__ __forceinline__ void rows_body(const Rows& rows, const typename D::xs
     constexpr int E = C::elems;
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // the wavefront index is uniform: said so, a wavefront's row tiles, and
+    // for one row per wavefront its row and row pointer, are scalars
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = lane & (L - 1);
     const int slot = lane / L;
     const int64_t tile0 = ((int64_t)blockIdx.x * kRowsWaves + wave) * U;

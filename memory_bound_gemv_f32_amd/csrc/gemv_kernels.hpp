@@ -29,17 +29,6 @@
 #include "gemv_device.hpp"
 
 namespace gemvdev {
-// 16 bytes per lane from global memory straight into LDS at lds + 16·lane
-// (global_load_lds_dwordx4; the device pass only: the host pass never
-// emits kernel bodies).
-__device__ __forceinline__ void load_to_lds16(const void* src, void* lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-#endif
-}
-}  // namespace gemvdev
-
-namespace gemvdev {
 
 // Wavefronts per workgroup of the rows and vector-ALU batched kernels: a
 // compile-time constant rather than the launch's block size, so that with
@@ -743,24 +732,32 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
 //
 // A workgroup owns 16 real rows (two groups of 8); its W wavefronts split
 // the 64-element steps of K into contiguous slices and walk them in chunks
-// of CH steps.  Per chunk a wavefront
-//   1. issues the loads of its 16 rows × CH steps of A,
-//   2. copies the same K range of every X column into its own LDS region
-//      with coalesced loads (one 1 KiB load per column; X columns are K
-//      elements apart, so reading the operands straight from memory would
-//      send each load to 16 addresses one column pitch apart, measured
-//      15-20 % slower); with one tile of vectors the loads go straight to
-//      LDS (global_load_lds), otherwise through registers,
-//   3. runs 2·CH·NT·2 MFMA steps, reading the X operands from LDS.
+// of CH steps.  Per chunk a wavefront issues the loads of X operands ahead
+// of the loads of A that they meet: loads complete in issue order, so the X
+// operands are ready when the A they meet lands and each step's MFMAs run as
+// its A arrives (with all A loads first, every MFMA waited for the last X
+// load: 16 vectors 9.04 -> 8.76 µs).  X columns
+// are K elements apart, so an X operand read straight from memory sends one
+// load to 16 addresses a column pitch apart:
+//   * with more than kMfmaFewVectors vectors, the chunk's K range of every X
+//     column is loaded with coalesced 16-byte loads (one 1 KiB load per
+//     column and step range), written to the wavefront's own LDS region
+//     and read back in operand layout (read straight from memory: 15-20 %
+//     slower at 16 vectors);
+//   * with at most kMfmaFewVectors (FEW) the operands come straight from
+//     memory, loaded step by step after the step's A (the lanes of the
+//     columns past nvec repeat column nvec-1, so a load touches at most nvec
+//     columns; 2 vectors: 7.44 -> 6.99 µs).
 // An MFMA output column depends on its own X column only, so the operand
-// columns of vectors past nvec are left as they are (their outputs are never
+// columns of vectors past nvec are never zeroed (their outputs are never
 // stored).  After one barrier wavefront 0 adds the W partial tiles in
-// wavefront order, adds the bias and writes Y.  Needs
-// 16-byte aligned A, X and row pitch and K % 8 == 0.  A chunk shorter than
-// CH steps at the end of a slice, and the last, partial 64-wide step
-// (K % 64 != 0, done by the last wavefront), read their operands directly.
-// FEW (at most kMfmaFewVectors vectors, one tile): only the X columns in use
-// are loaded and staged (2 vectors: 9.2 -> 8.6 µs at 4096 × 4096).
+// wavefront order and each lane finishes 4 consecutive rows of one column,
+// adds the bias and writes them with one 16-byte store where Y allows it
+// (four scattered 4-byte stores per lane before: 16 vectors 8.76 -> 8.38
+// µs).  Needs 16-byte aligned A, X and row pitch and K % 8 == 0.  A chunk
+// shorter than CH steps at the end of a slice, and the last, partial 64-wide
+// step (K % 64 != 0, done by the last wavefront), read their operands
+// directly.
 template <class D, int W, int NT, int CH, bool FEW>
 __global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2)))
 gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
@@ -773,6 +770,7 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     // padded by 16 bytes so that 16 lanes reading 16 columns hit distinct banks
     constexpr int kColQuads = CH * 8 + 1;
     static_assert(kCols * kColQuads >= NT * 64, "partials fit in the X region");
+    static_assert(!FEW || NT == 1, "few vectors: one tile");
     __shared__ quad xs[W][kCols * kColQuads];
 
     const int lane = threadIdx.x & 63;
@@ -800,77 +798,88 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     for (int q = 0; q < 2; ++q)
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[q][t][0] = acc[q][t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    constexpr int kQuads = kCols * 8 * CH;  // X quads (16 bytes) per chunk
     int c = s0;
-    for (; c + CH <= s1; c += CH) {
-        quad a[2][CH];
+    if constexpr (FEW) {
+        // X operands straight from memory: lane (column r, group g)
+        const S* xcol = X + (int64_t)(r < nvec ? r : nvec - 1) * K + 8 * g;
+        for (; c + CH <= s1; c += CH) {
+            // step by step, A then X: step i's MFMAs wait for its own four loads
+            // only (all X operands first measured 7.77 against 6.99 µs at 2 vectors)
+            quad a[2][CH], b[2][CH];
 #pragma unroll
-        for (int i = 0; i < CH; ++i)
+            for (int i = 0; i < CH; ++i) {
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
-                a[q][i] = __builtin_nontemporal_load(reinterpret_cast<const quad*>(ap[q] + (int64_t)(c + i) * 64));
-        // X chunk: quad qd is column qd / (8·CH), elements c·64 + 8·(qd % (8·CH)) .. +8.
-        // Load instruction t covers columns t·kLoadCols .. (t+1)·kLoadCols - 1.
-        // Columns past nvec hold anything finite or not: an MFMA output column
-        // depends on its own X column only, and those outputs are dropped.  So
-        // a load whose columns are all past nvec is skipped (FEW), and in a
-        // used one the columns past nvec repeat column nvec-1.
-        constexpr int kLoadCols = 64 / (8 * CH);
-        if constexpr (NT == 1) {
-            // one column per load, straight into the wavefront's LDS region
-            // (global_load_lds: no register round trip, no LDS write instructions)
-            static_assert(kLoadCols == 1, "one 1 KiB column per load");
-#pragma unroll
-            for (int t = 0; t < kQuads / 64; ++t) {
-                if (!FEW || t < nvec) {
-                    const int j = t < nvec ? t : nvec - 1;
-                    load_to_lds16(X + (int64_t)j * K + (int64_t)c * 64 + 8 * lane, xw + t * kColQuads);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // the loads into LDS (and the A loads) have landed
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-        } else {
-            quad xv[kQuads / 64];
-#pragma unroll
-            for (int t = 0; t < kQuads / 64; ++t) {
-                if (!FEW || t * kLoadCols < nvec) {
-                    const int qd = t * 64 + lane;
-                    const int j = qd / (8 * CH) < nvec ? qd / (8 * CH) : nvec - 1;
-                    xv[t] = *reinterpret_cast<const quad*>(X + (int64_t)j * K + (int64_t)c * 64 +
-                                                           8 * (qd % (8 * CH)));
-                }
+                for (int q = 0; q < 2; ++q)
+                    a[q][i] = __builtin_nontemporal_load(reinterpret_cast<const quad*>(ap[q] + (int64_t)(c + i) * 64));
+                b[0][i] = *reinterpret_cast<const quad*>(xcol + (int64_t)(c + i) * 64);
+                b[1][i] = *reinterpret_cast<const quad*>(xcol + (int64_t)(c + i) * 64 + 32);
             }
             __builtin_amdgcn_sched_barrier(0);  // all loads of the chunk in flight first
 #pragma unroll
-            for (int t = 0; t < kQuads / 64; ++t) {
-                if (!FEW || t * kLoadCols < nvec) {
-                    const int qd = t * 64 + lane;
-                    xw[(qd / (8 * CH)) * kColQuads + qd % (8 * CH)] = xv[t];
-                }
-            }
-        }
-        // the same wavefront reads back what its lanes wrote
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                // X operands of lane (column 16t + r, group g): the two halves of step i
-                const quad b0 = xw[(16 * t + r) * kColQuads + 8 * i + g];
-                const quad b1 = xw[(16 * t + r) * kColQuads + 8 * i + 4 + g];
+            for (int i = 0; i < CH; ++i)
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
-                    acc[q][t][0] = mma_16x16x32(D{}, a[q][i], b0, acc[q][t][0]);
-                    acc[q][t][1] = mma_16x16x32(D{}, a[q][i], b1, acc[q][t][1]);
+                    acc[q][0][0] = mma_16x16x32(D{}, a[q][i], b[0][i], acc[q][0][0]);
+                    acc[q][0][1] = mma_16x16x32(D{}, a[q][i], b[1][i], acc[q][0][1]);
+                }
+        }
+    } else {
+        // groups of G steps, X of the group (kCols columns × G steps) before A
+        // of the group: with one tile a group of 2 steps (the first MFMAs wait
+        // for a quarter of the chunk's X; 16 vectors 8.38 -> 8.10 µs), with
+        // more tiles the whole chunk (a group of 2 steps was 2 % slower at 32)
+        constexpr int G = NT == 1 && CH % 2 == 0 ? 2 : CH;
+        constexpr int kGroups = CH / G;
+        constexpr int kXLoads = kCols * G / 8;  // 1 KiB loads per group: 64/(8G) columns each
+        constexpr int kColsPerLoad = 64 / (8 * G);
+        static_assert(CH % G == 0 && kColsPerLoad * 8 * G == 64, "group shape");
+        for (; c + CH <= s1; c += CH) {
+            quad xv[kGroups][kXLoads], a[2][CH];
+#pragma unroll
+            for (int k = 0; k < kGroups; ++k) {
+#pragma unroll
+                for (int u = 0; u < kXLoads; ++u) {
+                    const int col = u * kColsPerLoad + lane / (8 * G);
+                    const int qq = lane % (8 * G);
+                    const int j = col < nvec ? col : nvec - 1;
+                    xv[k][u] = *reinterpret_cast<const quad*>(X + (int64_t)j * K + (int64_t)(c + G * k) * 64 + 8 * qq);
+                }
+#pragma unroll
+                for (int i = G * k; i < G * k + G; ++i)
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+                        a[q][i] = __builtin_nontemporal_load(reinterpret_cast<const quad*>(ap[q] + (int64_t)(c + i) * 64));
+            }
+            __builtin_amdgcn_sched_barrier(0);  // all loads of the chunk in flight first
+#pragma unroll
+            for (int k = 0; k < kGroups; ++k) {
+#pragma unroll
+                for (int u = 0; u < kXLoads; ++u) {
+                    const int col = u * kColsPerLoad + lane / (8 * G);
+                    const int qq = lane % (8 * G);
+                    xw[col * kColQuads + 8 * G * k + qq] = xv[k][u];
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+                for (int i = G * k; i < G * k + G; ++i) {
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        const quad b0 = xw[(16 * t + r) * kColQuads + 8 * i + g];
+                        const quad b1 = xw[(16 * t + r) * kColQuads + 8 * i + 4 + g];
+#pragma unroll
+                        for (int q = 0; q < 2; ++q) {
+                            acc[q][t][0] = mma_16x16x32(D{}, a[q][i], b0, acc[q][t][0]);
+                            acc[q][t][1] = mma_16x16x32(D{}, a[q][i], b1, acc[q][t][1]);
+                        }
+                    }
                 }
             }
+            // the next chunk overwrites this wavefront's LDS region
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
         }
-        // the next chunk overwrites this wavefront's LDS region
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
     }
     // a short last chunk (fewer than CH steps) one step at a time, and the
     // last, partial step (K % 64 != 0, done by the last wavefront), with X
@@ -914,17 +923,41 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     }
     __syncthreads();
     if (wave == 0) {
+        // lane (column j0, quad gq) finishes rows 4·gq .. 4·gq + 3 of column
+        // j0: rows 4·gq, 4·gq + 1 sit in the partials of lane (j0, 2·(gq % 2)),
+        // rows 4·gq + 2, 4·gq + 3 in those of lane (j0, 2·(gq % 2) + 1), as
+        // components 2·(gq / 2) and 2·(gq / 2) + 1
+        const int j0 = lane >> 2;
+        const int gq = lane & 3;
+        const int srcA = 32 * (gq & 1) + j0;
+        const int srcB = srcA + 16;
+        const int co = 2 * (gq >> 1);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            f32x4 v = partial[t * 64 + lane];
+            float o[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int w = 1; w < W; ++w) v += reinterpret_cast<const f32x4*>(xs[w])[t * 64 + lane];
-            const int j = 16 * t + r;
+            for (int w = 0; w < W; ++w) {
+                const float* P = reinterpret_cast<const float*>(reinterpret_cast<const f32x4*>(xs[w]) + t * 64);
+                o[0] += P[srcA * 4 + co];
+                o[1] += P[srcA * 4 + co + 1];
+                o[2] += P[srcB * 4 + co];
+                o[3] += P[srcB * 4 + co + 1];
+            }
+            const int j = 16 * t + j0;
+            const int64_t m0 = row0 + 4 * gq;
             if (j < nvec) {
+                float* yp = Y + (int64_t)j * M + m0;
+                if (m0 + 3 < M && ((uintptr_t)yp & 15) == 0) {
+                    f32x4 out = {o[0], o[1], o[2], o[3]};
+                    if (bias != nullptr) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t m = row0 + 8 * (i >> 1) + 2 * g + (i & 1);
-                    if (m < M) Y[(int64_t)j * M + m] = v[i] + (bias != nullptr ? bias[m] : 0.f);
+                        for (int i = 0; i < 4; ++i) out[i] += bias[m0 + i];
+                    }
+                    *reinterpret_cast<f32x4*>(yp) = out;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (m0 + i < M) yp[i] = o[i] + (bias != nullptr ? bias[m0 + i] : 0.f);
                 }
             }
         }

@@ -96,8 +96,9 @@ constexpr int batched_rows(int nvec) { return nvec <= 2 ? 4 : (nvec <= 4 ? 2 : 1
 constexpr int kMfmaRows = 16;
 constexpr int kMfmaWaves = 8;
 constexpr int kMfmaChunk = 8;
-// Up to this many vectors the matrix-core kernel loads and stages only the
-// X columns in use.
+// Up to this many vectors the matrix-core kernel reads its X operands
+// straight from memory (a load touches only the columns in use) instead of
+// staging X in LDS.
 constexpr int kMfmaFewVectors = 8;
 // 16-vector tiles for nvec vectors (1, 2 or 4); the chunk shrinks as the
 // tiles grow so that the X staged per chunk stays 16 KiB per wavefront.

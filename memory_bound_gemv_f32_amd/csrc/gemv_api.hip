@@ -146,15 +146,13 @@ const void* group_stream_fn_nx(int rows) {
 
 template <class D>
 const void* group_stream_fn(int chunks, int rows) {
-    static_assert(gemvplan::kGroupStreamMaxChunks == 7, "streaming kernels hold up to 7 x chunks");
+    // x longer than 8 KiB: at least 3 chunks per lane of 4 wavefronts
+    static_assert(gemvplan::kGroupStreamMaxChunks == 6, "streaming kernels hold up to 6 x chunks");
     switch (chunks) {
-    case 1: return group_stream_fn_nx<D, 1>(rows);
-    case 2: return group_stream_fn_nx<D, 2>(rows);
     case 3: return group_stream_fn_nx<D, 3>(rows);
     case 4: return group_stream_fn_nx<D, 4>(rows);
     case 5: return group_stream_fn_nx<D, 5>(rows);
     case 6: return group_stream_fn_nx<D, 6>(rows);
-    case 7: return group_stream_fn_nx<D, 7>(rows);
     default: return nullptr;
     }
 }

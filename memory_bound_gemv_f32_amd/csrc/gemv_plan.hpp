@@ -77,13 +77,23 @@ constexpr int64_t kGroupShareMinXBytes = 16 * 1024;
 constexpr int kGroupMaxTileRows = 2;
 constexpr int kGroupTileLoads = 16;
 constexpr int64_t kGroupTileMinGroups = 256;
-// When such an x is at most kGroupStreamMaxChunks 16-byte chunks per lane
-// (bf16 K <= 14336, fp32 K <= 7168) and K is whole chunks, each lane keeps
-// its x chunks in registers and the workgroup walks up to kGroupStreamRows
-// rows (halved while fewer than kGroupTileMinGroups workgroups would remain),
-// each row's loads issued before the previous row's multiply-adds.
+// When x is longer than kGroupStreamMinXBytes and at most
+// kGroupStreamMaxChunks 16-byte chunks per lane (8 KiB < x <= 24 KiB: bf16
+// 4096 < K <= 12288, fp32 2048 < K <= 6144) and K is whole chunks, each lane
+// keeps its x chunks in registers and the workgroup walks up to
+// kGroupStreamRows rows (halved while fewer than kGroupTileMinGroups
+// workgroups would remain), each row's loads issued before the previous
+// row's multiply-adds; such shapes take this family even where a wavefront
+// per row would otherwise run them.  Measured on MI355X (bf16, µs, before ->
+// after): 4096 × 6144 9.97 -> 8.95, 4096 × 8192 12.2 -> 11.4, 8192 × 8192
+// 22.0 -> 20.5, 2048 × 8192 7.41 -> 6.85; 4096 × 10240 15.2 (two rows per
+// workgroup) -> 13.5.  At 7 chunks (bf16 4096 × 14336) two rows per
+// workgroup were faster (18.1 against 18.4 µs on three boxes), and with an
+// 8 KiB x (4096 × 4096, 14336 × 4096) the wavefront and workgroup per row
+// were (6.60 against 6.70, 17.4 against 17.5).
+constexpr int64_t kGroupStreamMinXBytes = 8 * 1024;
 constexpr int kGroupStreamWaves = 4;
-constexpr int kGroupStreamMaxChunks = 7;
+constexpr int kGroupStreamMaxChunks = 6;
 constexpr int kGroupStreamRows = 4;
 // Batched family: loads in flight per row, and rows per wavefront, fewer as
 // the number of vectors grows so that rows × vectors accumulators plus the
@@ -213,6 +223,16 @@ inline bool vector_ok(int dtype, int K, int lda, int nvec, uintptr_t A, uintptr_
 // looks up its matrix per lane, which costs registers.
 constexpr int kMultiMaxRowTiles = 2;
 
+// Whether a single-vector problem keeps x in registers (see
+// kGroupStreamMinXBytes) with at least two rows per workgroup.
+inline bool stream_fits(int dtype, int64_t M, int64_t K, bool vec, int max_group_rows) {
+    if (dtype == Q8 || !vec || max_group_rows < 2) return false;
+    const int64_t elems = kLoadBytes / element_bytes(dtype);
+    if (K % elems != 0 || K * element_bytes(dtype) <= kGroupStreamMinXBytes) return false;
+    const int64_t chunks = ceil_div(K / elems, (int64_t)kWave * kGroupStreamWaves);
+    return chunks <= kGroupStreamMaxChunks && ceil_div(M, 2) >= kGroupTileMinGroups;
+}
+
 inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family, Plan* out,
                          int max_row_tiles = 8, int max_group_rows = kGroupStreamRows) {
     if (dtype < F32 || dtype > Q8 || M < 0 || K < 0 || nvec < 1 || nvec > kMaxVectors)
@@ -237,7 +257,8 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
             fam = mfma_ok ? BATCHED_MFMA : BATCHED;
         else if (loads <= kRowsPerWaveMaxLanes)
             fam = ROWS_PER_WAVE;
-        else if (M <= kGroupMaxRows || long_or_many)
+        else if (M <= kGroupMaxRows || long_or_many ||
+                 stream_fits(dtype, M, K, p.vector_loads != 0, max_group_rows))
             fam = GROUP_PER_ROW;
         else
             fam = WAVE_PER_ROW;
@@ -297,7 +318,8 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         // rows per workgroup (one x chunk serves all of them)
         int u = 1;
         const int umax = dtype == Q8 ? 1 : max_group_rows;
-        if ((int64_t)K * element_bytes(dtype) > kGroupShareMinXBytes) {
+        const int64_t xbytes = (int64_t)K * element_bytes(dtype);
+        if (xbytes > kGroupStreamMinXBytes) {
             const int64_t lanes = (int64_t)kWave * kGroupStreamWaves;
             const int64_t chunks = ceil_div(full, lanes);
             if (p.vector_loads && full * p.chunk_elems == K && chunks <= kGroupStreamMaxChunks) {
@@ -311,8 +333,10 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
                     u = r;
                 }
             }
+        }
+        if (!p.x_in_registers && xbytes > kGroupShareMinXBytes) {
             const int ushare = umax < kGroupMaxTileRows ? umax : kGroupMaxTileRows;
-            while (!p.x_in_registers && 2 * u <= ushare && 2 * u * p.batch <= kGroupTileLoads &&
+            while (2 * u <= ushare && 2 * u * p.batch <= kGroupTileLoads &&
                    ceil_div(M, 2 * u) >= kGroupTileMinGroups)
                 u *= 2;
         }

@@ -141,9 +141,9 @@ def test_mid_rows_get_a_wavefront_each():
 
 
 def test_long_or_many_rows_get_a_workgroup_each():
-    q = p("bf16", 4096, 14336)  # 1792 loads per row
+    q = p("bf16", 4096, 14336)  # 1792 loads per row: 7 per lane, batches of 8
     assert q["family"] == lg.FAMILY_GROUP_PER_ROW
-    assert q["lanes_per_row"] == 256 and q["batch"] == 7 and q["passes"] == 7
+    assert q["lanes_per_row"] == 256 and q["batch"] == 8 and q["passes"] == 7
     q = p("bf16", 14336, 4096)  # many rows of 512 loads: 2 per lane
     assert q["family"] == lg.FAMILY_GROUP_PER_ROW and q["batch"] == 2
     q = p("f32", 100, 1000)     # few rows: 250 loads, one per lane
@@ -424,37 +424,51 @@ def test_q8_families():
 
 
 def test_long_x_rows_share_a_workgroup():
-    """Rows whose x is longer than 16 KiB share a workgroup, as long as 256
-    workgroups remain.  Up to 7 x chunks per lane (bf16 K <= 14336, fp32 K <=
-    7168, K whole chunks) stay in registers while the workgroup walks 4 rows
-    (2 when 4 would leave too few workgroups); longer x, or K not whole
-    chunks, runs two rows per workgroup sharing each x chunk.  Shorter x
+    """An x longer than 8 KiB and at most 6 chunks per lane of a 4-wavefront
+    workgroup (bf16 4096 < K <= 12288, fp32 2048 < K <= 6144, K whole chunks)
+    stays in registers while the workgroup walks 4 rows (2 when 4 would leave
+    fewer than 256 workgroups), also for shapes a wavefront per row would
+    otherwise run.  Longer x, or K not whole chunks, runs two rows per
+    workgroup sharing each x chunk once x is longer than 16 KiB.  Shorter x
     keeps one row per workgroup."""
-    q = p("bf16", 4096, 14336)
+    q = p("bf16", 4096, 12288)
     assert (q["family"], q["row_tiles"], q["rows_per_group"], q["grid"], q["x_in_registers"]) == \
         (lg.FAMILY_GROUP_PER_ROW, 4, 4, 1024, 1)
-    assert (q["batch"], q["block"], q["lds_bytes"]) == (7, 256, 64)
-    q = p("bf16", 1000, 14336)
+    assert (q["batch"], q["block"], q["lds_bytes"]) == (6, 256, 64)
+    q = p("bf16", 1000, 12288)
     assert (q["row_tiles"], q["grid"], q["x_in_registers"]) == (2, 500, 1)
-    assert p("bf16", 300, 14336)["grid"] == 300
-    assert p("f32", 2051, 7168)["batch"] == 7 and p("f32", 1025, 4100)["batch"] == 5
-    for dtype, M, K in (("bf16", 4096, 14344), ("bf16", 4096, 14340), ("f32", 4096, 8192)):
+    assert p("bf16", 300, 12288)["grid"] == 300
+    # 8 KiB < x <= 16 KiB: rows a wavefront per row would run keep x in registers too
+    for dtype, M, K, chunks in (("bf16", 4096, 6144, 3), ("bf16", 4096, 8192, 4),
+                                ("f16", 2048, 4104, 3), ("f32", 4096, 2052, 3)):
+        q = p(dtype, M, K)
+        assert (q["family"], q["x_in_registers"], q["batch"], q["row_tiles"]) == \
+            (lg.FAMILY_GROUP_PER_ROW, 1, chunks, 4), (dtype, M, K)
+    # too few rows for two per workgroup: the families of before
+    assert p("bf16", 500, 6144)["family"] == lg.FAMILY_WAVE_PER_ROW
+    assert p("bf16", 4096, 4096)["family"] == lg.FAMILY_WAVE_PER_ROW
+    assert p("f32", 2051, 6144)["batch"] == 6 and p("f32", 1025, 4100)["batch"] == 5
+    # 7 chunks per lane (bf16 4096 x 14336: two rows per workgroup measured
+    # faster), x past 24 KiB, or K not whole chunks: two rows share each x chunk
+    for dtype, M, K in (("bf16", 4096, 14336), ("bf16", 4096, 14344), ("bf16", 4096, 14340),
+                        ("f32", 4096, 8192), ("f32", 2051, 7168)):
         q = p(dtype, M, K)
         assert (q["row_tiles"], q["batch"], q["x_in_registers"]) == (2, 8, 0), (dtype, K)
+    assert p("bf16", 1000, 14336)["grid"] == 500
     # element loads never keep x in registers
-    q = p("bf16", 4096, 14336, A=ALIGNED + 2)
+    q = p("bf16", 4096, 12288, A=ALIGNED + 2)
     assert q["vector_loads"] == 0 and q["x_in_registers"] == 0
     assert p("f32", 515, 8300, family=lg.FAMILY_GROUP_PER_ROW)["grid"] == 258
-    for dtype, M, K in (("bf16", 14336, 4096), ("bf16", 4096, 8192), ("bf16", 100, 100000),
+    for dtype, M, K in (("bf16", 14336, 4096), ("bf16", 510, 8192), ("bf16", 100, 100000),
                         ("bf16", 510, 50000)):
         q = p(dtype, M, K, family=lg.FAMILY_GROUP_PER_ROW)
         assert q["row_tiles"] == 1 and q["grid"] == M
     # the loads of both rows' batch stay within 16 per lane
-    for K in (8200, 14336, 14344, 30000, 1 << 20):
+    for K in (4104, 8200, 12288, 14336, 14344, 30000, 1 << 20):
         q = p("bf16", 4096, K, family=lg.FAMILY_GROUP_PER_ROW)
         assert q["x_in_registers"] or q["row_tiles"] * q["batch"] <= 16
         # with x in registers: the row's chunks and the next row's in flight
-        assert not q["x_in_registers"] or q["batch"] <= 7
+        assert not q["x_in_registers"] or 3 <= q["batch"] <= 6
 
 
 def test_read_probe_validation():

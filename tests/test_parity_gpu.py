@@ -111,11 +111,13 @@ def test_integer_every_family(dtype, M, K):
             assert_bit_exact(y, ref, f"{dtype} {M}x{K} lda={lda} misalign={misalign} family {fam}")
 
 
-# x of 16-28 KiB held in registers while a workgroup walks 2 or 4 rows: 5 to 7
+# x of 8-24 KiB held in registers while a workgroup walks 2 or 4 rows: 3 to 6
 # chunks per lane, the last one whole or partial; the last workgroup short
-STREAM_SHAPES = [("bf16", 1025, 8200), ("f16", 513, 12288), ("bf16", 4099, 14336),
-                 ("f16", 1030, 12296), ("bf16", 600, 10248), ("f32", 1025, 4100),
-                 ("f32", 517, 6144), ("f32", 2051, 7168), ("f32", 1026, 6148)]
+STREAM_SHAPES = [("bf16", 1025, 8200), ("f16", 513, 12288), ("bf16", 4099, 12288),
+                 ("f16", 1030, 10248), ("bf16", 600, 10248), ("f32", 1025, 4100),
+                 ("f32", 517, 6144), ("f32", 2051, 6140), ("f32", 1026, 5124),
+                 ("bf16", 1025, 4104), ("f16", 600, 6144), ("bf16", 2051, 8192),
+                 ("f32", 2050, 2052), ("f32", 777, 3000)]
 
 
 @pytest.mark.parametrize("dtype,M,K", STREAM_SHAPES)

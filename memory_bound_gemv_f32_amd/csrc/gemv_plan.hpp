@@ -145,7 +145,16 @@ constexpr int64_t kQ8PairRowsMinGroups = 256;
 constexpr int kBlock = 256;
 // Below this many workgroups the rows-per-wave family stops giving each
 // wavefront several row tiles, so that small problems still spread out.
+// At most kRowsMaxTiles tiles, and with a full 32-lane row group two tiles
+// while that still leaves kManyGroups workgroups: more, smaller workgroups
+// stream tall matrices faster (MI355X, 2^20 rows, µs with 8 -> 4 -> 2
+// tiles: fp32 K = 16 11.96, 11.96, 12.31; K = 32 21.71, 21.52, 22.17;
+// K = 64 40.89, 40.19, 40.00; K = 128 80.59, 78.05, 76.94; bf16 K = 256
+// 80.18, 77.77, 76.65; fp32 2^22 × 16 46.04, 44.31, 44.32; but fp32
+// 2^18 × 128 20.44, 20.31, 21.29).
 constexpr int64_t kTargetGroups = 1024;
+constexpr int kRowsMaxTiles = 4;
+constexpr int64_t kManyGroups = 65536;
 
 struct Plan {
     int family = -1;
@@ -282,13 +291,18 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         // as many row tiles per wavefront as keeps >= kTargetGroups groups
         p.row_tiles = 1;
         if (p.vector_loads) {
-            for (int u = max_row_tiles; u > 1; u >>= 1) {
-                const int64_t rows = (int64_t)u * p.rows_per_wave * p.waves_per_group;
-                if (ceil_div(M, rows) >= kTargetGroups) {
+            const int cap = max_row_tiles < kRowsMaxTiles ? max_row_tiles : kRowsMaxTiles;
+            auto groups = [&](int u) {
+                return ceil_div(M, (int64_t)u * p.rows_per_wave * p.waves_per_group);
+            };
+            for (int u = cap; u > 1; u >>= 1) {
+                if (groups(u) >= kTargetGroups) {
                     p.row_tiles = u;
                     break;
                 }
             }
+            if (p.lanes_per_row == kRowsPerWaveMaxLanes && p.row_tiles > 2 && groups(2) >= kManyGroups)
+                p.row_tiles = 2;
         }
         break;
     }

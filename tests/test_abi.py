@@ -121,9 +121,22 @@ def test_short_rows_share_a_wavefront(dtype, K, lanes):
 
 def test_skinny_k16_geometry():
     q = p("f32", 1 << 20, 16)
-    assert (q["lanes_per_row"], q["rows_per_wave"], q["row_tiles"]) == (4, 16, 8)
-    assert q["rows_per_group"] == 16 * 8 * 4
+    assert (q["lanes_per_row"], q["rows_per_wave"], q["row_tiles"]) == (4, 16, 4)
+    assert q["rows_per_group"] == 16 * 4 * 4
     assert q["grid"] == (1 << 20) // q["rows_per_group"]
+
+
+def test_row_tiles_of_tall_matrices():
+    """At most 4 row tiles per wavefront; full 32-lane row groups take 2
+    while that leaves 65536 workgroups, fewer rows keep 4, and problems
+    below 1024 workgroups' worth keep one."""
+    q = p("f32", 1 << 20, 128)  # 32 lanes per row, 2 rows per wavefront
+    assert (q["lanes_per_row"], q["row_tiles"], q["grid"]) == (32, 2, 1 << 16)
+    assert p("bf16", 1 << 20, 256)["row_tiles"] == 2
+    assert p("f32", 1 << 18, 128)["row_tiles"] == 4
+    assert p("f32", 1 << 20, 32)["row_tiles"] == 4
+    assert p("f32", 1 << 22, 16)["row_tiles"] == 4
+    assert p("f32", 1024 * 64, 16)["row_tiles"] == 1
 
 
 def test_small_problem_spreads_out():

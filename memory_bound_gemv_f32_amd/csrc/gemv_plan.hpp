@@ -108,8 +108,9 @@ constexpr int kMfmaWaves = 8;
 constexpr int kMfmaChunk = 8;
 // Up to this many vectors the matrix-core kernel reads its X operands
 // straight from memory (a load touches only the columns in use) instead of
-// staging X in LDS.
-constexpr int kMfmaFewVectors = 8;
+// staging X in LDS (fp16 4096 × 4096, µs, straight / staged: 3 vectors
+// 7.07 / 7.15, 4 7.19 / 7.25, 5 7.25 / 7.27, 6 7.38 / 7.30, 8 7.63 / 7.38).
+constexpr int kMfmaFewVectors = 5;
 // 16-vector tiles for nvec vectors (1, 2 or 4); the chunk shrinks as the
 // tiles grow so that the X staged per chunk stays 16 KiB per wavefront.
 constexpr int mfma_tiles(int nvec) { return nvec <= 16 ? 1 : (nvec <= 32 ? 2 : 4); }

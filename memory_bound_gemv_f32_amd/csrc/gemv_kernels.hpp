@@ -825,10 +825,12 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
         }
     } else {
         // groups of G steps, X of the group (kCols columns × G steps) before A
-        // of the group: with one tile a group of 2 steps (the first MFMAs wait
-        // for a quarter of the chunk's X; 16 vectors 8.38 -> 8.10 µs), with
-        // more tiles the whole chunk (a group of 2 steps was 2 % slower at 32)
-        constexpr int G = NT == 1 && CH % 2 == 0 ? 2 : CH;
+        // of the group: with up to two tiles one step per group, so that a
+        // step's MFMAs wait for its own X only (fp16 4096 × 4096, µs, whole
+        // chunk / 2 steps / 1 step: 16 vectors 8.38 / 8.07 / 7.82, 24
+        // vectors 10.12 (2 steps) / 9.52); with four tiles the whole chunk
+        // (64 vectors 14.11 against 15.02 one step at a time)
+        constexpr int G = NT <= 2 ? 1 : CH;
         constexpr int kGroups = CH / G;
         constexpr int kXLoads = kCols * G / 8;  // 1 KiB loads per group: 64/(8G) columns each
         constexpr int kColsPerLoad = 64 / (8 * G);

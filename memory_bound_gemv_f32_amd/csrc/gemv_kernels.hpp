@@ -117,22 +117,11 @@ constexpr int kFewSegments = 3;
 // from a selected address, which leaves the structure in scratch memory (or
 // makes an indexed memory load of the argument table) ahead of the first
 // A load.
-template <class T>
-__device__ __forceinline__ T uniform(T v) {
-    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
-    if constexpr (sizeof(T) == 4) {
-        return __builtin_bit_cast(T, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
-    } else {
-        const uint64_t u = __builtin_bit_cast(uint64_t, v);
-        const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
-        const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
-        return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
-    }
-}
-// A wave-uniform pointer to global memory, passed through readfirstlane like
-// uniform() and rebuilt as a pointer into the global address space: rebuilt
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+// A wave-uniform pointer to global memory: its two halves through
+// readfirstlane, rebuilt as a pointer into the global address space (rebuilt
 // as a generic pointer, every load and store through it was a flat
-// instruction (fused q/k/v, 6144 rows: 9.30 -> 9.09 µs).
+// instruction: fused q/k/v, 6144 rows, 9.30 -> 9.09 µs).
 template <class T>
 __device__ __forceinline__ T* uniform_global(T* p) {
     const uint64_t u = (uint64_t)(uintptr_t)p;

@@ -723,16 +723,17 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
 // the 64-element steps of K into contiguous slices and walk them in chunks
 // of CH steps.  Per chunk a wavefront issues the loads of X operands ahead
 // of the loads of A that they meet: loads complete in issue order, so the X
-// operands are ready when the A they meet lands and each step's MFMAs run as
-// its A arrives (with all A loads first, every MFMA waited for the last X
-// load: 16 vectors 9.04 -> 8.76 µs).  X columns
-// are K elements apart, so an X operand read straight from memory sends one
-// load to 16 addresses a column pitch apart:
-//   * with more than kMfmaFewVectors vectors, the chunk's K range of every X
-//     column is loaded with coalesced 16-byte loads (one 1 KiB load per
-//     column and step range), written to the wavefront's own LDS region
-//     and read back in operand layout (read straight from memory: 15-20 %
-//     slower at 16 vectors);
+// operands are ready when the A they meet lands and each step's MFMAs run
+// as its A arrives (with all A loads first, every MFMA waited for the last
+// X load: 16 vectors 9.04 -> 8.76 µs).  X columns are K elements apart, so
+// an X operand read straight from memory sends one load to 16 addresses a
+// column pitch apart:
+//   * with more than kMfmaFewVectors vectors, the K range of every X column
+//     is loaded with coalesced 16-byte loads (a load covers whole 128-byte
+//     pieces of 8 columns with one step per group, of 2 or 4 columns with a
+//     whole chunk), written to the wavefront's own LDS region and read back
+//     in operand layout (read straight from memory: 15-20 % slower at 16
+//     vectors);
 //   * with at most kMfmaFewVectors (FEW) the operands come straight from
 //     memory, loaded step by step after the step's A (the lanes of the
 //     columns past nvec repeat column nvec-1, so a load touches at most nvec

@@ -57,10 +57,14 @@ constexpr int kRowsPerWaveMaxLanes = 32;
 // automatically: few rows (fewer than there are CUs' worth of wavefronts),
 // long rows (a wavefront per row would walk them in several dependent
 // batches), or very many rows.
+// (Many rows: from 6144 rows of 512 loads the workgroup per row was ahead,
+// bf16 × 4096, µs, wavefront / workgroup per row: 4096 rows 6.60 / 6.70,
+// 6144 8.86 / 8.80, 7168 10.10 / 9.93, 8192 10.93 / 10.89; the fused q/k/v
+// call over 6144 rows 9.08 / 8.87.)
 constexpr int kGroupWaves = 4;
 constexpr int64_t kGroupMaxRows = 256;
 constexpr int64_t kGroupLongRowLoads = 1024;
-constexpr int64_t kGroupManyRows = 8192;
+constexpr int64_t kGroupManyRows = 6144;
 constexpr int64_t kGroupManyRowsMinLoads = 512;
 // Wave-per-row family: loads per lane kept in flight per row.
 constexpr int kWaveBatch = 8;

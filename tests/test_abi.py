@@ -159,6 +159,9 @@ def test_long_or_many_rows_get_a_workgroup_each():
     assert q["lanes_per_row"] == 256 and q["batch"] == 8 and q["passes"] == 7
     q = p("bf16", 14336, 4096)  # many rows of 512 loads: 2 per lane
     assert q["family"] == lg.FAMILY_GROUP_PER_ROW and q["batch"] == 2
+    # "many" starts at 6144 rows (the fused q/k/v rows of one decode token)
+    assert p("bf16", 6144, 4096)["family"] == lg.FAMILY_GROUP_PER_ROW
+    assert p("bf16", 6143, 4096)["family"] == lg.FAMILY_WAVE_PER_ROW
     q = p("f32", 100, 1000)     # few rows: 250 loads, one per lane
     assert q["family"] == lg.FAMILY_GROUP_PER_ROW and q["batch"] == 1
 

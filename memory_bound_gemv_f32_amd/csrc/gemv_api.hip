@@ -50,17 +50,39 @@ gemv_status_t finish(hipError_t err) {
 // kernels, kFewSegments the kernels that take up to three segments as scalar
 // arguments, any other value the segment-table kernels whose select chains
 // cover NSEG entries.
+// one wavefront per row: B loads per lane in flight per batch
+template <class D, bool VEC, int NSEG, int B>
+const void* wave_fn_b() {
+    if constexpr (NSEG == gemvdev::kFewSegments)
+        return (const void*)&gemvdev::gemv_rows_multi3_kernel<D, 64, 1, B, VEC>;
+    else if constexpr (NSEG > 0)
+        return (const void*)&gemvdev::gemv_rows_multi_kernel<D, 64, 1, B, VEC, NSEG>;
+    else
+        return (const void*)&gemvdev::gemv_rows_kernel<D, 64, 1, B, VEC>;
+}
+
+template <class D, bool VEC, int NSEG>
+const void* wave_fn(int batch) {
+    static_assert(gemvplan::kWaveBatch == 8, "wave-per-row kernels are built for batches of 1 to 8");
+    switch (batch) {
+    case 1: return wave_fn_b<D, VEC, NSEG, 1>();
+    case 2: return wave_fn_b<D, VEC, NSEG, 2>();
+    case 3: return wave_fn_b<D, VEC, NSEG, 3>();
+    case 4: return wave_fn_b<D, VEC, NSEG, 4>();
+    case 5: return wave_fn_b<D, VEC, NSEG, 5>();
+    case 6: return wave_fn_b<D, VEC, NSEG, 6>();
+    case 7: return wave_fn_b<D, VEC, NSEG, 7>();
+    case 8: return wave_fn_b<D, VEC, NSEG, 8>();
+    default: return nullptr;
+    }
+}
+
 template <class D, int L, bool VEC, int NSEG>
-const void* rows_fn(int tiles) {
+const void* rows_fn(int tiles, int batch) {
     if constexpr (L == 64) {
-        // one wavefront per row: a single row tile, kWaveBatch loads in flight
+        // one wavefront per row: a single row tile
         if (tiles != 1) return nullptr;
-        if constexpr (NSEG == gemvdev::kFewSegments)
-            return (const void*)&gemvdev::gemv_rows_multi3_kernel<D, 64, 1, gemvplan::kWaveBatch, VEC>;
-        else if constexpr (NSEG > 0)
-            return (const void*)&gemvdev::gemv_rows_multi_kernel<D, 64, 1, gemvplan::kWaveBatch, VEC, NSEG>;
-        else
-            return (const void*)&gemvdev::gemv_rows_kernel<D, 64, 1, gemvplan::kWaveBatch, VEC>;
+        return wave_fn<D, VEC, NSEG>(batch);
     } else if constexpr (NSEG > 0) {
         // per-lane segment lookups cost registers: at most two row tiles
         if constexpr (NSEG == gemvdev::kFewSegments) {
@@ -88,15 +110,17 @@ const void* rows_fn(int tiles) {
 }
 
 template <class D, bool VEC, int NSEG>
-const void* rows_fn(int lanes, int tiles) {
+const void* rows_fn(int lanes, int tiles, int batch) {
+    // several rows per wavefront: one load per lane per row tile
+    if (lanes < 64 && batch != 1) return nullptr;
     switch (lanes) {
-    case 1: return rows_fn<D, 1, VEC, NSEG>(tiles);
-    case 2: return rows_fn<D, 2, VEC, NSEG>(tiles);
-    case 4: return rows_fn<D, 4, VEC, NSEG>(tiles);
-    case 8: return rows_fn<D, 8, VEC, NSEG>(tiles);
-    case 16: return rows_fn<D, 16, VEC, NSEG>(tiles);
-    case 32: return rows_fn<D, 32, VEC, NSEG>(tiles);
-    case 64: return rows_fn<D, 64, VEC, NSEG>(tiles);
+    case 1: return rows_fn<D, 1, VEC, NSEG>(tiles, batch);
+    case 2: return rows_fn<D, 2, VEC, NSEG>(tiles, batch);
+    case 4: return rows_fn<D, 4, VEC, NSEG>(tiles, batch);
+    case 8: return rows_fn<D, 8, VEC, NSEG>(tiles, batch);
+    case 16: return rows_fn<D, 16, VEC, NSEG>(tiles, batch);
+    case 32: return rows_fn<D, 32, VEC, NSEG>(tiles, batch);
+    case 64: return rows_fn<D, 64, VEC, NSEG>(tiles, batch);
     default: return nullptr;
     }
 }
@@ -161,7 +185,7 @@ template <class D, bool VEC, int NSEG>
 const void* single_fn(const Plan& p) {
     switch (p.family) {
     case gemvplan::ROWS_PER_WAVE:
-    case gemvplan::WAVE_PER_ROW: return rows_fn<D, VEC, NSEG>(p.lanes_per_row, p.row_tiles);
+    case gemvplan::WAVE_PER_ROW: return rows_fn<D, VEC, NSEG>(p.lanes_per_row, p.row_tiles, p.batch);
     case gemvplan::GROUP_PER_ROW:
         if (p.x_in_registers) {
             if constexpr (NSEG == 0 && VEC) return group_stream_fn<D>(p.batch, p.row_tiles);

@@ -311,11 +311,17 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         }
         break;
     }
-    case WAVE_PER_ROW:
+    case WAVE_PER_ROW: {
         p.lanes_per_row = kWave;
         p.rows_per_wave = 1;
         p.waves_per_group = kBlock / kWave;
-        p.batch = kWaveBatch;
+        // the row's loads per lane in as few batches of at most kWaveBatch
+        // as possible, all batches of one size (a batch larger than the row
+        // needs costs registers and clamped loads: bf16 8192 × 1024, µs,
+        // batches of 8 / 2: 7.31 / 4.37; 8192 × 2048, 8 / 4: 8.38 / 6.62)
+        const int64_t per_lane = ceil_div(full, (int64_t)kWave);
+        const int64_t batches = ceil_div(per_lane, (int64_t)kWaveBatch);
+        p.batch = per_lane < 1 ? 1 : (int)ceil_div(per_lane, batches);
         p.row_tiles = 1;
         if (dtype == Q8) {
             // int8 rows: x chunks are 2-4 times the weight chunk, so batches
@@ -326,6 +332,7 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
             if (ceil_div(M, 2 * (kBlock / kWave)) >= kQ8PairRowsMinGroups) p.row_tiles = 2;
         }
         break;
+    }
     case GROUP_PER_ROW: {
         p.lanes_per_row = kWave * kGroupWaves;
         p.rows_per_wave = 0;  // a row spans the whole workgroup

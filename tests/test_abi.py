@@ -153,6 +153,20 @@ def test_mid_rows_get_a_wavefront_each():
     assert p("bf16", 1024, 4096)["family"] == lg.FAMILY_WAVE_PER_ROW
 
 
+def test_wavefront_batches_fit_the_row():
+    """A wavefront per row issues its row's loads in as few batches of at
+    most 8 loads per lane as possible, all of one size."""
+    for dtype, M, K, batch in (("bf16", 4096, 2048, 4), ("bf16", 4096, 1024, 2),
+                               ("bf16", 4096, 3072, 6), ("bf16", 300, 5120, 5),
+                               ("bf16", 300, 1000, 2), ("f32", 4096, 1024, 4),
+                               ("bf16", 300, 8184, 8), ("bf16", 300, 7000, 7)):
+        q = p(dtype, M, K)
+        assert (q["family"], q["batch"]) == (lg.FAMILY_WAVE_PER_ROW, batch), (dtype, M, K)
+        loads = -(-K // q["chunk_elems"])
+        per_lane = -(-loads // 64)
+        assert q["batch"] * -(-per_lane // q["batch"]) - per_lane < -(-per_lane // 8)
+
+
 def test_long_or_many_rows_get_a_workgroup_each():
     q = p("bf16", 4096, 14336)  # 1792 loads per row: 7 per lane, batches of 8
     assert q["family"] == lg.FAMILY_GROUP_PER_ROW

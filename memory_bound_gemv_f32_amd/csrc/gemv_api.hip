@@ -147,10 +147,15 @@ const void* group_fn_b(int rows) {
 
 template <class D, bool VEC, int NSEG>
 const void* group_fn(int batch, int rows) {
+    static_assert(gemvplan::kGroupBatch == 8, "workgroup-per-row kernels are built for batches of 1 to 8");
     switch (batch) {
     case 1: return group_fn_b<D, VEC, NSEG, 1>(rows);
     case 2: return group_fn_b<D, VEC, NSEG, 2>(rows);
+    case 3: return group_fn_b<D, VEC, NSEG, 3>(rows);
     case 4: return group_fn_b<D, VEC, NSEG, 4>(rows);
+    case 5: return group_fn_b<D, VEC, NSEG, 5>(rows);
+    case 6: return group_fn_b<D, VEC, NSEG, 6>(rows);
+    case 7: return group_fn_b<D, VEC, NSEG, 7>(rows);
     case 8: return group_fn_b<D, VEC, NSEG, 8>(rows);
     default: return nullptr;
     }
@@ -309,6 +314,7 @@ const void* q8_fn(const Plan& p) {
         switch (p.batch) {
         case 1: return (const void*)&gemvdev::gemv_group_q8_kernel<X, W, 1, VEC>;
         case 2: return (const void*)&gemvdev::gemv_group_q8_kernel<X, W, 2, VEC>;
+        case 3: return (const void*)&gemvdev::gemv_group_q8_kernel<X, W, 3, VEC>;
         case 4: return (const void*)&gemvdev::gemv_group_q8_kernel<X, W, 4, VEC>;
         default: return nullptr;
         }

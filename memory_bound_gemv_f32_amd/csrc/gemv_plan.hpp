@@ -337,10 +337,12 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         p.lanes_per_row = kWave * kGroupWaves;
         p.rows_per_wave = 0;  // a row spans the whole workgroup
         p.waves_per_group = kGroupWaves;
-        // as many loads per lane in flight as the row gives each lane, up to 8
+        // the row's loads per lane in as few batches of at most 8 (int8: 4)
+        // as possible, all of one size (as for a wavefront per row)
         const int64_t per_lane = ceil_div(full, (int64_t)p.lanes_per_row);
         const int cap = dtype == Q8 ? kQ8Batch : kGroupBatch;
-        p.batch = per_lane >= cap ? cap : next_pow2(per_lane < 1 ? 1 : per_lane);
+        const int64_t batches = ceil_div(per_lane, (int64_t)cap);
+        p.batch = per_lane < 1 ? 1 : (int)ceil_div(per_lane, batches);
         // rows per workgroup (one x chunk serves all of them)
         int u = 1;
         const int umax = dtype == Q8 ? 1 : max_group_rows;

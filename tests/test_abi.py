@@ -168,9 +168,9 @@ def test_wavefront_batches_fit_the_row():
 
 
 def test_long_or_many_rows_get_a_workgroup_each():
-    q = p("bf16", 4096, 14336)  # 1792 loads per row: 7 per lane, batches of 8
+    q = p("bf16", 4096, 14336)  # 1792 loads per row: 7 per lane, one batch
     assert q["family"] == lg.FAMILY_GROUP_PER_ROW
-    assert q["lanes_per_row"] == 256 and q["batch"] == 8 and q["passes"] == 7
+    assert q["lanes_per_row"] == 256 and q["batch"] == 7 and q["passes"] == 7
     q = p("bf16", 14336, 4096)  # many rows of 512 loads: 2 per lane
     assert q["family"] == lg.FAMILY_GROUP_PER_ROW and q["batch"] == 2
     # "many" starts at 6144 rows (the fused q/k/v rows of one decode token)
@@ -480,10 +480,11 @@ def test_long_x_rows_share_a_workgroup():
     assert p("f32", 2051, 6144)["batch"] == 6 and p("f32", 1025, 4100)["batch"] == 5
     # 7 chunks per lane (bf16 4096 x 14336: two rows per workgroup measured
     # faster), x past 24 KiB, or K not whole chunks: two rows share each x chunk
-    for dtype, M, K in (("bf16", 4096, 14336), ("bf16", 4096, 14344), ("bf16", 4096, 14340),
-                        ("f32", 4096, 8192), ("f32", 2051, 7168)):
+    for dtype, M, K, batch in (("bf16", 4096, 14336, 7), ("bf16", 4096, 14344, 8),
+                               ("bf16", 4096, 14340, 8), ("f32", 4096, 8192, 8),
+                               ("f32", 2051, 7168, 7)):
         q = p(dtype, M, K)
-        assert (q["row_tiles"], q["batch"], q["x_in_registers"]) == (2, 8, 0), (dtype, K)
+        assert (q["row_tiles"], q["batch"], q["x_in_registers"]) == (2, batch, 0), (dtype, K)
     assert p("bf16", 1000, 14336)["grid"] == 500
     # element loads never keep x in registers
     q = p("bf16", 4096, 12288, A=ALIGNED + 2)

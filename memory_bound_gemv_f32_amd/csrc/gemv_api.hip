@@ -264,7 +264,11 @@ const void* gated_fn(int batch) {
     switch (batch) {
     case 1: return (const void*)&gemvdev::gemv_gated_silu_kernel<D, W, 1, VEC>;
     case 2: return (const void*)&gemvdev::gemv_gated_silu_kernel<D, W, 2, VEC>;
+    case 3: return (const void*)&gemvdev::gemv_gated_silu_kernel<D, W, 3, VEC>;
     case 4: return (const void*)&gemvdev::gemv_gated_silu_kernel<D, W, 4, VEC>;
+    case 5: return (const void*)&gemvdev::gemv_gated_silu_kernel<D, W, 5, VEC>;
+    case 6: return (const void*)&gemvdev::gemv_gated_silu_kernel<D, W, 6, VEC>;
+    case 7: return (const void*)&gemvdev::gemv_gated_silu_kernel<D, W, 7, VEC>;
     case 8: return (const void*)&gemvdev::gemv_gated_silu_kernel<D, W, 8, VEC>;
     default: return nullptr;
     }
@@ -289,9 +293,11 @@ const void* q8_rows_fn(int tiles, int batch) {
         switch (batch * 4 + tiles) {
         case 1 * 4 + 1: return (const void*)&gemvdev::gemv_rows_q8_kernel<X, 64, 1, 1, VEC>;
         case 2 * 4 + 1: return (const void*)&gemvdev::gemv_rows_q8_kernel<X, 64, 1, 2, VEC>;
+        case 3 * 4 + 1: return (const void*)&gemvdev::gemv_rows_q8_kernel<X, 64, 1, 3, VEC>;
         case 4 * 4 + 1: return (const void*)&gemvdev::gemv_rows_q8_kernel<X, 64, 1, 4, VEC>;
         case 1 * 4 + 2: return (const void*)&gemvdev::gemv_rows_q8_kernel<X, 64, 2, 1, VEC>;
         case 2 * 4 + 2: return (const void*)&gemvdev::gemv_rows_q8_kernel<X, 64, 2, 2, VEC>;
+        case 3 * 4 + 2: return (const void*)&gemvdev::gemv_rows_q8_kernel<X, 64, 2, 3, VEC>;
         case 4 * 4 + 2: return (const void*)&gemvdev::gemv_rows_q8_kernel<X, 64, 2, 4, VEC>;
         default: return nullptr;
         }
@@ -339,13 +345,17 @@ const void* splitk_fn(int batch) {
     switch (batch) {
     case 1: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, 1, VEC>;
     case 2: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, 2, VEC>;
+    case 3: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, 3, VEC>;
     case 4: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, 4, VEC>;
+    case 5: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, 5, VEC>;
+    case 6: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, 6, VEC>;
+    case 7: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, 7, VEC>;
     case 8: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, 8, VEC>;
     default: return nullptr;
     }
 }
 
-static_assert(gemvplan::kQ8Batch == 4, "the int8 kernels are instantiated for batches 1, 2, 4");
+static_assert(gemvplan::kQ8Batch == 4, "the int8 kernels are instantiated for batches 1 to 4");
 static_assert(gemvplan::kGroupWaves == gemvdev::kGroupWavesDev,
               "the planner's split-K workgroup is the one the kernel is compiled for");
 

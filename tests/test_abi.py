@@ -343,7 +343,7 @@ def test_splitk_for_few_long_rows():
         assert p["splits"] < 8 or p["splits"] % 8 == 0
         assert p["grid"] == M * p["splits"] and p["block"] == 256
         per_lane = -(-p["slice_elems"] * s // 16 // 256)
-        assert p["batch"] == min(8, 1 << (per_lane - 1).bit_length())
+        assert p["batch"] == -(-per_lane // -(-per_lane // 8))  # equal batches of <= 8
 
 
 def test_splitk_keeps_the_plain_plan_when_it_fills_the_gpu():

@@ -61,6 +61,22 @@ const void* wave_fn_b() {
         return (const void*)&gemvdev::gemv_rows_kernel<D, 64, 1, B, VEC>;
 }
 
+// several rows per wavefront (U row tiles, U·B <= 8 loads per lane in
+// flight), one matrix only
+template <class D, bool VEC>
+const void* wave_tiles_fn(int tiles, int batch) {
+    switch (tiles * 16 + batch) {
+    case 2 * 16 + 1: return (const void*)&gemvdev::gemv_rows_kernel<D, 64, 2, 1, VEC>;
+    case 2 * 16 + 2: return (const void*)&gemvdev::gemv_rows_kernel<D, 64, 2, 2, VEC>;
+    case 2 * 16 + 3: return (const void*)&gemvdev::gemv_rows_kernel<D, 64, 2, 3, VEC>;
+    case 2 * 16 + 4: return (const void*)&gemvdev::gemv_rows_kernel<D, 64, 2, 4, VEC>;
+    case 4 * 16 + 1: return (const void*)&gemvdev::gemv_rows_kernel<D, 64, 4, 1, VEC>;
+    case 4 * 16 + 2: return (const void*)&gemvdev::gemv_rows_kernel<D, 64, 4, 2, VEC>;
+    case 8 * 16 + 1: return (const void*)&gemvdev::gemv_rows_kernel<D, 64, 8, 1, VEC>;
+    default: return nullptr;
+    }
+}
+
 template <class D, bool VEC, int NSEG>
 const void* wave_fn(int batch) {
     static_assert(gemvplan::kWaveBatch == 8, "wave-per-row kernels are built for batches of 1 to 8");
@@ -80,9 +96,10 @@ const void* wave_fn(int batch) {
 template <class D, int L, bool VEC, int NSEG>
 const void* rows_fn(int tiles, int batch) {
     if constexpr (L == 64) {
-        // one wavefront per row: a single row tile
-        if (tiles != 1) return nullptr;
-        return wave_fn<D, VEC, NSEG>(batch);
+        // one wavefront per row
+        if (tiles == 1) return wave_fn<D, VEC, NSEG>(batch);
+        if constexpr (NSEG == 0) return wave_tiles_fn<D, VEC>(tiles, batch);
+        return nullptr;
     } else if constexpr (NSEG > 0) {
         // per-lane segment lookups cost registers: at most two row tiles
         if constexpr (NSEG == gemvdev::kFewSegments) {
@@ -443,7 +460,7 @@ gemv_status_t launch_multi(const gemv_segment_t* segs, int count, const void* x,
     for (int i = count; i < gemvdev::kMaxSegments; ++i) rows.seg[i] = gemvdev::SegEntry<S>{nullptr, total, 0};
     Plan p;
     if (gemvplan::make_plan_vec(dtype_code<D>(), total, K, 1, vec, gemvplan::AUTO, &p,
-                                gemvplan::kMultiMaxRowTiles, 1) != gemvplan::OK)
+                                gemvplan::kMultiMaxRowTiles, 1, 1) != gemvplan::OK)
         return GEMV_ERROR_INVALID_VALUE;
     const void* fn = single_fn<D, NSEG>(p);
     if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;
@@ -471,7 +488,7 @@ gemv_status_t launch_multi3(const gemv_segment_t* segs, int count, const void* x
     }
     Plan p;
     if (gemvplan::make_plan_vec(dtype_code<D>(), total, K, 1, vec, gemvplan::AUTO, &p,
-                                gemvplan::kMultiMaxRowTiles, 1) != gemvplan::OK)
+                                gemvplan::kMultiMaxRowTiles, 1, 1) != gemvplan::OK)
         return GEMV_ERROR_INVALID_VALUE;
     const void* fn = single_fn<D, gemvdev::kFewSegments>(p);
     if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;

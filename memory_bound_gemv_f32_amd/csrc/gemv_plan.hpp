@@ -158,6 +158,7 @@ constexpr int kBlock = 256;
 // 80.18, 77.77, 76.65; fp32 2^22 × 16 46.04, 44.31, 44.32; but fp32
 // 2^18 × 128 20.44, 20.31, 21.29).
 constexpr int64_t kTargetGroups = 1024;
+constexpr int64_t kWaveMaxGroups = 16384;
 constexpr int kRowsMaxTiles = 4;
 constexpr int64_t kManyGroups = 65536;
 
@@ -258,7 +259,8 @@ inline bool stream_fits(int dtype, int64_t M, int64_t K, bool vec, int max_group
 }
 
 inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family, Plan* out,
-                         int max_row_tiles = 8, int max_group_rows = kGroupStreamRows) {
+                         int max_row_tiles = 8, int max_group_rows = kGroupStreamRows,
+                         int max_wave_tiles = kWaveBatch) {
     if (dtype < F32 || dtype > Q8 || M < 0 || K < 0 || nvec < 1 || nvec > kMaxVectors)
         return INVALID;
 
@@ -329,6 +331,18 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         const int64_t per_lane = ceil_div(full, (int64_t)kWave);
         p.batch = fitted_batch(per_lane, kWaveBatch);
         p.row_tiles = 1;
+        if (dtype != Q8 && p.vector_loads) {
+            // very many short rows: a wavefront takes several rows (one row
+            // tile each, all their loads in flight, at most kWaveBatch per
+            // lane) until at most kWaveMaxGroups workgroups remain; launching
+            // a workgroup costs about 0.2 ns (an empty kernel of 16384
+            // workgroups takes 4.5 µs), so 2^20 rows at one per wavefront
+            // were bound by the launch (fp32 2^20 × 256: 200 µs)
+            for (int u = 1; u <= max_wave_tiles && u * p.batch <= kWaveBatch; u *= 2) {
+                p.row_tiles = u;
+                if (ceil_div(M, (int64_t)u * p.waves_per_group) <= kWaveMaxGroups) break;
+            }
+        }
         if (dtype == Q8) {
             // int8 rows: x chunks are 2-4 times the weight chunk, so batches
             // stop at kQ8Batch and two rows share every x chunk when there

@@ -153,6 +153,24 @@ def test_mid_rows_get_a_wavefront_each():
     assert p("bf16", 1024, 4096)["family"] == lg.FAMILY_WAVE_PER_ROW
 
 
+def test_very_tall_short_rows_share_wavefronts():
+    """With more than 16384 workgroups' worth of short rows, a wavefront
+    takes 2, 4 or 8 rows (at most 8 loads per lane in flight); up to 65536
+    such rows keep one row per wavefront."""
+    q = p("f32", 1 << 20, 256)  # 64 loads: one per lane
+    assert (q["family"], q["batch"], q["row_tiles"], q["grid"]) == \
+        (lg.FAMILY_WAVE_PER_ROW, 1, 8, (1 << 20) // 32)
+    q = p("bf16", 1 << 20, 1024)  # 128 loads: two per lane
+    assert (q["batch"], q["row_tiles"], q["grid"]) == (2, 4, (1 << 20) // 16)
+    assert p("bf16", 1 << 20, 1536)["row_tiles"] == 2  # three per lane
+    assert p("bf16", 1 << 18, 4096)["row_tiles"] == 1 or p("bf16", 1 << 18, 4096)["family"] != \
+        lg.FAMILY_WAVE_PER_ROW
+    assert p("f32", 65536, 256)["row_tiles"] == 1
+    assert p("f32", 65540, 256)["row_tiles"] == 2
+    # element loads keep one row per wavefront
+    assert p("f32", 1 << 20, 256, A=ALIGNED + 4)["row_tiles"] == 1
+
+
 def test_wavefront_batches_fit_the_row():
     """A wavefront per row issues its row's loads in as few batches of at
     most 8 loads per lane as possible, all of one size."""

@@ -95,7 +95,8 @@ def test_one_hot(dtype, M, K, extra):
 INT_SHAPES = [(1, 1), (5, 3), (63, 8), (64, 15), (65, 16), (130, 17), (257, 31),
               (33, 32), (17, 33), (9, 127), (300, 128), (31, 129), (7, 255),
               (129, 256), (3, 257), (70, 1000), (40, 1024), (5, 4097), (3, 14337),
-              (513, 4200), (515, 8300)]  # last two: two rows per workgroup share x
+              (513, 4200), (515, 8300),  # two rows per workgroup share x
+              (300, 1536), (100, 12288), (50, 16384)]  # batches of 3, 6 and 8 loads per lane
 
 
 @pytest.mark.parametrize("dtype", gi.DTYPES)
@@ -130,6 +131,25 @@ def test_integer_x_in_registers(dtype, M, K):
         ref, _ = run_oracle(case)
         print(f"{dtype} {M}x{K} lda={lda}: {q['row_tiles']} rows per workgroup, "
               f"{q['batch']} x chunks per lane", flush=True)
+        assert_bit_exact(run_gpu(case, lg.FAMILY_AUTO), ref, f"{dtype} {M}x{K} lda={lda}")
+
+
+# very many short rows: a wavefront takes 2, 4 or 8 rows; the last
+# wavefront's rows run past M
+MANY_ROWS_SHAPES = [("bf16", 70001, 264, 2), ("f32", 140001, 132, 4), ("f16", 300003, 264, 8),
+                    ("bf16", 140000, 1024, 4)]
+
+
+@pytest.mark.parametrize("dtype,M,K,tiles", MANY_ROWS_SHAPES)
+def test_integer_many_short_rows(dtype, M, K, tiles):
+    per = 16 // gi.ELEMENT_BYTES[dtype]
+    for lda in (K, K + per):
+        q = lg.plan(dtype, M, K, lda, 1, 1 << 20, 1 << 20)
+        assert (q["family"], q["row_tiles"]) == (lg.FAMILY_WAVE_PER_ROW, tiles)
+        case = gi.make_integer(dtype, M, K, seed=M + K, lda=lda, bias=lda == K)
+        ref, _ = run_oracle(case)
+        print(f"{dtype} {M}x{K} lda={lda}: {q['row_tiles']} rows per wavefront, "
+              f"{q['batch']} loads per lane", flush=True)
         assert_bit_exact(run_gpu(case, lg.FAMILY_AUTO), ref, f"{dtype} {M}x{K} lda={lda}")
 
 

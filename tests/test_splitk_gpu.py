@@ -114,6 +114,25 @@ def test_workspace_reused_by_a_smaller_call():
                          f"M={case.M}")
 
 
+def test_back_to_back_calls_agree():
+    """Many calls queued on one stream with one workspace and no wait between
+    them give the same bits: the reduce adds each row's partials in an order
+    fixed by the slice count alone."""
+    case = gi.make_random("f32", 8, 1 << 21, seed=9, dist="normal", scale=0.02, bias=True)
+    A, X, bias = upload(case)
+    n = lg.splitk_workspace_size("f32", case.M, case.K)
+    ws = torch.empty(n // 4, dtype=torch.float32, device="cuda")
+    outs = [torch.empty(case.M, dtype=torch.float32, device="cuda") for _ in range(24)]
+    for o in outs:
+        lg.gemv_splitk(A, X[0], bias, out=o, workspace=ws)
+    torch.cuda.synchronize()
+    first = outs[0].cpu().numpy()
+    for i, o in enumerate(outs[1:], 1):
+        assert np.array_equal(o.cpu().numpy().view(np.uint32), first.view(np.uint32)), f"call {i}"
+    ref, absdot = run_oracle(case)
+    assert_within_bound(first.astype(np.float64)[None, :], ref, absdot, "f32 8x2^21")
+
+
 @pytest.mark.parametrize("name", gi.SPLITK_WORKLOADS)
 def test_full_size_split_workload(name):
     case = gi.make_workload(name)

@@ -170,9 +170,9 @@ typedef enum { GEMV_DTYPE_F32 = 0, GEMV_DTYPE_F16 = 1, GEMV_DTYPE_BF16 = 2 } gem
  * section "Kernel 1: k32", points out that with one row per warp a small M
  * (its example: M = 8) starts only a handful of blocks and leaves the rest
  * of the GPU idle.  Here each row is cut into `splits` slices of K; one
- * workgroup per (row, slice) writes a partial sum into a caller-provided
- * workspace, and a second kernel adds each row's partials in a fixed order
- * and the bias (two kernels on `stream`, no atomics).  The result is
+ * workgroup per (two rows, slice) writes their partial sums into a
+ * caller-provided workspace, and a second kernel adds each row's partials
+ * in a fixed order and the bias (two kernels on `stream`, no atomics).  The result is
  * y = A·x (+ bias) with the same tolerance as gemv_*, and identical bits on
  * every call with the same `splits`.
  *
@@ -254,7 +254,7 @@ typedef enum {
     GEMV_FAMILY_BATCHED = 3,       /* several rows × nvec vectors per wave */
     GEMV_FAMILY_BATCHED_MFMA = 4,  /* 16 rows × 16 vectors on the matrix cores */
     GEMV_FAMILY_GATED_SILU = 5,    /* a row of A_gate and of A_up per workgroup */
-    GEMV_FAMILY_SPLIT_K = 6        /* a workgroup per row and K-slice, then a reduce */
+    GEMV_FAMILY_SPLIT_K = 6        /* a workgroup per two rows and K-slice, then a reduce */
 } gemv_family_t;
 
 typedef struct {
@@ -274,7 +274,7 @@ typedef struct {
     int slice_elems;     /* elements per K-slice (the last may be shorter), else K */
     int x_in_registers;  /* workgroup per row: 1 if each lane keeps its x chunks in
                             registers while the workgroup walks its rows */
-    int64_t grid;        /* workgroups (split-K: rows × slices) */
+    int64_t grid;        /* workgroups (split-K: ceil(rows / rows_per_group) × slices) */
 } gemv_plan_t;
 
 /* Compute, on the host only, the mapping a call with these arguments would

@@ -357,17 +357,27 @@ const void* q8_fn(const Plan& p) {
 
 // ---- split-K ------------------------------------------------------------------
 
-template <class D, bool VEC>
-const void* splitk_fn(int batch) {
+template <class D, int U, bool VEC>
+const void* splitk_fn_u(int batch) {
     switch (batch) {
-    case 1: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, 1, VEC>;
-    case 2: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, 2, VEC>;
-    case 3: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, 3, VEC>;
-    case 4: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, 4, VEC>;
-    case 5: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, 5, VEC>;
-    case 6: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, 6, VEC>;
-    case 7: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, 7, VEC>;
-    case 8: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, 8, VEC>;
+    case 1: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, U, 1, VEC>;
+    case 2: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, U, 2, VEC>;
+    case 3: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, U, 3, VEC>;
+    case 4: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, U, 4, VEC>;
+    case 5: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, U, 5, VEC>;
+    case 6: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, U, 6, VEC>;
+    case 7: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, U, 7, VEC>;
+    case 8: return (const void*)&gemvdev::gemv_splitk_partial_kernel<D, U, 8, VEC>;
+    default: return nullptr;
+    }
+}
+
+template <class D, bool VEC>
+const void* splitk_fn(int rows, int batch) {
+    static_assert(gemvplan::kSplitRowsPerGroup == 2, "split-K is instantiated for 1 and 2 rows");
+    switch (rows) {
+    case 1: return splitk_fn_u<D, 1, VEC>(batch);
+    case 2: return splitk_fn_u<D, 2, VEC>(batch);
     default: return nullptr;
     }
 }
@@ -581,7 +591,8 @@ gemv_status_t run_splitk(const void* A, int lda, const void* x, const float* bia
     if (workspace == nullptr || (uintptr_t)workspace % sizeof(float) != 0 ||
         workspace_bytes < (size_t)need)
         return GEMV_ERROR_INVALID_VALUE;
-    const void* fn = p.vector_loads ? splitk_fn<D, true>(p.batch) : splitk_fn<D, false>(p.batch);
+    const void* fn = p.vector_loads ? splitk_fn<D, true>(p.rows_per_group, p.batch)
+                                    : splitk_fn<D, false>(p.rows_per_group, p.batch);
     if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;
 
     float* ws = static_cast<float*>(workspace);

@@ -553,15 +553,16 @@ gemv_group_q8_kernel(const int8_t* Q, int64_t ldq, const typename X::storage* __
                                          blockIdx.x);
 }
 
-// Split-K, pass 1: workgroup (m, s) forms the dot product of row m's slice s
-// (elements s·slice .. s·slice + slice - 1, the last slice shorter) with the
-// same slice of x, in the workgroup-per-row body, and writes it to
+// Split-K, pass 1: workgroup (t, s) forms the dot products of rows t·U ..
+// t·U + U - 1 (U = 1 or 2), slice s (elements s·slice .. s·slice + slice - 1,
+// the last slice shorter), with the same slice of x, in the workgroup-per-row
+// body (each x chunk serves the U rows), and writes row m's to
 // ws[m·splits + s].  The A and x pointers of a slice are offset by a whole
 // number of 16-byte loads, so the vector path's alignment holds in every
-// slice.  Workgroup id = m·splits + s: consecutive ids, which the dispatcher
-// deals round-robin to the 8 XCDs, walk the slices of one row, so with
-// splits a multiple of 8 every row's slice s runs on the same XCD and its x
-// slice is fetched into that XCD's L2 once, not once per row.
+// slice.  Workgroup id = t·splits + s: consecutive ids, which the dispatcher
+// deals round-robin to the 8 XCDs, walk the slices of one row tile, so with
+// splits a multiple of 8 every tile's slice s runs on the same XCD and its x
+// slice is fetched into that XCD's L2 once, not once per tile.
 template <class S>
 struct SliceOfRows {
     static constexpr bool kScaled = false;
@@ -576,19 +577,19 @@ struct SliceOfRows {
     __device__ __forceinline__ void store(int64_t m, float v) const { ws[m * splits] = v; }
 };
 
-template <class D, int BATCH, bool VEC>
+template <class D, int U, int BATCH, bool VEC>
 __global__ void __launch_bounds__(kGroupWavesDev * 64) __attribute__((amdgpu_waves_per_eu(4)))
 gemv_splitk_partial_kernel(const typename D::storage* A, int64_t lda, float* ws, int64_t M,
                            const typename D::storage* __restrict__ x, int K, int slice,
                            int splits) {
     const uint32_t id = blockIdx.x;
     const int s = (int)(id % (uint32_t)splits);
-    const int64_t m = id / (uint32_t)splits;
+    const int64_t tile = id / (uint32_t)splits;  // rows tile·U .. tile·U + U - 1
     const int64_t k0 = (int64_t)s * slice;
     const int64_t rest = (int64_t)K - k0;
     const int ks = rest < slice ? (int)rest : slice;
-    group_body<D, kGroupWavesDev, 1, BATCH, VEC>(
-        SliceOfRows<typename D::storage>{A + k0, lda, ws + s, splits, M}, x + k0, ks, m);
+    group_body<D, kGroupWavesDev, U, BATCH, VEC>(
+        SliceOfRows<typename D::storage>{A + k0, lda, ws + s, splits, M}, x + k0, ks, tile);
 }
 
 // Split-K, pass 2: one wavefront per row adds the row's `splits` partials in

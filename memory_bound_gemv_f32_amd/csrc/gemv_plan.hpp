@@ -126,8 +126,14 @@ constexpr int mfma_lds_bytes(int nvec) {
 // much more than a workgroup keeps in flight (page "SGEMV CUDA代码学习",
 // section "Kernel 1: k32": with M = 8 only two blocks run and the rest of the
 // machine idles), every row is cut into `splits` slices; a workgroup per
-// (row, slice) writes a partial sum, and a second kernel adds each row's
-// partials in slice order (a fixed order, so results are reproducible).
+// (pair of rows, slice) writes the two rows' partial sums, and a second
+// kernel adds each row's partials in slice order (a fixed order, so results
+// are reproducible).  Two rows per workgroup let each x chunk serve both
+// (a workgroup otherwise reads as many x bytes as A bytes); four were
+// slower.  MI355X, µs with 1 -> 2 rows per workgroup, reduce included: fp32
+// 8×2^21 15.49 -> 14.59, bf16 64×2^18 9.21 -> 8.77, fp16 32×2^19 9.34 ->
+// 8.62, fp32 100×2^18 23.87 -> 20.92, bf16 7×2^20 6.64 -> 6.26; with 4
+// rows 15.06, 9.55, 9.32, 21.70, 7.79 (and no better with 2-4x the slices).
 // Chosen automatically for fewer than kSplitMaxRows rows of at least
 // kSplitMinRowLoads 16-byte loads (4 batches of the workgroup-per-row
 // family); below that the second launch (~2 µs) costs more than it saves.
@@ -135,12 +141,15 @@ constexpr int mfma_lds_bytes(int nvec) {
 // loads, and their count a multiple of 8 when it is 8 or more (see the
 // pass-1 kernel: then every XCD serves whole slices of x).  Measured on
 // MI355X, the reduce launch included: fp32 8×2^21 265 -> 15.6 µs, fp32
-// 1×2^24 2147 -> 24.4 µs, bf16 64×2^18 20.7 -> 9.3 µs; bf16 256×2^16 and
-// 512×2^15 are faster unsplit.
-constexpr int64_t kSplitMaxRows = 256;
+// 1×2^24 2147 -> 24.4 µs, bf16 64×2^18 20.7 -> 9.3 µs, bf16 128×2^17
+// 12.26 -> 8.47 µs; but unsplit is faster from about 200 rows up (bf16
+// 200×2^16 7.81 against 8.05 split, 255×2^16 8.12 against 8.46, fp32
+// 255×2^15 8.03 against 8.43; 256×2^16 and 512×2^15 likewise).
+constexpr int64_t kSplitMaxRows = 192;
 constexpr int64_t kSplitMinRowLoads = 4 * kGroupWaves * kWave * kGroupBatch;
 constexpr int64_t kSplitMinSliceLoads = 512;
 constexpr int kSplitMaxSplits = 1024;
+constexpr int kSplitRowsPerGroup = 2;
 // Int8 weights: loads per lane per batch (each weight chunk brings a 32- or
 // 64-byte x chunk), and the workgroups below which a wavefront keeps one
 // row instead of two.
@@ -515,14 +524,15 @@ inline int make_split_plan(int dtype, int M, int K, bool vec, int requested, Pla
     p.rows_per_wave = 0;
     p.waves_per_group = kGroupWaves;
     const int64_t per_lane = ceil_div(full, (int64_t)p.lanes_per_row);
+    p.rows_per_group = M >= 2 ? kSplitRowsPerGroup : 1;
     p.batch = fitted_batch(per_lane, kGroupBatch);
     p.row_tiles = 1;
-    p.rows_per_group = 1;
     p.block = p.waves_per_group * kWave;
-    p.lds_bytes = (int)(kGroupWaves * sizeof(float));
+    p.lds_bytes = (int)(kGroupWaves * p.rows_per_group * sizeof(float));
     p.splits = splits;
     p.slice_elems = slice;
-    p.grid = (int64_t)M * splits;  // one workgroup per (row, slice)
+    // one workgroup per (row tile, slice)
+    p.grid = ceil_div((int64_t)M, (int64_t)p.rows_per_group) * splits;
     if (p.grid * p.block > 0xffffffffLL) return INVALID;  // HIP's 32-bit grid size
     p.passes = (int)per_lane;
     *out = p;

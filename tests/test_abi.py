@@ -344,12 +344,13 @@ def test_splitk_workspace_size():
 
 
 def test_splitk_for_few_long_rows():
-    """The small-M case: fewer than 256 rows of at least 8192 16-byte loads
+    """The small-M case: fewer than 192 rows of at least 8192 16-byte loads
     are cut into slices so that rows × slices approaches 1024 workgroups, each
     slice at least 512 loads and a whole number of 64-lane loads, and the
-    slice count a multiple of the 8 XCDs once it reaches 8."""
+    slice count a multiple of the 8 XCDs once it reaches 8; a workgroup takes
+    two rows of a slice (one when M = 1), so that each x chunk serves both."""
     for dtype, M, K in (("f32", 16, 1 << 20), ("f32", 8, 1 << 21), ("bf16", 64, 1 << 18),
-                        ("f16", 1, 1 << 24), ("bf16", 100, 100000), ("f32", 255, 1 << 15),
+                        ("f16", 1, 1 << 24), ("bf16", 100, 100000), ("f32", 191, 1 << 15),
                         ("bf16", 32, 65536)):
         p = lg.plan_splitk(dtype, M, K, A_addr=ALIGNED, x_addr=ALIGNED)
         s = 4 if dtype == "f32" else 2
@@ -359,7 +360,9 @@ def test_splitk_for_few_long_rows():
         assert p["slice_elems"] * s >= 512 * 16 and (p["slice_elems"] * s // 16) % 64 == 0
         assert (p["splits"] - 1) * p["slice_elems"] < K <= p["splits"] * p["slice_elems"]
         assert p["splits"] < 8 or p["splits"] % 8 == 0
-        assert p["grid"] == M * p["splits"] and p["block"] == 256
+        U = 2 if M >= 2 else 1
+        assert p["rows_per_group"] == U
+        assert p["grid"] == -(-M // U) * p["splits"] and p["block"] == 256
         per_lane = -(-p["slice_elems"] * s // 16 // 256)
         assert p["batch"] == -(-per_lane // -(-per_lane // 8))  # equal batches of <= 8
 
@@ -368,6 +371,7 @@ def test_splitk_keeps_the_plain_plan_when_it_fills_the_gpu():
     for dtype, M, K in (("bf16", 4096, 4096), ("bf16", 1024, 4096), ("bf16", 1000, 40000),
                         ("f32", 16, 1000), ("f32", 1 << 20, 16), ("bf16", 5, 0),
                         ("bf16", 256, 1 << 16), ("bf16", 512, 1 << 15), ("bf16", 64, 14336),
+                        ("bf16", 192, 1 << 16), ("f32", 255, 1 << 15),
                         ("f32", 100, 32764)):           # 8191 loads per row
         p = lg.plan_splitk(dtype, M, K, A_addr=ALIGNED, x_addr=ALIGNED)
         assert p["splits"] == 1 and p["slice_elems"] == K
@@ -411,7 +415,7 @@ def test_splitk_geometry_properties():
         assert (S - 1) * sl < K <= S * sl
         assert (sl * (4 if dtype == "f32" else 2)) % 16 == 0
         if splits == 0:
-            assert M < 256 and (S < 8 or S % 8 == 0) and M * S <= 1024
+            assert M < 192 and (S < 8 or S % 8 == 0) and M * S <= 1024
         else:
             assert S <= splits
         assert lg.splitk_workspace_size(dtype, M, K, splits) == 4 * M * S

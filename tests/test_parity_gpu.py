@@ -354,3 +354,37 @@ def test_seeded_random_shapes_integer():
         y = run_gpu(case, fam, misalign=misalign, batched=nvec > 1)
         assert_bit_exact(y, ref, f"trial {trial}: {dtype} {M}x{K} lda={lda} nvec={nvec} "
                                  f"misalign={misalign} family {fam}")
+
+
+def test_seeded_random_shapes_automatic_plan():
+    """A hundred shapes drawn from a fixed seed around the automatic planner's
+    boundaries (row counts near 256, 512, 6144 and the row-tile thresholds;
+    rows of 16 bytes to 32 KiB, x just below and above 8, 16 and 24 KiB; odd
+    row pitches and offsets), each run through the planner's own choice of
+    kernel: every result bit-exact."""
+    import memory_bound_gemv_f32_amd as lg
+    rng = np.random.default_rng(4242)
+    row_counts = [1, 3, 255, 256, 257, 510, 511, 512, 1023, 6143, 6144, 6145, 16383,
+                  65537, 131071, 262147]
+    row_bytes = [16, 48, 256, 512, 520, 1024, 2048, 4096, 8192, 8208, 12288, 16384, 16400,
+                 24576, 24592, 28672, 32768]
+    done = 0
+    while done < 100:
+        dtype = str(rng.choice(gi.DTYPES))
+        es = gi.ELEMENT_BYTES[dtype]
+        M = int(rng.choice(row_counts))
+        K = int(rng.choice(row_bytes)) // es + int(rng.choice([0, 0, 0, 0, 0, 1, -1]))
+        if K < 1 or M * K > 36_000_000:
+            continue
+        per = 16 // es
+        lda = K + int(rng.choice([0, 0, 0, 1, per]))
+        misalign = int(rng.choice([0, 0, 0, 0, 1]))
+        case = gi.make_integer(dtype, M, K, seed=1000 + done, lda=lda, bias=bool(rng.integers(2)))
+        A_addr = 1 << 20 if misalign == 0 else (1 << 20) + es
+        q = lg.plan(dtype, M, K, lda, 1, A_addr, A_addr)
+        what = (f"trial {done}: {dtype} {M}x{K} lda={lda} misalign={misalign}: family "
+                f"{lg.FAMILY_NAMES[q['family']]}, batch {q['batch']}, tiles {q['row_tiles']}")
+        print(what, flush=True)
+        ref, _ = run_oracle(case)
+        assert_bit_exact(run_gpu(case, lg.FAMILY_AUTO, misalign=misalign), ref, what)
+        done += 1

@@ -143,8 +143,20 @@ const void* rows_fn(int lanes, int tiles, int batch) {
 }
 
 template <class D, bool VEC, int NSEG, int B>
-const void* group_fn_b(int rows) {
+const void* group_fn_b(int rows, int waves) {
     constexpr int W = gemvplan::kGroupWaves;
+    // few long rows (plain GEMV only): 16 wavefronts for one row, 8 for two
+    if (waves != W) {
+        if constexpr (NSEG == 0) {
+            constexpr int W1 = gemvplan::kGroupWideWaves, W2 = gemvplan::kGroupWidePairWaves;
+            if (waves == W1 && rows == 1)
+                return (const void*)&gemvdev::gemv_group_kernel<D, W1, 1, B, VEC>;
+            if constexpr (2 * B <= gemvplan::kGroupTileLoads)
+                if (waves == W2 && rows == 2)
+                    return (const void*)&gemvdev::gemv_group_kernel<D, W2, 2, B, VEC>;
+        }
+        return nullptr;
+    }
     if constexpr (NSEG == gemvdev::kFewSegments) {
         return rows == 1 ? (const void*)&gemvdev::gemv_group_multi3_kernel<D, W, B, VEC> : nullptr;
     } else if constexpr (NSEG > 0) {
@@ -163,17 +175,17 @@ const void* group_fn_b(int rows) {
 }
 
 template <class D, bool VEC, int NSEG>
-const void* group_fn(int batch, int rows) {
+const void* group_fn(int batch, int rows, int waves) {
     static_assert(gemvplan::kGroupBatch == 8, "workgroup-per-row kernels are built for batches of 1 to 8");
     switch (batch) {
-    case 1: return group_fn_b<D, VEC, NSEG, 1>(rows);
-    case 2: return group_fn_b<D, VEC, NSEG, 2>(rows);
-    case 3: return group_fn_b<D, VEC, NSEG, 3>(rows);
-    case 4: return group_fn_b<D, VEC, NSEG, 4>(rows);
-    case 5: return group_fn_b<D, VEC, NSEG, 5>(rows);
-    case 6: return group_fn_b<D, VEC, NSEG, 6>(rows);
-    case 7: return group_fn_b<D, VEC, NSEG, 7>(rows);
-    case 8: return group_fn_b<D, VEC, NSEG, 8>(rows);
+    case 1: return group_fn_b<D, VEC, NSEG, 1>(rows, waves);
+    case 2: return group_fn_b<D, VEC, NSEG, 2>(rows, waves);
+    case 3: return group_fn_b<D, VEC, NSEG, 3>(rows, waves);
+    case 4: return group_fn_b<D, VEC, NSEG, 4>(rows, waves);
+    case 5: return group_fn_b<D, VEC, NSEG, 5>(rows, waves);
+    case 6: return group_fn_b<D, VEC, NSEG, 6>(rows, waves);
+    case 7: return group_fn_b<D, VEC, NSEG, 7>(rows, waves);
+    case 8: return group_fn_b<D, VEC, NSEG, 8>(rows, waves);
     default: return nullptr;
     }
 }
@@ -213,7 +225,7 @@ const void* single_fn(const Plan& p) {
             if constexpr (NSEG == 0 && VEC) return group_stream_fn<D>(p.batch, p.row_tiles);
             return nullptr;
         }
-        return group_fn<D, VEC, NSEG>(p.batch, p.row_tiles);
+        return group_fn<D, VEC, NSEG>(p.batch, p.row_tiles, p.waves_per_group);
     default: return nullptr;
     }
 }
@@ -470,7 +482,7 @@ gemv_status_t launch_multi(const gemv_segment_t* segs, int count, const void* x,
     for (int i = count; i < gemvdev::kMaxSegments; ++i) rows.seg[i] = gemvdev::SegEntry<S>{nullptr, total, 0};
     Plan p;
     if (gemvplan::make_plan_vec(dtype_code<D>(), total, K, 1, vec, gemvplan::AUTO, &p,
-                                gemvplan::kMultiMaxRowTiles, 1, 1) != gemvplan::OK)
+                                gemvplan::kMultiMaxRowTiles, 1, 1, gemvplan::kGroupWaves) != gemvplan::OK)
         return GEMV_ERROR_INVALID_VALUE;
     const void* fn = single_fn<D, NSEG>(p);
     if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;
@@ -498,7 +510,7 @@ gemv_status_t launch_multi3(const gemv_segment_t* segs, int count, const void* x
     }
     Plan p;
     if (gemvplan::make_plan_vec(dtype_code<D>(), total, K, 1, vec, gemvplan::AUTO, &p,
-                                gemvplan::kMultiMaxRowTiles, 1, 1) != gemvplan::OK)
+                                gemvplan::kMultiMaxRowTiles, 1, 1, gemvplan::kGroupWaves) != gemvplan::OK)
         return GEMV_ERROR_INVALID_VALUE;
     const void* fn = single_fn<D, gemvdev::kFewSegments>(p);
     if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;

@@ -62,6 +62,17 @@ constexpr int kRowsPerWaveMaxLanes = 32;
 // 6144 8.86 / 8.80, 7168 10.10 / 9.93, 8192 10.93 / 10.89; the fused q/k/v
 // call over 6144 rows 9.08 / 8.87.)
 constexpr int kGroupWaves = 4;
+// Few long rows: below kGroupWideMaxRows rows, workgroups of 4 wavefronts
+// keep too few bytes in flight when each lane needs more than one batch of
+// loads; then a workgroup of one row has kGroupWideWaves wavefronts and one
+// of two rows kGroupWidePairWaves.  MI355X, µs with 4 -> 8 -> 16 wavefronts:
+// one row, bf16 192 × 65536 7.77, 7.33, 6.94; bf16 256 × 65536 8.14, 7.64,
+// 7.38; fp32 256 × 32768 8.06, 7.54, 7.37; bf16 384 × 32768 7.20, 6.88,
+// 6.87; two rows, bf16 512 × 32768 7.28, 6.92, 7.23; fp16 1000 × 20000
+// 8.29, 8.01, 8.26; bf16 900 × 30000 11.13, 10.78, 11.00.
+constexpr int kGroupWideWaves = 16;
+constexpr int kGroupWidePairWaves = 8;
+constexpr int64_t kGroupWideMaxRows = 1024;
 constexpr int64_t kGroupMaxRows = 256;
 constexpr int64_t kGroupLongRowLoads = 1024;
 constexpr int64_t kGroupManyRows = 6144;
@@ -269,7 +280,7 @@ inline bool stream_fits(int dtype, int64_t M, int64_t K, bool vec, int max_group
 
 inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family, Plan* out,
                          int max_row_tiles = 8, int max_group_rows = kGroupStreamRows,
-                         int max_wave_tiles = kWaveBatch) {
+                         int max_wave_tiles = kWaveBatch, int max_group_waves = kGroupWideWaves) {
     if (dtype < F32 || dtype > Q8 || M < 0 || K < 0 || nvec < 1 || nvec > kMaxVectors)
         return INVALID;
 
@@ -395,6 +406,13 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
                 u *= 2;
         }
         p.row_tiles = u;
+        const int wide = u == 1 ? kGroupWideWaves : kGroupWidePairWaves;
+        if (!p.x_in_registers && dtype != Q8 && wide <= max_group_waves && M < kGroupWideMaxRows &&
+            per_lane > p.batch) {
+            p.waves_per_group = wide;
+            p.lanes_per_row = kWave * wide;
+            p.batch = fitted_batch(ceil_div(full, (int64_t)p.lanes_per_row), kGroupBatch);
+        }
         p.lds_bytes = (int)(p.waves_per_group * u * sizeof(float));
         break;
     }

@@ -530,3 +530,30 @@ def test_read_probe_validation():
     for buf, n, snk in ((None, 1024, sink), (GOOD, 1024, None), (GOOD, 1000, sink),
                         (GOOD + 8, 1024, sink), (GOOD, 1024, sink + 2)):
         assert lg.gemv_read_probe(buf, n, snk, None) == lg.GEMV_ERROR_INVALID_VALUE
+
+
+def test_few_long_rows_take_wider_workgroups():
+    """Below 1024 rows, rows that need more than one batch of loads per lane
+    of 4 wavefronts get wider workgroups: 16 wavefronts for one row, 8 for a
+    pair of rows sharing x; shorter rows, taller matrices and x held in
+    registers keep 4."""
+    def plan(dtype, M, K):
+        return lg.plan(dtype, M, K, A_addr=ALIGNED, X_addr=ALIGNED)
+    for dtype, M, K, waves, rows in (("bf16", 192, 65536, 16, 1), ("f32", 256, 32768, 16, 1),
+                                     ("bf16", 384, 32768, 16, 1), ("bf16", 512, 32768, 8, 2),
+                                     ("f16", 1000, 20000, 8, 2), ("bf16", 1023, 20000, 8, 2),
+                                     ("bf16", 1024, 20000, 4, 2), ("bf16", 768, 16384, 4, 2),
+                                     ("bf16", 256, 4096, 4, 1), ("bf16", 4096, 14336, 4, 2),
+                                     ("bf16", 600, 8192, 4, 2)):   # x in registers
+        p = plan(dtype, M, K)
+        assert p["family"] == lg.FAMILY_GROUP_PER_ROW, (dtype, M, K)
+        assert (p["waves_per_group"], p["row_tiles"]) == (waves, rows), (dtype, M, K, p)
+        assert p["block"] == 64 * waves and p["lanes_per_row"] == 64 * waves
+        assert p["grid"] == -(-M // rows) and p["lds_bytes"] == 4 * waves * rows
+        s = 4 if dtype == "f32" else 2
+        per_lane = -(-(K * s // 16) // (64 * waves))
+        assert p["batch"] == -(-per_lane // -(-per_lane // 8))  # equal batches of <= 8
+    assert plan("bf16", 600, 8192)["x_in_registers"] == 1
+    # int8 weights keep 4 wavefronts
+    q = lg.plan_q8("bf16", 256, 65536, Q_addr=ALIGNED, x_addr=ALIGNED)
+    assert q["family"] == lg.FAMILY_GROUP_PER_ROW and q["waves_per_group"] == 4

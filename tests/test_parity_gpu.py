@@ -153,6 +153,28 @@ def test_integer_many_short_rows(dtype, M, K, tiles):
         assert_bit_exact(run_gpu(case, lg.FAMILY_AUTO), ref, f"{dtype} {M}x{K} lda={lda}")
 
 
+# few long rows: workgroups of 16 wavefronts (one row) or 8 (two rows, the
+# last pair of an odd M half past the end); rows with and without a ragged
+# tail shorter than a 16-byte load
+WIDE_SHAPES = [("bf16", 192, 65536, 16), ("f32", 255, 20001, 16), ("f16", 300, 33000, 16),
+               ("f16", 511, 24600, 8), ("bf16", 999, 17001, 8), ("f32", 600, 12000, 8)]
+
+
+@pytest.mark.parametrize("dtype,M,K,waves", WIDE_SHAPES)
+def test_integer_wide_workgroups(dtype, M, K, waves):
+    per = 16 // gi.ELEMENT_BYTES[dtype]
+    for lda, misalign in ((K, 0), (K + per, 0), (K + 1, 1)):
+        A_addr = 1 << 20 if misalign == 0 else (1 << 20) + gi.ELEMENT_BYTES[dtype]
+        q = lg.plan(dtype, M, K, lda, 1, A_addr, A_addr)
+        assert q["family"] == lg.FAMILY_GROUP_PER_ROW and q["waves_per_group"] == waves, q
+        case = gi.make_integer(dtype, M, K, seed=M * 7 + K, lda=lda, bias=lda == K)
+        ref, _ = run_oracle(case)
+        what = (f"{dtype} {M}x{K} lda={lda} misalign={misalign}: {waves} wavefronts, "
+                f"{q['row_tiles']} rows, batch {q['batch']}")
+        print(what, flush=True)
+        assert_bit_exact(run_gpu(case, lg.FAMILY_AUTO, misalign=misalign), ref, what)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("nvec", list(range(1, 17)))
 def test_integer_batched(dtype, nvec):

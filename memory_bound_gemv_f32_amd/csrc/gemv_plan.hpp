@@ -253,10 +253,18 @@ inline bool vector_ok_q8(int ldq, uintptr_t Q, uintptr_t x) {
     return Q % kLoadBytes == 0 && x % kLoadBytes == 0 && ldq % kLoadBytes == 0;
 }
 
-// 16-byte loads need 16-byte aligned A, x (and every X column) and row pitch.
+// 16-byte loads need 16-byte aligned A and x.  With one vector the row pitch
+// may leave rows unaligned: the chunk loads take element-aligned addresses,
+// and one unaligned 16-byte load beats eight element loads (MI355X, bf16
+// 4096 × 4100 9.64 -> 6.98 µs, 384 × 43690 12.88 -> 8.97, 6144 × 2730
+// 9.14 -> 7.01; fp32 4096 × 4097 13.97 -> 12.06; only where few rows leave
+// CUs idle is it no faster: bf16 192 × 87381 12.25 -> 12.63).  Several
+// vectors also need the pitch and every X column aligned (the matrix-core
+// kernel reads whole aligned operand rows).
 inline bool vector_ok(int dtype, int K, int lda, int nvec, uintptr_t A, uintptr_t X) {
     const int64_t s = element_bytes(dtype);
     if (A % kLoadBytes != 0 || X % kLoadBytes != 0) return false;
+    if (nvec == 1) return true;
     if (((int64_t)lda * s) % kLoadBytes != 0) return false;
     if (nvec > 1 && ((int64_t)K * s) % kLoadBytes != 0) return false;
     return true;

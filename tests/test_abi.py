@@ -223,11 +223,22 @@ def test_worked_example_mapping():
     assert q["vector_loads"] == 1 and q["passes"] == 1
 
 
-@pytest.mark.parametrize("kw", [dict(A=ALIGNED + 4), dict(X=ALIGNED + 8),
-                                dict(lda=4097)])
+@pytest.mark.parametrize("kw", [dict(A=ALIGNED + 4), dict(X=ALIGNED + 8)])
 def test_misaligned_falls_back_to_element_loads(kw):
     q = p("f32", 4096, 4096, **kw)
     assert q["vector_loads"] == 0 and q["chunk_elems"] == 1
+
+
+def test_unaligned_rows_keep_16_byte_loads():
+    """With aligned A and x, a row pitch or K that is not a whole number of
+    16-byte loads still takes 16-byte loads for one vector (rows start at
+    element-aligned addresses; the tail shorter than a load is read element
+    by element); several vectors need the pitch aligned."""
+    for dtype, M, K, lda in (("f32", 4096, 4096, 4097), ("bf16", 384, 43690, 43690),
+                             ("f16", 4096, 4100, 4100), ("bf16", 6144, 2730, 2731)):
+        q = p(dtype, M, K, lda=lda)
+        assert q["vector_loads"] == 1 and q["chunk_elems"] == 16 // (4 if dtype == "f32" else 2)
+    assert p("f16", 4096, 4100, nvec=4)["vector_loads"] == 0
 
 
 def test_batched_plans():
@@ -503,7 +514,7 @@ def test_long_x_rows_share_a_workgroup():
     # 7 chunks per lane (bf16 4096 x 14336: two rows per workgroup measured
     # faster), x past 24 KiB, or K not whole chunks: two rows share each x chunk
     for dtype, M, K, batch in (("bf16", 4096, 14336, 7), ("bf16", 4096, 14344, 8),
-                               ("bf16", 4096, 14340, 8), ("f32", 4096, 8192, 8),
+                               ("bf16", 4096, 14340, 7), ("f32", 4096, 8192, 8),
                                ("f32", 2051, 7168, 7)):
         q = p(dtype, M, K)
         assert (q["row_tiles"], q["batch"], q["x_in_registers"]) == (2, batch, 0), (dtype, K)

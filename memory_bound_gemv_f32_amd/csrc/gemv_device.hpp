@@ -17,11 +17,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // 16 bytes as four 32-bit words: a native vector type (not HIP's uint4
 // struct), so that selects between quads stay in registers
 typedef unsigned int quad __attribute__((ext_vector_type(4)));
-// The same 16 bytes read from an address that need only be element-aligned:
-// one global_load_dwordx4 all the same (global memory is accessed in the
-// GPU's unaligned mode); a load that crosses a cache line costs the line
-// it crosses into.
-typedef unsigned int quad_any __attribute__((ext_vector_type(4), aligned(2)));
+// The same 16 bytes read from any address (rows whose pitch is not a whole
+// number of 16-byte loads): one global_load_dwordx4 all the same, global
+// memory being accessed in the GPU's unaligned mode; a load that crosses a
+// cache line costs the line it crosses into.
+typedef unsigned int quad_any __attribute__((ext_vector_type(4), aligned(1)));
 
 // Element types.  `storage` is what sits in memory; products are formed and
 // summed in fp32 (page "GEMM、GEMV、dtype 与算术强度", section "dtype 改变什么":
@@ -232,7 +232,7 @@ struct Chunk<TQ8<X>, true> {
         return *reinterpret_cast<const xtype*>(p + c * elems);
     }
     __device__ __forceinline__ static type stream(const int8_t* p, int64_t c) {
-        return __builtin_nontemporal_load(reinterpret_cast<const quad*>(p + c * elems));
+        return __builtin_nontemporal_load(reinterpret_cast<const quad_any*>(p + c * elems));
     }
     __device__ __forceinline__ static type zero() { return quad{0u, 0u, 0u, 0u}; }
     __device__ __forceinline__ static type keep_a(bool ok, type v) { return ok ? v : zero(); }

@@ -248,9 +248,11 @@ inline int validate_q8(int xdtype, int M, int K, int ldq, uintptr_t Q, uintptr_t
     return OK;
 }
 
-// 16-byte loads of int8 rows: Q, its row pitch and x 16-byte aligned.
+// 16-byte loads of int8 rows: Q and x 16-byte aligned; the row pitch may
+// leave rows unaligned, as for one vector of the other types.
 inline bool vector_ok_q8(int ldq, uintptr_t Q, uintptr_t x) {
-    return Q % kLoadBytes == 0 && x % kLoadBytes == 0 && ldq % kLoadBytes == 0;
+    (void)ldq;
+    return Q % kLoadBytes == 0 && x % kLoadBytes == 0;
 }
 
 // 16-byte loads need 16-byte aligned A and x.  With one vector the row pitch

@@ -225,8 +225,8 @@ gemv_status_t gemv_splitk_bf16(const uint16_t *A, int lda, const uint16_t *x,
  *       bfloat16 bit patterns).
  * Products q·x are exact in fp32 and summed in fp32 in the library's own
  * order; |y - exact| <= 1e-5·|scale[m]|·Σ_k|Q[m,k]·x[k]| + 1e-6.
- * Errors as for gemv_*, plus a NULL scale when M > 0.  16-byte aligned Q,
- * x and ldq select the widest loads; any other alignment works.
+ * Errors as for gemv_*, plus a NULL scale when M > 0.  16-byte aligned Q
+ * and x select the widest loads (for any ldq); any other alignment works.
  * ------------------------------------------------------------------------ */
 gemv_status_t gemv_q8_f32(const int8_t *Q, int ldq, const float *scale,
                           const float *x, const float *bias, float *y, int M,

@@ -115,6 +115,23 @@ const void* rows_fn(int tiles, int batch) {
         default: return nullptr;
         }
     } else {
+        // rows of a load count that is not a power of two: several loads
+        // per lane, one row tile
+        if (batch > 1) {
+            if constexpr (L >= gemvplan::kRowsMinSplitLanes && L < 32 && VEC) {
+                static_assert(gemvplan::kRowsMaxBatch == 6, "split rows are built for batches of 2 to 6");
+                if (tiles != 1) return nullptr;
+                switch (batch) {
+                case 2: return (const void*)&gemvdev::gemv_rows_kernel<D, L, 1, 2, VEC>;
+                case 3: return (const void*)&gemvdev::gemv_rows_kernel<D, L, 1, 3, VEC>;
+                case 4: return (const void*)&gemvdev::gemv_rows_kernel<D, L, 1, 4, VEC>;
+                case 5: return (const void*)&gemvdev::gemv_rows_kernel<D, L, 1, 5, VEC>;
+                case 6: return (const void*)&gemvdev::gemv_rows_kernel<D, L, 1, 6, VEC>;
+                default: return nullptr;
+                }
+            }
+            return nullptr;
+        }
         // several rows per wavefront: one load per row tile, several tiles
         switch (tiles) {
         case 1: return (const void*)&gemvdev::gemv_rows_kernel<D, L, 1, 1, VEC>;
@@ -128,8 +145,8 @@ const void* rows_fn(int tiles, int batch) {
 
 template <class D, bool VEC, int NSEG>
 const void* rows_fn(int lanes, int tiles, int batch) {
-    // several rows per wavefront: one load per lane per row tile
-    if (lanes < 64 && batch != 1) return nullptr;
+    // several rows per wavefront: one load per lane per row tile, or (rows
+    // of a load count that is not a power of two) several, one row tile
     switch (lanes) {
     case 1: return rows_fn<D, 1, VEC, NSEG>(tiles, batch);
     case 2: return rows_fn<D, 2, VEC, NSEG>(tiles, batch);

@@ -180,6 +180,8 @@ constexpr int kBlock = 256;
 constexpr int64_t kTargetGroups = 1024;
 constexpr int64_t kWaveMaxGroups = 16384;
 constexpr int kRowsMaxTiles = 4;
+constexpr int kRowsMinSplitLanes = 8;
+constexpr int kRowsMaxBatch = 6;
 constexpr int64_t kManyGroups = 65536;
 
 struct Plan {
@@ -337,6 +339,35 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         p.batch = 1;
         // as many row tiles per wavefront as keeps >= kTargetGroups groups
         p.row_tiles = 1;
+        // a load count that is not a power of two leaves lanes of a
+        // power-of-two row group idle: for very tall single matrices, fewer
+        // lanes per row (at least 8) with several loads each, when that
+        // wastes fewer loads.  MI355X, 2^20 rows, µs: fp32 K = 72 58.6 ->
+        // 53.0, K = 80 60.7 -> 52.2, K = 96 66.2 -> 57.1; bf16 K = 160 62.3 ->
+        // 52.2, 192 68.0 -> 57.2; fp16 K = 176 63.3 -> 59.9.  But fp32 2^18 ×
+        // 80 13.15 -> 14.45 (the row tiles of the power-of-two group won
+        // there), and 4 lanes per row lost everywhere but K = 80/160 (fp32
+        // 2^20 × 40 25.7 -> 37.6).
+        if (p.vector_loads && max_wave_tiles > 1 && loads > 2 && p.lanes_per_row != loads) {
+            int best_l = p.lanes_per_row, best_b = 1;
+            int64_t best_waste = p.lanes_per_row - loads;
+            for (int l = p.lanes_per_row / 2; l >= kRowsMinSplitLanes; l /= 2) {
+                const int64_t b = ceil_div(loads, (int64_t)l);
+                if (b > kRowsMaxBatch) break;
+                const int64_t grid = ceil_div(M, (int64_t)(kWave / l) * p.waves_per_group);
+                if (grid >= kWaveMaxGroups && l * b - loads < best_waste) {
+                    best_waste = l * b - loads;
+                    best_l = l;
+                    best_b = (int)b;
+                }
+            }
+            if (best_b > 1) {
+                p.lanes_per_row = best_l;
+                p.rows_per_wave = kWave / best_l;
+                p.batch = best_b;
+                break;  // one row tile
+            }
+        }
         if (p.vector_loads) {
             const int cap = max_row_tiles < kRowsMaxTiles ? max_row_tiles : kRowsMaxTiles;
             auto groups = [&](int u) {

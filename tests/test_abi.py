@@ -569,3 +569,19 @@ def test_few_long_rows_take_wider_workgroups():
     # int8 weights keep 4 wavefronts
     q = lg.plan_q8("bf16", 256, 65536, Q_addr=ALIGNED, x_addr=ALIGNED)
     assert q["family"] == lg.FAMILY_GROUP_PER_ROW and q["waves_per_group"] == 4
+
+
+def test_very_tall_rows_of_odd_load_counts_split_their_lanes():
+    """Rows of 3-32 loads that are not a power of two: a very tall matrix
+    (a grid of at least 16384 workgroups) gives each row 8 or 16 lanes with
+    several loads each when that leaves fewer lanes idle; shorter matrices and
+    power-of-two rows keep one load per lane."""
+    for dtype, M, K, lanes, batch in (("f32", 1 << 20, 80, 8, 3), ("f32", 1 << 20, 96, 8, 3),
+                                      ("bf16", 1 << 20, 160, 8, 3), ("f16", 530001, 176, 8, 3)):
+        q = p(dtype, M, K)
+        assert (q["family"], q["lanes_per_row"], q["batch"], q["row_tiles"]) == \
+            (lg.FAMILY_ROWS_PER_WAVE, lanes, batch, 1), (dtype, M, K)
+        assert q["grid"] == -(-M // (64 // lanes * 4)) >= 16384
+    for dtype, M, K in (("f32", 1 << 18, 80), ("f32", 1 << 20, 40), ("f32", 1 << 20, 64),
+                        ("f32", 1 << 20, 112)):
+        assert p(dtype, M, K)["batch"] == 1, (dtype, M, K)

@@ -153,6 +153,26 @@ def test_integer_many_short_rows(dtype, M, K, tiles):
         assert_bit_exact(run_gpu(case, lg.FAMILY_AUTO), ref, f"{dtype} {M}x{K} lda={lda}")
 
 
+# very tall matrices of rows of a load count that is not a power of two: 8
+# lanes per row with several loads each (ragged last wavefront, bias on half
+# the cases)
+SPLIT_LANE_SHAPES = [("f32", 524301, 80, 8), ("bf16", 524301, 160, 8), ("f16", 530001, 176, 8)]
+
+
+@pytest.mark.parametrize("dtype,M,K,lanes", SPLIT_LANE_SHAPES)
+def test_integer_split_lane_rows(dtype, M, K, lanes):
+    per = 16 // gi.ELEMENT_BYTES[dtype]
+    for lda in (K, K + 1):
+        q = lg.plan(dtype, M, K, lda, 1, 1 << 20, 1 << 20)
+        assert (q["family"], q["lanes_per_row"]) == (lg.FAMILY_ROWS_PER_WAVE, lanes), q
+        assert q["batch"] > 1
+        case = gi.make_integer(dtype, M, K, seed=M + 3 * K, lda=lda, bias=lda != K)
+        ref, _ = run_oracle(case)
+        what = f"{dtype} {M}x{K} lda={lda}: {lanes} lanes x {q['batch']} loads per row"
+        print(what, flush=True)
+        assert_bit_exact(run_gpu(case, lg.FAMILY_AUTO), ref, what)
+
+
 # few long rows: workgroups of 16 wavefronts (one row) or 8 (two rows, the
 # last pair of an odd M half past the end); rows with and without a ragged
 # tail shorter than a 16-byte load

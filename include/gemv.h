@@ -57,7 +57,9 @@
  * M > 0 and K > 0, a NULL y when M > 0, or a pointer not aligned to its
  * element size.  M == 0 succeeds without enqueuing anything.  K == 0 writes
  * y = bias (or 0): the empty sum.  GEMV_ERROR_LAUNCH_FAILURE if the HIP
- * runtime refuses the launch.  The library is stateless and reentrant.
+ * runtime refuses the launch (nothing was enqueued; the runtime's own "last
+ * error" is cleared again, see gemv_last_hip_error).  The library is
+ * stateless and reentrant.
  */
 #ifndef LIBGEMV_GEMV_H
 #define LIBGEMV_GEMV_H
@@ -276,6 +278,13 @@ typedef struct {
     int slice_elems;     /* elements per K-slice (the last may be shorter), else K */
     int x_in_registers;  /* workgroup per row: 1 if each lane keeps its x chunks in
                             registers while the workgroup walks its rows */
+    int rounding_chain;  /* n such that no product passes through more than n fp32
+                            roundings on its way to its output, so that
+                            |y - exact| <= γ_n·Σ_k|A[m,k]·x[k]|, γ_n ≈ n·2^-24;
+                            at most 150 for every plan (the tolerance's 1e-5
+                            holds up to n = 167) */
+    int column_blocks;   /* batched: launches, each one pass over A for a block of
+                            the vectors (1 = all vectors in one pass) */
     int64_t grid;        /* workgroups (split-K: ceil(rows / rows_per_group) × slices) */
 } gemv_plan_t;
 
@@ -320,6 +329,36 @@ gemv_status_t gemv_q8_run_family(gemv_dtype_t xdtype, int family,
  * GEMV_ERROR_INVALID_VALUE. */
 gemv_status_t gemv_read_probe(const void *buffer, size_t bytes, unsigned *sink,
                               hipStream_t stream);
+
+/* Read-probe variants (measurement only): the read probe's job with other
+ * read patterns, to map the streaming cost of `bytes` against the pattern.
+ * loads_per_lane: 2, 4, 8 or 16 sixteen-byte loads in flight per lane (that
+ * many KiB per wavefront); waves_per_group: 1, 2, 4, 8 or 16;
+ * blocks_per_wave >= 1 blocks of loads_per_lane KiB per wavefront;
+ * flags: bit 0 plain (cached) loads instead of nontemporal ones, bit 1 the
+ * wavefront's priority raised while it issues its loads, bit 2 blocks dealt
+ * grid-stride (block w + b·wavefronts) instead of consecutively.  The grid
+ * has ceil(ceil(bytes / (1024·loads_per_lane·blocks_per_wave)) /
+ * waves_per_group) workgroups.  wave_times (NULL, or 8-byte aligned device
+ * memory of at least 2 × workgroups × waves_per_group entries, given in
+ * wave_times_len): wavefront w writes its start and end readings of the
+ * GPU's constant-rate real-time counter to entries 2w and 2w + 1.  Nothing
+ * else is written (as gemv_read_probe).  Other values give
+ * GEMV_ERROR_INVALID_VALUE. */
+gemv_status_t gemv_read_probe_variant(const void *buffer, size_t bytes,
+                                      unsigned *sink, int loads_per_lane,
+                                      int waves_per_group, int blocks_per_wave,
+                                      int flags, unsigned long long *wave_times,
+                                      size_t wave_times_len, hipStream_t stream);
+
+/* Error-path check (testing only): asks the HIP runtime for a launch it
+ * must refuse before anything reaches the GPU (a workgroup of 2048 threads;
+ * the hardware allows 1024) through the same launch path as every entry
+ * point, and returns what an entry point returns when a launch is refused:
+ * GEMV_ERROR_LAUNCH_FAILURE, with the runtime's error available from
+ * gemv_last_hip_error().  The runtime's own "last error" is cleared, as after
+ * any refused launch of this library, so later calls are unaffected. */
+gemv_status_t gemv_test_refused_launch(hipStream_t stream);
 
 /* Run with a forced family (GEMV_FAMILY_AUTO = what the entry points do).
  * Same arguments, validation and results contract as the entry points;

@@ -79,7 +79,7 @@ class GemvPlan(ctypes.Structure):
         "family", "vector_loads", "chunk_elems", "lanes_per_row",
         "rows_per_wave", "row_tiles", "waves_per_group", "rows_per_group",
         "batch", "passes", "block", "lds_bytes", "splits", "slice_elems",
-        "x_in_registers")] + [
+        "x_in_registers", "rounding_chain", "column_blocks")] + [
         ("grid", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
@@ -127,9 +127,12 @@ gemv_q8_bf16 = _bind("gemv_q8_bf16", [_vp, _i, _vp, _vp, _vp, _vp, _i, _i, _st])
 gemv_q8_run_family = _bind("gemv_q8_run_family", [_i, _i, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _st])
 gemv_plan_q8 = _bind("gemv_plan_q8", [_i, _i, _i, _i, _vp, _vp, _i, ctypes.POINTER(GemvPlan)])
 gemv_read_probe = _bind("gemv_read_probe", [_vp, _sz, _vp, _st])
+gemv_read_probe_variant = _bind("gemv_read_probe_variant",
+                                [_vp, _sz, _vp, _i, _i, _i, _i, _vp, _sz, _st])
 gemv_plan = _bind("gemv_plan", [_i, _i, _i, _i, _i, _vp, _vp, _i, ctypes.POINTER(GemvPlan)])
 gemv_plan_splitk = _bind("gemv_plan_splitk", [_i, _i, _i, _i, _i, _vp, _vp, ctypes.POINTER(GemvPlan)])
 gemv_run_family = _bind("gemv_run_family", [_i, _i, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _st])
+gemv_test_refused_launch = _bind("gemv_test_refused_launch", [_st])
 
 EXPORTED = ("gemv_status_string", "gemv_last_hip_error",
             "gemv_last_hip_error_string", "gemv_f32", "gemv_f16", "gemv_bf16",
@@ -138,8 +141,9 @@ EXPORTED = ("gemv_status_string", "gemv_last_hip_error",
             "gemv_gate_up_silu_f16", "gemv_gate_up_silu_bf16",
             "gemv_splitk_workspace_size", "gemv_splitk_f32", "gemv_splitk_f16",
             "gemv_splitk_bf16", "gemv_q8_f32", "gemv_q8_f16", "gemv_q8_bf16",
-            "gemv_q8_run_family", "gemv_plan_q8", "gemv_read_probe", "gemv_plan",
-            "gemv_plan_splitk", "gemv_run_family")
+            "gemv_q8_run_family", "gemv_plan_q8", "gemv_read_probe",
+            "gemv_read_probe_variant", "gemv_plan",
+            "gemv_plan_splitk", "gemv_run_family", "gemv_test_refused_launch")
 
 
 class GemvError(RuntimeError):

@@ -39,6 +39,10 @@ hipError_t launch(const void* fn, const Plan& p, hipStream_t stream, void** argv
 gemv_status_t finish(hipError_t err) {
     if (err != hipSuccess) {
         g_last_launch_error = err;
+        // the runtime also keeps the error as the thread's "last error";
+        // reported here, it is cleared there, so that it does not surface
+        // later as the failure of someone else's unrelated call
+        (void)hipGetLastError();
         return GEMV_ERROR_LAUNCH_FAILURE;
     }
     return GEMV_SUCCESS;
@@ -421,12 +425,23 @@ template <class D>
 gemv_status_t run_single(const Plan& p, const void* A, int lda, const void* X, const float* bias,
                          float* Y, int M, int K, int nvec, hipStream_t stream) {
     if (p.family == gemvplan::BATCHED_MFMA) {
-        const void* fn = batched_kernel<D>(p, nvec);
-        if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;
-        int64_t lda64 = lda;
-        void* argv[] = {(void*)&A, (void*)&lda64, (void*)&X, (void*)&bias, (void*)&Y,
-                        (void*)&M, (void*)&K, (void*)&nvec};
-        return finish(launch(fn, p, stream, argv));
+        // one launch, or (long rows and more than 32 vectors) one per block of
+        // 32 vectors: columns j0 .. j0 + nb - 1 start at X + j0·K and Y + j0·M
+        using S = typename D::storage;
+        const int per = p.column_blocks > 1 ? (nvec + p.column_blocks - 1) / p.column_blocks : nvec;
+        for (int j0 = 0; j0 < nvec; j0 += per) {
+            int nb = nvec - j0 < per ? nvec - j0 : per;
+            const void* fn = batched_kernel<D>(p, nb);
+            if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;
+            int64_t lda64 = lda;
+            const S* Xb = static_cast<const S*>(X) + (int64_t)j0 * K;
+            float* Yb = Y + (int64_t)j0 * M;
+            void* argv[] = {(void*)&A, (void*)&lda64, (void*)&Xb, (void*)&bias, (void*)&Yb,
+                            (void*)&M, (void*)&K, (void*)&nb};
+            const gemv_status_t st = finish(launch(fn, p, stream, argv));
+            if (st != GEMV_SUCCESS) return st;
+        }
+        return GEMV_SUCCESS;
     }
     if (p.family == gemvplan::BATCHED) {
         // column blocks of at most kValuVectors vectors, one launch each
@@ -679,7 +694,58 @@ void export_plan(const Plan& p, gemv_plan_t* plan) {
     plan->splits = p.splits;
     plan->slice_elems = p.slice_elems;
     plan->x_in_registers = p.x_in_registers;
+    plan->rounding_chain = p.rounding_chain;
+    plan->column_blocks = p.column_blocks;
     plan->grid = p.grid;
+}
+
+// Whether the library holds a compiled kernel for a plan (the host-side plan
+// calls answer only for plans the entry points can launch).
+template <class D>
+bool has_kernel(const Plan& p, int nvec) {
+    if (p.family == gemvplan::BATCHED_MFMA) {
+        const int per = p.column_blocks > 1 ? (nvec + p.column_blocks - 1) / p.column_blocks : nvec;
+        return batched_kernel<D>(p, per) != nullptr &&
+               batched_kernel<D>(p, nvec - (p.column_blocks - 1) * per) != nullptr;
+    }
+    if (p.family == gemvplan::BATCHED)
+        return batched_kernel<D>(p, nvec < gemvplan::kValuVectors ? nvec : gemvplan::kValuVectors) !=
+               nullptr;
+    return single_fn<D, 0>(p) != nullptr;
+}
+
+bool has_kernel(int dtype, const Plan& p, int nvec) {
+    switch (dtype) {
+    case gemvplan::F32: return has_kernel<TF32>(p, nvec);
+    case gemvplan::F16: return has_kernel<TF16>(p, nvec);
+    case gemvplan::BF16: return has_kernel<TBF16>(p, nvec);
+    default: return false;
+    }
+}
+
+bool has_q8_kernel(int xdtype, const Plan& p) {
+    switch (xdtype) {
+    case gemvplan::F32: return (p.vector_loads ? q8_fn<TF32, true>(p) : q8_fn<TF32, false>(p)) != nullptr;
+    case gemvplan::F16: return (p.vector_loads ? q8_fn<TF16, true>(p) : q8_fn<TF16, false>(p)) != nullptr;
+    case gemvplan::BF16: return (p.vector_loads ? q8_fn<TBF16, true>(p) : q8_fn<TBF16, false>(p)) != nullptr;
+    default: return false;
+    }
+}
+
+bool has_splitk_kernel(int dtype, const Plan& p) {
+    if (p.family != gemvplan::SPLIT_K) return has_kernel(dtype, p, 1);
+    switch (dtype) {
+    case gemvplan::F32:
+        return (p.vector_loads ? splitk_fn<TF32, true>(p.rows_per_group, p.batch)
+                               : splitk_fn<TF32, false>(p.rows_per_group, p.batch)) != nullptr;
+    case gemvplan::F16:
+        return (p.vector_loads ? splitk_fn<TF16, true>(p.rows_per_group, p.batch)
+                               : splitk_fn<TF16, false>(p.rows_per_group, p.batch)) != nullptr;
+    case gemvplan::BF16:
+        return (p.vector_loads ? splitk_fn<TBF16, true>(p.rows_per_group, p.batch)
+                               : splitk_fn<TBF16, false>(p.rows_per_group, p.batch)) != nullptr;
+    default: return false;
+    }
 }
 
 }  // namespace
@@ -786,7 +852,8 @@ gemv_status_t gemv_plan_q8(gemv_dtype_t xdtype, int M, int K, int ldq, const voi
                            const void* x, int family, gemv_plan_t* plan) {
     Plan p;
     if (plan == nullptr || M < 0 ||
-        q8_plan((int)xdtype, M, K, ldq, Q, x, family, &p) != gemvplan::OK)
+        q8_plan((int)xdtype, M, K, ldq, Q, x, family, &p) != gemvplan::OK ||
+        !has_q8_kernel((int)xdtype, p))
         return GEMV_ERROR_INVALID_VALUE;
     export_plan(p, plan);
     return GEMV_SUCCESS;
@@ -809,12 +876,80 @@ gemv_status_t gemv_read_probe(const void* buffer, size_t bytes, unsigned* sink,
     return finish(launch((const void*)&gemvdev::gemv_read_probe_kernel, p, stream, argv));
 }
 
+}  // extern "C"
+
+namespace {
+
+template <int LOADS, int W>
+const void* probe_variant_fn(int flags) {
+    switch (flags & 3) {
+    case 0: return (const void*)&gemvdev::gemv_read_probe_variant_kernel<LOADS, W, false, false>;
+    case 1: return (const void*)&gemvdev::gemv_read_probe_variant_kernel<LOADS, W, true, false>;
+    case 2: return (const void*)&gemvdev::gemv_read_probe_variant_kernel<LOADS, W, false, true>;
+    default: return (const void*)&gemvdev::gemv_read_probe_variant_kernel<LOADS, W, true, true>;
+    }
+}
+
+template <int LOADS>
+const void* probe_variant_fn(int waves, int flags) {
+    switch (waves) {
+    case 1: return probe_variant_fn<LOADS, 1>(flags);
+    case 2: return probe_variant_fn<LOADS, 2>(flags);
+    case 4: return probe_variant_fn<LOADS, 4>(flags);
+    case 8: return probe_variant_fn<LOADS, 8>(flags);
+    case 16: return probe_variant_fn<LOADS, 16>(flags);
+    default: return nullptr;
+    }
+}
+
+const void* probe_variant_fn(int loads, int waves, int flags) {
+    switch (loads) {
+    case 2: return probe_variant_fn<2>(waves, flags);
+    case 4: return probe_variant_fn<4>(waves, flags);
+    case 8: return probe_variant_fn<8>(waves, flags);
+    case 16: return probe_variant_fn<16>(waves, flags);
+    default: return nullptr;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+gemv_status_t gemv_read_probe_variant(const void* buffer, size_t bytes, unsigned* sink,
+                                      int loads_per_lane, int waves_per_group, int blocks_per_wave,
+                                      int flags, unsigned long long* wave_times,
+                                      size_t wave_times_len, hipStream_t stream) {
+    if (bytes == 0) return GEMV_SUCCESS;
+    if (buffer == nullptr || sink == nullptr || bytes % 16 != 0 || (uintptr_t)buffer % 16 != 0 ||
+        (uintptr_t)sink % 4 != 0 || blocks_per_wave < 1 || (flags & ~7) != 0)
+        return GEMV_ERROR_INVALID_VALUE;
+    const void* fn = probe_variant_fn(loads_per_lane, waves_per_group, flags);
+    if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;
+    const int64_t n16 = (int64_t)(bytes / 16);
+    const int64_t per_wave = (int64_t)loads_per_lane * 64 * blocks_per_wave;
+    const int64_t waves = (n16 + per_wave - 1) / per_wave;
+    Plan p;
+    p.grid = (waves + waves_per_group - 1) / waves_per_group;
+    p.block = waves_per_group * 64;
+    if (p.grid > 0x7fffffff) return GEMV_ERROR_INVALID_VALUE;
+    if (wave_times != nullptr &&
+        ((uintptr_t)wave_times % 8 != 0 || wave_times_len < (size_t)(2 * p.grid * waves_per_group)))
+        return GEMV_ERROR_INVALID_VALUE;
+    const gemvdev::quad* q = static_cast<const gemvdev::quad*>(buffer);
+    int blocks = blocks_per_wave, stride = (flags & 4) ? 1 : 0;
+    void* argv[] = {(void*)&q, (void*)&n16, (void*)&sink, (void*)&blocks, (void*)&stride,
+                    (void*)&wave_times};
+    return finish(launch(fn, p, stream, argv));
+}
+
 gemv_status_t gemv_plan(gemv_dtype_t dtype, int M, int K, int lda, int nvec, const void* A,
                         const void* X, int family, gemv_plan_t* plan) {
     if (plan == nullptr || (int)dtype > gemvplan::BF16) return GEMV_ERROR_INVALID_VALUE;
     Plan p;
     if (gemvplan::make_plan((int)dtype, M, K, lda, nvec, (uintptr_t)A, (uintptr_t)X, family,
-                            &p) != gemvplan::OK)
+                            &p) != gemvplan::OK ||
+        !has_kernel((int)dtype, p, nvec))
         return GEMV_ERROR_INVALID_VALUE;
     export_plan(p, plan);
     return GEMV_SUCCESS;
@@ -825,7 +960,8 @@ gemv_status_t gemv_plan_splitk(gemv_dtype_t dtype, int M, int K, int lda, int sp
     if (plan == nullptr || lda < K) return GEMV_ERROR_INVALID_VALUE;
     Plan p;
     const bool vec = gemvplan::vector_ok((int)dtype, K, lda, 1, (uintptr_t)A, (uintptr_t)x);
-    if (gemvplan::make_split_plan((int)dtype, M, K, vec, splits, &p) != gemvplan::OK)
+    if (gemvplan::make_split_plan((int)dtype, M, K, vec, splits, &p) != gemvplan::OK ||
+        !has_splitk_kernel((int)dtype, p))
         return GEMV_ERROR_INVALID_VALUE;
     export_plan(p, plan);
     return GEMV_SUCCESS;
@@ -857,6 +993,21 @@ gemv_status_t gemv_splitk_bf16(const uint16_t* A, int lda, const uint16_t* x, co
                                float* y, int M, int K, int splits, void* workspace,
                                size_t workspace_bytes, hipStream_t stream) {
     return run_splitk<TBF16>(A, lda, x, bias, y, M, K, splits, workspace, workspace_bytes, stream);
+}
+
+gemv_status_t gemv_test_refused_launch(hipStream_t stream) {
+    // A workgroup of 2048 threads, twice what the hardware allows: the
+    // runtime refuses the launch before anything reaches the GPU.  The kernel
+    // is the split-K reduce with no rows (M = 0), which would touch no memory
+    // even if it ran.
+    const float* ws = nullptr;
+    const float* bias = nullptr;
+    float* y = nullptr;
+    int splits = 1;
+    int64_t M = 0;
+    void* argv[] = {(void*)&ws, (void*)&splits, (void*)&bias, (void*)&y, (void*)&M};
+    return finish(hipLaunchKernel((const void*)&gemvdev::gemv_splitk_reduce_kernel, dim3(1),
+                                  dim3(2048), argv, 0, stream));
 }
 
 gemv_status_t gemv_run_family(gemv_dtype_t dtype, int family, const void* A, int lda,

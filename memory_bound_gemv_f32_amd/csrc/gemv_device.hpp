@@ -263,6 +263,25 @@ struct Chunk<TQ8<X>, false> {
     }
 };
 
+// A running fp32 sum that carries the rounding error of every addition
+// (Knuth's error-free two-sum: s + a = t + e exactly, with t = fl(s + a)),
+// for adding the partial sums of a lane's batches of loads: the error of the
+// result is about one rounding of the total plus (n·2^-24)² of the sum of
+// |partials| over n additions, instead of growing with n, so the rounding
+// chain of a long row stays bounded (page "GEMM、GEMV、dtype 与算术强度",
+// section "dtype 改变什么": the accumulator must keep what the inputs carry).
+struct Sum2 {
+    float s;
+    float c;
+    __device__ __forceinline__ void add(float a) {
+        const float t = s + a;
+        const float z = t - s;
+        c += (s - (t - z)) + (a - z);
+        s = t;
+    }
+    __device__ __forceinline__ float value() const { return s + c; }
+};
+
 // DPP lane exchange within 16-lane rows (bound_ctrl: no lane is disabled).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {

@@ -27,6 +27,7 @@
 #pragma once
 
 #include "gemv_device.hpp"
+#include "gemv_plan.hpp"
 
 namespace gemvdev {
 
@@ -236,10 +237,14 @@ struct ThreeSegments {
 
 // One batch of the rows kernels: BATCH chunks per row tile, chunk c + i·L
 // for i < BATCH, all loads issued before any is used.  CHECK: chunks at or
-// past nfull load chunk nfull-1 instead and are replaced by zero.
+// past nfull load chunk nfull-1 instead and are replaced by zero.  The
+// batch's products are summed in two fresh accumulators (alternate chunks),
+// whose sum is then added to the row tile's running compensated sum: the
+// rounding chain of a batch is at most ceil(BATCH/2) chunks of elements,
+// whatever the row length.
 template <class C, int L, int U, int BATCH, bool CHECK, class S, class XS>
 __device__ __forceinline__ void rows_batch(const S* const (&rp)[U], const XS* x, int c, int nfull,
-                                           float (&acc)[U][2]) {
+                                           Sum2 (&sum)[U]) {
     using CT = typename C::type;
     using XT = typename C::xtype;
     CT a[U][BATCH];
@@ -256,6 +261,9 @@ __device__ __forceinline__ void rows_batch(const S* const (&rp)[U], const XS* x,
     // fence the scheduler may interleave each load with its multiply-adds
     // and leave one load in flight at a time
     __builtin_amdgcn_sched_barrier(0);
+    float acc[U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u][0] = acc[u][1] = 0.f;
 #pragma unroll
     for (int i = 0; i < BATCH; ++i) {
         XT xi = xv[i];
@@ -267,6 +275,8 @@ __device__ __forceinline__ void rows_batch(const S* const (&rp)[U], const XS* x,
             acc[u][i & 1] = C::dot(ai, xi, acc[u][i & 1]);
         }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) sum[u].add(acc[u][0] + acc[u][1]);
 }
 
 // Rows-per-wave (L < 64) and wave-per-row (L == 64) kernel.
@@ -313,29 +323,34 @@ __device__ __forceinline__ void rows_body(const Rows& rows, const typename D::xs
         sv[o] = in ? scale_of(rows, row) : 0.f;
     }
 
-    float acc[U][2];
+    Sum2 sum[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) acc[u][0] = acc[u][1] = 0.f;
+    for (int u = 0; u < U; ++u) sum[u] = Sum2{0.f, 0.f};
 
     const int nfull = K / E;  // whole chunks per row
     // Batches where every lane's chunks are in range need no checks; at most
     // one final batch straddles the end of the row.
     const int nsafe = nfull - nfull % (BATCH * L);
     int c0 = 0;
-    for (; c0 < nsafe; c0 += BATCH * L) rows_batch<C, L, U, BATCH, false>(rp, x, c0 + sub, nfull, acc);
-    if (c0 < nfull) rows_batch<C, L, U, BATCH, true>(rp, x, c0 + sub, nfull, acc);
+    for (; c0 < nsafe; c0 += BATCH * L) rows_batch<C, L, U, BATCH, false>(rp, x, c0 + sub, nfull, sum);
+    if (c0 < nfull) rows_batch<C, L, U, BATCH, true>(rp, x, c0 + sub, nfull, sum);
     if constexpr (VEC) {
         // elements past the last whole chunk (fewer than E of them)
+        float tail[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) tail[u] = 0.f;
         for (int k = nfull * E + sub; k < K; k += L) {
             const float xe = widen_x(D{}, x[k]);
 #pragma unroll
-            for (int u = 0; u < U; ++u) acc[u][1] = __builtin_fmaf(widen_a(D{}, rp[u][k]), xe, acc[u][1]);
+            for (int u = 0; u < U; ++u) tail[u] = __builtin_fmaf(widen_a(D{}, rp[u][k]), xe, tail[u]);
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u) sum[u].add(tail[u]);
     }
 
     float v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = segment_sum<L>(acc[u][0] + acc[u][1]);
+    for (int u = 0; u < U; ++u) v[u] = segment_sum<L>(sum[u].value());
 #pragma unroll
     for (int o = 0; o < kOut; ++o) {
         const int u = sub + o * L;
@@ -409,25 +424,30 @@ __device__ __forceinline__ void group_body(const Rows& rows, const typename D::x
     const float b = (rows.any_bias() && writer) ? rows.bias_of(row0 + sub) : 0.f;
     const float sc = writer ? scale_of(rows, row0 + sub) : 0.f;
 
-    float acc[U][2];
+    Sum2 sum[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) acc[u][0] = acc[u][1] = 0.f;
+    for (int u = 0; u < U; ++u) sum[u] = Sum2{0.f, 0.f};
     const int nfull = K / E;
     const int nsafe = nfull - nfull % (BATCH * L);
     int c0 = 0;
-    for (; c0 < nsafe; c0 += BATCH * L) rows_batch<C, L, U, BATCH, false>(rp, x, c0 + sub, nfull, acc);
-    if (c0 < nfull) rows_batch<C, L, U, BATCH, true>(rp, x, c0 + sub, nfull, acc);
+    for (; c0 < nsafe; c0 += BATCH * L) rows_batch<C, L, U, BATCH, false>(rp, x, c0 + sub, nfull, sum);
+    if (c0 < nfull) rows_batch<C, L, U, BATCH, true>(rp, x, c0 + sub, nfull, sum);
     if constexpr (VEC) {
+        float tail[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) tail[u] = 0.f;
         for (int k = nfull * E + sub; k < K; k += L) {
             const float xe = widen_x(D{}, x[k]);
 #pragma unroll
-            for (int u = 0; u < U; ++u) acc[u][1] = __builtin_fmaf(widen_a(D{}, rp[u][k]), xe, acc[u][1]);
+            for (int u = 0; u < U; ++u) tail[u] = __builtin_fmaf(widen_a(D{}, rp[u][k]), xe, tail[u]);
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u) sum[u].add(tail[u]);
     }
 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const float v = segment_sum<64>(acc[u][0] + acc[u][1]);
+        const float v = segment_sum<64>(sum[u].value());
         if ((threadIdx.x & 63) == 0) partial[threadIdx.x >> 6][u] = v;
     }
     __syncthreads();
@@ -639,15 +659,27 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
         rp[r] = A + (m < M ? m : (int64_t)M - 1) * lda;
     }
 
+    // each lane sums kBatchedGroup of its chunks into fresh accumulators,
+    // then adds them to its compensated running sums (a bounded rounding
+    // chain whatever K)
+    Sum2 sum[RB][NV];
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int j = 0; j < NV; ++j) sum[r][j] = Sum2{0.f, 0.f};
+
+    const int nfull = K / E;
+    constexpr int kGroup = gemvplan::kBatchedGroup * 64;  // chunks per group of the wavefront
+#pragma unroll 1
+    for (int g0 = 0; g0 < nfull; g0 += kGroup) {
     float acc[RB][NV];
 #pragma unroll
     for (int r = 0; r < RB; ++r)
 #pragma unroll
         for (int j = 0; j < NV; ++j) acc[r][j] = 0.f;
-
-    const int nfull = K / E;
+    const int gend = g0 + kGroup < nfull ? g0 + kGroup : nfull;
 #pragma unroll 1
-    for (int c0 = 0; c0 < nfull; c0 += BATCH * 64) {
+    for (int c0 = g0; c0 < gend; c0 += BATCH * 64) {
         CT a[RB][BATCH];
         bool ok[BATCH];
         int cc[BATCH];
@@ -674,16 +706,30 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
             }
         }
     }
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int j = 0; j < NV; ++j) sum[r][j].add(acc[r][j]);
+    }
     if constexpr (VEC) {
+        float tail[RB][NV];
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+            for (int j = 0; j < NV; ++j) tail[r][j] = 0.f;
         for (int k = nfull * E + lane; k < K; k += 64) {
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
                 const float xe = widen(D{}, X[(int64_t)j * K + k]);
 #pragma unroll
                 for (int r = 0; r < RB; ++r)
-                    acc[r][j] = __builtin_fmaf(widen(D{}, rp[r][k]), xe, acc[r][j]);
+                    tail[r][j] = __builtin_fmaf(widen(D{}, rp[r][k]), xe, tail[r][j]);
             }
         }
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+            for (int j = 0; j < NV; ++j) sum[r][j].add(tail[r][j]);
     }
 
 #pragma unroll
@@ -692,7 +738,7 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
         const float b = (bias != nullptr && m < M) ? bias[m] : 0.f;
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-            const float v = segment_sum<64>(acc[r][j]);
+            const float v = segment_sum<64>(sum[r][j].value());
             if (lane == 0 && m < M) Y[(int64_t)j * M + m] = v + b;
         }
     }
@@ -745,10 +791,11 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
 // wavefront order and each lane finishes 4 consecutive rows of one column,
 // adds the bias and writes them with one 16-byte store where Y allows it
 // (four scattered 4-byte stores per lane before: 16 vectors 8.76 -> 8.38
-// µs).  Needs 16-byte aligned A, X and row pitch and K % 8 == 0.  A chunk
-// shorter than CH steps at the end of a slice, and the last, partial 64-wide
-// step (K % 64 != 0, done by the last wavefront), read their operands
-// directly.
+// µs).  Needs 16-byte aligned A, X and row pitch and K % 8 == 0.  The
+// ceil(K/64) steps, the partial last one (K % 64 != 0) included, are dealt
+// to the wavefronts by gemvplan::mfma_step_range; the steps of a run that do
+// not fill a whole chunk, and the partial step, read their operands
+// directly, one step at a time.
 template <class D, int W, int NT, int CH, bool FEW>
 __global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2)))
 gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
@@ -777,19 +824,61 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
         ap[q] = A + (row < M ? row : (int64_t)M - 1) * lda + 32 * half + 8 * g;
     }
 
-    const int steps = K / 64;
-    const int per = (steps + W - 1) / W;
-    const int s0 = wave * per;
-    const int s1 = s0 + per < steps ? s0 + per : steps;
+    // This wavefront's 64-element steps [rg.first, rg.end): whole steps run
+    // in chunks of CH; what is left of the run, the partial last step
+    // (K % 64 != 0) included, runs one step at a time below.
+    const gemvplan::StepRange rg = gemvplan::mfma_step_range(K, W, wave);
+    const int whole = K / 64;
+    const int s1 = rg.end < whole ? rg.end : whole;
     const quad zero = quad{0u, 0u, 0u, 0u};
     quad* xw = xs[wave];
 
-    f32x4 acc[2][NT][2];
+    // Up to 32 vectors (FRESH) every chunk's steps are summed into fresh
+    // accumulators, which are then added into running totals with an
+    // error-free two-sum per element (the rounding error of each addition is
+    // carried in `cmp`), so a result's rounding chain does not grow with K.
+    // With 4 tiles the registers do not allow it: the steps of all chunks
+    // are summed into `acc` directly (the planner bounds K for that form).
+    constexpr bool FRESH = NT <= 2;
+    f32x4 acc[2][NT][2], tot[2][NT][2], cmp[2][NT][2];
+    // Every MFMA step starts from a zero accumulator and its outputs are
+    // added to `acc` by the vector ALUs.  The matrix core aligns the terms of
+    // a step (its 32 products and the accumulator passed in) to the largest
+    // and drops the bits more than about 24 places below it (measured on
+    // gfx950: 2^k + 1 - 2^k gives 1 for k <= 24 and 0 from k = 25, whether
+    // the 1 is a product or the accumulator); with a running sum passed in,
+    // every step could lose small products against the whole sum so far.
+    // From zero, a step's error is bounded by its own products.
+    const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto clear = [](f32x4(&v)[2][NT][2]) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+        for (int q = 0; q < 2; ++q)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[q][t][0] = acc[q][t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    int c = s0;
+            for (int t = 0; t < NT; ++t) v[q][t][0] = v[q][t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    auto fold = [&]() {
+        if constexpr (FRESH) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const f32x4 a = acc[q][t][h], s = tot[q][t][h];
+                        const f32x4 sum = s + a;
+                        const f32x4 z = sum - s;
+                        cmp[q][t][h] += (s - (sum - z)) + (a - z);
+                        tot[q][t][h] = sum;
+                    }
+            clear(acc);
+        }
+    };
+    clear(acc);
+    if constexpr (FRESH) {
+        clear(tot);
+        clear(cmp);
+    }
+    int c = rg.first;
     if constexpr (FEW) {
         // X operands straight from memory: lane (column r, group g)
         const S* xcol = X + (int64_t)(r < nvec ? r : nvec - 1) * K + 8 * g;
@@ -810,9 +899,10 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
             for (int i = 0; i < CH; ++i)
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
-                    acc[q][0][0] = mma_16x16x32(D{}, a[q][i], b[0][i], acc[q][0][0]);
-                    acc[q][0][1] = mma_16x16x32(D{}, a[q][i], b[1][i], acc[q][0][1]);
+                    acc[q][0][0] += mma_16x16x32(D{}, a[q][i], b[0][i], zero4);
+                    acc[q][0][1] += mma_16x16x32(D{}, a[q][i], b[1][i], zero4);
                 }
+            fold();
         }
     } else {
         // groups of G steps, X of the group (kCols columns × G steps) before A
@@ -863,26 +953,26 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
                         const quad b1 = xw[(16 * t + r) * kColQuads + 8 * i + 4 + g];
 #pragma unroll
                         for (int q = 0; q < 2; ++q) {
-                            acc[q][t][0] = mma_16x16x32(D{}, a[q][i], b0, acc[q][t][0]);
-                            acc[q][t][1] = mma_16x16x32(D{}, a[q][i], b1, acc[q][t][1]);
+                            acc[q][t][0] += mma_16x16x32(D{}, a[q][i], b0, zero4);
+                            acc[q][t][1] += mma_16x16x32(D{}, a[q][i], b1, zero4);
                         }
                     }
                 }
             }
+            fold();
             // the next chunk overwrites this wavefront's LDS region
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
         }
     }
-    // a short last chunk (fewer than CH steps) one step at a time, and the
-    // last, partial step (K % 64 != 0, done by the last wavefront), with X
-    // read straight from memory; groups of 8 wholly past K are zero (K % 8 == 0)
+    // the rest of the run (fewer than CH steps, the partial last step among
+    // them when it is this wavefront's) one step at a time, with X read
+    // straight from memory; groups of 8 wholly past K are zero (K % 8 == 0)
     const S* xq[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) xq[t] = X + (int64_t)(16 * t + r < nvec ? 16 * t + r : 0) * K + 8 * g;
-    const int last = (wave == W - 1 && steps * 64 < K) ? steps + 1 : s1;
 #pragma unroll 1
-    for (; c < last; ++c) {
+    for (; c < rg.end; ++c) {
         const int e = c * 64;
         const bool ina = e + 32 * half + 8 * g < K;
         quad a[2];
@@ -896,10 +986,20 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
             const quad b1 = (col && e + 32 + 8 * g < K) ? *reinterpret_cast<const quad*>(xq[t] + e + 32) : zero;
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                acc[q][t][0] = mma_16x16x32(D{}, a[q], b0, acc[q][t][0]);
-                acc[q][t][1] = mma_16x16x32(D{}, a[q], b1, acc[q][t][1]);
+                acc[q][t][0] += mma_16x16x32(D{}, a[q], b0, zero4);
+                acc[q][t][1] += mma_16x16x32(D{}, a[q], b1, zero4);
             }
         }
+    }
+
+    fold();
+    if constexpr (FRESH) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) acc[q][t][h] = tot[q][t][h] + cmp[q][t][h];
     }
 
     // lane (column j, group g) holds operand rows 4g .. 4g+3, i.e. real rows
@@ -979,22 +1079,25 @@ gemv_gated_silu_kernel(const typename D::storage* Ag, const typename D::storage*
     const int sub = threadIdx.x;
     const S* const rps[2] = {Ag + row * lda, Au + row * lda};
 
-    float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+    Sum2 sum[2] = {Sum2{0.f, 0.f}, Sum2{0.f, 0.f}};
     const int nfull = K / E;
     const int nsafe = nfull - nfull % (BATCH * L);
     int c0 = 0;
-    for (; c0 < nsafe; c0 += BATCH * L) rows_batch<C, L, 2, BATCH, false>(rps, x, c0 + sub, nfull, acc);
-    if (c0 < nfull) rows_batch<C, L, 2, BATCH, true>(rps, x, c0 + sub, nfull, acc);
+    for (; c0 < nsafe; c0 += BATCH * L) rows_batch<C, L, 2, BATCH, false>(rps, x, c0 + sub, nfull, sum);
+    if (c0 < nfull) rows_batch<C, L, 2, BATCH, true>(rps, x, c0 + sub, nfull, sum);
     if constexpr (VEC) {
+        float tail[2] = {0.f, 0.f};
         for (int k = nfull * E + sub; k < K; k += L) {
             const float xe = widen(D{}, x[k]);
-            acc[0][1] = __builtin_fmaf(widen(D{}, rps[0][k]), xe, acc[0][1]);
-            acc[1][1] = __builtin_fmaf(widen(D{}, rps[1][k]), xe, acc[1][1]);
+            tail[0] = __builtin_fmaf(widen(D{}, rps[0][k]), xe, tail[0]);
+            tail[1] = __builtin_fmaf(widen(D{}, rps[1][k]), xe, tail[1]);
         }
+        sum[0].add(tail[0]);
+        sum[1].add(tail[1]);
     }
 
-    float g = segment_sum<64>(acc[0][0] + acc[0][1]);
-    float u = segment_sum<64>(acc[1][0] + acc[1][1]);
+    float g = segment_sum<64>(sum[0].value());
+    float u = segment_sum<64>(sum[1].value());
     if constexpr (W > 1) {
         if ((threadIdx.x & 63) == 0) {
             partial[threadIdx.x >> 6][0] = g;
@@ -1038,6 +1141,60 @@ gemv_read_probe_kernel(const quad* __restrict__ p, int64_t n16, unsigned* sink) 
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
     if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
+// Read-probe variants, for mapping what streaming a buffer costs on this
+// GPU against the read pattern (the table of patterns the GEMV families are
+// chosen from): LOADS 16-byte loads per lane in flight (LOADS KiB per
+// wavefront), W wavefronts per workgroup, CACHED plain instead of
+// nontemporal loads, PRIO the wavefront's priority raised while it issues
+// its loads.  Each wavefront streams `blocks` blocks of LOADS KiB: with
+// `stride` the grid walks the buffer together (block b of wavefront w is
+// block w + b·(number of wavefronts)), otherwise each wavefront takes
+// `blocks` consecutive blocks.  With `times`, lane 0 of every wavefront
+// writes its start and end (the GPU's constant-rate real-time counter) to
+// times[2w], times[2w + 1] with ordinary vector stores.  Nothing else is
+// written (see gemv_read_probe_kernel).
+template <int LOADS, int W, bool CACHED, bool PRIO>
+__global__ void __launch_bounds__(W * 64)
+gemv_read_probe_variant_kernel(const quad* __restrict__ p, int64_t n16, unsigned* sink, int blocks,
+                               int stride, unsigned long long* times) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * W + (threadIdx.x >> 6);
+    const int64_t waves = (int64_t)gridDim.x * W;
+    unsigned long long t0 = 0;
+    if (times != nullptr) t0 = __builtin_amdgcn_s_memrealtime();
+    unsigned acc = 0;
+    for (int b = 0; b < blocks; ++b) {
+        const int64_t blk = stride ? wave + (int64_t)b * waves : wave * blocks + b;
+        const int64_t base = blk * LOADS * 64 + lane;
+        quad v[LOADS];
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(3);
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int64_t q = base + (int64_t)i * 64;
+            const quad* a = p + (q < n16 ? q : n16 - 1);
+            if constexpr (CACHED)
+                v[i] = *a;
+            else
+                v[i] = __builtin_nontemporal_load(a);
+        }
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+    }
+    if (acc == 0x9e3779b9u) sink[0] = acc;
+    if (times != nullptr) {
+        // read once every load has arrived (acc needed them all; the fence
+        // keeps the counter read after it)
+        __builtin_amdgcn_sched_barrier(0);
+        const unsigned long long t1 = __builtin_amdgcn_s_memrealtime();
+        if (lane == 0) {
+            times[2 * wave] = t0;
+            times[2 * wave + 1] = t1;
+        }
+    }
 }
 
 }  // namespace gemvdev

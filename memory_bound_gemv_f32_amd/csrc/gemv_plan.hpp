@@ -112,8 +112,11 @@ constexpr int kGroupStreamMaxChunks = 6;
 constexpr int kGroupStreamRows = 4;
 // Batched family: loads in flight per row, and rows per wavefront, fewer as
 // the number of vectors grows so that rows × vectors accumulators plus the
-// loaded chunks fit the register budget of four wavefronts per SIMD.
+// loaded chunks fit the register budget of four wavefronts per SIMD; a lane
+// sums kBatchedGroup of its chunks into fresh accumulators before adding
+// them to its compensated running sums.
 constexpr int kBatchedBatch = 1;
+constexpr int kBatchedGroup = 8;
 constexpr int batched_rows(int nvec) { return nvec <= 2 ? 4 : (nvec <= 4 ? 2 : 1); }
 // Matrix-core batched family: 16 rows per workgroup, its wavefronts split K
 // and walk their slice in chunks of this many 64-wide steps (the A loads of a
@@ -132,6 +135,103 @@ constexpr int mfma_tiles(int nvec) { return nvec <= 16 ? 1 : (nvec <= 32 ? 2 : 4
 constexpr int mfma_chunk(int nvec) { return kMfmaChunk / mfma_tiles(nvec); }
 constexpr int mfma_lds_bytes(int nvec) {
     return kMfmaWaves * 16 * mfma_tiles(nvec) * (mfma_chunk(nvec) * 128 + 16);
+}
+// The 64-element steps of a row that wavefront `wave` of a matrix-core
+// workgroup of `waves` wavefronts walks: steps [first, end) of the
+// ceil(K/64) steps, the last of which may be partial (K % 64 != 0).  The
+// steps are dealt in contiguous runs of ceil(steps/waves); trailing
+// wavefronts may get an empty run.  Every step, the partial one included,
+// belongs to exactly one wavefront.  (A constexpr function: the kernel calls
+// it on the device, the host tests call it on the CPU.)
+struct StepRange {
+    int first;
+    int end;
+};
+constexpr StepRange mfma_step_range(int K, int waves, int wave) {
+    const int steps = K / 64 + (K % 64 != 0 ? 1 : 0);
+    const int per = (steps + waves - 1) / waves;
+    const int first = wave * per < steps ? wave * per : steps;
+    const int end = first + per < steps ? first + per : steps;
+    return StepRange{first, end};
+}
+
+// ---- rounding-chain bound --------------------------------------------------
+//
+// Every output is a sum of K exact products (fp16/bf16 products are exact in
+// fp32; fp32 products are fused into FMAs) formed through a tree of fp32
+// additions.  If no product passes through more than n roundings on its way
+// to the output, |y - exact| <= γ_n·Σ_k|A[m,k]·x[k]|, γ_n = n·u/(1 - n·u),
+// u = 2^-24: n <= 167 keeps every output within 1e-5·Σ|A·x| for every input,
+// not only for inputs whose rounding errors happen to cancel.  (Page "GEMM、
+// GEMV、dtype 与算术强度", section "dtype 改变什么": the accumulator is where
+// precision is kept.)  rounding_chain() gives n for a plan; the planner keeps
+// it within kMaxRoundingChain.
+constexpr int kMaxRoundingChain = 150;
+// v_dot2_f32_{f16,bf16}: two exact products and the accumulator; its
+// rounding is not specified as one IEEE rounding, so it is charged two.
+constexpr int kDot2Roundings = 2;
+// One 16×16×32 matrix-core step from a zero accumulator: the matrix core
+// aligns an output's 32 products to the largest and keeps about 24 bits
+// below it (measured on gfx950: 2^k + 1 - 2^k gives 1 for k <= 24, 0 from
+// k = 25), dropping the rest, then rounds once to fp32.  Each product can
+// lose less than 2^-23 of the largest, so the step's error is below
+// (32·2 + 1)·u·Σ|products|: charged as 65 roundings.  The kernel adds each
+// step's outputs to its accumulators with fp32 additions (one rounding per
+// step), never passing a running sum into the matrix core.
+constexpr int kMfmaProductRoundings = 65;
+
+inline int ceil_log2(int64_t v) {
+    int r = 0;
+    while (((int64_t)1 << r) < v) ++r;
+    return r;
+}
+
+// Roundings a compensated (error-free two-sum) running sum of n terms adds:
+// its result is within u·|sum| + γ_{n-1}²·Σ|terms| (Ogita, Rump and Oishi,
+// "Accurate sum and dot product", algorithm Sum2): one rounding plus
+// γ_{n-1}²/u.  One term is exact.
+inline int compensated_roundings(int64_t n) {
+    if (n <= 1) return 0;
+    const double u = 1.0 / 16777216.0;
+    const double g = (double)(n - 1) * u / (1.0 - (double)(n - 1) * u);
+    const double extra = g * g / u;
+    return 1 + (int)(extra + 0.999999);
+}
+
+// The vector-ALU bodies (rows per wavefront, wave per row, workgroup per
+// row, gated, split-K pass 1): `elems` elements per row (or slice), chunks
+// of `chunk` elements, `lanes` lanes per row of which `wave_lanes` share a
+// wavefront, `batch` chunks per lane per batch summed into two fresh
+// accumulators (alternate chunks), the batches' sums (and the sum of the
+// element-wise tail) added with a compensated running sum, then a tree over
+// the wavefront's lanes and a sequential fold of `waves` wavefronts' partials.
+// `per_elem` roundings per element within an accumulator (1 for FMA).
+// `accs` accumulators take the chunks of a batch in turn (2, or 1 in the
+// vector-ALU batched kernel).
+inline int valu_chain(int64_t elems, int chunk, int lanes, int wave_lanes, int batch, int waves,
+                      int per_elem = 1, int accs = 2) {
+    const int64_t full = elems / chunk;
+    const int64_t tail = elems - full * chunk;
+    const int64_t per_lane = (full + lanes - 1) / lanes;
+    const int64_t b = per_lane < batch ? (per_lane < 1 ? 1 : per_lane) : batch;
+    const int64_t batches = (per_lane + batch - 1) / batch;
+    const int64_t in_batch = (b + accs - 1) / accs * chunk * per_elem + (accs - 1);
+    const int64_t in_tail = (tail + lanes - 1) / lanes;
+    const int64_t first = in_batch > in_tail ? in_batch : in_tail;
+    const int64_t terms = batches + (tail > 0 ? 1 : 0);
+    return (int)(first + compensated_roundings(terms) + ceil_log2(wave_lanes) + (waves - 1));
+}
+
+// The matrix-core kernel: each wavefront's run of 64-wide steps in chunks of
+// `ch` steps; with `fresh` every chunk (and the leftover steps) sums into
+// fresh accumulators added with a compensated running sum, otherwise all
+// steps accumulate in place.  Then the two half-row tiles are added and the
+// `waves` wavefronts' partial tiles folded in order.
+inline int mfma_chain(int K, int waves, int ch, bool fresh) {
+    const int steps = mfma_step_range(K, waves, 0).end;  // the longest run
+    if (!fresh) return kMfmaProductRoundings + steps + 1 + (waves - 1);
+    const int chunks = steps / ch + (steps % ch != 0 ? 1 : 0);
+    return kMfmaProductRoundings + ch + compensated_roundings(chunks) + 1 + (waves - 1);
 }
 // Split-K: when there are too few rows to fill the chip and each row holds
 // much more than a workgroup keeps in flight (page "SGEMV CUDA代码学习",
@@ -200,6 +300,8 @@ struct Plan {
     int splits = 1;       // K-slices per row (split-K), else 1
     int slice_elems = 0;  // elements per slice (split-K), else K
     int x_in_registers = 0;  // workgroup per row: x kept in registers across its rows
+    int rounding_chain = 0;  // bound on the fp32 roundings between a product and its output
+    int column_blocks = 1;   // batched: launches (passes over A), each for a block of vectors
     int64_t grid = 0;     // workgroups (split-K: rows × slices)
 };
 
@@ -297,6 +399,7 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         return INVALID;
 
     Plan p;
+    const int nvec_all = nvec;
     p.vector_loads = vec ? 1 : 0;
     p.chunk_elems = p.vector_loads ? kLoadBytes / element_bytes(dtype) : 1;
     // loads needed to cover one row (the last may be a partial, element-wise tail)
@@ -348,7 +451,10 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         // 80 13.15 -> 14.45 (the row tiles of the power-of-two group won
         // there), and 4 lanes per row lost everywhere but K = 80/160 (fp32
         // 2^20 × 40 25.7 -> 37.6).
-        if (p.vector_loads && max_wave_tiles > 1 && loads > 2 && p.lanes_per_row != loads) {
+        // (int8 rows keep one load per lane: their rows kernels exist for
+        // batches of one only below 64 lanes per row)
+        if (dtype != Q8 && p.vector_loads && max_wave_tiles > 1 && loads > 2 &&
+            p.lanes_per_row != loads) {
             int best_l = p.lanes_per_row, best_b = 1;
             int64_t best_waste = p.lanes_per_row - loads;
             for (int l = p.lanes_per_row / 2; l >= kRowsMinSplitLanes; l /= 2) {
@@ -504,11 +610,46 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         p.rows_per_group = p.rows_per_wave * p.row_tiles * p.waves_per_group;
     p.grid = ceil_div(M, p.rows_per_group);
     p.slice_elems = K;
-    if (fam == BATCHED_MFMA)  // 64-wide steps per wavefront
-        p.passes = (int)ceil_div(K / 64, (int64_t)kMfmaWaves);
+    if (fam == BATCHED_MFMA)  // 64-wide steps (the last may be partial) per wavefront
+        p.passes = mfma_step_range(K, kMfmaWaves, 0).end;
     else
         p.passes = (int)ceil_div(full, (int64_t)p.lanes_per_row);
     if (p.grid > 0x7fffffff) return INVALID;
+
+    // The rounding-chain bound (+ 1: the bias, or the int8 scale and bias in
+    // one fused multiply-add, added last).  The matrix-core kernel's 4-tile
+    // form accumulates in place, so for long rows its vectors run as blocks
+    // of 32 (2 tiles, compensated; one pass over A per block).
+    int64_t chain = 0;
+    switch (fam) {
+    case BATCHED_MFMA: {
+        int blk = nvec;
+        chain = mfma_chain(K, kMfmaWaves, mfma_chunk(blk), mfma_tiles(blk) <= 2) + 1;
+        if (chain > kMaxRoundingChain && mfma_tiles(nvec) > 2) {
+            blk = 32;
+            p.column_blocks = (int)ceil_div(nvec, (int64_t)blk);
+            p.batch = mfma_chunk(blk);
+            p.lds_bytes = mfma_lds_bytes(blk);
+            chain = mfma_chain(K, kMfmaWaves, mfma_chunk(blk), true) + 1;
+        }
+        break;
+    }
+    case BATCHED:
+        p.column_blocks = (int)ceil_div(nvec_all, (int64_t)kValuVectors);
+        chain = valu_chain(K, p.chunk_elems, kWave, kWave, kBatchedGroup, 1,
+                           p.vector_loads ? kDot2Roundings / 2 : 1, 1) + 1;
+        break;
+    default:
+        if (p.x_in_registers)  // one batch per row, no running sum
+            chain = (p.batch + 1) / 2 * p.chunk_elems + 1 + ceil_log2(kWave) + (p.waves_per_group - 1) + 1;
+        else
+            chain = valu_chain(K, p.chunk_elems, p.lanes_per_row,
+                               p.lanes_per_row < kWave ? p.lanes_per_row : kWave, p.batch,
+                               p.waves_per_group) + 1;
+        break;
+    }
+    if (chain > kMaxRoundingChain) return INVALID;
+    p.rounding_chain = (int)chain;
     *out = p;
     return OK;
 }
@@ -594,6 +735,13 @@ inline int make_split_plan(int dtype, int M, int K, bool vec, int requested, Pla
     p.grid = ceil_div((int64_t)M, (int64_t)p.rows_per_group) * splits;
     if (p.grid * p.block > 0xffffffffLL) return INVALID;  // HIP's 32-bit grid size
     p.passes = (int)per_lane;
+    // pass 1 over a slice (no bias), then the reduce: each lane adds up to
+    // ceil(splits/64) partials in turn, a 64-lane tree, the bias
+    const int64_t chain = valu_chain(slice, p.chunk_elems, p.lanes_per_row, kWave, p.batch,
+                                     p.waves_per_group) +
+                          ceil_div(splits, (int64_t)kWave) + ceil_log2(kWave) + 1;
+    if (chain > kMaxRoundingChain) return INVALID;
+    p.rounding_chain = (int)chain;
     *out = p;
     return OK;
 }

@@ -272,8 +272,9 @@ def test_wide_batched_plans():
         assert q["grid"] == 256 and q["block"] == 512
         assert q["lds_bytes"] == 8 * 16 * tiles * (chunk * 128 + 16) <= 160 * 1024
     for nvec in (17, 40, 64):
-        assert p("f16", 999, 1000, nvec=nvec, A=ALIGNED + 2) == p("f16", 999, 1000, nvec=16,
-                                                                  A=ALIGNED + 2)
+        wide = p("f16", 999, 1000, nvec=nvec, A=ALIGNED + 2)
+        assert wide["column_blocks"] == -(-nvec // 16)
+        assert {**wide, "column_blocks": 1} == p("f16", 999, 1000, nvec=16, A=ALIGNED + 2)
 
 
 # ---------------------------------------------------------------------------

@@ -16,7 +16,7 @@ import torch
 import gemv_inputs as gi
 import memory_bound_gemv_f32_amd as lg
 from gpu_helpers import (assert_bit_exact, assert_within_bound, run_gpu,
-                         run_oracle)
+                         run_oracle, upload)
 from oracle_pins import lib_decode
 
 pytestmark = pytest.mark.gpu
@@ -430,3 +430,76 @@ def test_seeded_random_shapes_automatic_plan():
         ref, _ = run_oracle(case)
         assert_bit_exact(run_gpu(case, lg.FAMILY_AUTO, misalign=misalign), ref, what)
         done += 1
+
+
+# the lengths whose last, partial 64-element step the matrix-core kernel
+# once dropped (K % 8 == 0, K % 64 != 0, 7·ceil(steps/8) > steps), and
+# neighbours; every vector-tile count
+MFMA_TAIL_K = [8, 72, 120, 136, 200, 392, 600, 840, 1096, 1608, 2120, 2632, 2680]
+MFMA_TAIL_NVEC = [2, 5, 6, 16, 17, 32, 33, 64]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("nvec", MFMA_TAIL_NVEC)
+def test_integer_batched_partial_last_step(dtype, nvec):
+    for K in MFMA_TAIL_K:
+        case = gi.make_integer(dtype, 33, K, seed=K + nvec, nvec=nvec, bias=K % 16 == 8)
+        ref, _ = run_oracle(case)
+        q = lg.plan(dtype, case.M, K, K, nvec, 1 << 20, 1 << 20)
+        assert q["family"] == lg.FAMILY_BATCHED_MFMA, q
+        for fam in (lg.FAMILY_AUTO, lg.FAMILY_BATCHED_MFMA):
+            assert_bit_exact(run_gpu(case, fam, batched=True), ref,
+                             f"{dtype} 33x{K} nvec={nvec} family {fam}")
+
+
+def test_refused_launch_reports_launch_failure():
+    """A launch the runtime refuses comes back as GEMV_ERROR_LAUNCH_FAILURE
+    with the runtime's error code, and leaves nothing behind: the runtime's
+    last error is cleared, so torch and later calls work as before."""
+    stream = torch.cuda.current_stream().cuda_stream
+    assert lg.gemv_test_refused_launch(stream) == lg.GEMV_ERROR_LAUNCH_FAILURE
+    code = lg.gemv_last_hip_error()
+    name = lg.gemv_last_hip_error_string().decode()
+    print(f"refused launch: hipError {code} ({name})", flush=True)
+    assert code != 0 and name.startswith("hip")
+    err = lg.GemvError(lg.GEMV_ERROR_LAUNCH_FAILURE, "gemv_test_refused_launch")
+    assert name in str(err)
+    t = torch.arange(1000, dtype=torch.float32, device="cuda") * 2
+    torch.cuda.synchronize()
+    assert float(t.sum()) == 999000.0
+    case = gi.make_integer("bf16", 100, 300, seed=3, bias=True)
+    ref, _ = run_oracle(case)
+    assert_bit_exact(run_gpu(case, lg.FAMILY_AUTO), ref, "after a refused launch")
+
+
+@pytest.mark.parametrize("dtype", gi.DTYPES)
+def test_long_rows_of_positive_terms_within_bound(dtype):
+    """All-positive A and x (no cancellation: rounding errors all push the
+    same way) on rows of 2^20 elements, every family that takes them and
+    split-K: every output within 1e-5·Σ|A·x| + 1e-6, as the plans'
+    rounding-chain bound promises."""
+    M, K = 24, 1 << 20
+    rng = np.random.default_rng(77)
+    a = rng.uniform(0.0, 1.0, size=(M, K))
+    x = rng.uniform(0.0, 1.0, size=(1, K))
+    case = gi.Case("pos", dtype, M, K, gi.quantise(dtype, a), gi.quantise(dtype, x), None, K)
+    ref, absdot = run_oracle(case)
+    for fam in families_for(case):
+        q = lg.plan(dtype, M, K, K, 1, 1 << 20, 1 << 20, fam)
+        y = run_gpu(case, fam)
+        err = np.abs(y - ref) / (1e-5 * absdot + 1e-6)
+        print(f"{dtype} {M}x{K} family {fam}: chain {q['rounding_chain']}, "
+              f"worst error / bound {err.max():.3g}", flush=True)
+        assert_within_bound(y, ref, absdot, f"{dtype} positive {M}x{K} family {fam}")
+    A, X, _ = upload(case)
+    y = lg.gemv_splitk(A, X[0]).cpu().numpy().astype(np.float64)[None, :]
+    assert_within_bound(y, ref, absdot, f"{dtype} positive {M}x{K} split-K")
+    if dtype != "f32":
+        Kb = 1 << 17
+        bc = gi.Case("posb", dtype, 64, Kb, gi.quantise(dtype, rng.uniform(0, 1, (64, Kb))),
+                     gi.quantise(dtype, rng.uniform(0, 1, (40, Kb))), None, Kb, 40)
+        refb, absb = run_oracle(bc)
+        for fam in (lg.FAMILY_AUTO, lg.FAMILY_BATCHED):
+            assert_within_bound(run_gpu(bc, fam, batched=True), refb, absb,
+                                f"{dtype} positive 64x{Kb} nvec=40 family {fam}")
+

@@ -167,3 +167,16 @@ def test_full_size_q8_workload(name):
     print(f"workload {name}: {case.xdtype} M={case.M} K={case.K}", flush=True)
     ref, absdot = run_oracle_q8(case)
     assert_within_bound(run_q8(case), ref, absdot, name)
+
+
+@pytest.mark.parametrize("xdtype", gi.DTYPES)
+def test_integer_tall_rows_of_17_to_24_loads(xdtype):
+    """A very tall int8 matrix of 320-byte rows (20 loads): rows of a load
+    count that is not a power of two keep one load per lane for int8 weights
+    (their rows kernels exist for one load per lane only), bit-exact."""
+    M, K = 524301, 320
+    q = lg.plan_q8(xdtype, M, K, K, 1 << 20, 1 << 20)
+    assert q["family"] == lg.FAMILY_ROWS_PER_WAVE and q["batch"] == 1, q
+    case = gi.make_q8_integer(xdtype, M, K, seed=17, bias=True)
+    ref, _ = run_oracle_q8(case)
+    assert_bit_exact(run_q8(case), ref, f"int8 x {xdtype} {M}x{K}")

@@ -70,6 +70,11 @@ def parse():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="CPU only: read the counter CSVs of the two --counters runs and write "
                          "the traffic summary used for roofline.traffic")
+    ap.add_argument("--probe-sweep", action="store_true",
+                    help="time the read probe's variants (loads per lane, wavefronts per "
+                         "workgroup, blocks per wavefront, cached/nontemporal, priority) over "
+                         "rotated buffers of 8, 32 and 112 MiB, and the per-wavefront finish "
+                         "times of the GEMV's own pattern; prints one JSON object")
     ap.add_argument("--counters", action="store_true",
                     help="for rocprofv3 --pmc runs: a few eager launches of --workload over the "
                          "rotated buffers, then a plain device copy of COPY_BYTES for scaling")
@@ -323,6 +328,97 @@ class ProbeRotation:
                 for A in self.rot.A]
 
 
+class ProbeVariantRotation:
+    """R buffers of `nbytes` (together more than 2x the Infinity Cache),
+    each step streamed by one read-probe variant."""
+
+    def __init__(self, torch, nbytes, min_bytes=2 * INFINITY_CACHE_BYTES):
+        self.nbytes = nbytes
+        self.R = max(2, math.ceil(min_bytes / nbytes) + 1)
+        self.bufs = [torch.full((nbytes // 4,), 1, dtype=torch.int32, device="cuda")
+                     for _ in range(self.R)]
+        self.sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.variant = (8, 4, 1, 0)
+
+    def callers(self, lg, stream_handle):
+        loads, waves, blocks, flags = self.variant
+        return [(lg.gemv_read_probe_variant, (b.data_ptr(), self.nbytes, self.sink.data_ptr(), loads,
+                                              waves, blocks, flags, None, 0, stream_handle))
+                for b in self.bufs]
+
+
+PROBE_SIZES = {"8MiB": 8 << 20, "32MiB": 32 << 20, "112MiB": 112 << 20}
+
+
+def probe_variants():
+    """(loads per lane, wavefronts per workgroup, blocks per wavefront, flags):
+    flags bit 0 cached loads, bit 1 raised priority, bit 2 grid-stride."""
+    out = [(8, 4, 1, 0)]  # the GEMV families' pattern (gemv_read_probe)
+    for loads in (2, 4, 8, 16):
+        for waves in (1, 2, 4, 8, 16):
+            if (loads, waves) != (8, 4):
+                out.append((loads, waves, 1, 0))
+    for loads, waves in ((4, 4), (8, 4), (8, 8), (16, 4)):
+        for blocks in (2, 4, 8):
+            out.append((loads, waves, blocks, 4))
+            out.append((loads, waves, blocks, 0))
+    for v in ((8, 4, 1, 1), (8, 4, 1, 2), (8, 4, 1, 3), (4, 4, 1, 2), (16, 4, 1, 2), (8, 8, 1, 2),
+              (8, 4, 2, 6), (8, 4, 4, 6)):
+        out.append(v)
+    return out
+
+
+def probe_sweep(torch, lg, steps):
+    """µs per launch of every read-probe variant at each size, graph loops of
+    `steps` launches over rotated buffers; and, for the GEMV pattern, the
+    spread of wavefront finish times within one launch."""
+    import numpy as np
+    result = {"steps": steps, "sizes": {}, "wave_finish": {}}
+    for label, nbytes in PROBE_SIZES.items():
+        rot = ProbeVariantRotation(torch, nbytes)
+        rows = []
+        for v in probe_variants():
+            rot.variant = v
+            loop = GraphLoop(torch, rot, lg, steps, per=rot.R * max(1, 256 // rot.R))
+            us = 1e3 * loop.time(warmup=min(steps, 500)) / steps
+            del loop
+            rows.append({"loads_per_lane": v[0], "waves_per_group": v[1], "blocks_per_wave": v[2],
+                         "cached": bool(v[3] & 1), "priority": bool(v[3] & 2),
+                         "grid_stride": bool(v[3] & 4), "us": round(us, 3),
+                         "GBps": round(nbytes / us / 1e3, 1)})
+            log(f"probe {label} {v}: {us:.3f} us, {nbytes / us / 1e3:.1f} GB/s")
+        result["sizes"][label] = {"bytes": nbytes, "rotation_sets": rot.R, "variants": rows}
+        # wavefront finish times of the GEMV pattern: one launch, timed per wavefront
+        n_waves = -(-nbytes // (8 * 1024))
+        times = torch.zeros(2 * n_waves + 64, dtype=torch.int64, device="cuda")
+        stream = torch.cuda.current_stream().cuda_stream
+        for rep in range(3):
+            b = rot.bufs[rep % rot.R]
+            rc = lg.gemv_read_probe_variant(b.data_ptr(), nbytes, rot.sink.data_ptr(), 8, 4, 1, 0,
+                                            times.data_ptr(), times.numel(), stream)
+            if rc != 0:
+                raise RuntimeError(f"gemv_read_probe_variant returned {rc}")
+        torch.cuda.synchronize()
+        t = times[:2 * n_waves].cpu().numpy().reshape(n_waves, 2).astype(np.int64)
+        t0 = t[:, 0].min()
+        start, end = (t[:, 0] - t0) * 10e-3, (t[:, 1] - t0) * 10e-3  # 100 MHz counter -> µs
+        group = np.arange(n_waves) // 4
+        xcd = group % 8
+        late = end >= np.percentile(end, 90)
+        result["wave_finish"][label] = {
+            "waves": int(n_waves),
+            "start_us_p50_p90_max": [round(float(np.percentile(start, q)), 3) for q in (50, 90, 100)],
+            "end_us_p10_p50_p90_max": [round(float(np.percentile(end, q)), 3) for q in (10, 50, 90, 100)],
+            "late_decile_share_by_xcd": [round(float((late & (xcd == i)).sum() / max(late.sum(), 1)), 3)
+                                         for i in range(8)],
+            "late_decile_mean_position": round(float(np.flatnonzero(late).mean() / n_waves), 3),
+        }
+        log(f"wave finish {label}: {result['wave_finish'][label]}")
+        del rot, times
+        torch.cuda.empty_cache()
+    return result
+
+
 def call(fn_args):
     f, args = fn_args
     rc = f(*args)
@@ -550,6 +646,10 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     log(f"device {torch.cuda.get_device_name(0)} ({torch.cuda.get_device_properties(0).gcnArchName})")
+
+    if args.probe_sweep:
+        print(json.dumps(probe_sweep(torch, lg, args.steps)), flush=True)
+        return
 
     if args.kernel_only:
         # only the timed graph loop of one named shape (for profilers)

@@ -26,6 +26,7 @@ contiguous, i.e. Y as M×nvec column-major.
 from __future__ import annotations
 
 import ctypes
+import os
 from pathlib import Path
 
 # torch ships its own HIP runtime under the same soname (libamdhip64.so.7) as
@@ -38,7 +39,9 @@ except ImportError:  # a C-only user of the library has no torch
     _torch_runtime = None
 
 PACKAGE = Path(__file__).resolve().parent
-LIBRARY = PACKAGE / "libgemv.so"
+# LIBGEMV_LIBRARY: another build of the same library (e.g. for comparing two
+# builds in one process tree); the in-tree build by default
+LIBRARY = Path(os.environ.get("LIBGEMV_LIBRARY", PACKAGE / "libgemv.so"))
 
 if not LIBRARY.exists():
     raise ImportError(

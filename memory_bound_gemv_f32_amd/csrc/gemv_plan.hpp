@@ -113,10 +113,10 @@ constexpr int kGroupStreamRows = 4;
 // Batched family: loads in flight per row, and rows per wavefront, fewer as
 // the number of vectors grows so that rows × vectors accumulators plus the
 // loaded chunks fit the register budget of four wavefronts per SIMD; a lane
-// sums kBatchedGroup of its chunks into fresh accumulators before adding
-// them to its compensated running sums.
+// sums kBatchedGroup of its chunks (4 chained v_dot2 each) into fresh
+// accumulators before adding them to its compensated running sums.
 constexpr int kBatchedBatch = 1;
-constexpr int kBatchedGroup = 8;
+constexpr int kBatchedGroup = 2;
 constexpr int batched_rows(int nvec) { return nvec <= 2 ? 4 : (nvec <= 4 ? 2 : 1); }
 // Matrix-core batched family: 16 rows per workgroup, its wavefronts split K
 // and walk their slice in chunks of this many 64-wide steps (the A loads of a
@@ -167,9 +167,13 @@ constexpr StepRange mfma_step_range(int K, int waves, int wave) {
 // precision is kept.)  rounding_chain() gives n for a plan; the planner keeps
 // it within kMaxRoundingChain.
 constexpr int kMaxRoundingChain = 150;
-// v_dot2_f32_{f16,bf16}: two exact products and the accumulator; its
-// rounding is not specified as one IEEE rounding, so it is charged two.
-constexpr int kDot2Roundings = 2;
+// v_dot2_f32_{f16,bf16}: two exact products and the accumulator passed in,
+// aligned to the largest of the three with the bits more than about 24
+// places below it dropped, then rounded once (measured on gfx950: with
+// 2^k, -2^k and an accumulator of 1 the 1 survives up to k = 24; 2^23 +
+// 0.75 gives 2^23).  Each term can lose less than 2^-23 of the largest:
+// charged 3·2 + 1 = 7 roundings of the running sum per instruction.
+constexpr int kDot2Roundings = 7;
 // One 16×16×32 matrix-core step from a zero accumulator: the matrix core
 // aligns an output's 32 products to the largest and keeps about 24 bits
 // below it (measured on gfx950: 2^k + 1 - 2^k gives 1 for k <= 24, 0 from
@@ -636,8 +640,9 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
     }
     case BATCHED:
         p.column_blocks = (int)ceil_div(nvec_all, (int64_t)kValuVectors);
+        // a 16-byte chunk is 4 chained v_dot2 (8 elements), an element one FMA
         chain = valu_chain(K, p.chunk_elems, kWave, kWave, kBatchedGroup, 1,
-                           p.vector_loads ? kDot2Roundings / 2 : 1, 1) + 1;
+                           p.vector_loads ? (kDot2Roundings + 1) / 2 : 1, 1) + 1;
         break;
     default:
         if (p.x_in_registers)  // one batch per row, no running sum

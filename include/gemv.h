@@ -212,6 +212,27 @@ gemv_status_t gemv_splitk_bf16(const uint16_t *A, int lda, const uint16_t *x,
                                int splits, void *workspace,
                                size_t workspace_bytes, hipStream_t stream);
 
+/* Split-K for callers that cannot allocate (code under stream capture,
+ * tight serving loops, harnesses that forbid hipMalloc): y = A·x (+ bias)
+ * exactly as gemv_splitk_* with the same `splits` (the same kernels, the
+ * same bits), A, x, bias and y of element type `dtype`, with no workspace
+ * argument: the partial sums live in a static device buffer of
+ * GEMV_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  The call allocates and frees nothing.  Its first
+ * call on a device looks the buffer's address up (hipGetSymbolAddress) and
+ * keeps it.  The buffer needs no clearing: each call writes every partial
+ * it reads.  Every call on one GPU shares that GPU's buffer, so calls that
+ * may run at the same time on one GPU (other streams, other host threads)
+ * race and give wrong results: serialise them (one stream).  Errors as for
+ * gemv_splitk_*, plus GEMV_ERROR_INVALID_VALUE when the call needs more than
+ * GEMV_NOALLOC_SCRATCH_BYTES (4·M·splits bytes with the effective slice
+ * count; gemv_splitk_workspace_size gives it).  The stream may belong to any
+ * device. */
+#define GEMV_NOALLOC_SCRATCH_BYTES (256 * 1024)
+gemv_status_t gemv_splitk_noalloc(gemv_dtype_t dtype, const void *A, int lda,
+                                  const void *x, const float *bias, float *y,
+                                  int M, int K, int splits, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Weight-only int8.  The lqnn.cn NPU MatMul essay (sections 1.2, 4.2 and
  * 5.2) stores weights as int8 with a per-channel scale while activations

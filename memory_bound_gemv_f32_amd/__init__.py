@@ -124,6 +124,8 @@ gemv_splitk_workspace_size = _bind("gemv_splitk_workspace_size", [_i, _i, _i, _i
 gemv_splitk_f32 = _bind("gemv_splitk_f32", [_vp, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _st])
 gemv_splitk_f16 = _bind("gemv_splitk_f16", [_vp, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _st])
 gemv_splitk_bf16 = _bind("gemv_splitk_bf16", [_vp, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _st])
+gemv_splitk_noalloc = _bind("gemv_splitk_noalloc", [_i, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _st])
+NOALLOC_SCRATCH_BYTES = 256 * 1024
 gemv_q8_f32 = _bind("gemv_q8_f32", [_vp, _i, _vp, _vp, _vp, _vp, _i, _i, _st])
 gemv_q8_f16 = _bind("gemv_q8_f16", [_vp, _i, _vp, _vp, _vp, _vp, _i, _i, _st])
 gemv_q8_bf16 = _bind("gemv_q8_bf16", [_vp, _i, _vp, _vp, _vp, _vp, _i, _i, _st])
@@ -143,7 +145,7 @@ EXPORTED = ("gemv_status_string", "gemv_last_hip_error",
             "gemv_multi_f16", "gemv_multi_bf16", "gemv_gate_up_silu_f32",
             "gemv_gate_up_silu_f16", "gemv_gate_up_silu_bf16",
             "gemv_splitk_workspace_size", "gemv_splitk_f32", "gemv_splitk_f16",
-            "gemv_splitk_bf16", "gemv_q8_f32", "gemv_q8_f16", "gemv_q8_bf16",
+            "gemv_splitk_bf16", "gemv_splitk_noalloc", "gemv_q8_f32", "gemv_q8_f16", "gemv_q8_bf16",
             "gemv_q8_run_family", "gemv_plan_q8", "gemv_read_probe",
             "gemv_read_probe_variant", "gemv_plan",
             "gemv_plan_splitk", "gemv_run_family", "gemv_test_refused_launch")

@@ -6,6 +6,7 @@
 // chosen by row length and row count (gemv_plan.hpp).
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/gemv.h"
@@ -615,6 +616,51 @@ gemv_status_t run_gated(const void* Ag, const void* Au, int lda, const void* x, 
     return finish(launch(fn, p, stream, argv));
 }
 
+// ---- scratch for the entry point that allocates nothing ---------------------
+//
+// gemv_splitk_noalloc keeps split-K's partial sums here instead of in a
+// caller's workspace: a file-scope device array of kScratchBytes, of which
+// every GPU the library runs on holds its own copy until the process ends.
+// Its address on a device is looked up once (hipGetSymbolAddress, with that
+// device current) and kept; host code uses only that address, never the
+// array's name (which on the host is a stand-in, not a device address).
+constexpr size_t kScratchBytes = 256 * 1024;
+static_assert(kScratchBytes == GEMV_NOALLOC_SCRATCH_BYTES, "the header states the scratch size");
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the device that `stream` belongs to (the current
+// device for the null stream).
+gemv_status_t device_scratch(hipStream_t stream, void** out) {
+    int current = 0;
+    hipError_t err = hipGetDevice(&current);
+    if (err != hipSuccess) return finish(err);
+    int dev = current;
+    if (stream != nullptr) {
+        hipDevice_t d = 0;
+        err = hipStreamGetDevice(stream, &d);
+        if (err != hipSuccess) return finish(err);
+        dev = (int)d;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return GEMV_ERROR_INVALID_VALUE;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        if (dev != current && (err = hipSetDevice(dev)) != hipSuccess) return finish(err);
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t back = dev != current ? hipSetDevice(current) : hipSuccess;
+        if (err != hipSuccess) return finish(err);
+        if (back != hipSuccess) return finish(back);
+        if (p == nullptr) return GEMV_ERROR_LAUNCH_FAILURE;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GEMV_SUCCESS;
+}
+
 template <class D>
 gemv_status_t run_splitk(const void* A, int lda, const void* x, const float* bias, float* y, int M,
                          int K, int splits, void* workspace, size_t workspace_bytes,
@@ -1008,6 +1054,32 @@ gemv_status_t gemv_test_refused_launch(hipStream_t stream) {
     void* argv[] = {(void*)&ws, (void*)&splits, (void*)&bias, (void*)&y, (void*)&M};
     return finish(hipLaunchKernel((const void*)&gemvdev::gemv_splitk_reduce_kernel, dim3(1),
                                   dim3(2048), argv, 0, stream));
+}
+
+gemv_status_t gemv_splitk_noalloc(gemv_dtype_t dtype, const void* A, int lda, const void* x,
+                                  const float* bias, float* y, int M, int K, int splits,
+                                  hipStream_t stream) {
+    // the checks and the plan of gemv_splitk_*, before the scratch is touched
+    if (splits < 0 || gemvplan::validate((int)dtype, M, K, lda, 1, (uintptr_t)A, (uintptr_t)x,
+                                         (uintptr_t)bias, (uintptr_t)y) != gemvplan::OK)
+        return GEMV_ERROR_INVALID_VALUE;
+    if (M == 0) return GEMV_SUCCESS;
+    int n = 1, slice = 0;
+    if (gemvplan::split_geometry((int)dtype, M, K, splits, &n, &slice) != gemvplan::OK)
+        return GEMV_ERROR_INVALID_VALUE;
+    const int64_t need = gemvplan::split_workspace_bytes(M, n);
+    if (need > (int64_t)kScratchBytes) return GEMV_ERROR_INVALID_VALUE;
+    void* ws = nullptr;
+    if (need > 0) {
+        const gemv_status_t st = device_scratch(stream, &ws);
+        if (st != GEMV_SUCCESS) return st;
+    }
+    switch ((int)dtype) {
+    case gemvplan::F32: return run_splitk<TF32>(A, lda, x, bias, y, M, K, splits, ws, kScratchBytes, stream);
+    case gemvplan::F16: return run_splitk<TF16>(A, lda, x, bias, y, M, K, splits, ws, kScratchBytes, stream);
+    case gemvplan::BF16: return run_splitk<TBF16>(A, lda, x, bias, y, M, K, splits, ws, kScratchBytes, stream);
+    default: return GEMV_ERROR_INVALID_VALUE;
+    }
 }
 
 gemv_status_t gemv_run_family(gemv_dtype_t dtype, int family, const void* A, int lda,

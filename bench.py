@@ -11,13 +11,16 @@ Cache defeat: ``R`` copies of A (and x, y) are allocated so that together
 they exceed twice the 256 MB Infinity Cache, and consecutive steps cycle
 through them, so every step streams its A from HBM.
 
-Timed region: ``--steps`` back-to-back calls issued as replays of a HIP graph
-that holds one launch per rotation set (host launch cost would otherwise
-exceed the ~5 µs kernel), bracketed by ``torch.cuda.synchronize()`` and a
-pair of HIP events on the launch stream.  ``value`` is algorithmic bytes ×
-steps ÷ elapsed; ``roofline.achieved`` divides the same bytes by the average
-launch duration over that region (graph replays leave no host gap, so it is
-the kernel's own duration, which rocprofv3's kernel trace confirms).  Also
+Timed region: exactly ``--steps`` calls through the C ABI, bracketed by
+``torch.cuda.synchronize()`` and a pair of HIP events on the launch stream.
+The calls are enqueued while untimed lead-in work (replays of a HIP graph of
+the same calls) keeps the GPU busy, after a warm-up of at least ``--warmup``
+launches and 0.25 s, so they run back to back with no host gap between them
+(host launch cost would otherwise exceed the ~5 µs kernel) and no graph
+replay cost (about 10 µs per replay on this runtime).  ``value`` is
+algorithmic bytes × steps ÷ elapsed; ``roofline.achieved`` divides the same
+bytes by the average launch duration over that region; rocprofv3's kernel
+trace of the same command gives the per-dispatch durations.  Also
 measured:
   * eager calls through the C ABI (one ctypes call per step);
   * µs/call, GB/s and GFLOP/s for every other configured shape, including
@@ -48,6 +51,12 @@ INFINITY_CACHE_BYTES = 256 << 20
 METRIC = "achieved HBM GB/s (% of 8 TB/s) for 4096x4096 bf16 GEMV; µs/call per shape"
 DEFAULT_WORKLOAD = "sweep_q"
 SHAPE_WARMUP = 1000                # launches before each per-shape timed loop
+# Before the timed region, graph replays run untimed for at least this long,
+# whatever --warmup says (--warmup launches are a lower bound): a run of 20
+# steps right after start-up read ~5 % slower than the same loop once the
+# GPU had been busy for a while.
+WARM_SECONDS = 0.25
+LEAD_LAUNCHES = 256              # untimed launches in flight when timing starts
 
 
 def log(*a):
@@ -313,6 +322,20 @@ class Q8Rotation:
         return worst <= 1.0, worst
 
 
+HOT_MAX_BYTES = 4 << 20   # shapes this small also get a cache-hot figure
+
+
+class HotRotation:
+    """Set 0 of a Rotation on every call: inputs stay in the caches."""
+
+    def __init__(self, rot):
+        self.rot = rot
+        self.R = 1
+
+    def callers(self, lg, stream_handle):
+        return self.rot.callers(lg, stream_handle)[:1]
+
+
 class ProbeRotation:
     """The read probe over the A buffers of a Rotation: every step streams
     one copy of A (no x, no output) with the GEMV kernels' access pattern."""
@@ -348,6 +371,7 @@ class ProbeVariantRotation:
 
 
 PROBE_SIZES = {"8MiB": 8 << 20, "32MiB": 32 << 20, "112MiB": 112 << 20}
+PROBE_ROUNDS = 5
 
 
 def probe_variants():
@@ -373,18 +397,27 @@ def probe_sweep(torch, lg, steps):
     `steps` launches over rotated buffers; and, for the GEMV pattern, the
     spread of wavefront finish times within one launch."""
     import numpy as np
-    result = {"steps": steps, "sizes": {}, "wave_finish": {}}
+    result = {"steps": steps, "rounds": PROBE_ROUNDS, "sizes": {}, "wave_finish": {}}
     for label, nbytes in PROBE_SIZES.items():
         rot = ProbeVariantRotation(torch, nbytes)
+        variants = probe_variants()
+        times = {v: [] for v in variants}
+        # rounds over all variants, so that drifts of the GPU's state spread
+        # over every variant alike; the median of the rounds is reported
+        for rnd in range(PROBE_ROUNDS):
+            for v in variants:
+                rot.variant = v
+                loop = GraphLoop(torch, rot, lg, steps, per=rot.R * max(1, 256 // rot.R))
+                times[v].append(1e3 * loop.time(warmup=min(steps, 500)) / steps)
+                del loop
+            log(f"probe {label}: round {rnd + 1} of {PROBE_ROUNDS} done")
         rows = []
-        for v in probe_variants():
-            rot.variant = v
-            loop = GraphLoop(torch, rot, lg, steps, per=rot.R * max(1, 256 // rot.R))
-            us = 1e3 * loop.time(warmup=min(steps, 500)) / steps
-            del loop
+        for v in variants:
+            us = statistics.median(times[v])
             rows.append({"loads_per_lane": v[0], "waves_per_group": v[1], "blocks_per_wave": v[2],
                          "cached": bool(v[3] & 1), "priority": bool(v[3] & 2),
                          "grid_stride": bool(v[3] & 4), "us": round(us, 3),
+                         "us_rounds": [round(t, 3) for t in times[v]],
                          "GBps": round(nbytes / us / 1e3, 1)})
             log(f"probe {label} {v}: {us:.3f} us, {nbytes / us / 1e3:.1f} GB/s")
         result["sizes"][label] = {"bytes": nbytes, "rotation_sets": rot.R, "variants": rows}
@@ -461,18 +494,78 @@ class GraphLoop:
         if self.tail is not None:
             self.tail.replay()
 
-    def time(self, warmup):
+    def warm(self, warmup, seconds=0.0):
+        """Untimed replays: at least `warmup` launches and `seconds` of
+        wall time; returns the launches run."""
         torch = self.torch
-        for _ in range(max(1, math.ceil(warmup / self.per))):
-            self.main.replay()
-        torch.cuda.synchronize()
+        n = 0
+        t_end = time.perf_counter() + seconds
+        while True:
+            for _ in range(max(1, math.ceil(warmup / self.per))):
+                self.main.replay()
+                n += self.per
+            torch.cuda.synchronize()
+            if time.perf_counter() >= t_end:
+                return n
+            warmup = max(warmup, 100 * self.per)
+
+    def time(self, warmup, seconds=0.0):
+        torch = self.torch
+        self.warm_launches = self.warm(warmup, seconds)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        # untimed lead-in replays keep the GPU busy while the host submits the
+        # start event and the timed graphs, so the timed launches run back to
+        # back from the start event on (recorded on an idle GPU, the graphs'
+        # submission latency would land inside a short timed region)
+        for _ in range(max(1, math.ceil(LEAD_LAUNCHES / self.per))):
+            self.main.replay()
         e0.record()
         self.run()
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
+
+
+def time_queued(torch, loop, fns, steps, warmup, seconds):
+    """Exactly `steps` launches through the C ABI (one ctypes call each),
+    enqueued while untimed graph replays keep the GPU busy, bracketed by an
+    event pair on the launch stream: the launches run back to back with no
+    host gap and no graph-replay cost between them.  (A graph replay costs
+    about 10 µs of its own on this runtime: a short timed region of one
+    replayed graph read ~0.5 µs per launch slower.)  Returns (ms, lead
+    launches, whether the queue stayed ahead of the GPU)."""
+    loop.warm(warmup, seconds)
+    # per-launch GPU time and host cost per call, to size the lead-in
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    loop.main.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    gpu_us = 1e3 * e0.elapsed_time(e1) / loop.per
+    t0 = time.perf_counter()
+    for i in range(64):
+        call(fns[i % len(fns)])
+    host_us = 1e6 * (time.perf_counter() - t0) / 64
+    torch.cuda.synchronize()
+    lead = max(LEAD_LAUNCHES, math.ceil(4 * steps * host_us / max(gpu_us, 1e-3)))
+    replays = math.ceil(lead / loop.per)
+    ea = torch.cuda.Event(enable_timing=True)
+    ea.record()
+    for _ in range(replays):
+        loop.main.replay()
+    e0.record()
+    t_submit = time.perf_counter()
+    for i in range(steps):
+        call(fns[i % len(fns)])
+    t_submit = time.perf_counter() - t_submit
+    e1.record()
+    torch.cuda.synchronize()
+    # the lead-in's GPU time must have outlasted the host's submission of
+    # the timed launches, or the GPU went idle inside the timed region
+    lead_ms = ea.elapsed_time(e0)
+    return e0.elapsed_time(e1), replays * loop.per, 1e3 * t_submit < lead_ms
 
 
 def time_eager(torch, fns, steps, warmup):
@@ -570,6 +663,14 @@ def measure_shape(name, torch, lg, gi, steps):
             plan = lg.plan(case.dtype, case.M, case.K, case.lda, case.nvec,
                            rot.A[0].data_ptr(), rot.X[0].data_ptr())
             family = lg.FAMILY_NAMES[plan["family"]]
+    hot_us = None
+    if not fused and not q8 and not rot.splitk and case.algorithmic_bytes() <= HOT_MAX_BYTES:
+        # the same buffers on every call (the caches stay warm), as the
+        # SGEMV page's timing loop does
+        hot = HotRotation(rot)
+        hloop = GraphLoop(torch, hot, lg, steps, per=256)
+        hot_us = round(1e3 * hloop.time(warmup=SHAPE_WARMUP) / steps, 3)
+        del hloop, hot
     single_us = None
     if not fused and not q8 and rot.splitk:  # the same problem in one pass, for comparison
         rot.splitk = False
@@ -592,6 +693,8 @@ def measure_shape(name, torch, lg, gi, steps):
         "frac_of_8TBps": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
         "GFLOPps": round(flops / us / 1e3, 1),
         **({"us_per_call_single_pass": single_us} if single_us is not None else {}),
+        **({"us_per_call_graph_hot": hot_us,
+            "GBps_hot": round(nbytes / hot_us / 1e3, 1)} if hot_us is not None else {}),
     }
 
 
@@ -677,21 +780,31 @@ def main():
     if not ok:
         sys.exit(1)
 
-    # timed region: graph replays, exactly --steps launches
+    # timed region: exactly --steps launches through the C ABI, queued behind
+    # untimed lead-in work, after at least --warmup launches and WARM_SECONDS
+    # of untimed replays
+    fns = rot.callers(lg, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
-    ms, launches = loop.time(args.warmup), args.steps
+    ms, lead_launches, queue_ahead = time_queued(torch, loop, fns, args.steps, args.warmup,
+                                                 WARM_SECONDS)
+    launches = args.steps
     nbytes = case.algorithmic_bytes()
     us_step = 1e3 * ms / launches
     value = nbytes / us_step / 1e3  # GB/s
-    log(f"graph: {launches} launches in {ms:.3f} ms -> {us_step:.3f} us/step, {value:.1f} GB/s")
+    log(f"queued: {launches} launches in {ms:.3f} ms -> {us_step:.3f} us/step, {value:.1f} GB/s "
+        f"(lead-in {lead_launches} launches; queue ahead of the GPU: {queue_ahead})")
+    graph_ms = loop.time(args.warmup)
+    log(f"graph replays: {1e3 * graph_ms / launches:.3f} us/step")
 
-    fns = rot.callers(lg, torch.cuda.current_stream().cuda_stream)
     eager_ms = time_eager(torch, fns, args.steps, args.warmup)
     log(f"eager: {1e3 * eager_ms / args.steps:.3f} us/step")
-    # Average launch duration over the timed region.  Graph replays leave no
-    # host gap between launches, so this is the kernel's own duration (it
-    # agrees with rocprofv3's kernel trace); an event pair around a single
-    # launch would add the events' own ~2 us.
+    # Average launch duration over the timed region, from the event pair on
+    # the launch stream: graph replays leave no host gap between launches,
+    # so this is the launches' own back-to-back duration (each includes the
+    # runtime's fixed cost between dependent kernels); the committed
+    # rocprofv3 kernel trace of the same command gives the per-dispatch
+    # durations.  An event pair around a single launch would add the events'
+    # own ~2 us.
     k_mean = us_step
     achieved = nbytes / k_mean / 1e3
 
@@ -775,8 +888,13 @@ def main():
                         f"accumulate and output, no bias ({args.workload})",
             "M": case.M, "K": case.K, "nvec": case.nvec,
             "family": lg.FAMILY_NAMES[plan["family"]],
-            "timing": "HIP graph replays of back-to-back launches; event pair on the launch stream",
+            "timing": ("back-to-back launches through the C ABI, queued behind untimed lead-in "
+                       "work (graph replays) after a warm-up of at least 0.25 s; event pair on "
+                       "the launch stream"),
+            "lead_in_launches": lead_launches,
+            "queue_stayed_ahead": queue_ahead,
             "us_per_call": round(us_step, 3),
+            "us_per_call_graph_replays": round(1e3 * graph_ms / launches, 3),
             "us_per_call_eager": round(1e3 * eager_ms / args.steps, 3),
             "frac_of_8TBps": round(value / HBM_PEAK_GBS, 4),
         },
@@ -788,7 +906,9 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_bytes,
             "traffic_note": traffic_note,
-            "kernel_us_mean": round(k_mean, 3),
+            "us_per_launch_events": round(k_mean, 3),
+            "us_per_launch_what": "mean over the timed region of back-to-back launches, HIP "
+                                  "events on the launch stream",
             "bytes_per_launch": nbytes,
         },
         "cpu_baseline": cpu,

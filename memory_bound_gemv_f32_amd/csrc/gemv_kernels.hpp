@@ -812,7 +812,8 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     __shared__ quad xs[W][kCols * kColQuads];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // uniform: the wavefront's step range, chunk count and folds are scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15;  // operand row (A) / column within a tile (X)
     const int g = lane >> 4;  // 8-element group within a 32-element half-step
     const int half = r & 1;
@@ -856,28 +857,37 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
 #pragma unroll
             for (int t = 0; t < NT; ++t) v[q][t][0] = v[q][t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
+    int folds = 0;  // chunks added to the totals so far (uniform)
     auto fold = [&]() {
         if constexpr (FRESH) {
+            if (folds == 0) {  // the first chunk is the total
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
+                for (int q = 0; q < 2; ++q)
 #pragma unroll
-                for (int t = 0; t < NT; ++t)
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const f32x4 a = acc[q][t][h], s = tot[q][t][h];
-                        const f32x4 sum = s + a;
-                        const f32x4 z = sum - s;
-                        cmp[q][t][h] += (s - (sum - z)) + (a - z);
-                        tot[q][t][h] = sum;
+                    for (int t = 0; t < NT; ++t) {
+                        tot[q][t][0] = acc[q][t][0];
+                        tot[q][t][1] = acc[q][t][1];
                     }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const f32x4 a = acc[q][t][h], s = tot[q][t][h];
+                            const f32x4 sum = s + a;
+                            const f32x4 z = sum - s;
+                            cmp[q][t][h] += (s - (sum - z)) + (a - z);
+                            tot[q][t][h] = sum;
+                        }
+            }
+            ++folds;
             clear(acc);
         }
     };
     clear(acc);
-    if constexpr (FRESH) {
-        clear(tot);
-        clear(cmp);
-    }
+    if constexpr (FRESH) clear(cmp);  // tot is set by the first fold
     int c = rg.first;
     if constexpr (FEW) {
         // X operands straight from memory: lane (column r, group g)
@@ -971,6 +981,7 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     const S* xq[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) xq[t] = X + (int64_t)(16 * t + r < nvec ? 16 * t + r : 0) * K + 8 * g;
+    const int c_left = c;
 #pragma unroll 1
     for (; c < rg.end; ++c) {
         const int e = c * 64;
@@ -992,14 +1003,24 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
         }
     }
 
-    fold();
+    if (c > c_left) fold();  // the leftover steps, if any ran
     if constexpr (FRESH) {
+        if (folds > 1) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+            for (int q = 0; q < 2; ++q)
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
+                for (int t = 0; t < NT; ++t)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) acc[q][t][h] = tot[q][t][h] + cmp[q][t][h];
+                    for (int h = 0; h < 2; ++h) acc[q][t][h] = tot[q][t][h] + cmp[q][t][h];
+        } else if (folds == 1) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    acc[q][t][0] = tot[q][t][0];
+                    acc[q][t][1] = tot[q][t][1];
+                }
+        }  // no steps: acc is zero
     }
 
     // lane (column j, group g) holds operand rows 4g .. 4g+3, i.e. real rows

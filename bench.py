@@ -84,6 +84,10 @@ def parse():
                          "workgroup, blocks per wavefront, cached/nontemporal, priority) over "
                          "rotated buffers of 8, 32 and 112 MiB, and the per-wavefront finish "
                          "times of the GEMV's own pattern; prints one JSON object")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="CPU only: per-kernel duration statistics of a rocprofv3 --kernel-trace "
+                         "output directory (all dispatches, and the last --steps of each kernel: "
+                         "the timed region of a --kernel-only run); prints one JSON object")
     ap.add_argument("--counters", action="store_true",
                     help="for rocprofv3 --pmc runs: a few eager launches of --workload over the "
                          "rotated buffers, then a plain device copy of COPY_BYTES for scaling")
@@ -129,6 +133,33 @@ def summarize_counters(fetch_dir, write_dir, workload):
         out[f"{key}_scale"] = scale
         out[f"{key}_bytes_per_launch"] = sum(gemv) / len(gemv) * 1024 * scale
     out["traffic_bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
+    return out
+
+
+def summarize_trace(trace_dir, steps):
+    """Duration statistics (ns) per kernel from rocprofv3's kernel trace:
+    over every dispatch, and over each kernel's last `steps` dispatches (in
+    a --kernel-only run, its timed region)."""
+    import csv
+    import numpy as np
+    rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))))
+    by = {}
+    for r in rows:
+        d = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        by.setdefault(r["Kernel_Name"], []).append((int(r["Start_Timestamp"]), d))
+
+    def stats(d):
+        d = np.asarray(d, dtype=np.float64)
+        return {"calls": int(d.size), "mean": round(float(d.mean()), 1),
+                "p10": round(float(np.percentile(d, 10)), 1),
+                "p50": round(float(np.percentile(d, 50)), 1),
+                "p90": round(float(np.percentile(d, 90)), 1),
+                "min": round(float(d.min()), 1), "max": round(float(d.max()), 1)}
+    out = {}
+    for name, v in by.items():
+        v.sort()
+        d = [x[1] for x in v]
+        out[name] = {"all": stats(d), "last": stats(d[-steps:])}
     return out
 
 
@@ -724,6 +755,9 @@ def cpu_baseline(case, seconds):
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        print(json.dumps(summarize_trace(args.summarize_trace, args.steps), indent=1))
+        return
     if args.summarize_counters:
         t = summarize_counters(*args.summarize_counters, args.workload)
         os.makedirs(PROFILES, exist_ok=True)
@@ -755,12 +789,14 @@ def main():
         return
 
     if args.kernel_only:
-        # only the timed graph loop of one named shape (for profilers)
+        # only the timed region of one named shape (for profilers), timed as
+        # the headline is: launches queued behind lead-in work after a warm-up
         krot = rotation_for(args.workload, gi, torch)
         kloop = GraphLoop(torch, krot, lg, args.steps, per=krot.R * max(1, 256 // krot.R))
-        ms = kloop.time(args.warmup)
+        kfns = krot.callers(lg, torch.cuda.current_stream().cuda_stream)
+        ms, lead, ahead = time_queued(torch, kloop, kfns, args.steps, args.warmup, WARM_SECONDS)
         log(f"kernel-only {args.workload}: {args.steps} launches, {1e3 * ms / args.steps:.3f} us "
-            f"per launch")
+            f"per launch (queue ahead of the GPU: {ahead})")
         return
 
     case = gi.make_workload(args.workload)
@@ -810,10 +846,13 @@ def main():
 
     plan = lg.plan(case.dtype, case.M, case.K, case.lda, case.nvec,
                    rot.A[0].data_ptr(), rot.X[0].data_ptr())
-    # the practical ceiling: the same A buffers streamed by the read probe
+    # the practical ceiling: the same A buffers streamed by the read probe,
+    # timed the same way as the GEMV
     probe = ProbeRotation(rot, torch)
     ploop = GraphLoop(torch, probe, lg, args.steps, per=rot.R * max(1, 256 // rot.R))
-    probe_us = 1e3 * ploop.time(args.warmup) / args.steps
+    pfns = probe.callers(lg, torch.cuda.current_stream().cuda_stream)
+    probe_ms, _, _ = time_queued(torch, ploop, pfns, args.steps, args.warmup, WARM_SECONDS)
+    probe_us = 1e3 * probe_ms / args.steps
     a_bytes = case.A.nbytes
     read_probe = {
         "bytes": a_bytes, "us": round(probe_us, 3),

@@ -47,9 +47,9 @@
  * call only enqueues its kernel on `stream` (NULL = the null stream; split-K
  * enqueues two) and returns.  y/Y must not overlap A, x/X or bias.  Pointers must be aligned
  * to their element size; any further alignment is optional (16-byte aligned
- * A and x select the widest loads, for any row pitch with one vector; with
- * several vectors the row pitch lda·element_size must be a multiple of 16
- * bytes as well).
+ * A and x/X select the widest loads, for any row pitch and K; the matrix
+ * cores, for several vectors, also need lda·element_size and K·element_size
+ * to be multiples of 16 bytes and K % 8 == 0).
  *
  * Errors.  Every entry point validates its arguments before touching the
  * GPU.  GEMV_ERROR_INVALID_VALUE (nothing enqueued, y untouched) for:

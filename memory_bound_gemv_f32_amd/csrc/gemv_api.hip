@@ -262,7 +262,8 @@ const void* single_fn(const Plan& p) {
 template <class D, int NV, bool VEC>
 const void* batched_fn_nv() {
     return (const void*)&gemvdev::gemv_batched_kernel<D, NV, gemvplan::batched_rows(NV),
-                                                      gemvplan::kBatchedBatch, VEC>;
+                                                      gemvplan::batched_batch(NV),
+                                                      gemvplan::batched_x_ahead(NV), VEC>;
 }
 
 template <class D, bool VEC>
@@ -456,11 +457,11 @@ gemv_status_t run_single(const Plan& p, const void* A, int lda, const void* X, c
                 return GEMV_ERROR_INVALID_VALUE;
             const void* fn = batched_kernel<D>(pb, nv);
             if (fn == nullptr) return GEMV_ERROR_INVALID_VALUE;
-            int64_t lda64 = lda;
+            int64_t lda64 = lda, M64 = M;
             const S* Xb = static_cast<const S*>(X) + (int64_t)j0 * K;
             float* Yb = Y + (int64_t)j0 * M;
             void* argv[] = {(void*)&A, (void*)&lda64, (void*)&Xb, (void*)&bias, (void*)&Yb,
-                            (void*)&M, (void*)&K, (void*)&nv};
+                            (void*)&M64, (void*)&K};
             const gemv_status_t st = finish(launch(fn, pb, stream, argv));
             if (st != GEMV_SUCCESS) return st;
         }

@@ -631,116 +631,137 @@ gemv_splitk_reduce_kernel(const float* __restrict__ ws, int splits, const float*
     if (lane == 0) y[m] = acc + (bias != nullptr ? bias[m] : 0.f);
 }
 
-// Batched kernel: Y = A·X (+ bias) for NV right-hand vectors with one pass
-// over A.  A wavefront owns RB consecutive rows; its lanes walk the chunks of
-// those rows with stride 64, and every A chunk is multiplied against the
-// same chunk of all NV columns of X (X is K×NV column-major and stays in the
-// caches).  RB·NV fp32 accumulators per lane, one 64-lane reduction each, and
-// lane 0 writes the RB·NV outputs.
-template <class D, int NV, int RB, int BATCH, bool VEC>
-__global__ void __launch_bounds__(kRowsWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
+// Batched kernel on the vector ALUs: Y = A·X (+ bias) for NV right-hand
+// vectors with one pass over A, the wave-per-row mapping with several
+// vectors.  A wavefront owns U consecutive rows; its 64 lanes walk the rows'
+// chunks with stride 64, B chunks per lane per batch.  Every chunk of X is
+// loaded once per wavefront and meets the matching chunk of all U rows
+// (X is K×NV column-major: column j at X + j·K, read through the caches).
+// With XAHEAD the X chunks of a batch are loaded with its A chunks (all in
+// flight together); otherwise (many vectors, whose X chunks would not fit
+// the registers) each chunk's X loads follow the batch's A loads.  The
+// arithmetic is the single-vector path's: exactly widened elements, IEEE
+// fp32 FMA in element order into a fresh accumulator per (row, vector) per
+// batch, added to a compensated running sum.  Then one 64-lane reduction
+// per (row, vector) and lane u·NV + j writes Y[j·M + row u] (+ bias).  16-byte
+// loads take any row pitch and K (rows and X columns start at
+// element-aligned addresses: unaligned global loads).
+template <class D, int NV, int U, int B, bool XAHEAD, bool VEC>
+__global__ void __launch_bounds__(kRowsWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
                     const typename D::storage* __restrict__ X,
                     const float* __restrict__ bias, float* __restrict__ Y,
-                    int M, int K) {
+                    int64_t M, int K) {
     using S = typename D::storage;
     using C = Chunk<D, VEC>;
     using CT = typename C::type;
     constexpr int E = C::elems;
+    static_assert(U * NV <= 64, "one writer lane per (row, vector)");
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t row0 = ((int64_t)blockIdx.x * kRowsWaves + wave) * RB;
-
-    const S* rp[RB];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t row0 = ((int64_t)blockIdx.x * kRowsWaves + wave) * U;
+    const S* rp[U];
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-        const int64_t m = row0 + r;
-        rp[r] = A + (m < M ? m : (int64_t)M - 1) * lda;
+    for (int u = 0; u < U; ++u) {
+        const int64_t m = row0 + u;
+        rp[u] = A + (m < M ? m : M - 1) * lda;
     }
+    const S* xp[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) xp[j] = X + (int64_t)j * K;
 
-    // each lane sums kBatchedGroup of its chunks into fresh accumulators,
-    // then adds them to its compensated running sums (a bounded rounding
-    // chain whatever K)
-    Sum2 sum[RB][NV];
+    Sum2 sum[U][NV];
 #pragma unroll
-    for (int r = 0; r < RB; ++r)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int j = 0; j < NV; ++j) sum[r][j] = Sum2{0.f, 0.f};
+        for (int j = 0; j < NV; ++j) sum[u][j] = Sum2{0.f, 0.f};
 
     const int nfull = K / E;
-    constexpr int kGroup = gemvplan::kBatchedGroup * 64;  // chunks per group of the wavefront
-#pragma unroll 1
-    for (int g0 = 0; g0 < nfull; g0 += kGroup) {
-    float acc[RB][NV];
+    auto batch = [&](int c0, bool check) {
+        CT a[U][B];
+        CT xa[XAHEAD ? NV : 1][B];
 #pragma unroll
-    for (int r = 0; r < RB; ++r)
+        for (int i = 0; i < B; ++i) {
+            int c = c0 + i * 64 + lane;
+            c = (check && c >= nfull) ? nfull - 1 : c;
 #pragma unroll
-        for (int j = 0; j < NV; ++j) acc[r][j] = 0.f;
-    const int gend = g0 + kGroup < nfull ? g0 + kGroup : nfull;
-#pragma unroll 1
-    for (int c0 = g0; c0 < gend; c0 += BATCH * 64) {
-        CT a[RB][BATCH];
-        bool ok[BATCH];
-        int cc[BATCH];
+            for (int u = 0; u < U; ++u) a[u][i] = C::stream(rp[u], c);
+            if constexpr (XAHEAD)
 #pragma unroll
-        for (int i = 0; i < BATCH; ++i) {
-            const int c = c0 + i * 64 + lane;
-            ok[i] = c < nfull;
-            cc[i] = ok[i] ? c : nfull - 1;
-#pragma unroll
-            for (int r = 0; r < RB; ++r) a[r][i] = C::stream(rp[r], cc[i]);
+                for (int j = 0; j < NV; ++j) xa[j][i] = C::load(xp[j], c);
         }
-        __builtin_amdgcn_sched_barrier(0);  // A loads in flight before X is fetched
+        __builtin_amdgcn_sched_barrier(0);  // the batch's loads in flight first
+        float acc[U][NV];
 #pragma unroll
-        for (int i = 0; i < BATCH; ++i) {
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < NV; ++j) acc[u][j] = 0.f;
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+            const int c = c0 + i * 64 + lane;
+            const bool ok = !check || c < nfull;
+            CT ai[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) ai[u] = C::keep_a(ok, a[u][i]);
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
-                CT xv = C::load(X + (int64_t)j * K, cc[i]);
-                xv = ok[i] ? xv : C::zero();
+                CT xv;
+                if constexpr (XAHEAD)
+                    xv = xa[j][i];
+                else
+                    xv = C::load(xp[j], ok ? c : nfull - 1);
+                xv = C::keep_x(ok, xv);
 #pragma unroll
-                for (int r = 0; r < RB; ++r) {
-                    const CT ar = ok[i] ? a[r][i] : C::zero();
-                    acc[r][j] = C::dot2(ar, xv, acc[r][j]);
-                }
+                for (int u = 0; u < U; ++u) acc[u][j] = C::dot(ai[u], xv, acc[u][j]);
             }
+            // X loaded chunk by chunk: one chunk's X operands live at a time
+            if constexpr (!XAHEAD) __builtin_amdgcn_sched_barrier(0);
         }
-    }
 #pragma unroll
-    for (int r = 0; r < RB; ++r)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int j = 0; j < NV; ++j) sum[r][j].add(acc[r][j]);
-    }
+            for (int j = 0; j < NV; ++j) sum[u][j].add(acc[u][j]);
+    };
+    const int nsafe = nfull - nfull % (B * 64);
+    int c0 = 0;
+#pragma unroll 1
+    for (; c0 < nsafe; c0 += B * 64) batch(c0, false);
+    if (c0 < nfull) batch(c0, true);
     if constexpr (VEC) {
-        float tail[RB][NV];
+        // elements past the last whole chunk (fewer than E of them)
+        float tail[U][NV];
 #pragma unroll
-        for (int r = 0; r < RB; ++r)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int j = 0; j < NV; ++j) tail[r][j] = 0.f;
+            for (int j = 0; j < NV; ++j) tail[u][j] = 0.f;
         for (int k = nfull * E + lane; k < K; k += 64) {
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
-                const float xe = widen(D{}, X[(int64_t)j * K + k]);
+                const float xe = widen(D{}, xp[j][k]);
 #pragma unroll
-                for (int r = 0; r < RB; ++r)
-                    tail[r][j] = __builtin_fmaf(widen(D{}, rp[r][k]), xe, tail[r][j]);
+                for (int u = 0; u < U; ++u) tail[u][j] = __builtin_fmaf(widen(D{}, rp[u][k]), xe, tail[u][j]);
             }
         }
 #pragma unroll
-        for (int r = 0; r < RB; ++r)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int j = 0; j < NV; ++j) sum[r][j].add(tail[r][j]);
+            for (int j = 0; j < NV; ++j) sum[u][j].add(tail[u][j]);
     }
 
+    // every lane holds every total after the reductions; lane u·NV + j writes
+    float out = 0.f;
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-        const int64_t m = row0 + r;
-        const float b = (bias != nullptr && m < M) ? bias[m] : 0.f;
+    for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-            const float v = segment_sum<64>(sum[r][j].value());
-            if (lane == 0 && m < M) Y[(int64_t)j * M + m] = v + b;
+            const float v = segment_sum<64>(sum[u][j].value());
+            out = lane == u * NV + j ? v : out;
         }
+    if (lane < U * NV) {
+        const int u = lane / NV, j = lane % NV;
+        const int64_t m = row0 + u;
+        if (m < M) Y[(int64_t)j * M + m] = out + (bias != nullptr ? bias[m] : 0.f);
     }
 }
 

@@ -74,6 +74,14 @@ constexpr int kGroupWideWaves = 16;
 constexpr int kGroupWidePairWaves = 8;
 constexpr int64_t kGroupWideMaxRows = 1024;
 constexpr int64_t kGroupMaxRows = 256;
+// Rows of at least kGroupMidMinLoads loads (every lane of a workgroup busy)
+// take a workgroup each up to kGroupMidRows rows.  MI355X, bf16, µs, wave /
+// workgroup per row: 384 × 4096 2.86 / 2.62, 512 × 4096 2.88 / 2.73, 640 ×
+// 4096 2.99 / 2.93, 768 × 4096 3.03 / 3.05, 896 × 4096 3.12 / 3.24, 1024 ×
+// 4096 3.20 / 3.37; 384 × 2048 2.37 / 2.30, 640 × 2048 2.48 / 2.47, 768 ×
+// 2048 2.55 / 2.54, 896 × 2048 2.62 / 2.63.
+constexpr int64_t kGroupMidRows = 704;
+constexpr int64_t kGroupMidMinLoads = 256;
 constexpr int64_t kGroupLongRowLoads = 1024;
 constexpr int64_t kGroupManyRows = 6144;
 constexpr int64_t kGroupManyRowsMinLoads = 512;
@@ -110,14 +118,15 @@ constexpr int64_t kGroupStreamMinXBytes = 8 * 1024;
 constexpr int kGroupStreamWaves = 4;
 constexpr int kGroupStreamMaxChunks = 6;
 constexpr int kGroupStreamRows = 4;
-// Batched family: loads in flight per row, and rows per wavefront, fewer as
-// the number of vectors grows so that rows × vectors accumulators plus the
-// loaded chunks fit the register budget of four wavefronts per SIMD; a lane
-// sums kBatchedGroup of its chunks (4 chained v_dot2 each) into fresh
-// accumulators before adding them to its compensated running sums.
-constexpr int kBatchedBatch = 1;
-constexpr int kBatchedGroup = 2;
-constexpr int batched_rows(int nvec) { return nvec <= 2 ? 4 : (nvec <= 4 ? 2 : 1); }
+// Batched family on the vector ALUs (a wavefront per group of rows, all
+// vectors at once): rows per wavefront (they share every X chunk), loads of
+// A per lane per batch, and whether a batch's X chunks are loaded with its A
+// chunks (few vectors) or chunk by chunk after them (many: their X chunks
+// would not fit the registers), chosen so that the loaded chunks, the
+// accumulators and the compensated sums fit two wavefronts per SIMD.
+constexpr int batched_rows(int nvec) { return nvec <= 4 ? 2 : 1; }
+constexpr int batched_batch(int nvec) { return nvec <= 2 ? 4 : 2; }
+constexpr bool batched_x_ahead(int nvec) { return nvec <= 8; }
 // Matrix-core batched family: 16 rows per workgroup, its wavefronts split K
 // and walk their slice in chunks of this many 64-wide steps (the A loads of a
 // chunk are in flight together; X's chunk is staged in LDS).
@@ -363,21 +372,24 @@ inline bool vector_ok_q8(int ldq, uintptr_t Q, uintptr_t x) {
     return Q % kLoadBytes == 0 && x % kLoadBytes == 0;
 }
 
-// 16-byte loads need 16-byte aligned A and x.  With one vector the row pitch
-// may leave rows unaligned: the chunk loads take element-aligned addresses,
-// and one unaligned 16-byte load beats eight element loads (MI355X, bf16
-// 4096 × 4100 9.64 -> 6.98 µs, 384 × 43690 12.88 -> 8.97, 6144 × 2730
-// 9.14 -> 7.01; fp32 4096 × 4097 13.97 -> 12.06; only where few rows leave
-// CUs idle is it no faster: bf16 192 × 87381 12.25 -> 12.63).  Several
-// vectors also need the pitch and every X column aligned (the matrix-core
-// kernel reads whole aligned operand rows).
+// 16-byte loads need 16-byte aligned A and x (or X).  The row pitch and K
+// may leave rows and X columns unaligned: the chunk loads take
+// element-aligned addresses, and one unaligned 16-byte load beats eight
+// element loads (MI355X, bf16 4096 × 4100 9.64 -> 6.98 µs, 384 × 43690
+// 12.88 -> 8.97, 6144 × 2730 9.14 -> 7.01; fp32 4096 × 4097 13.97 -> 12.06;
+// only where few rows leave CUs idle is it no faster: bf16 192 × 87381
+// 12.25 -> 12.63).
 inline bool vector_ok(int dtype, int K, int lda, int nvec, uintptr_t A, uintptr_t X) {
+    (void)dtype, (void)K, (void)lda, (void)nvec;
+    return A % kLoadBytes == 0 && X % kLoadBytes == 0;
+}
+
+// The matrix-core batched kernel reads whole aligned 16-byte operand rows:
+// A and X aligned, and the row pitch and K whole 16-byte units.
+inline bool mfma_rows_ok(int dtype, int K, int lda, uintptr_t A, uintptr_t X) {
     const int64_t s = element_bytes(dtype);
-    if (A % kLoadBytes != 0 || X % kLoadBytes != 0) return false;
-    if (nvec == 1) return true;
-    if (((int64_t)lda * s) % kLoadBytes != 0) return false;
-    if (nvec > 1 && ((int64_t)K * s) % kLoadBytes != 0) return false;
-    return true;
+    return A % kLoadBytes == 0 && X % kLoadBytes == 0 && ((int64_t)lda * s) % kLoadBytes == 0 &&
+           ((int64_t)K * s) % kLoadBytes == 0;
 }
 
 // Plan for a problem whose 16-byte-load eligibility `vec` the caller has
@@ -396,9 +408,13 @@ inline bool stream_fits(int dtype, int64_t M, int64_t K, bool vec, int max_group
     return chunks <= kGroupStreamMaxChunks && ceil_div(M, 2) >= kGroupTileMinGroups;
 }
 
+// `vec`: 16-byte loads of A and x (or X) are possible; `mfma_rows`: with
+// several vectors, also every row and X column starts 16-byte aligned (the
+// matrix-core kernel reads aligned operand rows).
 inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family, Plan* out,
                          int max_row_tiles = 8, int max_group_rows = kGroupStreamRows,
-                         int max_wave_tiles = kWaveBatch, int max_group_waves = kGroupWideWaves) {
+                         int max_wave_tiles = kWaveBatch, int max_group_waves = kGroupWideWaves,
+                         bool mfma_rows = false) {
     if (dtype < F32 || dtype > Q8 || M < 0 || K < 0 || nvec < 1 || nvec > kMaxVectors)
         return INVALID;
 
@@ -412,7 +428,7 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
 
     // the matrix-core kernel reads every 8-element group of a row with one
     // aligned 16-byte load
-    const bool mfma_ok = dtype != F32 && p.vector_loads && K % 8 == 0;
+    const bool mfma_ok = dtype != F32 && p.vector_loads && mfma_rows && K % 8 == 0;
 
     int fam = family;
     const bool long_or_many = loads >= kGroupLongRowLoads ||
@@ -423,6 +439,7 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         else if (loads <= kRowsPerWaveMaxLanes)
             fam = ROWS_PER_WAVE;
         else if (M <= kGroupMaxRows || long_or_many ||
+                 (M <= kGroupMidRows && loads >= kGroupMidMinLoads) ||
                  stream_fits(dtype, M, K, p.vector_loads != 0, max_group_rows))
             fam = GROUP_PER_ROW;
         else
@@ -575,7 +592,7 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         p.lanes_per_row = kWave;
         p.rows_per_wave = batched_rows(nvec);
         p.waves_per_group = kBlock / kWave;
-        p.batch = kBatchedBatch;
+        p.batch = batched_batch(nvec);
         p.row_tiles = 1;
         break;
     case GATED_SILU: {
@@ -639,10 +656,9 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         break;
     }
     case BATCHED:
+        // one fresh accumulator per (row, vector) per batch, FMA per element
         p.column_blocks = (int)ceil_div(nvec_all, (int64_t)kValuVectors);
-        // a 16-byte chunk is 4 chained v_dot2 (8 elements), an element one FMA
-        chain = valu_chain(K, p.chunk_elems, kWave, kWave, kBatchedGroup, 1,
-                           p.vector_loads ? (kDot2Roundings + 1) / 2 : 1, 1) + 1;
+        chain = valu_chain(K, p.chunk_elems, kWave, kWave, p.batch, 1, 1, 1) + 1;
         break;
     default:
         if (p.x_in_registers)  // one batch per row, no running sum
@@ -754,7 +770,9 @@ inline int make_split_plan(int dtype, int M, int K, bool vec, int requested, Pla
 inline int make_plan(int dtype, int M, int K, int lda, int nvec, uintptr_t A, uintptr_t X,
                      int family, Plan* out) {
     if (lda < K) return INVALID;
-    return make_plan_vec(dtype, M, K, nvec, vector_ok(dtype, K, lda, nvec, A, X), family, out);
+    return make_plan_vec(dtype, M, K, nvec, vector_ok(dtype, K, lda, nvec, A, X), family, out, 8,
+                         kGroupStreamRows, kWaveBatch, kGroupWideWaves,
+                         mfma_rows_ok(dtype, K, lda, A, X));
 }
 
 }  // namespace gemvplan

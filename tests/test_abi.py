@@ -178,7 +178,8 @@ def test_wavefront_batches_fit_the_row():
                                ("bf16", 4096, 3072, 6), ("bf16", 300, 5120, 5),
                                ("bf16", 300, 1000, 2), ("f32", 4096, 1024, 4),
                                ("bf16", 300, 8184, 8), ("bf16", 300, 7000, 7)):
-        q = p(dtype, M, K)
+        # (300 rows of 256 loads or more take a workgroup each automatically)
+        q = p(dtype, M, K, family=lg.FAMILY_WAVE_PER_ROW if M == 300 else lg.FAMILY_AUTO)
         assert (q["family"], q["batch"]) == (lg.FAMILY_WAVE_PER_ROW, batch), (dtype, M, K)
         loads = -(-K // q["chunk_elems"])
         per_lane = -(-loads // 64)
@@ -202,7 +203,14 @@ def test_few_long_rows_get_a_workgroup_each():
     q = p("bf16", 256, 4096)
     assert q["family"] == lg.FAMILY_GROUP_PER_ROW
     assert q["grid"] == 256 and q["block"] == 256 and q["rows_per_group"] == 1
-    # 1024 rows already give every CU several wavefronts
+    # rows of at least 256 loads keep a workgroup each up to 704 rows
+    for M in (257, 384, 512, 704):
+        assert p("bf16", M, 4096)["family"] == lg.FAMILY_GROUP_PER_ROW, M
+        assert p("bf16", M, 2048)["family"] == lg.FAMILY_GROUP_PER_ROW, M
+    # shorter rows (some lanes of a workgroup would idle) and more rows: a
+    # wavefront per row; 1024 rows already give every CU several wavefronts
+    assert p("bf16", 512, 1024)["family"] == lg.FAMILY_WAVE_PER_ROW
+    assert p("bf16", 705, 4096)["family"] == lg.FAMILY_WAVE_PER_ROW
     assert p("bf16", 1024, 4096)["family"] == lg.FAMILY_WAVE_PER_ROW
 
 
@@ -238,7 +246,10 @@ def test_unaligned_rows_keep_16_byte_loads():
                              ("f16", 4096, 4100, 4100), ("bf16", 6144, 2730, 2731)):
         q = p(dtype, M, K, lda=lda)
         assert q["vector_loads"] == 1 and q["chunk_elems"] == 16 // (4 if dtype == "f32" else 2)
-    assert p("f16", 4096, 4100, nvec=4)["vector_loads"] == 0
+    # several vectors on unaligned rows: the vector-ALU batched family, still
+    # with 16-byte loads (the matrix cores need aligned operand rows)
+    q = p("f16", 4096, 4100, nvec=4)
+    assert q["family"] == lg.FAMILY_BATCHED and q["vector_loads"] == 1
 
 
 def test_batched_plans():
@@ -256,7 +267,8 @@ def test_batched_plans():
         p("f32", 4096, 4096, nvec=1, family=lg.FAMILY_BATCHED_MFMA)
     q1 = p("f16", 4096, 4096, nvec=1)
     assert q1["family"] != lg.FAMILY_BATCHED   # nvec 1 is plain GEMV
-    assert p("f16", 4096, 4095, nvec=4)["vector_loads"] == 0  # X columns misaligned
+    q = p("f16", 4096, 4095, nvec=4)  # X columns misaligned: unaligned 16-byte loads
+    assert q["family"] == lg.FAMILY_BATCHED and q["vector_loads"] == 1
     with pytest.raises(lg.GemvError):
         p("f16", 4096, 4096, nvec=65)
 
@@ -509,8 +521,11 @@ def test_long_x_rows_share_a_workgroup():
         q = p(dtype, M, K)
         assert (q["family"], q["x_in_registers"], q["batch"], q["row_tiles"]) == \
             (lg.FAMILY_GROUP_PER_ROW, 1, chunks, 4), (dtype, M, K)
-    # too few rows for two per workgroup: the families of before
-    assert p("bf16", 500, 6144)["family"] == lg.FAMILY_WAVE_PER_ROW
+    # too few rows for two per workgroup: one row per workgroup (x from the caches)
+    q = p("bf16", 500, 6144)
+    assert q["family"] == lg.FAMILY_GROUP_PER_ROW and q["x_in_registers"] == 0
+    q = p("bf16", 800, 6144)  # 400 pairs of rows: x in registers, two rows per workgroup
+    assert q["x_in_registers"] == 1 and q["row_tiles"] == 2
     assert p("bf16", 4096, 4096)["family"] == lg.FAMILY_WAVE_PER_ROW
     assert p("f32", 2051, 6144)["batch"] == 6 and p("f32", 1025, 4100)["batch"] == 5
     # 7 chunks per lane (bf16 4096 x 14336: two rows per workgroup measured

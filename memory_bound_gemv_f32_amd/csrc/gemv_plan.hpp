@@ -663,10 +663,11 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
     default:
         if (p.x_in_registers)  // one batch per row, no running sum
             chain = (p.batch + 1) / 2 * p.chunk_elems + 1 + ceil_log2(kWave) + (p.waves_per_group - 1) + 1;
-        else
+        else  // (only the workgroup families fold several wavefronts' partials)
             chain = valu_chain(K, p.chunk_elems, p.lanes_per_row,
                                p.lanes_per_row < kWave ? p.lanes_per_row : kWave, p.batch,
-                               p.waves_per_group) + 1;
+                               fam == GROUP_PER_ROW || fam == GATED_SILU ? p.waves_per_group : 1) +
+                    1;
         break;
     }
     if (chain > kMaxRoundingChain) return INVALID;

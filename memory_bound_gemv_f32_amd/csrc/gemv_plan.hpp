@@ -279,6 +279,11 @@ constexpr int kSplitRowsPerGroup = 2;
 // row instead of two.
 constexpr int kQ8Batch = 4;
 constexpr int64_t kQ8PairRowsMinGroups = 256;
+// Int8 rows of at least kGroupMidMinLoads loads take a workgroup each up to
+// kQ8GroupMaxRows rows (MI355X, µs, wave per row with two rows per
+// wavefront / workgroup per row: int8 4096 × 4096 with fp16 x 5.08 / 4.77;
+// 14336 × 4096 with bf16 x 10.63 / 12.04).
+constexpr int64_t kQ8GroupMaxRows = 4096;
 // Threads per workgroup of the rows/wave and batched families.
 constexpr int kBlock = 256;
 // Below this many workgroups the rows-per-wave family stops giving each
@@ -440,6 +445,7 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
             fam = ROWS_PER_WAVE;
         else if (M <= kGroupMaxRows || long_or_many ||
                  (M <= kGroupMidRows && loads >= kGroupMidMinLoads) ||
+                 (dtype == Q8 && M <= kQ8GroupMaxRows && loads >= kGroupMidMinLoads) ||
                  stream_fits(dtype, M, K, p.vector_loads != 0, max_group_rows))
             fam = GROUP_PER_ROW;
         else

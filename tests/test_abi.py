@@ -483,11 +483,16 @@ def test_q8_families():
     p = lg.plan_q8("f16", 1000, 16, Q_addr=ALIGNED, x_addr=ALIGNED)
     assert (p["family"], p["lanes_per_row"], p["rows_per_wave"]) == (lg.FAMILY_ROWS_PER_WAVE, 1, 64)
     assert p["chunk_elems"] == 16
-    # 4096 weights are 256 loads: a wavefront per row, 4 loads per lane in
-    # flight, two rows per wavefront once there are workgroups enough
+    # 4096 weights are 256 loads: a workgroup per row up to 4096 rows; past
+    # that a wavefront per row, 4 loads per lane in flight, two rows per
+    # wavefront once there are workgroups enough
     p = lg.plan_q8("bf16", 4096, 4096, Q_addr=ALIGNED, x_addr=ALIGNED)
+    assert (p["family"], p["batch"], p["grid"]) == (lg.FAMILY_GROUP_PER_ROW, 1, 4096)
+    p = lg.plan_q8("bf16", 14336, 4096, Q_addr=ALIGNED, x_addr=ALIGNED)
     assert (p["family"], p["batch"], p["row_tiles"]) == (lg.FAMILY_WAVE_PER_ROW, 4, 2)
-    assert p["grid"] == 4096 // 8
+    assert p["grid"] == 14336 // 8
+    assert lg.plan_q8("bf16", 4096, 2048, Q_addr=ALIGNED, x_addr=ALIGNED)["family"] == \
+        lg.FAMILY_WAVE_PER_ROW  # 128 loads: half a workgroup's lanes would idle
     p = lg.plan_q8("bf16", 300, 4096, family=lg.FAMILY_WAVE_PER_ROW, Q_addr=ALIGNED,
                    x_addr=ALIGNED)
     assert p["row_tiles"] == 1 and p["grid"] == 75

@@ -606,3 +606,24 @@ def test_very_tall_rows_of_odd_load_counts_split_their_lanes():
     for dtype, M, K in (("f32", 1 << 18, 80), ("f32", 1 << 20, 40), ("f32", 1 << 20, 64),
                         ("f32", 1 << 20, 112)):
         assert p(dtype, M, K)["batch"] == 1, (dtype, M, K)
+
+
+def test_read_probe_variant_validation():
+    """The read-pattern probe takes 2/4/8/16 loads per lane, 1/2/4/8/16
+    wavefronts per workgroup, at least one block per wavefront, flags in
+    bits 0-2, and a timestamp buffer of 2 entries per wavefront."""
+    f = lg.gemv_read_probe_variant
+    ok = dict(buf=GOOD, n=1 << 20, sink=GOOD, loads=8, waves=4, blocks=1, flags=0,
+              times=None, tlen=0)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["buf"], a["n"], a["sink"], a["loads"], a["waves"], a["blocks"], a["flags"],
+                 a["times"], a["tlen"], None)
+    assert call(n=0, buf=None) == lg.GEMV_SUCCESS  # nothing to read
+    for bad in (dict(loads=3), dict(loads=32), dict(waves=3), dict(waves=32), dict(blocks=0),
+                dict(flags=8), dict(buf=None), dict(sink=None), dict(n=1000), dict(buf=GOOD + 8),
+                dict(times=GOOD + 4, tlen=1 << 20)):
+        assert call(**bad) == lg.GEMV_ERROR_INVALID_VALUE, bad
+    # 1 MiB with 8 KiB per wavefront: 128 wavefronts, 256 timestamps needed
+    assert call(times=GOOD, tlen=255) == lg.GEMV_ERROR_INVALID_VALUE

@@ -375,6 +375,31 @@ def test_read_probe_reads_and_writes_nothing():
     assert sink.cpu().tolist() == [7, 7, 7, 7]
 
 
+def test_read_probe_variants_write_only_timestamps():
+    """Every read-pattern variant streams the buffer and writes nothing but
+    its per-wavefront timestamps (start <= end, every wavefront's pair
+    written, entries past them untouched)."""
+    buf = torch.full(((2 << 20) // 4,), 0x01010101, dtype=torch.int32, device="cuda")
+    sink = torch.full((4,), 7, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    for loads, waves, blocks, flags in ((8, 4, 1, 0), (2, 16, 1, 1), (16, 1, 3, 4), (4, 8, 2, 6),
+                                        (8, 2, 1, 3)):
+        per_wave = loads * 1024 * blocks
+        n_waves = -(-buf.numel() * 4 // per_wave)
+        n_waves = -(-n_waves // waves) * waves
+        times = torch.full((2 * n_waves + 8,), -1, dtype=torch.int64, device="cuda")
+        rc = lg.gemv_read_probe_variant(buf.data_ptr(), buf.numel() * 4, sink.data_ptr(), loads,
+                                        waves, blocks, flags, times.data_ptr(), times.numel(),
+                                        stream)
+        assert rc == lg.GEMV_SUCCESS
+        torch.cuda.synchronize()
+        t = times.cpu().numpy()
+        pairs = t[:2 * n_waves].reshape(n_waves, 2)
+        assert np.all(pairs >= 0) and np.all(pairs[:, 1] >= pairs[:, 0]), (loads, waves, blocks)
+        assert np.all(t[2 * n_waves:] == -1)
+    assert sink.cpu().tolist() == [7, 7, 7, 7]
+
+
 def test_seeded_random_shapes_integer():
     """Sixty shapes drawn from a fixed seed (M, K, row pitch, pointer
     offset, bias, dtype, family, batch size), all in the exact-integer

@@ -583,18 +583,20 @@ def time_queued(torch, loop, fns, steps, warmup, seconds):
     lead = max(LEAD_LAUNCHES, math.ceil(4 * steps * host_us / max(gpu_us, 1e-3)))
     replays = math.ceil(lead / loop.per)
     ea = torch.cuda.Event(enable_timing=True)
+    t_submit = time.perf_counter()
     ea.record()
     for _ in range(replays):
         loop.main.replay()
     e0.record()
-    t_submit = time.perf_counter()
     for i in range(steps):
         call(fns[i % len(fns)])
     t_submit = time.perf_counter() - t_submit
     e1.record()
     torch.cuda.synchronize()
-    # the lead-in's GPU time must have outlasted the host's submission of
-    # the timed launches, or the GPU went idle inside the timed region
+    # the GPU started the lead-in about when the host started submitting it
+    # (it was idle); the lead-in's GPU time must have outlasted the host's
+    # submission of it and of the timed launches, or the GPU went idle
+    # inside the timed region
     lead_ms = ea.elapsed_time(e0)
     return e0.elapsed_time(e1), replays * loop.per, 1e3 * t_submit < lead_ms
 

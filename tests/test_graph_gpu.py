@@ -34,6 +34,9 @@ def _inputs():
     b = gi.make_random("f16", 1000, 2048, seed=2, nvec=24, dist="normal")
     dev["Ab"] = to_device("f16", b.A.reshape(b.M, b.lda))
     dev["Xb"] = to_device("f16", b.X)
+    b2 = gi.make_random("bf16", 1000, 2050, seed=7, nvec=5, dist="normal")  # K % 8 != 0
+    dev["Ab2"] = to_device("bf16", b2.A.reshape(b2.M, b2.lda))
+    dev["Xb2"] = to_device("bf16", b2.X)
     s = gi.make_random("f32", 8, 1 << 18, seed=3)
     dev["As"] = to_device("f32", s.A.reshape(s.M, s.lda))
     dev["xs"] = to_device("f32", s.X[0])
@@ -57,6 +60,8 @@ def _outputs():
     return {
         "y": torch.empty(4096, device="cuda"),
         "Y": torch.empty((24, 1000), device="cuda"),
+        "Y2": torch.empty((5, 1000), device="cuda"),
+        "yn": torch.empty(8, device="cuda"),
         "ys": torch.empty(8, device="cuda"),
         "yqkv": [torch.empty(M, device="cuda") for M in (512, 128, 128)],
         "h": torch.empty(1024, device="cuda"),
@@ -69,13 +74,19 @@ def _calls(d, o):
     lg.gemv(d["A"], d["x"], d["bias"], out=o["y"])
     lg.gemv_batched(d["Ab"], d["Xb"], out=o["Y"])
     lg.gemv_splitk(d["As"], d["xs"], out=o["ys"], workspace=d["ws"])
+    lg.gemv_batched(d["Ab2"], d["Xb2"], out=o["Y2"])  # the vector-ALU batched kernel
+    rc = lg.gemv_splitk_noalloc(lg.DTYPE_F32, d["As"].data_ptr(), d["As"].stride(0),
+                                d["xs"].data_ptr(), None, o["yn"].data_ptr(), d["As"].shape[0],
+                                d["As"].shape[1], 0, torch.cuda.current_stream().cuda_stream)
+    assert rc == lg.GEMV_SUCCESS
     lg.gemv_multi(d["qkv"], d["x"], None, o["yqkv"])
     lg.gemv_gate_up_silu(d["Ag"], d["Au"], d["x"], out=o["h"])
     lg.gemv_q8(d["Q"], d["scale"], d["xq"], out=o["yq"])
 
 
 def _flat(o):
-    parts = [o["y"], o["Y"].reshape(-1), o["ys"], *o["yqkv"], o["h"], o["yq"]]
+    parts = [o["y"], o["Y"].reshape(-1), o["ys"], o["Y2"].reshape(-1), o["yn"], *o["yqkv"], o["h"],
+             o["yq"]]
     return torch.cat([p.reshape(-1) for p in parts]).cpu().numpy()
 
 
@@ -86,6 +97,8 @@ def test_captured_calls_replay_like_eager_ones():
     torch.cuda.synchronize()
     want = _flat(eager)
     assert np.isfinite(want).all()
+    # the allocation-free split-K gives the workspace split-K's bits
+    assert torch.equal(eager["yn"], eager["ys"])
 
     out = _outputs()
     s = torch.cuda.Stream()
@@ -98,7 +111,8 @@ def test_captured_calls_replay_like_eager_ones():
         _calls(d, out)
     torch.cuda.synchronize()
     for replay in range(3):
-        for t in (out["y"], out["Y"], out["ys"], *out["yqkv"], out["h"], out["yq"]):
+        for t in (out["y"], out["Y"], out["ys"], out["Y2"], out["yn"], *out["yqkv"], out["h"],
+                  out["yq"]):
             t.fill_(float("nan"))  # eager work between replays
         torch.cuda.synchronize()
         g.replay()

@@ -365,17 +365,27 @@ const void* q8_rows_fn(int tiles, int batch) {
     }
 }
 
+template <class X, int U, bool VEC>
+const void* q8_group_fn(int batch) {
+    constexpr int W = gemvplan::kGroupWaves;
+    switch (batch) {
+    case 1: return (const void*)&gemvdev::gemv_group_q8_kernel<X, W, U, 1, VEC>;
+    case 2: return (const void*)&gemvdev::gemv_group_q8_kernel<X, W, U, 2, VEC>;
+    case 3: return (const void*)&gemvdev::gemv_group_q8_kernel<X, W, U, 3, VEC>;
+    case 4: return (const void*)&gemvdev::gemv_group_q8_kernel<X, W, U, 4, VEC>;
+    default: return nullptr;
+    }
+}
+
 template <class X, bool VEC>
 const void* q8_fn(const Plan& p) {
     if (p.family == gemvplan::GROUP_PER_ROW) {
-        constexpr int W = gemvplan::kGroupWaves;
-        switch (p.batch) {
-        case 1: return (const void*)&gemvdev::gemv_group_q8_kernel<X, W, 1, VEC>;
-        case 2: return (const void*)&gemvdev::gemv_group_q8_kernel<X, W, 2, VEC>;
-        case 3: return (const void*)&gemvdev::gemv_group_q8_kernel<X, W, 3, VEC>;
-        case 4: return (const void*)&gemvdev::gemv_group_q8_kernel<X, W, 4, VEC>;
-        default: return nullptr;
+        if (p.row_tiles == 1) return q8_group_fn<X, 1, VEC>(p.batch);
+        // two rows per workgroup only with 16-byte loads
+        if constexpr (VEC) {
+            if (p.row_tiles == 2) return q8_group_fn<X, 2, VEC>(p.batch);
         }
+        return nullptr;
     }
     if (p.family != gemvplan::ROWS_PER_WAVE && p.family != gemvplan::WAVE_PER_ROW) return nullptr;
     switch (p.lanes_per_row) {
@@ -704,7 +714,9 @@ gemv_status_t run_splitk(const void* A, int lda, const void* x, const float* bia
 int q8_plan(int xdtype, int M, int K, int ldq, const void* Q, const void* x, int family, Plan* p) {
     if (xdtype < gemvplan::F32 || xdtype > gemvplan::BF16 || ldq < K) return gemvplan::INVALID;
     const bool vec = gemvplan::vector_ok_q8(ldq, (uintptr_t)Q, (uintptr_t)x);
-    return gemvplan::make_plan_vec(gemvplan::Q8, M, K, 1, vec, family, p);
+    return gemvplan::make_plan_vec(gemvplan::Q8, M, K, 1, vec, family, p, 8, gemvplan::kGroupStreamRows,
+                                   gemvplan::kWaveBatch, gemvplan::kGroupWideWaves, false,
+                                   gemvplan::element_bytes(xdtype));
 }
 
 template <class X>

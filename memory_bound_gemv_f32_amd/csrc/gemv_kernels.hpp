@@ -565,11 +565,13 @@ gemv_rows_q8_kernel(const int8_t* Q, int64_t ldq, const typename X::storage* __r
     rows_body<TQ8<X>, L, U, BATCH, VEC>(ScaledMatrix<int8_t>{Q, ldq, scale, bias, y, M}, x, K);
 }
 
-template <class X, int W, int BATCH, bool VEC>
+// U rows per workgroup: every x chunk a lane loads serves U weight chunks,
+// all of them in flight together.
+template <class X, int W, int U, int BATCH, bool VEC>
 __global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4)))
 gemv_group_q8_kernel(const int8_t* Q, int64_t ldq, const typename X::storage* __restrict__ x,
                      int64_t M, int K, const float* scale, const float* bias, float* y) {
-    group_body<TQ8<X>, W, 1, BATCH, VEC>(ScaledMatrix<int8_t>{Q, ldq, scale, bias, y, M}, x, K,
+    group_body<TQ8<X>, W, U, BATCH, VEC>(ScaledMatrix<int8_t>{Q, ldq, scale, bias, y, M}, x, K,
                                          blockIdx.x);
 }
 

@@ -279,11 +279,20 @@ constexpr int kSplitRowsPerGroup = 2;
 // row instead of two.
 constexpr int kQ8Batch = 4;
 constexpr int64_t kQ8PairRowsMinGroups = 256;
-// Int8 rows of at least kGroupMidMinLoads loads take a workgroup each up to
-// kQ8GroupMaxRows rows (MI355X, µs, wave per row with two rows per
-// wavefront / workgroup per row: int8 4096 × 4096 with fp16 x 5.08 / 4.77;
-// 14336 × 4096 with bf16 x 10.63 / 12.04).
-constexpr int64_t kQ8GroupMaxRows = 4096;
+// Int8 rows of at least kGroupMidMinLoads loads run the workgroup-per-row
+// family up to kQ8GroupMaxRows rows.  Up to kQ8OneRowMaxRows rows with an
+// x row under kQ8PairMinXBytes a workgroup takes one row; otherwise two,
+// which share every x chunk, while at least kQ8PairMinGroups workgroups
+// remain.  MI355X, µs, wave per row (two rows per wavefront) / workgroup of
+// one row / of two rows / of four: int8 4096 × 4096 with fp16 x 5.08 /
+// 4.76 / 4.90 / 5.15, with fp32 x - / 6.24 / 5.46 / 5.40; 4096 × 11008 fp16
+// x - / 11.34 / 9.64 / 9.62; 2048 × 8192 fp16 x - / 5.20 / 5.21 / 5.58;
+// 11008 × 4096 fp16 x 9.40 / 9.27 / 8.47 / 9.06; 14336 × 4096 bf16 x 10.52
+// / 11.74 / 10.42 / 10.89.
+constexpr int64_t kQ8GroupMaxRows = 14336;
+constexpr int64_t kQ8OneRowMaxRows = 4096;
+constexpr int64_t kQ8PairMinXBytes = 16 * 1024;
+constexpr int64_t kQ8PairMinGroups = 1024;
 // Threads per workgroup of the rows/wave and batched families.
 constexpr int kBlock = 256;
 // Below this many workgroups the rows-per-wave family stops giving each
@@ -403,6 +412,12 @@ inline bool mfma_rows_ok(int dtype, int K, int lda, uintptr_t A, uintptr_t X) {
 // looks up its matrix per lane, which costs registers.
 constexpr int kMultiMaxRowTiles = 2;
 
+// rows per workgroup of an int8 plan of the workgroup-per-row family
+inline int q8_group_rows(int64_t M, int64_t K, int x_bytes, bool vec) {
+    if (!vec || ceil_div(M, (int64_t)2) < kQ8PairMinGroups) return 1;
+    return (M > kQ8OneRowMaxRows || K * x_bytes >= kQ8PairMinXBytes) ? 2 : 1;
+}
+
 // Whether a single-vector problem keeps x in registers (see
 // kGroupStreamMinXBytes) with at least two rows per workgroup.
 inline bool stream_fits(int dtype, int64_t M, int64_t K, bool vec, int max_group_rows) {
@@ -415,11 +430,12 @@ inline bool stream_fits(int dtype, int64_t M, int64_t K, bool vec, int max_group
 
 // `vec`: 16-byte loads of A and x (or X) are possible; `mfma_rows`: with
 // several vectors, also every row and X column starts 16-byte aligned (the
-// matrix-core kernel reads aligned operand rows).
+// matrix-core kernel reads aligned operand rows); `q8_x_bytes`: for int8
+// weights, the bytes of one x element.
 inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family, Plan* out,
                          int max_row_tiles = 8, int max_group_rows = kGroupStreamRows,
                          int max_wave_tiles = kWaveBatch, int max_group_waves = kGroupWideWaves,
-                         bool mfma_rows = false) {
+                         bool mfma_rows = false, int q8_x_bytes = 2) {
     if (dtype < F32 || dtype > Q8 || M < 0 || K < 0 || nvec < 1 || nvec > kMaxVectors)
         return INVALID;
 
@@ -556,9 +572,11 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         p.batch = fitted_batch(per_lane, dtype == Q8 ? kQ8Batch : kGroupBatch);
         // rows per workgroup (one x chunk serves all of them)
         int u = 1;
-        const int umax = dtype == Q8 ? 1 : max_group_rows;
+        const int umax = max_group_rows;
         const int64_t xbytes = (int64_t)K * element_bytes(dtype);
-        if (xbytes > kGroupStreamMinXBytes) {
+        if (dtype == Q8) {
+            u = q8_group_rows(M, K, q8_x_bytes, p.vector_loads != 0);
+        } else if (xbytes > kGroupStreamMinXBytes) {
             const int64_t lanes = (int64_t)kWave * kGroupStreamWaves;
             const int64_t chunks = ceil_div(full, lanes);
             if (p.vector_loads && full * p.chunk_elems == K && chunks <= kGroupStreamMaxChunks) {
@@ -573,7 +591,7 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
                 }
             }
         }
-        if (!p.x_in_registers && xbytes > kGroupShareMinXBytes) {
+        if (dtype != Q8 && !p.x_in_registers && xbytes > kGroupShareMinXBytes) {
             const int ushare = umax < kGroupMaxTileRows ? umax : kGroupMaxTileRows;
             while (2 * u <= ushare && 2 * u * p.batch <= kGroupTileLoads &&
                    ceil_div(M, 2 * u) >= kGroupTileMinGroups)

@@ -483,14 +483,25 @@ def test_q8_families():
     p = lg.plan_q8("f16", 1000, 16, Q_addr=ALIGNED, x_addr=ALIGNED)
     assert (p["family"], p["lanes_per_row"], p["rows_per_wave"]) == (lg.FAMILY_ROWS_PER_WAVE, 1, 64)
     assert p["chunk_elems"] == 16
-    # 4096 weights are 256 loads: a workgroup per row up to 4096 rows; past
-    # that a wavefront per row, 4 loads per lane in flight, two rows per
+    # 4096 weights are 256 loads: a workgroup per row up to 4096 rows, a
+    # workgroup per two rows up to 14336 rows (or from a 16 KiB x row on);
+    # past that a wavefront per row, 4 loads per lane in flight, two rows per
     # wavefront once there are workgroups enough
     p = lg.plan_q8("bf16", 4096, 4096, Q_addr=ALIGNED, x_addr=ALIGNED)
-    assert (p["family"], p["batch"], p["grid"]) == (lg.FAMILY_GROUP_PER_ROW, 1, 4096)
+    assert (p["family"], p["batch"], p["row_tiles"], p["grid"]) == \
+        (lg.FAMILY_GROUP_PER_ROW, 1, 1, 4096)
+    p = lg.plan_q8("f32", 4096, 4096, Q_addr=ALIGNED, x_addr=ALIGNED)
+    assert (p["family"], p["row_tiles"], p["grid"]) == (lg.FAMILY_GROUP_PER_ROW, 2, 2048)
     p = lg.plan_q8("bf16", 14336, 4096, Q_addr=ALIGNED, x_addr=ALIGNED)
+    assert (p["family"], p["batch"], p["row_tiles"], p["grid"]) == \
+        (lg.FAMILY_GROUP_PER_ROW, 1, 2, 7168)
+    assert p["lds_bytes"] == 4 * 2 * 4
+    p = lg.plan_q8("bf16", 16384, 4096, Q_addr=ALIGNED, x_addr=ALIGNED)
     assert (p["family"], p["batch"], p["row_tiles"]) == (lg.FAMILY_WAVE_PER_ROW, 4, 2)
-    assert p["grid"] == 14336 // 8
+    assert p["grid"] == 16384 // 8
+    # element loads keep one row per workgroup
+    p = lg.plan_q8("f32", 4096, 4096, Q_addr=ALIGNED + 1, x_addr=ALIGNED)
+    assert (p["family"], p["row_tiles"], p["vector_loads"]) == (lg.FAMILY_GROUP_PER_ROW, 1, 0)
     assert lg.plan_q8("bf16", 4096, 2048, Q_addr=ALIGNED, x_addr=ALIGNED)["family"] == \
         lg.FAMILY_WAVE_PER_ROW  # 128 loads: half a workgroup's lanes would idle
     p = lg.plan_q8("bf16", 300, 4096, family=lg.FAMILY_WAVE_PER_ROW, Q_addr=ALIGNED,

@@ -106,6 +106,23 @@ def test_integer_every_family(xdtype, M, K):
                              f"{xdtype} {M}x{K} ldq={ldq} misalign={misalign} family {fam}")
 
 
+@pytest.mark.parametrize("xdtype", gi.DTYPES)
+def test_integer_two_rows_per_workgroup(xdtype):
+    """Workgroups of two int8 rows sharing each x chunk (more than 4096
+    rows, or an x row of 16 KiB or more): an odd row count leaves the last
+    workgroup one row, and a row length that is not a whole number of
+    16-byte loads leaves a tail; bit-exact with padded and tight pitches."""
+    shapes = [(4099, 4100, 4112), (4099, 4096, 4096)]
+    if xdtype == "f32":
+        shapes.append((2049, 4096, 4096))  # two rows for the 16 KiB x row alone
+    for M, K, ldq in shapes:
+        q = lg.plan_q8(xdtype, M, K, ldq, 1 << 20, 1 << 20)
+        assert q["family"] == lg.FAMILY_GROUP_PER_ROW and q["row_tiles"] == 2, (M, K, q)
+        case = gi.make_q8_integer(xdtype, M, K, seed=M + K + ldq, ldq=ldq, bias=True)
+        ref, _ = run_oracle_q8(case)
+        assert_bit_exact(run_q8(case), ref, f"{xdtype} {M}x{K} ldq={ldq}")
+
+
 RANDOM_SHAPES = [(1000, 16), (4096, 100), (2000, 1000), (513, 4096), (64, 14336),
                  (4096, 4096), (300, 50000)]
 

@@ -365,9 +365,8 @@ const void* q8_rows_fn(int tiles, int batch) {
     }
 }
 
-template <class X, int U, bool VEC>
+template <class X, int U, bool VEC, int W = gemvplan::kGroupWaves>
 const void* q8_group_fn(int batch) {
-    constexpr int W = gemvplan::kGroupWaves;
     switch (batch) {
     case 1: return (const void*)&gemvdev::gemv_group_q8_kernel<X, W, U, 1, VEC>;
     case 2: return (const void*)&gemvdev::gemv_group_q8_kernel<X, W, U, 2, VEC>;
@@ -380,11 +379,16 @@ const void* q8_group_fn(int batch) {
 template <class X, bool VEC>
 const void* q8_fn(const Plan& p) {
     if (p.family == gemvplan::GROUP_PER_ROW) {
-        if (p.row_tiles == 1) return q8_group_fn<X, 1, VEC>(p.batch);
-        // two rows per workgroup only with 16-byte loads
-        if constexpr (VEC) {
-            if (p.row_tiles == 2) return q8_group_fn<X, 2, VEC>(p.batch);
+        if (p.waves_per_group == gemvplan::kGroupWaves) {
+            if (p.row_tiles == 1) return q8_group_fn<X, 1, VEC>(p.batch);
+            // two rows per workgroup only with 16-byte loads
+            if constexpr (VEC)
+                if (p.row_tiles == 2) return q8_group_fn<X, 2, VEC>(p.batch);
         }
+        // narrow workgroups (one row, 16-byte loads)
+        if constexpr (VEC)
+            if (p.waves_per_group == gemvplan::kQ8NarrowWaves && p.row_tiles == 1)
+                return q8_group_fn<X, 1, VEC, gemvplan::kQ8NarrowWaves>(p.batch);
         return nullptr;
     }
     if (p.family != gemvplan::ROWS_PER_WAVE && p.family != gemvplan::WAVE_PER_ROW) return nullptr;

@@ -566,7 +566,8 @@ gemv_rows_q8_kernel(const int8_t* Q, int64_t ldq, const typename X::storage* __r
 }
 
 // U rows per workgroup: every x chunk a lane loads serves U weight chunks,
-// all of them in flight together.
+// all of them in flight together.  W is 4, or 2 for one row of at most two
+// loads per lane.
 template <class X, int W, int U, int BATCH, bool VEC>
 __global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4)))
 gemv_group_q8_kernel(const int8_t* Q, int64_t ldq, const typename X::storage* __restrict__ x,

@@ -293,6 +293,14 @@ constexpr int64_t kQ8GroupMaxRows = 14336;
 constexpr int64_t kQ8OneRowMaxRows = 4096;
 constexpr int64_t kQ8PairMinXBytes = 16 * 1024;
 constexpr int64_t kQ8PairMinGroups = 1024;
+// A one-row int8 workgroup whose row is at most two 16-byte loads per lane
+// of kQ8NarrowWaves wavefronts has that many wavefronts instead of
+// kGroupWaves: half the wavefronts, two loads per lane in flight (MI355X,
+// µs, int8 with fp16 x, workgroups of 4 / 2 / 1 wavefronts: 4096 × 4096
+// 4.76 / 4.69 / 4.87, 2048 × 4096 3.41 / 3.39 / 3.52; bf16 x 4096 × 4096
+// 4.86 / 4.75 / 4.86; two rows per workgroup of 2 or 1 wavefronts 4.81,
+// 5.15).
+constexpr int kQ8NarrowWaves = 2;
 // Threads per workgroup of the rows/wave and batched families.
 constexpr int kBlock = 256;
 // Below this many workgroups the rows-per-wave family stops giving each
@@ -576,6 +584,11 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         const int64_t xbytes = (int64_t)K * element_bytes(dtype);
         if (dtype == Q8) {
             u = q8_group_rows(M, K, q8_x_bytes, p.vector_loads != 0);
+            if (u == 1 && p.vector_loads && full <= 2 * kWave * kQ8NarrowWaves) {
+                p.waves_per_group = kQ8NarrowWaves;
+                p.lanes_per_row = kWave * kQ8NarrowWaves;
+                p.batch = fitted_batch(ceil_div(full, (int64_t)p.lanes_per_row), kQ8Batch);
+            }
         } else if (xbytes > kGroupStreamMinXBytes) {
             const int64_t lanes = (int64_t)kWave * kGroupStreamWaves;
             const int64_t chunks = ceil_div(full, lanes);

@@ -489,7 +489,9 @@ def test_q8_families():
     # wavefront once there are workgroups enough
     p = lg.plan_q8("bf16", 4096, 4096, Q_addr=ALIGNED, x_addr=ALIGNED)
     assert (p["family"], p["batch"], p["row_tiles"], p["grid"]) == \
-        (lg.FAMILY_GROUP_PER_ROW, 1, 1, 4096)
+        (lg.FAMILY_GROUP_PER_ROW, 2, 1, 4096)
+    # (a row of at most two loads per lane of two wavefronts: two wavefronts)
+    assert (p["waves_per_group"], p["lanes_per_row"], p["lds_bytes"]) == (2, 128, 8)
     p = lg.plan_q8("f32", 4096, 4096, Q_addr=ALIGNED, x_addr=ALIGNED)
     assert (p["family"], p["row_tiles"], p["grid"]) == (lg.FAMILY_GROUP_PER_ROW, 2, 2048)
     p = lg.plan_q8("bf16", 14336, 4096, Q_addr=ALIGNED, x_addr=ALIGNED)

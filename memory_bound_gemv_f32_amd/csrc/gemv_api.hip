@@ -237,11 +237,36 @@ const void* group_stream_fn(int chunks, int rows) {
     }
 }
 
+// one row per wavefront, workgroups of kNarrowRowsWaves wavefronts (one
+// matrix, one row tile, 16-byte loads)
+template <class D>
+const void* narrow_wave_fn(int batch) {
+    constexpr int NW = gemvplan::kNarrowRowsWaves;
+    switch (batch) {
+    case 1: return (const void*)&gemvdev::gemv_rows_kernel<D, 64, 1, 1, true, NW>;
+    case 2: return (const void*)&gemvdev::gemv_rows_kernel<D, 64, 1, 2, true, NW>;
+    case 3: return (const void*)&gemvdev::gemv_rows_kernel<D, 64, 1, 3, true, NW>;
+    case 4: return (const void*)&gemvdev::gemv_rows_kernel<D, 64, 1, 4, true, NW>;
+    case 5: return (const void*)&gemvdev::gemv_rows_kernel<D, 64, 1, 5, true, NW>;
+    case 6: return (const void*)&gemvdev::gemv_rows_kernel<D, 64, 1, 6, true, NW>;
+    case 7: return (const void*)&gemvdev::gemv_rows_kernel<D, 64, 1, 7, true, NW>;
+    case 8: return (const void*)&gemvdev::gemv_rows_kernel<D, 64, 1, 8, true, NW>;
+    default: return nullptr;
+    }
+}
+
 template <class D, bool VEC, int NSEG>
 const void* single_fn(const Plan& p) {
     switch (p.family) {
     case gemvplan::ROWS_PER_WAVE:
-    case gemvplan::WAVE_PER_ROW: return rows_fn<D, VEC, NSEG>(p.lanes_per_row, p.row_tiles, p.batch);
+    case gemvplan::WAVE_PER_ROW:
+        if (p.waves_per_group == gemvplan::kNarrowRowsWaves) {
+            if constexpr (NSEG == 0 && VEC)
+                if (p.family == gemvplan::WAVE_PER_ROW && p.row_tiles == 1) return narrow_wave_fn<D>(p.batch);
+            return nullptr;
+        }
+        if (p.waves_per_group != gemvdev::kRowsWaves) return nullptr;
+        return rows_fn<D, VEC, NSEG>(p.lanes_per_row, p.row_tiles, p.batch);
     case gemvplan::GROUP_PER_ROW:
         if (p.x_in_registers) {
             if constexpr (NSEG == 0 && VEC) return group_stream_fn<D>(p.batch, p.row_tiles);

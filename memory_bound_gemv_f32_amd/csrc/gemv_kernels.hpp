@@ -282,8 +282,8 @@ __device__ __forceinline__ void rows_batch(const S* const (&rp)[U], const XS* x,
 // Rows-per-wave (L < 64) and wave-per-row (L == 64) kernel.
 // A wavefront covers R = 64/L rows per row tile and takes U consecutive row
 // tiles; lanes sub = lane % L of one row walk its chunks with stride L, BATCH
-// chunks in flight per row tile.
-template <class D, int L, int U, int BATCH, bool VEC, class Rows>
+// chunks in flight per row tile.  NW wavefronts per workgroup.
+template <class D, int L, int U, int BATCH, bool VEC, int NW = kRowsWaves, class Rows>
 __device__ __forceinline__ void rows_body(const Rows& rows, const typename D::xstorage* __restrict__ x,
                                           int K) {
     using S = typename D::storage;
@@ -297,7 +297,7 @@ __device__ __forceinline__ void rows_body(const Rows& rows, const typename D::xs
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = lane & (L - 1);
     const int slot = lane / L;
-    const int64_t tile0 = ((int64_t)blockIdx.x * kRowsWaves + wave) * U;
+    const int64_t tile0 = ((int64_t)blockIdx.x * NW + wave) * U;
 
     const int64_t M = rows.M;
     const S* rp[U];
@@ -364,11 +364,14 @@ __device__ __forceinline__ void rows_body(const Rows& rows, const typename D::xs
 }
 
 // One matrix: the arguments are scalars, so they arrive preloaded in SGPRs.
-template <class D, int L, int U, int BATCH, bool VEC>
-__global__ void __launch_bounds__(kRowsWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
+// (Workgroups of NW = 2 wavefronts spread a wave-per-row grid of a few
+// workgroups per compute unit more evenly where 4 would leave some units
+// one workgroup more than others.)
+template <class D, int L, int U, int BATCH, bool VEC, int NW = kRowsWaves>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4)))
 gemv_rows_kernel(const typename D::storage* A, int64_t lda, const float* bias, float* y, int64_t M,
                  const typename D::storage* __restrict__ x, int K) {
-    rows_body<D, L, U, BATCH, VEC>(OneMatrix<typename D::storage>{A, lda, bias, y, M}, x, K);
+    rows_body<D, L, U, BATCH, VEC, NW>(OneMatrix<typename D::storage>{A, lda, bias, y, M}, x, K);
 }
 
 // Several row-stacked matrices sharing x (the segment table is a kernel

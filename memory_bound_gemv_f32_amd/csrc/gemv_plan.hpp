@@ -805,12 +805,42 @@ inline int make_split_plan(int dtype, int M, int K, bool vec, int requested, Pla
     return OK;
 }
 
+// Workgroups of a single matrix's wave-per-row plan (one row per wavefront,
+// one row tile, 16-byte loads): kBlock / kWave wavefronts, or
+// kNarrowRowsWaves when that spreads the grid more evenly over the kCUs
+// compute units, i.e. when the busiest unit's share of workgroups, over the
+// mean, is smaller (g workgroups: ceil(g / kCUs)·kCUs / g).  A grid of 384
+// four-wavefront workgroups leaves half the units two and half one; 768 of
+// two leave every unit three.  MI355X, bf16 K = 4096, µs, 4 / 2 wavefronts:
+// 1280 rows 3.97 / 3.85, 1536 4.09 / 3.93, 2304 5.13 / 4.89, 2560 5.23 /
+// 5.09, 3584 6.36 / 6.24, 5632 8.58 / 8.56; fp32 1536 × 2048 4.06 / 3.79;
+// where the shares tie, 4 stays (768 3.04 / 3.26, 1024 3.22 / 3.45, 1792
+// 4.22 / 4.36, 2048 4.32 / 4.44, 2816 5.38 / 5.58, 4096 6.66 / 6.73).
+constexpr int64_t kCUs = 256;
+constexpr int kNarrowRowsWaves = 2;
+inline bool narrow_rows_balance_better(int64_t M) {
+    const int64_t g4 = ceil_div(M, (int64_t)(kBlock / kWave)), g2 = ceil_div(M, (int64_t)kNarrowRowsWaves);
+    // ceil(g2/C)·C/g2 < ceil(g4/C)·C/g4, cross-multiplied
+    return g4 > 0 && ceil_div(g2, kCUs) * g4 < ceil_div(g4, kCUs) * g2;
+}
+inline void balance_rows_workgroups(int dtype, int nvec, int64_t M, Plan* p) {
+    if (p->family != WAVE_PER_ROW || dtype == Q8 || nvec != 1 || p->row_tiles != 1 ||
+        !p->vector_loads || !narrow_rows_balance_better(M))
+        return;
+    p->waves_per_group = kNarrowRowsWaves;
+    p->block = kNarrowRowsWaves * kWave;
+    p->rows_per_group = kNarrowRowsWaves;
+    p->grid = ceil_div(M, (int64_t)p->rows_per_group);
+}
+
 inline int make_plan(int dtype, int M, int K, int lda, int nvec, uintptr_t A, uintptr_t X,
                      int family, Plan* out) {
     if (lda < K) return INVALID;
-    return make_plan_vec(dtype, M, K, nvec, vector_ok(dtype, K, lda, nvec, A, X), family, out, 8,
-                         kGroupStreamRows, kWaveBatch, kGroupWideWaves,
-                         mfma_rows_ok(dtype, K, lda, A, X));
+    const int rc = make_plan_vec(dtype, M, K, nvec, vector_ok(dtype, K, lda, nvec, A, X), family,
+                                 out, 8, kGroupStreamRows, kWaveBatch, kGroupWideWaves,
+                                 mfma_rows_ok(dtype, K, lda, A, X));
+    if (rc == OK) balance_rows_workgroups(dtype, nvec, M, out);
+    return rc;
 }
 
 }  // namespace gemvplan

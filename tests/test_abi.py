@@ -153,6 +153,24 @@ def test_mid_rows_get_a_wavefront_each():
     assert p("bf16", 1024, 4096)["family"] == lg.FAMILY_WAVE_PER_ROW
 
 
+def test_wave_per_row_workgroups_balance_the_compute_units():
+    """One row per wavefront: workgroups of 4 wavefronts, or of 2 when that
+    leaves the busiest of the 256 compute units a smaller share of
+    workgroups over the mean (384 workgroups of 4 put two on half the units
+    and one on the rest; 768 of 2 put three on every unit)."""
+    for M, waves in ((768, 4), (1024, 4), (1280, 2), (1535, 2), (1536, 2), (1537, 4), (1792, 4),
+                     (2048, 4), (2304, 2), (2560, 2), (2816, 4), (3072, 4), (3584, 2), (4096, 4)):
+        q = p("bf16", M, 4096)
+        assert q["family"] == lg.FAMILY_WAVE_PER_ROW
+        assert (q["waves_per_group"], q["block"], q["rows_per_group"]) == (waves, 64 * waves, waves), M
+        assert q["grid"] == -(-M // waves)
+    # the same for the forced family; element loads and short-row plans keep 4
+    assert p("bf16", 1536, 4096, family=lg.FAMILY_WAVE_PER_ROW)["waves_per_group"] == 2
+    assert p("bf16", 1536, 4096, A=ALIGNED + 2)["waves_per_group"] == 4
+    assert p("f32", 1536, 2050)["waves_per_group"] == 2
+    assert p("bf16", 1536, 256)["waves_per_group"] == 4  # rows per wavefront
+
+
 def test_very_tall_short_rows_share_wavefronts():
     """With more than 16384 workgroups' worth of short rows, a wavefront
     takes 2, 4 or 8 rows (at most 8 loads per lane in flight); up to 65536

@@ -195,6 +195,29 @@ def test_integer_wide_workgroups(dtype, M, K, waves):
         assert_bit_exact(run_gpu(case, lg.FAMILY_AUTO, misalign=misalign), ref, what)
 
 
+# one row per wavefront in workgroups of two wavefronts (a grid that spreads
+# more evenly over the compute units than one of four-wavefront workgroups):
+# an odd row count leaves the last workgroup one row past the end; rows with
+# and without a ragged tail, tight and padded pitches
+NARROW_SHAPES = [("bf16", 1535, 4096), ("f16", 2560, 4100), ("f32", 1536, 2050),
+                 ("bf16", 1280, 3000)]
+
+
+@pytest.mark.parametrize("dtype,M,K", NARROW_SHAPES)
+def test_integer_two_wavefront_workgroups(dtype, M, K):
+    per = 16 // gi.ELEMENT_BYTES[dtype]
+    for lda in (K, pad16(dtype, K) + per):
+        q = lg.plan(dtype, M, K, lda, 1, 1 << 20, 1 << 20)
+        assert (q["family"], q["waves_per_group"], q["grid"]) == \
+            (lg.FAMILY_WAVE_PER_ROW, 2, (M + 1) // 2), q
+        case = gi.make_integer(dtype, M, K, seed=M * 5 + K, lda=lda, bias=lda == K)
+        ref, _ = run_oracle(case)
+        for fam in (lg.FAMILY_AUTO, lg.FAMILY_WAVE_PER_ROW):
+            what = f"{dtype} {M}x{K} lda={lda} family {fam}: 2 wavefronts, batch {q['batch']}"
+            print(what, flush=True)
+            assert_bit_exact(run_gpu(case, fam), ref, what)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("nvec", list(range(1, 17)))
 def test_integer_batched(dtype, nvec):

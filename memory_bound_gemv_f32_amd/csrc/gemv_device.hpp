@@ -9,8 +9,6 @@
 
 namespace gemvdev {
 
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -113,33 +111,6 @@ __device__ __forceinline__ float chunk_dot(D, quad a, quad x, float acc) {
     return acc;
 }
 
-// The packed two-element dot products with fp32 accumulation
-// (v_dot2_f32_f16 / v_dot2_f32_bf16): one instruction per element pair, for
-// the batched kernel where every A element meets up to 16 vectors and VALU
-// issue, not memory, is the limit.  Their products are exact, but their
-// internal rounding is not IEEE round-to-nearest (measured: negating x does
-// not exactly negate the result), which the tolerance absorbs.
-// (Each 32-bit word is passed by value before it is reinterpreted: a bit
-// cast applied directly to an element of a native vector read element 0.)
-__device__ __forceinline__ float dot2_word(TF16, uint32_t a, uint32_t x, float acc) {
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, x), acc, false);
-}
-__device__ __forceinline__ float dot2_word(TBF16, uint32_t a, uint32_t x, float acc) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, x), acc,
-                                           false);
-}
-template <class D>
-__device__ __forceinline__ float chunk_dot2(D, quad a, quad x, float acc) {
-    acc = dot2_word(D{}, a.x, x.x, acc);
-    acc = dot2_word(D{}, a.y, x.y, acc);
-    acc = dot2_word(D{}, a.z, x.z, acc);
-    acc = dot2_word(D{}, a.w, x.w, acc);
-    return acc;
-}
-__device__ __forceinline__ float chunk_dot2(TF32, quad a, quad x, float acc) {
-    return chunk_dot(TF32{}, a, x, acc);
-}
-
 // One 16×16×32 matrix-core step, D = A·B + C with fp32 accumulation:
 // A is 16 rows × 32 k, B is 32 k × 16 columns.  Lane l supplies row (or
 // column) l % 16 and the 8 consecutive k of group l / 16 as one 16-byte
@@ -176,9 +147,6 @@ struct Chunk<D, true> {
     __device__ __forceinline__ static float dot(type a, type x, float acc) {
         return chunk_dot(D{}, a, x, acc);
     }
-    __device__ __forceinline__ static float dot2(type a, type x, float acc) {
-        return chunk_dot2(D{}, a, x, acc);
-    }
 };
 template <class D>
 struct Chunk<D, false> {
@@ -196,9 +164,6 @@ struct Chunk<D, false> {
     __device__ __forceinline__ static type keep_x(bool ok, type v) { return ok ? v : zero(); }
     __device__ __forceinline__ static float dot(type a, type x, float acc) {
         return __builtin_fmaf(widen(D{}, a), widen(D{}, x), acc);
-    }
-    __device__ __forceinline__ static float dot2(type a, type x, float acc) {
-        return dot(a, x, acc);
     }
 };
 

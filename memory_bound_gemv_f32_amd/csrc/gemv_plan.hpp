@@ -288,8 +288,9 @@ constexpr int64_t kQ8PairRowsMinGroups = 256;
 // 4.76 / 4.90 / 5.15, with fp32 x - / 6.24 / 5.46 / 5.40; 4096 × 11008 fp16
 // x - / 11.34 / 9.64 / 9.62; 2048 × 8192 fp16 x - / 5.20 / 5.21 / 5.58;
 // 11008 × 4096 fp16 x 9.40 / 9.27 / 8.47 / 9.06; 14336 × 4096 bf16 x 10.52
-// / 11.74 / 10.42 / 10.89.
-constexpr int64_t kQ8GroupMaxRows = 14336;
+// / 11.74 / 10.42 / 10.89; wave per row / workgroup of two rows: 16384 ×
+// 4096 fp16 x 12.07 / 11.28, 28672 × 4096 bf16 x 18.19 / 18.82.
+constexpr int64_t kQ8GroupMaxRows = 16384;
 constexpr int64_t kQ8OneRowMaxRows = 4096;
 constexpr int64_t kQ8PairMinXBytes = 16 * 1024;
 constexpr int64_t kQ8PairMinGroups = 1024;

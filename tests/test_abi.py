@@ -502,7 +502,7 @@ def test_q8_families():
     assert (p["family"], p["lanes_per_row"], p["rows_per_wave"]) == (lg.FAMILY_ROWS_PER_WAVE, 1, 64)
     assert p["chunk_elems"] == 16
     # 4096 weights are 256 loads: a workgroup per row up to 4096 rows, a
-    # workgroup per two rows up to 14336 rows (or from a 16 KiB x row on);
+    # workgroup per two rows up to 16384 rows (or from a 16 KiB x row on);
     # past that a wavefront per row, 4 loads per lane in flight, two rows per
     # wavefront once there are workgroups enough
     p = lg.plan_q8("bf16", 4096, 4096, Q_addr=ALIGNED, x_addr=ALIGNED)
@@ -517,8 +517,10 @@ def test_q8_families():
         (lg.FAMILY_GROUP_PER_ROW, 1, 2, 7168)
     assert p["lds_bytes"] == 4 * 2 * 4
     p = lg.plan_q8("bf16", 16384, 4096, Q_addr=ALIGNED, x_addr=ALIGNED)
+    assert (p["family"], p["row_tiles"], p["grid"]) == (lg.FAMILY_GROUP_PER_ROW, 2, 8192)
+    p = lg.plan_q8("bf16", 16392, 4096, Q_addr=ALIGNED, x_addr=ALIGNED)
     assert (p["family"], p["batch"], p["row_tiles"]) == (lg.FAMILY_WAVE_PER_ROW, 4, 2)
-    assert p["grid"] == 16384 // 8
+    assert p["grid"] == 16392 // 8
     # element loads keep one row per workgroup
     p = lg.plan_q8("f32", 4096, 4096, Q_addr=ALIGNED + 1, x_addr=ALIGNED)
     assert (p["family"], p["row_tiles"], p["vector_loads"]) == (lg.FAMILY_GROUP_PER_ROW, 1, 0)

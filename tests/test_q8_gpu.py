@@ -112,7 +112,7 @@ def test_integer_two_rows_per_workgroup(xdtype):
     rows, or an x row of 16 KiB or more): an odd row count leaves the last
     workgroup one row, and a row length that is not a whole number of
     16-byte loads leaves a tail; bit-exact with padded and tight pitches."""
-    shapes = [(4099, 4100, 4112), (4099, 4096, 4096)]
+    shapes = [(4099, 4100, 4112), (4099, 4096, 4096), (16383, 4096, 4096)]
     if xdtype == "f32":
         shapes.append((2049, 4096, 4096))  # two rows for the 16 KiB x row alone
     for M, K, ldq in shapes:

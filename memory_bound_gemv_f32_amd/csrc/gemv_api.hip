@@ -314,21 +314,28 @@ const void* batched_fn(int nvec) {
     }
 }
 
+// matrix-core kernels of W wavefronts per workgroup
+template <class D, int W>
+const void* mfma_fn(int nvec) {
+    if (nvec <= gemvplan::kMfmaFewVectors)
+        return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 1, gemvplan::mfma_chunk(16), true>;
+    switch (gemvplan::mfma_tiles(nvec)) {
+    case 1: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 1, gemvplan::mfma_chunk(16), false>;
+    case 2: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 2, gemvplan::mfma_chunk(32), false>;
+    case 4: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 4, gemvplan::mfma_chunk(64), false>;
+    default: return nullptr;
+    }
+}
+
 template <class D>
 const void* batched_kernel(const Plan& p, int nvec) {
     if constexpr (D::bytes == 2) {
         if (p.family == gemvplan::BATCHED)
             return p.vector_loads ? batched_fn<D, true>(nvec) : batched_fn<D, false>(nvec);
         if (p.family == gemvplan::BATCHED_MFMA && p.vector_loads) {
-            constexpr int W = gemvplan::kMfmaWaves;
-            if (nvec <= gemvplan::kMfmaFewVectors)
-                return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 1, gemvplan::mfma_chunk(16), true>;
-            switch (gemvplan::mfma_tiles(nvec)) {
-            case 1: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 1, gemvplan::mfma_chunk(16), false>;
-            case 2: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 2, gemvplan::mfma_chunk(32), false>;
-            case 4: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 4, gemvplan::mfma_chunk(64), false>;
-            default: return nullptr;
-            }
+            if (p.waves_per_group == gemvplan::kMfmaWaves) return mfma_fn<D, gemvplan::kMfmaWaves>(nvec);
+            if (p.waves_per_group == gemvplan::kMfmaManyTilesWaves)
+                return mfma_fn<D, gemvplan::kMfmaManyTilesWaves>(nvec);
         }
     }
     return nullptr;

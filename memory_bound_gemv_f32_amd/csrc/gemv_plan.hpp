@@ -133,6 +133,22 @@ constexpr bool batched_x_ahead(int nvec) { return nvec <= 8; }
 constexpr int kMfmaRows = 16;
 constexpr int kMfmaWaves = 8;
 constexpr int kMfmaChunk = 8;
+// Compute units of the GPU this library is built for (MI355X).
+constexpr int64_t kCUs = 256;
+// With more 16-row tiles than compute units, workgroups of
+// kMfmaManyTilesWaves wavefronts (each walking two chunks of its longer K
+// run, half the LDS): two fit on a compute unit, so one's loads overlap the
+// other's tail, where a workgroup of 8 (130 KiB of LDS) runs alone, start to
+// finish.  MI355X, fp16 K = 4096, µs, 8 / 4 wavefronts, 4 and 16 vectors:
+// 6144 rows 11.96 / 11.68 and 13.63 / 13.08, 8192 13.11 / 12.63 and 14.39 /
+// 13.73, 14336 23.49 / 21.03 and 26.50 / 24.16, 28672 41.53 / 36.90 and
+// 46.71 / 41.64; at one tile per unit or fewer 8 stays (4096 7.24 / 8.05 and
+// 7.87 / 8.50, 1024 6.04 / 6.66).  (2 wavefronts: 14336 22.2 and 23.7,
+// 28672 42.8 and 47.5.)
+constexpr int kMfmaManyTilesWaves = 4;
+constexpr int mfma_waves(int64_t M) {
+    return (M + kMfmaRows - 1) / kMfmaRows > kCUs ? kMfmaManyTilesWaves : kMfmaWaves;
+}
 // Up to this many vectors the matrix-core kernel reads its X operands
 // straight from memory (a load touches only the columns in use) instead of
 // staging X in LDS (fp16 4096 × 4096, µs, straight / staged: 3 vectors
@@ -142,8 +158,8 @@ constexpr int kMfmaFewVectors = 5;
 // tiles grow so that the X staged per chunk stays 16 KiB per wavefront.
 constexpr int mfma_tiles(int nvec) { return nvec <= 16 ? 1 : (nvec <= 32 ? 2 : 4); }
 constexpr int mfma_chunk(int nvec) { return kMfmaChunk / mfma_tiles(nvec); }
-constexpr int mfma_lds_bytes(int nvec) {
-    return kMfmaWaves * 16 * mfma_tiles(nvec) * (mfma_chunk(nvec) * 128 + 16);
+constexpr int mfma_lds_bytes(int nvec, int waves) {
+    return waves * 16 * mfma_tiles(nvec) * (mfma_chunk(nvec) * 128 + 16);
 }
 // The 64-element steps of a row that wavefront `wave` of a matrix-core
 // workgroup of `waves` wavefronts walks: steps [first, end) of the
@@ -648,12 +664,12 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
     }
     case BATCHED_MFMA:
         // each wavefront: 4 lanes per row and step, 16 rows; rows span the group
-        p.lanes_per_row = 4 * kMfmaWaves;
+        p.waves_per_group = mfma_waves(M);
+        p.lanes_per_row = 4 * p.waves_per_group;
         p.rows_per_wave = kMfmaRows;
-        p.waves_per_group = kMfmaWaves;
         p.batch = mfma_chunk(nvec);
         p.row_tiles = 1;
-        p.lds_bytes = mfma_lds_bytes(nvec);
+        p.lds_bytes = mfma_lds_bytes(nvec, p.waves_per_group);
         break;
     default:
         return INVALID;
@@ -670,7 +686,7 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
     p.grid = ceil_div(M, p.rows_per_group);
     p.slice_elems = K;
     if (fam == BATCHED_MFMA)  // 64-wide steps (the last may be partial) per wavefront
-        p.passes = mfma_step_range(K, kMfmaWaves, 0).end;
+        p.passes = mfma_step_range(K, p.waves_per_group, 0).end;
     else
         p.passes = (int)ceil_div(full, (int64_t)p.lanes_per_row);
     if (p.grid > 0x7fffffff) return INVALID;
@@ -683,13 +699,13 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
     switch (fam) {
     case BATCHED_MFMA: {
         int blk = nvec;
-        chain = mfma_chain(K, kMfmaWaves, mfma_chunk(blk), mfma_tiles(blk) <= 2) + 1;
+        chain = mfma_chain(K, p.waves_per_group, mfma_chunk(blk), mfma_tiles(blk) <= 2) + 1;
         if (chain > kMaxRoundingChain && mfma_tiles(nvec) > 2) {
             blk = 32;
             p.column_blocks = (int)ceil_div(nvec, (int64_t)blk);
             p.batch = mfma_chunk(blk);
-            p.lds_bytes = mfma_lds_bytes(blk);
-            chain = mfma_chain(K, kMfmaWaves, mfma_chunk(blk), true) + 1;
+            p.lds_bytes = mfma_lds_bytes(blk, p.waves_per_group);
+            chain = mfma_chain(K, p.waves_per_group, mfma_chunk(blk), true) + 1;
         }
         break;
     }
@@ -817,7 +833,6 @@ inline int make_split_plan(int dtype, int M, int K, bool vec, int requested, Pla
 // 5.09, 3584 6.36 / 6.24, 5632 8.58 / 8.56; fp32 1536 × 2048 4.06 / 3.79;
 // where the shares tie, 4 stays (768 3.04 / 3.26, 1024 3.22 / 3.45, 1792
 // 4.22 / 4.36, 2048 4.32 / 4.44, 2816 5.38 / 5.58, 4096 6.66 / 6.73).
-constexpr int64_t kCUs = 256;
 constexpr int kNarrowRowsWaves = 2;
 inline bool narrow_rows_balance_better(int64_t M) {
     const int64_t g4 = ceil_div(M, (int64_t)(kBlock / kWave)), g2 = ceil_div(M, (int64_t)kNarrowRowsWaves);

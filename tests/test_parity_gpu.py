@@ -500,6 +500,22 @@ def test_integer_batched_partial_last_step(dtype, nvec):
                              f"{dtype} 33x{K} nvec={nvec} family {fam}")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_integer_batched_many_tiles(dtype):
+    """More 16-row tiles than compute units: the matrix-core kernel in
+    workgroups of 4 wavefronts, each walking two chunks and the leftover
+    steps of its longer K run; the last tile one row deep."""
+    M = 4113
+    for K, nvec in ((4096, 3), (4096, 16), (1000, 33), (2680, 17)):
+        q = lg.plan(dtype, M, K, K, nvec, 1 << 20, 1 << 20)
+        assert q["family"] == lg.FAMILY_BATCHED_MFMA and q["waves_per_group"] == 4, q
+        case = gi.make_integer(dtype, M, K, seed=K + nvec, nvec=nvec, bias=nvec % 2 == 1)
+        ref, _ = run_oracle(case)
+        what = f"{dtype} {M}x{K} nvec={nvec}: 4 wavefronts, chunk {q['batch']}"
+        print(what, flush=True)
+        assert_bit_exact(run_gpu(case, lg.FAMILY_AUTO, batched=True), ref, what)
+
+
 def test_refused_launch_reports_launch_failure():
     """A launch the runtime refuses comes back as GEMV_ERROR_LAUNCH_FAILURE
     with the runtime's error code, and leaves nothing behind: the runtime's

@@ -314,17 +314,23 @@ const void* batched_fn(int nvec) {
     }
 }
 
-// matrix-core kernels of W wavefronts per workgroup
-template <class D, int W>
+// matrix-core kernels of W wavefronts and Q groups of 8 rows per workgroup
+template <class D, int W, int Q>
 const void* mfma_fn(int nvec) {
     if (nvec <= gemvplan::kMfmaFewVectors)
-        return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 1, gemvplan::mfma_chunk(16), true>;
+        return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 1, gemvplan::mfma_chunk(16), true, Q>;
     switch (gemvplan::mfma_tiles(nvec)) {
-    case 1: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 1, gemvplan::mfma_chunk(16), false>;
-    case 2: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 2, gemvplan::mfma_chunk(32), false>;
-    case 4: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 4, gemvplan::mfma_chunk(64), false>;
+    case 1: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 1, gemvplan::mfma_chunk(16), false, Q>;
+    case 2: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 2, gemvplan::mfma_chunk(32), false, Q>;
+    case 4: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 4, gemvplan::mfma_chunk(64), false, Q>;
     default: return nullptr;
     }
+}
+template <class D, int W>
+const void* mfma_fn(int nvec, int groups) {
+    if (groups == 2) return mfma_fn<D, W, 2>(nvec);
+    if (groups == 1) return mfma_fn<D, W, 1>(nvec);
+    return nullptr;
 }
 
 template <class D>
@@ -333,9 +339,10 @@ const void* batched_kernel(const Plan& p, int nvec) {
         if (p.family == gemvplan::BATCHED)
             return p.vector_loads ? batched_fn<D, true>(nvec) : batched_fn<D, false>(nvec);
         if (p.family == gemvplan::BATCHED_MFMA && p.vector_loads) {
-            if (p.waves_per_group == gemvplan::kMfmaWaves) return mfma_fn<D, gemvplan::kMfmaWaves>(nvec);
+            if (p.waves_per_group == gemvplan::kMfmaWaves)
+                return mfma_fn<D, gemvplan::kMfmaWaves>(nvec, p.row_tiles);
             if (p.waves_per_group == gemvplan::kMfmaManyTilesWaves)
-                return mfma_fn<D, gemvplan::kMfmaManyTilesWaves>(nvec);
+                return mfma_fn<D, gemvplan::kMfmaManyTilesWaves>(nvec, p.row_tiles);
         }
     }
     return nullptr;

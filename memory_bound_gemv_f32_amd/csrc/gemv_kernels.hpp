@@ -793,9 +793,10 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
 // and the others are dropped.  Real row R's sum is the even row of the first
 // step's tile plus the odd row of the second's.
 //
-// A workgroup owns 16 real rows (two groups of 8); its W wavefronts split
-// the 64-element steps of K into contiguous slices and walk them in chunks
-// of CH steps.  Per chunk a wavefront issues the loads of X operands ahead
+// A workgroup owns Q groups of 8 real rows (Q = 2, or 1 where that spreads
+// a small matrix over more compute units); its W wavefronts split the
+// 64-element steps of K into contiguous slices and walk them in chunks of CH
+// steps.  Per chunk a wavefront issues the loads of X operands ahead
 // of the loads of A that they meet: loads complete in issue order, so the X
 // operands are ready when the A they meet lands and each step's MFMAs run
 // as its A arrives (with all A loads first, every MFMA waited for the last
@@ -823,7 +824,7 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
 // to the wavefronts by gemvplan::mfma_step_range; the steps of a run that do
 // not fill a whole chunk, and the partial step, read their operands
 // directly, one step at a time.
-template <class D, int W, int NT, int CH, bool FEW>
+template <class D, int W, int NT, int CH, bool FEW, int Q = 2>
 __global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2)))
 gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
                          const typename D::storage* __restrict__ X,
@@ -844,10 +845,11 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     const int r = lane & 15;  // operand row (A) / column within a tile (X)
     const int g = lane >> 4;  // 8-element group within a 32-element half-step
     const int half = r & 1;
-    const int64_t row0 = (int64_t)blockIdx.x * 16;
-    const S* ap[2];
+    static_assert(Q == 1 || Q == 2, "one or two groups of 8 rows");
+    const int64_t row0 = (int64_t)blockIdx.x * (8 * Q);
+    const S* ap[Q];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < Q; ++q) {
         const int64_t row = row0 + 8 * q + (r >> 1);
         ap[q] = A + (row < M ? row : (int64_t)M - 1) * lda + 32 * half + 8 * g;
     }
@@ -868,7 +870,7 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     // With 4 tiles the registers do not allow it: the steps of all chunks
     // are summed into `acc` directly (the planner bounds K for that form).
     constexpr bool FRESH = NT <= 2;
-    f32x4 acc[2][NT][2], tot[2][NT][2], cmp[2][NT][2];
+    f32x4 acc[Q][NT][2], tot[Q][NT][2], cmp[Q][NT][2];
     // Every MFMA step starts from a zero accumulator and its outputs are
     // added to `acc` by the vector ALUs.  The matrix core aligns the terms of
     // a step (its 32 products and the accumulator passed in) to the largest
@@ -878,9 +880,9 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     // every step could lose small products against the whole sum so far.
     // From zero, a step's error is bounded by its own products.
     const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto clear = [](f32x4(&v)[2][NT][2]) {
+    auto clear = [](f32x4(&v)[Q][NT][2]) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+        for (int q = 0; q < Q; ++q)
 #pragma unroll
             for (int t = 0; t < NT; ++t) v[q][t][0] = v[q][t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
@@ -889,7 +891,7 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
         if constexpr (FRESH) {
             if (folds == 0) {  // the first chunk is the total
 #pragma unroll
-                for (int q = 0; q < 2; ++q)
+                for (int q = 0; q < Q; ++q)
 #pragma unroll
                     for (int t = 0; t < NT; ++t) {
                         tot[q][t][0] = acc[q][t][0];
@@ -897,7 +899,7 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
                     }
             } else {
 #pragma unroll
-                for (int q = 0; q < 2; ++q)
+                for (int q = 0; q < Q; ++q)
 #pragma unroll
                     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -922,11 +924,11 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
         for (; c + CH <= s1; c += CH) {
             // step by step, A then X: step i's MFMAs wait for its own four loads
             // only (all X operands first measured 7.77 against 6.99 µs at 2 vectors)
-            quad a[2][CH], b[2][CH];
+            quad a[Q][CH], b[2][CH];
 #pragma unroll
             for (int i = 0; i < CH; ++i) {
 #pragma unroll
-                for (int q = 0; q < 2; ++q)
+                for (int q = 0; q < Q; ++q)
                     a[q][i] = __builtin_nontemporal_load(reinterpret_cast<const quad*>(ap[q] + (int64_t)(c + i) * 64));
                 b[0][i] = *reinterpret_cast<const quad*>(xcol + (int64_t)(c + i) * 64);
                 b[1][i] = *reinterpret_cast<const quad*>(xcol + (int64_t)(c + i) * 64 + 32);
@@ -935,7 +937,7 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
 #pragma unroll
             for (int i = 0; i < CH; ++i)
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
+                for (int q = 0; q < Q; ++q) {
                     acc[q][0][0] += mma_16x16x32(D{}, a[q][i], b[0][i], zero4);
                     acc[q][0][1] += mma_16x16x32(D{}, a[q][i], b[1][i], zero4);
                 }
@@ -954,7 +956,7 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
         constexpr int kColsPerLoad = 64 / (8 * G);
         static_assert(CH % G == 0 && kColsPerLoad * 8 * G == 64, "group shape");
         for (; c + CH <= s1; c += CH) {
-            quad xv[kGroups][kXLoads], a[2][CH];
+            quad xv[kGroups][kXLoads], a[Q][CH];
 #pragma unroll
             for (int k = 0; k < kGroups; ++k) {
 #pragma unroll
@@ -967,7 +969,7 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
 #pragma unroll
                 for (int i = G * k; i < G * k + G; ++i)
 #pragma unroll
-                    for (int q = 0; q < 2; ++q)
+                    for (int q = 0; q < Q; ++q)
                         a[q][i] = __builtin_nontemporal_load(reinterpret_cast<const quad*>(ap[q] + (int64_t)(c + i) * 64));
             }
             __builtin_amdgcn_sched_barrier(0);  // all loads of the chunk in flight first
@@ -989,7 +991,7 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
                         const quad b0 = xw[(16 * t + r) * kColQuads + 8 * i + g];
                         const quad b1 = xw[(16 * t + r) * kColQuads + 8 * i + 4 + g];
 #pragma unroll
-                        for (int q = 0; q < 2; ++q) {
+                        for (int q = 0; q < Q; ++q) {
                             acc[q][t][0] += mma_16x16x32(D{}, a[q][i], b0, zero4);
                             acc[q][t][1] += mma_16x16x32(D{}, a[q][i], b1, zero4);
                         }
@@ -1013,9 +1015,9 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     for (; c < rg.end; ++c) {
         const int e = c * 64;
         const bool ina = e + 32 * half + 8 * g < K;
-        quad a[2];
+        quad a[Q];
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+        for (int q = 0; q < Q; ++q)
             a[q] = ina ? *reinterpret_cast<const quad*>(ap[q] + (int64_t)e) : zero;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -1023,7 +1025,7 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
             const quad b0 = (col && e + 8 * g < K) ? *reinterpret_cast<const quad*>(xq[t] + e) : zero;
             const quad b1 = (col && e + 32 + 8 * g < K) ? *reinterpret_cast<const quad*>(xq[t] + e + 32) : zero;
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
+            for (int q = 0; q < Q; ++q) {
                 acc[q][t][0] += mma_16x16x32(D{}, a[q], b0, zero4);
                 acc[q][t][1] += mma_16x16x32(D{}, a[q], b1, zero4);
             }
@@ -1034,14 +1036,14 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     if constexpr (FRESH) {
         if (folds > 1) {
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
+            for (int q = 0; q < Q; ++q)
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
 #pragma unroll
                     for (int h = 0; h < 2; ++h) acc[q][t][h] = tot[q][t][h] + cmp[q][t][h];
         } else if (folds == 1) {
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
+            for (int q = 0; q < Q; ++q)
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
                     acc[q][t][0] = tot[q][t][0];
@@ -1058,8 +1060,12 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
         f32x4 v;
         v[0] = acc[0][t][0][0] + acc[0][t][1][1];
         v[1] = acc[0][t][0][2] + acc[0][t][1][3];
-        v[2] = acc[1][t][0][0] + acc[1][t][1][1];
-        v[3] = acc[1][t][0][2] + acc[1][t][1][3];
+        if constexpr (Q == 2) {
+            v[2] = acc[1][t][0][0] + acc[1][t][1][1];
+            v[3] = acc[1][t][0][2] + acc[1][t][1][3];
+        } else {
+            v[2] = v[3] = 0.f;  // no second row group
+        }
         partial[t * 64 + lane] = v;
     }
     __syncthreads();
@@ -1086,7 +1092,7 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
             }
             const int j = 16 * t + j0;
             const int64_t m0 = row0 + 4 * gq;
-            if (j < nvec) {
+            if (j < nvec && gq < 2 * Q) {
                 float* yp = Y + (int64_t)j * M + m0;
                 if (m0 + 3 < M && ((uintptr_t)yp & 15) == 0) {
                     f32x4 out = {o[0], o[1], o[2], o[3]};

@@ -146,8 +146,14 @@ constexpr int64_t kCUs = 256;
 // 7.87 / 8.50, 1024 6.04 / 6.66).  (2 wavefronts: 14336 22.2 and 23.7,
 // 28672 42.8 and 47.5.)
 constexpr int kMfmaManyTilesWaves = 4;
-constexpr int mfma_waves(int64_t M) {
-    return (M + kMfmaRows - 1) / kMfmaRows > kCUs ? kMfmaManyTilesWaves : kMfmaWaves;
+// Groups of 8 real rows per matrix-core workgroup: one while 8-row
+// workgroups fill the compute units at most once (M <= 2048), else two
+// (kMfmaRows).  fp16 K = 4096, µs, two groups / one, 4 and 16 vectors: 1024
+// rows 6.04 / 4.89 and 7.02 / 5.75, 2048 6.21 / 5.17 and 7.23 / 6.04; 3072
+// (one group in 384 workgroups of 4 wavefronts) 6.66 / 8.04 and 7.64 / 9.63.
+constexpr int mfma_row_groups(int64_t M) { return (M + 7) / 8 <= kCUs ? 1 : 2; }
+constexpr int mfma_waves(int64_t M, int groups) {
+    return (M + 8 * groups - 1) / (8 * groups) > kCUs ? kMfmaManyTilesWaves : kMfmaWaves;
 }
 // Up to this many vectors the matrix-core kernel reads its X operands
 // straight from memory (a load touches only the columns in use) instead of
@@ -664,11 +670,11 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
     }
     case BATCHED_MFMA:
         // each wavefront: 4 lanes per row and step, 16 rows; rows span the group
-        p.waves_per_group = mfma_waves(M);
+        p.row_tiles = mfma_row_groups(M);
+        p.waves_per_group = mfma_waves(M, p.row_tiles);
         p.lanes_per_row = 4 * p.waves_per_group;
-        p.rows_per_wave = kMfmaRows;
+        p.rows_per_wave = 8 * p.row_tiles;
         p.batch = mfma_chunk(nvec);
-        p.row_tiles = 1;
         p.lds_bytes = mfma_lds_bytes(nvec, p.waves_per_group);
         break;
     default:
@@ -680,7 +686,7 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
     else if (fam == GATED_SILU)
         p.rows_per_group = 1;
     else if (fam == BATCHED_MFMA)
-        p.rows_per_group = kMfmaRows;
+        p.rows_per_group = 8 * p.row_tiles;
     else
         p.rows_per_group = p.rows_per_wave * p.row_tiles * p.waves_per_group;
     p.grid = ceil_div(M, p.rows_per_group);

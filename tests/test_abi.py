@@ -291,15 +291,19 @@ def test_batched_plans():
         p("f16", 4096, 4096, nvec=65)
 
 
-def test_matrix_core_workgroups_past_one_tile_per_compute_unit():
-    """More 16-row tiles than the 256 compute units: workgroups of 4
-    wavefronts (half the LDS, so two share a unit), each walking twice the
-    64-wide steps; at most one tile per unit keeps 8."""
-    for M, waves in ((16, 8), (1024, 8), (4096, 8), (4097, 4), (6144, 4), (14336, 4)):
+def test_matrix_core_workgroup_shapes():
+    """Up to 2048 rows (8-row groups fill at most the 256 compute units once)
+    a workgroup takes one group of 8 rows, else two; more 16-row tiles than
+    compute units: workgroups of 4 wavefronts (half the LDS, so two share a
+    unit), each walking twice the 64-wide steps; otherwise 8."""
+    for M, waves, groups in ((16, 8, 1), (1024, 8, 1), (2048, 8, 1), (2049, 8, 2), (4096, 8, 2),
+                             (4097, 4, 2), (6144, 4, 2), (14336, 4, 2)):
         for nvec in (3, 16, 33):
             q = p("f16", M, 4096, nvec=nvec)
             assert q["family"] == lg.FAMILY_BATCHED_MFMA
-            assert (q["waves_per_group"], q["block"], q["grid"]) == (waves, 64 * waves, -(-M // 16))
+            assert (q["row_tiles"], q["rows_per_group"]) == (groups, 8 * groups)
+            assert (q["waves_per_group"], q["block"], q["grid"]) == \
+                (waves, 64 * waves, -(-M // (8 * groups)))
             assert q["passes"] == 4096 // 64 // waves
             tiles = 1 if nvec <= 16 else (2 if nvec <= 32 else 4)
             assert q["lds_bytes"] == waves * 16 * tiles * (q["batch"] * 128 + 16) <= 20 * 1024 * waves

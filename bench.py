@@ -75,7 +75,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the CPU oracle timing (0 = skip)")
     ap.add_argument("--kernel-only", action="store_true",
-                    help="only run the timed graph loop of --workload (for profilers)")
+                    help="only run the timed region of --workload, then as many launches "
+                         "as event-timed graph replays (for profilers)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="CPU only: read the counter CSVs of the two --counters runs and write "
                          "the traffic summary used for roofline.traffic")
@@ -87,7 +88,7 @@ def parse():
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="CPU only: per-kernel duration statistics of a rocprofv3 --kernel-trace "
                          "output directory (all dispatches, and the last --steps of each kernel: "
-                         "the timed region of a --kernel-only run); prints one JSON object")
+                         "the final graph replays of a --kernel-only run); prints one JSON object")
     ap.add_argument("--counters", action="store_true",
                     help="for rocprofv3 --pmc runs: a few eager launches of --workload over the "
                          "rotated buffers, then a plain device copy of COPY_BYTES for scaling")
@@ -139,7 +140,7 @@ def summarize_counters(fetch_dir, write_dir, workload):
 def summarize_trace(trace_dir, steps):
     """Duration statistics (ns) per kernel from rocprofv3's kernel trace:
     over every dispatch, and over each kernel's last `steps` dispatches (in
-    a --kernel-only run, its timed region)."""
+    a --kernel-only run, its final event-timed graph replays)."""
     import csv
     import numpy as np
     rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))))
@@ -799,6 +800,12 @@ def main():
         ms, lead, ahead = time_queued(torch, kloop, kfns, args.steps, args.warmup, WARM_SECONDS)
         log(f"kernel-only {args.workload}: {args.steps} launches, {1e3 * ms / args.steps:.3f} us "
             f"per launch (queue ahead of the GPU: {ahead})")
+        # then the same number of launches as replayed graphs, event-timed: the
+        # last `steps` dispatches of a trace of this run are these, back to
+        # back on the GPU even under a tracer that slows the host
+        gms = kloop.time(warmup=0)
+        log(f"kernel-only {args.workload}: then {args.steps} launches as graph replays, "
+            f"{1e3 * gms / args.steps:.3f} us per launch (event pair around the replays)")
         return
 
     case = gi.make_workload(args.workload)

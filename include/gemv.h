@@ -277,7 +277,7 @@ typedef enum {
     GEMV_FAMILY_WAVE_PER_ROW = 1,  /* one 64-lane wavefront per row */
     GEMV_FAMILY_GROUP_PER_ROW = 2, /* one workgroup per row, LDS reduction */
     GEMV_FAMILY_BATCHED = 3,       /* several rows × nvec vectors per wave */
-    GEMV_FAMILY_BATCHED_MFMA = 4,  /* 16 rows × 16 vectors on the matrix cores */
+    GEMV_FAMILY_BATCHED_MFMA = 4,  /* 8 or 16 rows × 16 vectors on the matrix cores */
     GEMV_FAMILY_GATED_SILU = 5,    /* a row of A_gate and of A_up per workgroup */
     GEMV_FAMILY_SPLIT_K = 6        /* a workgroup per two rows and K-slice, then a reduce */
 } gemv_family_t;
@@ -287,8 +287,12 @@ typedef struct {
     int vector_loads;    /* 1: 16-byte loads; 0: one element per load */
     int chunk_elems;     /* elements per load (16/size, or 1) */
     int lanes_per_row;   /* lanes that share one row's dot product */
-    int rows_per_wave;   /* rows one wavefront covers per row tile */
-    int row_tiles;       /* row tiles each wavefront takes in one pass */
+    int rows_per_wave;   /* rows one wavefront covers per row tile (matrix
+                            cores: the workgroup's rows, which its wavefronts
+                            share, each taking a slice of K) */
+    int row_tiles;       /* row tiles each wavefront takes in one pass
+                            (workgroup per row: rows per workgroup; matrix
+                            cores: groups of 8 rows per workgroup) */
     int waves_per_group; /* wavefronts per workgroup */
     int rows_per_group;  /* rows one workgroup produces */
     int batch;           /* loads per lane kept in flight per row */

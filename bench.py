@@ -85,6 +85,10 @@ def parse():
                          "workgroup, blocks per wavefront, cached/nontemporal, priority) over "
                          "rotated buffers of 8, 32 and 112 MiB, and the per-wavefront finish "
                          "times of the GEMV's own pattern; prints one JSON object")
+    ap.add_argument("--shard-sweep", action="store_true",
+                    help="time one GPU's share of the decode layer's seven projections when "
+                         "2, 4 or 8 GPUs share it, cut by rows and by K (one GPU; collectives "
+                         "not included); prints one JSON object")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="CPU only: per-kernel duration statistics of a rocprofv3 --kernel-trace "
                          "output directory (all dispatches, and the last --steps of each kernel: "
@@ -260,10 +264,12 @@ class FusedRotation:
     (``fused_qkv``) or the gate/up pair with the SiLU product
     (``fused_gate_up``); the matrices of one set share one x."""
 
-    def __init__(self, kind, gi, torch, min_bytes=2 * INFINITY_CACHE_BYTES):
+    def __init__(self, kind, gi, torch, min_bytes=2 * INFINITY_CACHE_BYTES, parts=None):
         import numpy as np
         self.kind = kind
-        self.parts = gi.make_fused_qkv() if kind == "fused_qkv" else list(gi.make_fused_gate_up())
+        if parts is None:
+            parts = gi.make_fused_qkv() if kind == "fused_qkv" else list(gi.make_fused_gate_up())
+        self.parts = parts
         p0 = self.parts[0]
         self.dtype, self.K = p0.dtype, p0.K
         a_bytes = sum(p.A.nbytes for p in self.parts)
@@ -276,7 +282,9 @@ class FusedRotation:
         for _ in range(self.R):
             self.sets.append(([a.to("cuda") for a in hA], hx.to("cuda"),
                               [torch.empty(m, dtype=torch.float32, device="cuda") for m in n_out]))
-        self.bytes = gi.fused_qkv_bytes() if kind == "fused_qkv" else gi.fused_gate_up_bytes()
+        # every matrix once, x once, the outputs once (fp32)
+        self.bytes = (sum(p.M * p.K * gi.ELEMENT_BYTES[p.dtype] for p in self.parts) +
+                      self.K * gi.ELEMENT_BYTES[p0.dtype] + 4 * sum(n_out))
         self.M = sum(p.M for p in self.parts)
 
     def callers(self, lg, stream_handle):
@@ -482,6 +490,102 @@ def probe_sweep(torch, lg, steps):
         del rot, times
         torch.cuda.empty_cache()
     return result
+
+
+SHARD_GPUS = (1, 2, 4, 8)
+
+
+def fused_shard_layer(torch, lg, gi, G, steps):
+    """One GPU's rows of the decode layer in four launches when G GPUs
+    share it by rows: q/k/v in one multi-GEMV, o, gate/up with the SiLU
+    product, down."""
+    seeds = {n: 640 + i for i, n in enumerate(gi.SWEEP_SHAPES)}
+
+    def part(name, x_of=None):
+        M, K = gi.SWEEP_SHAPES[name]
+        c = gi.make_random("bf16", M // G, K, seed=seeds[name], dist="normal", scale=0.02)
+        if x_of is not None:
+            c.X = x_of.X
+        return c
+
+    total_us, total_bytes, launches = 0.0, 0, {}
+    q = part("q")
+    gate = part("gate")
+    for label, rot in (("qkv", lambda: FusedRotation("fused_qkv", gi, torch,
+                                                     parts=[q, part("k", q), part("v", q)])),
+                       ("o", lambda: Rotation(part("o"), torch)),
+                       ("gate_up", lambda: FusedRotation("fused_gate_up", gi, torch,
+                                                         parts=[gate, part("up", gate)])),
+                       ("down", lambda: Rotation(part("down"), torch))):
+        r = rot()
+        call(r.callers(lg, torch.cuda.current_stream().cuda_stream)[0])
+        torch.cuda.synchronize()
+        if isinstance(r, FusedRotation):
+            ok, worst = r.sanity_check(torch)
+            nbytes = r.bytes
+        else:
+            ok, worst = sanity_check(r.case, r, torch)
+            nbytes = r.case.algorithmic_bytes()
+        if not ok:
+            raise RuntimeError(f"fused layer shard {G} {label}: output check failed ({worst:.3g})")
+        loop = GraphLoop(torch, r, lg, steps, per=r.R * max(1, 256 // r.R))
+        us = 1e3 * loop.time(warmup=min(steps, 500)) / steps
+        launches[label] = round(us, 3)
+        total_us += us
+        total_bytes += nbytes
+        del loop, r
+        torch.cuda.empty_cache()
+    return {"us_per_gpu": round(total_us, 3), "GBps_per_gpu": round(total_bytes / total_us / 1e3, 1),
+            "launches_us": launches}
+
+
+def shard_sweep(torch, lg, gi, steps):
+    """One GPU's share of the decode layer's seven bf16 projections when G
+    GPUs share it, at the share's real shape: cut by rows (M/G × K: each GPU
+    writes its own slice of y, no collective in the GEMV) or by K (M × K/G:
+    each GPU writes a partial y for a sum all-reduce of 4·M bytes, not
+    included here).  Graph loops of `steps` launches over rotated inputs per
+    shape; every output checked against torch's fp64 product first."""
+    out = {"steps": steps, "what": "us per launch of one GPU's share; collectives not included",
+           "cuts": []}
+    base = None
+    for G in SHARD_GPUS:
+        for cut in (("rows",) if G == 1 else ("rows", "k")):
+            shapes, total_us, total_bytes = {}, 0.0, 0
+            for i, (name, (M, K)) in enumerate(gi.SWEEP_SHAPES.items()):
+                m, k = (M // G, K) if cut == "rows" else (M, K // G)
+                case = gi.make_random("bf16", m, k, seed=640 + i, dist="normal", scale=0.02)
+                rot = Rotation(case, torch)
+                call(rot.callers(lg, torch.cuda.current_stream().cuda_stream)[0])
+                torch.cuda.synchronize()
+                ok, worst = sanity_check(case, rot, torch)
+                if not ok:
+                    raise RuntimeError(f"shard {G} {cut} {name}: output check failed ({worst:.3g})")
+                loop = GraphLoop(torch, rot, lg, steps, per=rot.R * max(1, 256 // rot.R))
+                us = 1e3 * loop.time(warmup=min(steps, 500)) / steps
+                nbytes = case.algorithmic_bytes()
+                plan = lg.plan("bf16", m, k, A_addr=rot.A[0].data_ptr(), X_addr=rot.X[0].data_ptr())
+                shapes[name] = {"M": m, "K": k, "us": round(us, 3),
+                                "GBps": round(nbytes / us / 1e3, 1),
+                                "family": lg.FAMILY_NAMES.get(plan["family"], "?")}
+                total_us += us
+                total_bytes += nbytes
+                del loop, rot
+                torch.cuda.empty_cache()
+            row = {"gpus": G, "cut": cut, "layer_us_per_gpu": round(total_us, 3),
+                   "layer_GBps_per_gpu": round(total_bytes / total_us / 1e3, 1), "shapes": shapes}
+            if cut == "rows":
+                row["fused_layer"] = fused_shard_layer(torch, lg, gi, G, steps)
+            if base is None:
+                base = total_us
+            row["speedup_vs_1_gpu"] = round(base / total_us, 3)
+            row["efficiency"] = round(base / (G * total_us), 3)
+            out["cuts"].append(row)
+            log(f"shards: {G} GPUs by {cut}: {total_us:.3f} us per GPU for the layer "
+                f"({row['speedup_vs_1_gpu']}x one GPU)"
+                + (f"; in four fused launches {row['fused_layer']['us_per_gpu']:.3f} us"
+                   if "fused_layer" in row else ""))
+    return out
 
 
 def call(fn_args):
@@ -789,6 +893,10 @@ def main():
 
     if args.probe_sweep:
         print(json.dumps(probe_sweep(torch, lg, args.steps)), flush=True)
+        return
+
+    if args.shard_sweep:
+        print(json.dumps(shard_sweep(torch, lg, gi, args.steps)), flush=True)
         return
 
     if args.kernel_only:

@@ -259,6 +259,14 @@ class Rotation:
 FUSED = ("fused_qkv", "fused_gate_up")
 
 
+def fused_bytes(kind, parts, gi):
+    """Algorithmic bytes of a fused call: every matrix once, x once, the
+    outputs once in fp32 (q/k/v: one output per matrix; gate/up: h)."""
+    n_out = sum(p.M for p in parts) if kind == "fused_qkv" else parts[0].M
+    return (sum(p.M * p.K * gi.ELEMENT_BYTES[p.dtype] for p in parts) +
+            parts[0].K * gi.ELEMENT_BYTES[parts[0].dtype] + 4 * n_out)
+
+
 class FusedRotation:
     """R device sets of a fused decode problem: q/k/v as one multi-GEMV
     (``fused_qkv``) or the gate/up pair with the SiLU product
@@ -282,9 +290,7 @@ class FusedRotation:
         for _ in range(self.R):
             self.sets.append(([a.to("cuda") for a in hA], hx.to("cuda"),
                               [torch.empty(m, dtype=torch.float32, device="cuda") for m in n_out]))
-        # every matrix once, x once, the outputs once (fp32)
-        self.bytes = (sum(p.M * p.K * gi.ELEMENT_BYTES[p.dtype] for p in self.parts) +
-                      self.K * gi.ELEMENT_BYTES[p0.dtype] + 4 * sum(n_out))
+        self.bytes = fused_bytes(kind, self.parts, gi)
         self.M = sum(p.M for p in self.parts)
 
     def callers(self, lg, stream_handle):

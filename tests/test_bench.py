@@ -49,3 +49,13 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, str(ROOT / "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, cwd=ROOT)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_fused_bytes_of_the_named_and_sharded_layers():
+    import gemv_inputs as gi
+    assert bench.fused_bytes("fused_qkv", gi.make_fused_qkv(), gi) == gi.fused_qkv_bytes()
+    assert bench.fused_bytes("fused_gate_up", list(gi.make_fused_gate_up()), gi) == \
+        gi.fused_gate_up_bytes()
+    # a row shard: 1/8 of the rows, the same x
+    parts = [gi.make_random("bf16", M // 8, K, seed=1) for M, K in ((4096, 4096), (1024, 4096))]
+    assert bench.fused_bytes("fused_qkv", parts, gi) == (512 + 128) * 4096 * 2 + 4096 * 2 + 4 * 640

@@ -314,22 +314,29 @@ const void* batched_fn(int nvec) {
     }
 }
 
-// matrix-core kernels of W wavefronts and Q groups of 8 rows per workgroup
-template <class D, int W, int Q>
+// matrix-core kernels of W wavefronts and Q groups of RG rows per workgroup
+template <class D, int W, int Q, int RG>
 const void* mfma_fn(int nvec) {
-    if (nvec <= gemvplan::kMfmaFewVectors)
-        return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 1, gemvplan::mfma_chunk(16), true, Q>;
+    if (nvec <= gemvplan::kMfmaFewVectors) {
+        // (groups of 4 rows only with X staged in LDS)
+        if constexpr (RG == 8)
+            return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 1, gemvplan::mfma_chunk(16), true, Q, RG>;
+        return nullptr;
+    }
     switch (gemvplan::mfma_tiles(nvec)) {
-    case 1: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 1, gemvplan::mfma_chunk(16), false, Q>;
-    case 2: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 2, gemvplan::mfma_chunk(32), false, Q>;
-    case 4: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 4, gemvplan::mfma_chunk(64), false, Q>;
+    case 1: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 1, gemvplan::mfma_chunk(16), false, Q, RG>;
+    case 2: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 2, gemvplan::mfma_chunk(32), false, Q, RG>;
+    case 4: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 4, gemvplan::mfma_chunk(64), false, Q, RG>;
     default: return nullptr;
     }
 }
 template <class D, int W>
-const void* mfma_fn(int nvec, int groups) {
-    if (groups == 2) return mfma_fn<D, W, 2>(nvec);
-    if (groups == 1) return mfma_fn<D, W, 1>(nvec);
+const void* mfma_fn(int nvec, int groups, int rows) {
+    if (groups == 2 && rows == 16) return mfma_fn<D, W, 2, 8>(nvec);
+    if (groups == 1 && rows == 8) return mfma_fn<D, W, 1, 8>(nvec);
+    // one group of 4 rows only at one workgroup per compute unit or fewer
+    if constexpr (W == gemvplan::kMfmaWaves)
+        if (groups == 1 && rows == 4) return mfma_fn<D, W, 1, 4>(nvec);
     return nullptr;
 }
 
@@ -340,9 +347,9 @@ const void* batched_kernel(const Plan& p, int nvec) {
             return p.vector_loads ? batched_fn<D, true>(nvec) : batched_fn<D, false>(nvec);
         if (p.family == gemvplan::BATCHED_MFMA && p.vector_loads) {
             if (p.waves_per_group == gemvplan::kMfmaWaves)
-                return mfma_fn<D, gemvplan::kMfmaWaves>(nvec, p.row_tiles);
+                return mfma_fn<D, gemvplan::kMfmaWaves>(nvec, p.row_tiles, p.rows_per_group);
             if (p.waves_per_group == gemvplan::kMfmaManyTilesWaves)
-                return mfma_fn<D, gemvplan::kMfmaManyTilesWaves>(nvec, p.row_tiles);
+                return mfma_fn<D, gemvplan::kMfmaManyTilesWaves>(nvec, p.row_tiles, p.rows_per_group);
         }
     }
     return nullptr;

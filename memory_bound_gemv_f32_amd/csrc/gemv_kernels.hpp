@@ -794,7 +794,8 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
 // step's tile plus the odd row of the second's.
 //
 // A workgroup owns Q groups of 8 real rows (Q = 2, or 1 where that spreads
-// a small matrix over more compute units); its W wavefronts split the
+// a small matrix over more compute units, or one group of 4 for smaller
+// matrices still); its W wavefronts split the
 // 64-element steps of K into contiguous slices and walk them in chunks of CH
 // steps.  Per chunk a wavefront issues the loads of X operands ahead
 // of the loads of A that they meet: loads complete in issue order, so the X
@@ -824,7 +825,7 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
 // to the wavefronts by gemvplan::mfma_step_range; the steps of a run that do
 // not fill a whole chunk, and the partial step, read their operands
 // directly, one step at a time.
-template <class D, int W, int NT, int CH, bool FEW, int Q = 2>
+template <class D, int W, int NT, int CH, bool FEW, int Q = 2, int RG = 8>
 __global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2)))
 gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
                          const typename D::storage* __restrict__ X,
@@ -845,12 +846,17 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     const int r = lane & 15;  // operand row (A) / column within a tile (X)
     const int g = lane >> 4;  // 8-element group within a 32-element half-step
     const int half = r & 1;
-    static_assert(Q == 1 || Q == 2, "one or two groups of 8 rows");
-    const int64_t row0 = (int64_t)blockIdx.x * (8 * Q);
+    // Q groups of RG real rows: RG = 8 fills the 16 operand rows with the
+    // halves of 8 rows; RG = 4 (one group) gives the operand rows of real
+    // rows 4..7 the addresses of rows 0..3, so their loads fetch no bytes of
+    // their own and their duplicate outputs are never stored
+    static_assert(Q == 1 || Q == 2, "one or two groups of rows");
+    static_assert(RG == 8 || (RG == 4 && Q == 1), "groups of 8 rows, or one group of 4");
+    const int64_t row0 = (int64_t)blockIdx.x * (RG * Q);
     const S* ap[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
-        const int64_t row = row0 + 8 * q + (r >> 1);
+        const int64_t row = row0 + RG * q + ((r >> 1) & (RG - 1));
         ap[q] = A + (row < M ? row : (int64_t)M - 1) * lda + 32 * half + 8 * g;
     }
 
@@ -1092,7 +1098,7 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
             }
             const int j = 16 * t + j0;
             const int64_t m0 = row0 + 4 * gq;
-            if (j < nvec && gq < 2 * Q) {
+            if (j < nvec && 4 * gq < RG * Q) {
                 float* yp = Y + (int64_t)j * M + m0;
                 if (m0 + 3 < M && ((uintptr_t)yp & 15) == 0) {
                     f32x4 out = {o[0], o[1], o[2], o[3]};

@@ -127,12 +127,18 @@ constexpr int kGroupStreamRows = 4;
 constexpr int batched_rows(int nvec) { return nvec <= 4 ? 2 : 1; }
 constexpr int batched_batch(int nvec) { return nvec <= 2 ? 4 : 2; }
 constexpr bool batched_x_ahead(int nvec) { return nvec <= 8; }
-// Matrix-core batched family: 16 rows per workgroup, its wavefronts split K
-// and walk their slice in chunks of this many 64-wide steps (the A loads of a
-// chunk are in flight together; X's chunk is staged in LDS).
+// Matrix-core batched family: up to kMfmaRows rows per workgroup (4, 8 or
+// 16, below), its wavefronts split K and walk their slice in chunks of this
+// many 64-wide steps (the A loads of a chunk are in flight together; X's
+// chunk is staged in LDS).
 constexpr int kMfmaRows = 16;
 constexpr int kMfmaWaves = 8;
 constexpr int kMfmaChunk = 8;
+// Up to this many vectors the matrix-core kernel reads its X operands
+// straight from memory (a load touches only the columns in use) instead of
+// staging X in LDS (fp16 4096 × 4096, µs, straight / staged: 3 vectors
+// 7.07 / 7.15, 4 7.19 / 7.25, 5 7.25 / 7.27, 6 7.38 / 7.30, 8 7.63 / 7.38).
+constexpr int kMfmaFewVectors = 5;
 // Compute units of the GPU this library is built for (MI355X).
 constexpr int64_t kCUs = 256;
 // With more 16-row tiles than compute units, workgroups of
@@ -152,14 +158,18 @@ constexpr int kMfmaManyTilesWaves = 4;
 // rows 6.04 / 4.89 and 7.02 / 5.75, 2048 6.21 / 5.17 and 7.23 / 6.04; 3072
 // (one group in 384 workgroups of 4 wavefronts) 6.66 / 8.04 and 7.64 / 9.63.
 constexpr int mfma_row_groups(int64_t M) { return (M + 7) / 8 <= kCUs ? 1 : 2; }
-constexpr int mfma_waves(int64_t M, int groups) {
-    return (M + 8 * groups - 1) / (8 * groups) > kCUs ? kMfmaManyTilesWaves : kMfmaWaves;
+// Real rows per group: 8, or, with X staged in LDS (more than
+// kMfmaFewVectors vectors), 4 (one group) while 4-row workgroups fill the
+// compute units at most once (M <= 1024).  fp16 K = 4096, µs, 8 / 4 rows per
+// workgroup: 16 vectors 256 rows 5.53 / 5.01, 1024 rows 5.75 / 5.29; 33
+// vectors 1024 rows 10.18 / 10.09; with X read straight from memory 4 rows
+// gained nothing (2 vectors 4.73 / 4.75, 4 vectors 4.89 / 4.95 at 1024 rows).
+constexpr int mfma_group_rows(int64_t M, int nvec) {
+    return nvec > kMfmaFewVectors && (M + 3) / 4 <= kCUs ? 4 : 8;
 }
-// Up to this many vectors the matrix-core kernel reads its X operands
-// straight from memory (a load touches only the columns in use) instead of
-// staging X in LDS (fp16 4096 × 4096, µs, straight / staged: 3 vectors
-// 7.07 / 7.15, 4 7.19 / 7.25, 5 7.25 / 7.27, 6 7.38 / 7.30, 8 7.63 / 7.38).
-constexpr int kMfmaFewVectors = 5;
+constexpr int mfma_waves(int64_t M, int rows_per_group) {
+    return (M + rows_per_group - 1) / rows_per_group > kCUs ? kMfmaManyTilesWaves : kMfmaWaves;
+}
 // 16-vector tiles for nvec vectors (1, 2 or 4); the chunk shrinks as the
 // tiles grow so that the X staged per chunk stays 16 KiB per wavefront.
 constexpr int mfma_tiles(int nvec) { return nvec <= 16 ? 1 : (nvec <= 32 ? 2 : 4); }
@@ -671,9 +681,9 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
     case BATCHED_MFMA:
         // each wavefront: 4 lanes per row and step, 16 rows; rows span the group
         p.row_tiles = mfma_row_groups(M);
-        p.waves_per_group = mfma_waves(M, p.row_tiles);
+        p.rows_per_wave = mfma_group_rows(M, nvec) * p.row_tiles;
+        p.waves_per_group = mfma_waves(M, p.rows_per_wave);
         p.lanes_per_row = 4 * p.waves_per_group;
-        p.rows_per_wave = 8 * p.row_tiles;
         p.batch = mfma_chunk(nvec);
         p.lds_bytes = mfma_lds_bytes(nvec, p.waves_per_group);
         break;
@@ -686,7 +696,7 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
     else if (fam == GATED_SILU)
         p.rows_per_group = 1;
     else if (fam == BATCHED_MFMA)
-        p.rows_per_group = 8 * p.row_tiles;
+        p.rows_per_group = p.rows_per_wave;
     else
         p.rows_per_group = p.rows_per_wave * p.row_tiles * p.waves_per_group;
     p.grid = ceil_div(M, p.rows_per_group);

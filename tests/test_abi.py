@@ -292,18 +292,21 @@ def test_batched_plans():
 
 
 def test_matrix_core_workgroup_shapes():
-    """Up to 2048 rows (8-row groups fill at most the 256 compute units once)
-    a workgroup takes one group of 8 rows, else two; more 16-row tiles than
-    compute units: workgroups of 4 wavefronts (half the LDS, so two share a
-    unit), each walking twice the 64-wide steps; otherwise 8."""
-    for M, waves, groups in ((16, 8, 1), (1024, 8, 1), (2048, 8, 1), (2049, 8, 2), (4096, 8, 2),
-                             (4097, 4, 2), (6144, 4, 2), (14336, 4, 2)):
+    """Up to 1024 rows a workgroup takes 4 rows (with X staged in LDS: more
+    than 5 vectors), up to 2048 one group of 8 (each size fills the 256
+    compute units at most once), else two groups of 8; more 16-row tiles
+    than compute units: workgroups of 4 wavefronts (half the LDS, so two
+    share a unit), each walking twice the 64-wide steps; otherwise 8."""
+    for M, waves, groups, rows in ((16, 8, 1, 4), (1024, 8, 1, 4), (1025, 8, 1, 8), (2048, 8, 1, 8),
+                                   (2049, 8, 2, 16), (4096, 8, 2, 16), (4097, 4, 2, 16),
+                                   (6144, 4, 2, 16), (14336, 4, 2, 16)):
         for nvec in (3, 16, 33):
+            want = 8 if nvec <= 5 and rows == 4 else rows  # X read straight from memory: 8
             q = p("f16", M, 4096, nvec=nvec)
             assert q["family"] == lg.FAMILY_BATCHED_MFMA
-            assert (q["row_tiles"], q["rows_per_group"]) == (groups, 8 * groups)
+            assert (q["row_tiles"], q["rows_per_group"]) == (groups, want)
             assert (q["waves_per_group"], q["block"], q["grid"]) == \
-                (waves, 64 * waves, -(-M // (8 * groups)))
+                (waves, 64 * waves, -(-M // want))
             assert q["passes"] == 4096 // 64 // waves
             tiles = 1 if nvec <= 16 else (2 if nvec <= 32 else 4)
             assert q["lds_bytes"] == waves * 16 * tiles * (q["batch"] * 128 + 16) <= 20 * 1024 * waves

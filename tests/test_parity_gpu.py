@@ -500,20 +500,22 @@ def test_integer_batched_partial_last_step(dtype, nvec):
                              f"{dtype} 33x{K} nvec={nvec} family {fam}")
 
 
-# matrix-core workgroup shapes: (rows, wavefronts, groups of 8 rows).  Up to
-# 2048 rows one group per workgroup; more 16-row tiles than compute units:
-# 4 wavefronts, each walking two chunks and the leftover steps of its longer
-# K run.  Every row count leaves the last workgroup partly past the end.
-MFMA_GEOMETRIES = [(1031, 8, 1), (2057, 8, 2), (4113, 4, 2)]
+# matrix-core workgroup shapes: (rows, wavefronts, row groups, rows per
+# workgroup).  Up to 1024 rows one group of 4, up to 2048 one group of 8;
+# more 16-row tiles than compute units: 4 wavefronts, each walking two chunks
+# and the leftover steps of its longer K run.  Every row count leaves the
+# last workgroup partly past the end.
+MFMA_GEOMETRIES = [(1021, 8, 1, 4), (1031, 8, 1, 8), (2057, 8, 2, 16), (4113, 4, 2, 16)]
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("M,waves,groups", MFMA_GEOMETRIES)
-def test_integer_batched_workgroup_shapes(dtype, M, waves, groups):
+@pytest.mark.parametrize("M,waves,groups,rows", MFMA_GEOMETRIES)
+def test_integer_batched_workgroup_shapes(dtype, M, waves, groups, rows):
     for K, nvec in ((4096, 3), (4096, 16), (1000, 33), (2680, 17)):
         q = lg.plan(dtype, M, K, K, nvec, 1 << 20, 1 << 20)
         assert q["family"] == lg.FAMILY_BATCHED_MFMA, q
-        assert (q["waves_per_group"], q["row_tiles"], q["rows_per_group"]) == (waves, groups, 8 * groups), q
+        want = 8 if rows == 4 and nvec <= 5 else rows  # 4-row groups: X staged in LDS only
+        assert (q["waves_per_group"], q["row_tiles"], q["rows_per_group"]) == (waves, groups, want), q
         case = gi.make_integer(dtype, M, K, seed=K + nvec, nvec=nvec, bias=nvec % 2 == 1)
         ref, _ = run_oracle(case)
         what = f"{dtype} {M}x{K} nvec={nvec}: {waves} wavefronts, {groups} row groups, chunk {q['batch']}"

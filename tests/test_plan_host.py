@@ -14,7 +14,7 @@ import memory_bound_gemv_f32_amd as lg
 
 TESTS = Path(__file__).resolve().parent
 ALIGNED = 1 << 20
-WAVES = 8  # wavefronts of a matrix-core workgroup
+WAVES = (8, 4)  # wavefronts of a matrix-core workgroup (4 past one tile per compute unit)
 
 
 @pytest.fixture(scope="module")
@@ -31,21 +31,21 @@ def shim(tmp_path_factory):
     return lib
 
 
-def step_range(lib, K, wave):
+def step_range(lib, K, wave, waves):
     f, e = ctypes.c_int(), ctypes.c_int()
-    lib.shim_mfma_step_range(K, WAVES, wave, ctypes.byref(f), ctypes.byref(e))
+    lib.shim_mfma_step_range(K, waves, wave, ctypes.byref(f), ctypes.byref(e))
     return f.value, e.value
 
 
-def groups_covered(lib, K, ch):
+def groups_covered(lib, K, ch, waves):
     """How often the matrix-core kernel's loops visit each 8-element group of
     a row: whole chunks of `ch` 64-element steps, then the rest of the run
     one step at a time, reading only groups that start below K."""
     n_groups = K // 8
     seen = np.zeros(n_groups + 16, dtype=np.int64)
     whole = K // 64
-    for wave in range(WAVES):
-        first, end = step_range(lib, K, wave)
+    for wave in range(waves):
+        first, end = step_range(lib, K, wave, waves)
         c = first
         s1 = min(end, whole)
         while c + ch <= s1:
@@ -63,20 +63,22 @@ def test_mfma_steps_cover_every_group_once(shim):
     takes), for the chunk lengths of 1, 2 and 4 vector tiles: each 8-element
     group of a row is visited exactly once, nothing past K is, the partial
     last step included (the K = 72..120, 136..184, ... lengths that lost it)."""
-    for ch in (8, 4, 2):
-        for K in range(8, (1 << 16) + 1, 8):
-            inside, past = groups_covered(shim, K, ch)
-            assert np.all(inside == 1), (K, ch, np.flatnonzero(inside != 1)[:5])
-            assert not past.any(), (K, ch)
+    for waves in WAVES:
+        for ch in (8, 4, 2):
+            for K in range(8, (1 << 16) + 1, 8):
+                inside, past = groups_covered(shim, K, ch, waves)
+                assert np.all(inside == 1), (K, ch, waves, np.flatnonzero(inside != 1)[:5])
+                assert not past.any(), (K, ch, waves)
 
 
 def test_mfma_step_runs_are_contiguous(shim):
-    for K in (0, 8, 64, 72, 200, 4096, 4104, 2680, 65536, 1 << 20):
-        steps = -(-K // 64)
-        runs = [step_range(shim, K, w) for w in range(WAVES)]
-        assert runs[0][0] == 0 and runs[-1][1] == steps
-        for (f0, e0), (f1, e1) in zip(runs, runs[1:]):
-            assert f0 <= e0 == f1 <= e1
+    for waves in WAVES:
+        for K in (0, 8, 64, 72, 200, 4096, 4104, 2680, 65536, 1 << 20):
+            steps = -(-K // 64)
+            runs = [step_range(shim, K, w, waves) for w in range(waves)]
+            assert runs[0][0] == 0 and runs[-1][1] == steps
+            for (f0, e0), (f1, e1) in zip(runs, runs[1:]):
+                assert f0 <= e0 == f1 <= e1
 
 
 def test_compensated_roundings(shim):
@@ -115,6 +117,54 @@ def test_every_automatic_plan_has_a_kernel(dtype):
                             lg.plan(dtype, M, K, lda, nvec, A, A)
 
 
+def _launchable(q, M):
+    """What every plan must satisfy to be launched as planned: whole
+    wavefronts, at most 1024 threads and 160 KiB of LDS per workgroup, and a
+    grid whose workgroups cover the rows exactly (the last one possibly
+    partly past the end)."""
+    assert q["block"] % 64 == 0 and 64 <= q["block"] <= 1024, q
+    assert q["block"] == 64 * q["waves_per_group"], q
+    assert 0 <= q["lds_bytes"] <= 160 * 1024, q
+    rows = q["rows_per_group"]
+    tiles = q["grid"] // q["splits"] if q["family"] == lg.FAMILY_SPLIT_K else q["grid"]
+    assert rows >= 1 and (tiles - 1) * rows < M <= tiles * rows, (M, q)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_every_plan_is_launchable(dtype):
+    checked = 0
+    es = {"f32": 4, "f16": 2, "bf16": 2}[dtype]
+    for M in ROW_COUNTS + [1025, 1535, 1536, 2048, 2049, 2560, 4097, 4113]:
+        for rb in ROW_BYTES:
+            K = rb // es
+            if K == 0 or M * K > 1 << 34:
+                continue
+            for lda, A in ((K, ALIGNED), (K + 1, ALIGNED), (K, ALIGNED + es)):
+                for fam in (lg.FAMILY_AUTO, lg.FAMILY_ROWS_PER_WAVE, lg.FAMILY_WAVE_PER_ROW,
+                            lg.FAMILY_GROUP_PER_ROW):
+                    try:
+                        q = lg.plan(dtype, M, K, lda, 1, A, A, fam)
+                    except lg.GemvError:
+                        continue
+                    _launchable(q, M)
+                    checked += 1
+                if dtype != "f32":
+                    for nvec in (2, 5, 6, 16, 33, 64):
+                        if M * K * nvec > 1 << 34:
+                            continue
+                        for fam in (lg.FAMILY_AUTO, lg.FAMILY_BATCHED, lg.FAMILY_BATCHED_MFMA):
+                            try:
+                                q = lg.plan(dtype, M, K, lda, nvec, A, A, fam)
+                            except lg.GemvError:
+                                continue
+                            _launchable(q, M)
+                            checked += 1
+            if M < 192 and K >= 8192:
+                q = lg.plan_splitk(dtype, M, K, A_addr=ALIGNED, x_addr=ALIGNED)
+                _launchable(q, M)
+    assert checked > 1000
+
+
 @pytest.mark.parametrize("xdtype", ["f32", "f16", "bf16"])
 def test_every_automatic_int8_plan_has_a_kernel(xdtype):
     """Int8 rows of 17-24 loads on very tall matrices (K 257..384 at 2^19 rows
@@ -126,6 +176,8 @@ def test_every_automatic_int8_plan_has_a_kernel(xdtype):
                 q = lg.plan_q8(xdtype, M, K, ldq, Q, ALIGNED)
                 assert q["batch"] == 1 or q["lanes_per_row"] == 64 or \
                     q["family"] == lg.FAMILY_GROUP_PER_ROW, (M, K, q)
+                if K > 0:
+                    _launchable(q, M)
 
 
 def test_tall_int8_rows_keep_one_load_per_lane():

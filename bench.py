@@ -103,15 +103,41 @@ COPY_BYTES = 256 << 20   # the calibration copy: reads and writes this many byte
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+def source_code_only(text: str) -> str:
+    """C++ source with its comments removed and whitespace runs collapsed
+    (string and character literals kept as they are)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        ch = text[i]
+        if ch in "\"'":  # a literal: copy up to its closing quote
+            j = i + 1
+            while j < n and text[j] != ch:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(ch)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
-    """Hash of every HIP / host source of the library: counter figures taken
-    from one version of the kernels are not reported for another."""
+    """Hash of every HIP / host source of the library, comments and layout
+    aside: counter figures taken from one version of the code are not
+    reported for another."""
     import hashlib
     csrc = os.path.join(ROOT, "memory_bound_gemv_f32_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + source_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

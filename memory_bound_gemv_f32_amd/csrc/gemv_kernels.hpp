@@ -793,15 +793,14 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
 // and the others are dropped.  Real row R's sum is the even row of the first
 // step's tile plus the odd row of the second's.
 //
-// A workgroup owns Q groups of 8 real rows (Q = 2, or 1 where that spreads
-// a small matrix over more compute units, or one group of 4 for smaller
-// matrices still); its W wavefronts split the
-// 64-element steps of K into contiguous slices and walk them in chunks of CH
-// steps.  Per chunk a wavefront issues the loads of X operands ahead
-// of the loads of A that they meet: loads complete in issue order, so the X
-// operands are ready when the A they meet lands and each step's MFMAs run
-// as its A arrives (with all A loads first, every MFMA waited for the last
-// X load: 16 vectors 9.04 -> 8.76 µs).  X columns are K elements apart, so
+// A workgroup owns Q groups of RG real rows (two groups of 8; one group of 8
+// or of 4 where that spreads a small matrix over more compute units); its W
+// wavefronts split the 64-element steps of K into contiguous slices and walk
+// them in chunks of CH steps.  Per chunk a wavefront issues the loads of X
+// operands ahead of the loads of A that they meet: loads complete in issue
+// order, so the X operands are ready when the A they meet lands and each
+// step's MFMAs run as its A arrives (with all A loads first, every MFMA
+// waited for the last X load: 16 vectors 9.04 -> 8.76 µs).  X columns are K elements apart, so
 // an X operand read straight from memory sends one load to 16 addresses a
 // column pitch apart:
 //   * with more than kMfmaFewVectors vectors, the K range of every X column

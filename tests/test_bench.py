@@ -59,3 +59,12 @@ def test_fused_bytes_of_the_named_and_sharded_layers():
     # a row shard: 1/8 of the rows, the same x
     parts = [gi.make_random("bf16", M // 8, K, seed=1) for M, K in ((4096, 4096), (1024, 4096))]
     assert bench.fused_bytes("fused_qkv", parts, gi) == (512 + 128) * 4096 * 2 + 4096 * 2 + 4 * 640
+
+
+def test_source_hash_ignores_comments_and_layout():
+    code = 'int f(int a) {\n  return a + 1;  // one more\n}\n/* note */ const char* s = "// not a comment";\n'
+    same = 'int f(int a) { return a + 1;\n}   const char* s = "// not a comment";'
+    assert bench.source_code_only(code) == bench.source_code_only(same)
+    assert bench.source_code_only("a = 1; // x") != bench.source_code_only("a = 2; // x")
+    assert '"// not a comment"' in bench.source_code_only(code)
+    assert bench.source_code_only("x /* a */ y") == "x y"

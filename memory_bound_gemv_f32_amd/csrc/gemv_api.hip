@@ -284,34 +284,41 @@ const void* single_fn(const Plan& p) {
 
 // ---- batched ----------------------------------------------------------------
 
-template <class D, int NV, bool VEC>
+template <class D, int NV, int R, bool VEC>
 const void* batched_fn_nv() {
-    return (const void*)&gemvdev::gemv_batched_kernel<D, NV, gemvplan::batched_rows(NV),
-                                                      gemvplan::batched_batch(NV),
+    return (const void*)&gemvdev::gemv_batched_kernel<D, NV, R, gemvplan::batched_batch(NV),
                                                       gemvplan::batched_x_ahead(NV), VEC>;
 }
 
-template <class D, bool VEC>
+template <class D, int R, bool VEC>
 const void* batched_fn(int nvec) {
     switch (nvec) {
-    case 1: return batched_fn_nv<D, 1, VEC>();
-    case 2: return batched_fn_nv<D, 2, VEC>();
-    case 3: return batched_fn_nv<D, 3, VEC>();
-    case 4: return batched_fn_nv<D, 4, VEC>();
-    case 5: return batched_fn_nv<D, 5, VEC>();
-    case 6: return batched_fn_nv<D, 6, VEC>();
-    case 7: return batched_fn_nv<D, 7, VEC>();
-    case 8: return batched_fn_nv<D, 8, VEC>();
-    case 9: return batched_fn_nv<D, 9, VEC>();
-    case 10: return batched_fn_nv<D, 10, VEC>();
-    case 11: return batched_fn_nv<D, 11, VEC>();
-    case 12: return batched_fn_nv<D, 12, VEC>();
-    case 13: return batched_fn_nv<D, 13, VEC>();
-    case 14: return batched_fn_nv<D, 14, VEC>();
-    case 15: return batched_fn_nv<D, 15, VEC>();
-    case 16: return batched_fn_nv<D, 16, VEC>();
+    case 1: return batched_fn_nv<D, 1, R, VEC>();
+    case 2: return batched_fn_nv<D, 2, R, VEC>();
+    case 3: return batched_fn_nv<D, 3, R, VEC>();
+    case 4: return batched_fn_nv<D, 4, R, VEC>();
+    case 5: return batched_fn_nv<D, 5, R, VEC>();
+    case 6: return batched_fn_nv<D, 6, R, VEC>();
+    case 7: return batched_fn_nv<D, 7, R, VEC>();
+    case 8: return batched_fn_nv<D, 8, R, VEC>();
+    case 9: return batched_fn_nv<D, 9, R, VEC>();
+    case 10: return batched_fn_nv<D, 10, R, VEC>();
+    case 11: return batched_fn_nv<D, 11, R, VEC>();
+    case 12: return batched_fn_nv<D, 12, R, VEC>();
+    case 13: return batched_fn_nv<D, 13, R, VEC>();
+    case 14: return batched_fn_nv<D, 14, R, VEC>();
+    case 15: return batched_fn_nv<D, 15, R, VEC>();
+    case 16: return batched_fn_nv<D, 16, R, VEC>();
     default: return nullptr;
     }
+}
+
+// R rows per wavefront (1 or 2), from the plan
+template <class D, bool VEC>
+const void* batched_fn(int nvec, int rows) {
+    if (rows == 1) return batched_fn<D, 1, VEC>(nvec);
+    if (rows == 2) return batched_fn<D, 2, VEC>(nvec);
+    return nullptr;
 }
 
 // matrix-core kernels of W wavefronts and Q groups of RG rows per workgroup
@@ -344,7 +351,8 @@ template <class D>
 const void* batched_kernel(const Plan& p, int nvec) {
     if constexpr (D::bytes == 2) {
         if (p.family == gemvplan::BATCHED)
-            return p.vector_loads ? batched_fn<D, true>(nvec) : batched_fn<D, false>(nvec);
+            return p.vector_loads ? batched_fn<D, true>(nvec, p.rows_per_wave)
+                                  : batched_fn<D, false>(nvec, p.rows_per_wave);
         if (p.family == gemvplan::BATCHED_MFMA && p.vector_loads) {
             if (p.waves_per_group == gemvplan::kMfmaWaves)
                 return mfma_fn<D, gemvplan::kMfmaWaves>(nvec, p.row_tiles, p.rows_per_group);

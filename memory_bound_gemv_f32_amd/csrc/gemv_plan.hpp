@@ -118,13 +118,27 @@ constexpr int64_t kGroupStreamMinXBytes = 8 * 1024;
 constexpr int kGroupStreamWaves = 4;
 constexpr int kGroupStreamMaxChunks = 6;
 constexpr int kGroupStreamRows = 4;
+// Compute units of the GPU this library is built for (MI355X).
+constexpr int64_t kCUs = 256;
 // Batched family on the vector ALUs (a wavefront per group of rows, all
 // vectors at once): rows per wavefront (they share every X chunk), loads of
 // A per lane per batch, and whether a batch's X chunks are loaded with its A
 // chunks (few vectors) or chunk by chunk after them (many: their X chunks
 // would not fit the registers), chosen so that the loaded chunks, the
 // accumulators and the compensated sums fit two wavefronts per SIMD.
-constexpr int batched_rows(int nvec) { return nvec <= 4 ? 2 : 1; }
+// Two rows per wavefront once the grid of 2-row workgroups (4 wavefronts,
+// 8 rows) covers every compute unit at least twice, or more than once with
+// 4 or more vectors; else one, whose grid of twice as many workgroups keeps
+// more wavefronts in flight.  fp16, K = 4100 (the unaligned rows this
+// family serves), µs, one row / two: 1024 rows, 2 vectors 3.87 / 5.02 and
+// 16 vectors 10.93 / 15.66; 2048 rows, 4 vectors 6.45 / 8.05; 3072 rows,
+// 2 vectors 6.76 / 7.68 and 8 vectors 15.00 / 13.47; 4096 rows, 4 vectors
+// 11.34 / 9.14 and 16 vectors 30.20 / 24.24; 8192 rows, 2 vectors 14.61 /
+// 13.13 and 16 vectors 57.30 / 44.11.
+constexpr int batched_rows(int64_t M, int nvec) {
+    const int64_t groups = (M + 7) / 8;
+    return groups >= 2 * kCUs || (groups > kCUs && nvec >= 4) ? 2 : 1;
+}
 constexpr int batched_batch(int nvec) { return nvec <= 2 ? 4 : 2; }
 constexpr bool batched_x_ahead(int nvec) { return nvec <= 8; }
 // Matrix-core batched family: up to kMfmaRows rows per workgroup (4, 8 or
@@ -139,8 +153,6 @@ constexpr int kMfmaChunk = 8;
 // staging X in LDS (fp16 4096 × 4096, µs, straight / staged: 3 vectors
 // 7.07 / 7.15, 4 7.19 / 7.25, 5 7.25 / 7.27, 6 7.38 / 7.30, 8 7.63 / 7.38).
 constexpr int kMfmaFewVectors = 5;
-// Compute units of the GPU this library is built for (MI355X).
-constexpr int64_t kCUs = 256;
 // With more 16-row tiles than compute units, workgroups of
 // kMfmaManyTilesWaves wavefronts (each walking two chunks of its longer K
 // run, half the LDS): two fit on a compute unit, so one's loads overlap the
@@ -660,7 +672,7 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         // the first block's
         if (nvec > kValuVectors) nvec = kValuVectors;
         p.lanes_per_row = kWave;
-        p.rows_per_wave = batched_rows(nvec);
+        p.rows_per_wave = batched_rows(M, nvec);
         p.waves_per_group = kBlock / kWave;
         p.batch = batched_batch(nvec);
         p.row_tiles = 1;

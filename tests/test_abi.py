@@ -291,6 +291,23 @@ def test_batched_plans():
         p("f16", 4096, 4096, nvec=65)
 
 
+def test_vector_alu_batched_rows_per_wavefront():
+    """Two rows per wavefront once the 2-row grid (8 rows per workgroup)
+    covers the 256 compute units twice, or more than once with 4 or more
+    vectors; else one row, with twice as many workgroups."""
+    for M, nvec, rows in ((1024, 2, 1), (2048, 16, 1), (2049, 3, 1), (2049, 4, 2),
+                          (3072, 2, 1), (3072, 8, 2), (4088, 2, 1), (4089, 2, 2),
+                          (4096, 16, 2), (8192, 5, 2), (7, 16, 1)):
+        q = p("f16", M, 4100, nvec=nvec)
+        assert q["family"] == lg.FAMILY_BATCHED, (M, nvec)
+        assert q["rows_per_wave"] == rows, (M, nvec)
+        assert q["rows_per_group"] == 4 * rows and q["grid"] == -(-M // (4 * rows)), (M, nvec)
+    # blocks of at most 16 vectors are planned one by one: 17 vectors on
+    # 3000 rows run 16 on two rows per wavefront, then 1 on one
+    assert p("bf16", 3000, 4100, nvec=17)["rows_per_wave"] == 2
+    assert p("bf16", 3000, 4100, nvec=1, family=lg.FAMILY_BATCHED)["rows_per_wave"] == 1
+
+
 def test_matrix_core_workgroup_shapes():
     """Up to 1024 rows a workgroup takes 4 rows (with X staged in LDS: more
     than 5 vectors), up to 2048 one group of 8 (each size fills the 256

@@ -314,6 +314,25 @@ def test_integer_wide_batched(dtype, nvec):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("M,nvec", [(2049, 3), (2049, 4), (3001, 2), (3001, 17), (4089, 2),
+                                    (4087, 5), (5003, 16), (1025, 33)])
+def test_integer_batched_row_counts(dtype, M, nvec):
+    """The vector-ALU batched kernels with one and with two rows per
+    wavefront, on row counts either side of the switch between them and not
+    a multiple of a workgroup's rows (17 and 33 vectors: blocks of 16 and a
+    remainder, each planned on its own); aligned and unaligned rows."""
+    for K, lda in ((4100, 4100), (4100, 4104), (1000, 1000)):
+        case = gi.make_integer(dtype, M, K, seed=M + nvec + K, nvec=nvec, lda=lda, bias=True)
+        ref, _ = run_oracle(case)
+        q = lg.plan(dtype, M, K, lda, nvec, 1 << 20, 1 << 20, family=lg.FAMILY_BATCHED)
+        what = f"{dtype} {M}x{K} lda={lda} nvec={nvec}, {q['rows_per_wave']} rows per wavefront"
+        print(what, flush=True)
+        assert_bit_exact(run_gpu(case, lg.FAMILY_BATCHED, batched=True), ref, what)
+        assert_bit_exact(run_gpu(case, lg.FAMILY_BATCHED, batched=True, misalign=1), ref,
+                         what + ", element loads")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("nvec", [2, 3, 8, 13, 16, 20, 32, 64])
 def test_random_batched(dtype, nvec):
     for M, K in ((4096, 4096), (1000, 1000), (64, 14336)):

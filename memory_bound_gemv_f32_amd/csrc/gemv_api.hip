@@ -286,8 +286,10 @@ const void* single_fn(const Plan& p) {
 
 template <class D, int NV, int R, bool VEC>
 const void* batched_fn_nv() {
-    return (const void*)&gemvdev::gemv_batched_kernel<D, NV, R, gemvplan::batched_batch(NV),
-                                                      gemvplan::batched_x_ahead(NV), VEC>;
+    constexpr int B = gemvplan::batched_batch(NV);
+    constexpr int E = VEC ? gemvplan::kLoadBytes / D::bytes : 1;
+    return (const void*)&gemvdev::gemv_batched_kernel<D, NV, R, B, gemvplan::batched_x_ahead(NV), VEC,
+                                                      gemvplan::batched_run(NV, B, E)>;
 }
 
 template <class D, int R, bool VEC>

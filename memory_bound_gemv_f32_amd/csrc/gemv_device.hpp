@@ -147,6 +147,12 @@ struct Chunk<D, true> {
     __device__ __forceinline__ static float dot(type a, type x, float acc) {
         return chunk_dot(D{}, a, x, acc);
     }
+    // the chunk as `words` steps, in element order: dot(a, x, acc) is
+    // dot_word(a, x, words - 1, ... dot_word(a, x, 0, acc)) (2-byte elements)
+    static constexpr int words = 4;
+    __device__ __forceinline__ static float dot_word(type a, type x, int w, float acc) {
+        return pair_dot(D{}, a[w], x[w], acc);
+    }
 };
 template <class D>
 struct Chunk<D, false> {
@@ -164,6 +170,10 @@ struct Chunk<D, false> {
     __device__ __forceinline__ static type keep_x(bool ok, type v) { return ok ? v : zero(); }
     __device__ __forceinline__ static float dot(type a, type x, float acc) {
         return __builtin_fmaf(widen(D{}, a), widen(D{}, x), acc);
+    }
+    static constexpr int words = 1;
+    __device__ __forceinline__ static float dot_word(type a, type x, int, float acc) {
+        return dot(a, x, acc);
     }
 };
 

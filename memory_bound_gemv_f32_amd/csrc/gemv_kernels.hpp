@@ -647,12 +647,15 @@ gemv_splitk_reduce_kernel(const float* __restrict__ ws, int splits, const float*
 // flight together); otherwise (many vectors, whose X chunks would not fit
 // the registers) each chunk's X loads follow the batch's A loads.  The
 // arithmetic is the single-vector path's: exactly widened elements, IEEE
-// fp32 FMA in element order into a fresh accumulator per (row, vector) per
-// batch, added to a compensated running sum.  Then one 64-lane reduction
+// fp32 FMA in element order into an accumulator per (row, vector) that runs
+// over RUN batches and is then added to a compensated running sum (with
+// many vectors the compensated add costs nearly as much as a batch's FMAs
+// for one (row, vector), so it is not paid every batch there, and the FMAs
+// of all (row, vector) pairs are interleaved).  Then one 64-lane reduction
 // per (row, vector) and lane u·NV + j writes Y[j·M + row u] (+ bias).  16-byte
 // loads take any row pitch and K (rows and X columns start at
 // element-aligned addresses: unaligned global loads).
-template <class D, int NV, int U, int B, bool XAHEAD, bool VEC>
+template <class D, int NV, int U, int B, bool XAHEAD, bool VEC, int RUN>
 __global__ void __launch_bounds__(kRowsWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
                     const typename D::storage* __restrict__ X,
@@ -683,6 +686,21 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
 #pragma unroll
         for (int j = 0; j < NV; ++j) sum[u][j] = Sum2{0.f, 0.f};
 
+    float acc[U][NV];
+    auto clear = [&]() {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < NV; ++j) acc[u][j] = 0.f;
+    };
+    auto flush = [&]() {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < NV; ++j) sum[u][j].add(acc[u][j]);
+    };
+    clear();
+
     const int nfull = K / E;
     auto batch = [&](int c0, bool check) {
         CT a[U][B];
@@ -698,11 +716,6 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
                 for (int j = 0; j < NV; ++j) xa[j][i] = C::load(xp[j], c);
         }
         __builtin_amdgcn_sched_barrier(0);  // the batch's loads in flight first
-        float acc[U][NV];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int j = 0; j < NV; ++j) acc[u][j] = 0.f;
 #pragma unroll
         for (int i = 0; i < B; ++i) {
             const int c = c0 + i * 64 + lane;
@@ -710,30 +723,55 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
             CT ai[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) ai[u] = C::keep_a(ok, a[u][i]);
+            CT xc[XAHEAD ? 1 : NV];
+            if constexpr (!XAHEAD) {
+                // X chunk by chunk: the chunk's NV loads in flight together
 #pragma unroll
-            for (int j = 0; j < NV; ++j) {
-                CT xv;
-                if constexpr (XAHEAD)
-                    xv = xa[j][i];
-                else
-                    xv = C::load(xp[j], ok ? c : nfull - 1);
-                xv = C::keep_x(ok, xv);
-#pragma unroll
-                for (int u = 0; u < U; ++u) acc[u][j] = C::dot(ai[u], xv, acc[u][j]);
+                for (int j = 0; j < NV; ++j) xc[j] = C::load(xp[j], ok ? c : nfull - 1);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            // X loaded chunk by chunk: one chunk's X operands live at a time
+            CT xs[NV];
+#pragma unroll
+            for (int j = 0; j < NV; ++j) xs[j] = C::keep_x(ok, XAHEAD ? xa[j][i] : xc[j]);
+            if constexpr (RUN == 1) {
+#pragma unroll
+                for (int j = 0; j < NV; ++j)
+#pragma unroll
+                    for (int u = 0; u < U; ++u) acc[u][j] = C::dot(ai[u], xs[j], acc[u][j]);
+            } else {
+                // word by word across all (row, vector) accumulators, so that
+                // independent multiply-adds follow each other; each
+                // accumulator still takes its chunk's elements in order
+#pragma unroll
+                for (int w = 0; w < C::words; ++w)
+#pragma unroll
+                    for (int j = 0; j < NV; ++j)
+#pragma unroll
+                        for (int u = 0; u < U; ++u)
+                            acc[u][j] = C::dot_word(ai[u], xs[j], w, acc[u][j]);
+            }
+            // one chunk's X operands live at a time
             if constexpr (!XAHEAD) __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int j = 0; j < NV; ++j) sum[u][j].add(acc[u][j]);
     };
+    // runs of at most RUN batches per accumulator (the last, checked batch
+    // included)
     const int nsafe = nfull - nfull % (B * 64);
-    int c0 = 0;
+    int c0 = 0, run = 0;
 #pragma unroll 1
-    for (; c0 < nsafe; c0 += B * 64) batch(c0, false);
-    if (c0 < nfull) batch(c0, true);
+    for (; c0 < nsafe; c0 += B * 64) {
+        batch(c0, false);
+        if (++run == RUN) {
+            flush();
+            clear();
+            run = 0;
+        }
+    }
+    if (c0 < nfull) {
+        batch(c0, true);
+        ++run;
+    }
+    if (run > 0) flush();
     if constexpr (VEC) {
         // elements past the last whole chunk (fewer than E of them)
         float tail[U][NV];

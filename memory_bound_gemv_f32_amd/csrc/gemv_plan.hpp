@@ -141,6 +141,23 @@ constexpr int batched_rows(int64_t M, int nvec) {
 }
 constexpr int batched_batch(int nvec) { return nvec <= 2 ? 4 : 2; }
 constexpr bool batched_x_ahead(int nvec) { return nvec <= 8; }
+// Batches whose products run into one accumulator before it is added to
+// the compensated sum.  Past 8 vectors (X loaded chunk by chunk) the kernel
+// is bound by its vector-ALU work, and the compensated add of each (row,
+// vector) costs nearly as much as the batch's 16 multiply-adds: there an
+// accumulator runs over kBatchedRunElems elements per lane (a batch of B
+// chunks of E elements covers B·E) and the multiply-adds of all (row,
+// vector) pairs are interleaved word by word.  fp16 K = 4100, 16 vectors,
+// µs, one batch per run / runs of 64 elements: 512 rows 10.58 / 8.99, 3072
+// 23.62 / 21.72, 4096 24.22 / 22.36, 8192 44.07 / 40.58; bf16 1024 rows
+// 13.13 / 10.65.  Up to 8 vectors the same form changed times by -12 to +8 %
+// from shape to shape (mostly slower), so there every batch is added.
+constexpr int kBatchedRunElems = 64;
+constexpr int batched_run(int nvec, int batch, int chunk_elems) {
+    return batched_x_ahead(nvec) || batch * chunk_elems >= kBatchedRunElems
+               ? 1
+               : kBatchedRunElems / (batch * chunk_elems);
+}
 // Matrix-core batched family: up to kMfmaRows rows per workgroup (4, 8 or
 // 16, below), its wavefronts split K and walk their slice in chunks of this
 // many 64-wide steps (the A loads of a chunk are in flight together; X's
@@ -738,9 +755,10 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         break;
     }
     case BATCHED:
-        // one fresh accumulator per (row, vector) per batch, FMA per element
+        // one accumulator per (row, vector) per run of batches, FMA per element
         p.column_blocks = (int)ceil_div(nvec_all, (int64_t)kValuVectors);
-        chain = valu_chain(K, p.chunk_elems, kWave, kWave, p.batch, 1, 1, 1) + 1;
+        chain = valu_chain(K, p.chunk_elems, kWave, kWave,
+                           p.batch * batched_run(nvec, p.batch, p.chunk_elems), 1, 1, 1) + 1;
         break;
     default:
         if (p.x_in_registers)  // one batch per row, no running sum

@@ -326,23 +326,34 @@ const void* batched_fn(int nvec, int rows) {
 // matrix-core kernels of W wavefronts and Q groups of RG rows per workgroup
 template <class D, int W, int Q, int RG>
 const void* mfma_fn(int nvec) {
-    if (nvec <= gemvplan::kMfmaFewVectors) {
-        // (groups of 4 rows only with X staged in LDS)
-        if constexpr (RG == 8)
-            return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 1, gemvplan::mfma_chunk(16), true, Q, RG>;
+    if constexpr (Q == 4) {
+        // four groups: one tile of vectors staged in LDS, half-size chunks
+        if (nvec > gemvplan::kMfmaFewVectors && gemvplan::mfma_tiles(nvec) == 1)
+            return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 1, gemvplan::mfma_chunk(16, 4),
+                                                                   false, Q, RG>;
         return nullptr;
-    }
-    switch (gemvplan::mfma_tiles(nvec)) {
-    case 1: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 1, gemvplan::mfma_chunk(16), false, Q, RG>;
-    case 2: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 2, gemvplan::mfma_chunk(32), false, Q, RG>;
-    case 4: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 4, gemvplan::mfma_chunk(64), false, Q, RG>;
-    default: return nullptr;
+    } else {
+        if (nvec <= gemvplan::kMfmaFewVectors) {
+            // (groups of 4 rows only with X staged in LDS)
+            if constexpr (RG == 8)
+                return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 1, gemvplan::mfma_chunk(16), true, Q, RG>;
+            return nullptr;
+        }
+        switch (gemvplan::mfma_tiles(nvec)) {
+        case 1: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 1, gemvplan::mfma_chunk(16), false, Q, RG>;
+        case 2: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 2, gemvplan::mfma_chunk(32), false, Q, RG>;
+        case 4: return (const void*)&gemvdev::gemv_batched_mfma_kernel<D, W, 4, gemvplan::mfma_chunk(64), false, Q, RG>;
+        default: return nullptr;
+        }
     }
 }
 template <class D, int W>
 const void* mfma_fn(int nvec, int groups, int rows) {
     if (groups == 2 && rows == 16) return mfma_fn<D, W, 2, 8>(nvec);
     if (groups == 1 && rows == 8) return mfma_fn<D, W, 1, 8>(nvec);
+    // four groups only with more workgroups than compute units
+    if constexpr (W == gemvplan::kMfmaManyTilesWaves)
+        if (groups == 4 && rows == 32) return mfma_fn<D, W, 4, 8>(nvec);
     // one group of 4 rows only at one workgroup per compute unit or fewer
     if constexpr (W == gemvplan::kMfmaWaves)
         if (groups == 1 && rows == 4) return mfma_fn<D, W, 1, 4>(nvec);

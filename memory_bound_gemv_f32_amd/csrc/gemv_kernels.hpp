@@ -832,7 +832,8 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
 // step's tile plus the odd row of the second's.
 //
 // A workgroup owns Q groups of RG real rows (two groups of 8; one group of 8
-// or of 4 where that spreads a small matrix over more compute units); its W
+// or of 4 where that spreads a small matrix over more compute units; four
+// groups of 8 on tall matrices, which halves the X bytes per A byte); its W
 // wavefronts split the 64-element steps of K into contiguous slices and walk
 // them in chunks of CH steps.  Per chunk a wavefront issues the loads of X
 // operands ahead of the loads of A that they meet: loads complete in issue
@@ -873,7 +874,9 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     // per wavefront: kCols columns × CH steps × 64 elements, each column
     // padded by 16 bytes so that 16 lanes reading 16 columns hit distinct banks
     constexpr int kColQuads = CH * 8 + 1;
-    static_assert(kCols * kColQuads >= NT * 64, "partials fit in the X region");
+    // the partial tiles: one quad per lane per tile and pair of row groups
+    constexpr int kPairs = Q == 4 ? 2 : 1;
+    static_assert(kCols * kColQuads >= NT * 64 * kPairs, "partials fit in the X region");
     static_assert(!FEW || NT == 1, "few vectors: one tile");
     __shared__ quad xs[W][kCols * kColQuads];
 
@@ -887,7 +890,7 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     // halves of 8 rows; RG = 4 (one group) gives the operand rows of real
     // rows 4..7 the addresses of rows 0..3, so their loads fetch no bytes of
     // their own and their duplicate outputs are never stored
-    static_assert(Q == 1 || Q == 2, "one or two groups of rows");
+    static_assert(Q == 1 || Q == 2 || Q == 4, "one, two or four groups of rows");
     static_assert(RG == 8 || (RG == 4 && Q == 1), "groups of 8 rows, or one group of 4");
     const int64_t row0 = (int64_t)blockIdx.x * (RG * Q);
     const S* ap[Q];
@@ -1096,26 +1099,30 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     }
 
     // lane (column j, group g) holds operand rows 4g .. 4g+3, i.e. real rows
-    // 2g (halves 0, 1) and 2g+1 of each row group: pair them up
+    // 2g (halves 0, 1) and 2g+1 of each row group: pair them up, row groups
+    // 2p and 2p + 1 in partial quad p
     f32x4* partial = reinterpret_cast<f32x4*>(xw);  // this wavefront's region, now free
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        f32x4 v;
-        v[0] = acc[0][t][0][0] + acc[0][t][1][1];
-        v[1] = acc[0][t][0][2] + acc[0][t][1][3];
-        if constexpr (Q == 2) {
-            v[2] = acc[1][t][0][0] + acc[1][t][1][1];
-            v[3] = acc[1][t][0][2] + acc[1][t][1][3];
-        } else {
-            v[2] = v[3] = 0.f;  // no second row group
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int pp = 0; pp < kPairs; ++pp) {
+            f32x4 v;
+            v[0] = acc[2 * pp][t][0][0] + acc[2 * pp][t][1][1];
+            v[1] = acc[2 * pp][t][0][2] + acc[2 * pp][t][1][3];
+            if constexpr (Q >= 2) {
+                v[2] = acc[2 * pp + 1][t][0][0] + acc[2 * pp + 1][t][1][1];
+                v[3] = acc[2 * pp + 1][t][0][2] + acc[2 * pp + 1][t][1][3];
+            } else {
+                v[2] = v[3] = 0.f;  // no second row group
+            }
+            partial[(t * kPairs + pp) * 64 + lane] = v;
         }
-        partial[t * 64 + lane] = v;
-    }
     __syncthreads();
     if (wave == 0) {
-        // lane (column j0, quad gq) finishes rows 4·gq .. 4·gq + 3 of column
-        // j0: rows 4·gq, 4·gq + 1 sit in the partials of lane (j0, 2·(gq % 2)),
-        // rows 4·gq + 2, 4·gq + 3 in those of lane (j0, 2·(gq % 2) + 1), as
+        // lane (column j0, quad gq) finishes rows 16·p + 4·gq .. 16·p + 4·gq
+        // + 3 of column j0 for each pair p of row groups: rows 4·gq, 4·gq + 1
+        // of the pair sit in the partials of lane (j0, 2·(gq % 2)), rows
+        // 4·gq + 2, 4·gq + 3 in those of lane (j0, 2·(gq % 2) + 1), as
         // components 2·(gq / 2) and 2·(gq / 2) + 1
         const int j0 = lane >> 2;
         const int gq = lane & 3;
@@ -1123,19 +1130,22 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
         const int srcB = srcA + 16;
         const int co = 2 * (gq >> 1);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int pp = 0; pp < kPairs; ++pp) {
             float o[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int w = 0; w < W; ++w) {
-                const float* P = reinterpret_cast<const float*>(reinterpret_cast<const f32x4*>(xs[w]) + t * 64);
+                const float* P = reinterpret_cast<const float*>(reinterpret_cast<const f32x4*>(xs[w]) +
+                                                                (t * kPairs + pp) * 64);
                 o[0] += P[srcA * 4 + co];
                 o[1] += P[srcA * 4 + co + 1];
                 o[2] += P[srcB * 4 + co];
                 o[3] += P[srcB * 4 + co + 1];
             }
             const int j = 16 * t + j0;
-            const int64_t m0 = row0 + 4 * gq;
-            if (j < nvec && 4 * gq < RG * Q) {
+            const int64_t m0 = row0 + 16 * pp + 4 * gq;
+            if (j < nvec && 16 * pp + 4 * gq < RG * Q) {
                 float* yp = Y + (int64_t)j * M + m0;
                 if (m0 + 3 < M && ((uintptr_t)yp & 15) == 0) {
                     f32x4 out = {o[0], o[1], o[2], o[3]};

@@ -158,11 +158,11 @@ constexpr int batched_run(int nvec, int batch, int chunk_elems) {
                ? 1
                : kBatchedRunElems / (batch * chunk_elems);
 }
-// Matrix-core batched family: up to kMfmaRows rows per workgroup (4, 8 or
-// 16, below), its wavefronts split K and walk their slice in chunks of this
-// many 64-wide steps (the A loads of a chunk are in flight together; X's
-// chunk is staged in LDS).
-constexpr int kMfmaRows = 16;
+// Matrix-core batched family: up to kMfmaRows rows per workgroup (4, 8, 16
+// or 32, below), its wavefronts split K and walk their slice in chunks of
+// this many 64-wide steps (the A loads of a chunk are in flight together;
+// X's chunk is staged in LDS).
+constexpr int kMfmaRows = 32;
 constexpr int kMfmaWaves = 8;
 constexpr int kMfmaChunk = 8;
 // Up to this many vectors the matrix-core kernel reads its X operands
@@ -182,11 +182,32 @@ constexpr int kMfmaFewVectors = 5;
 // 28672 42.8 and 47.5.)
 constexpr int kMfmaManyTilesWaves = 4;
 // Groups of 8 real rows per matrix-core workgroup: one while 8-row
-// workgroups fill the compute units at most once (M <= 2048), else two
-// (kMfmaRows).  fp16 K = 4096, µs, two groups / one, 4 and 16 vectors: 1024
-// rows 6.04 / 4.89 and 7.02 / 5.75, 2048 6.21 / 5.17 and 7.23 / 6.04; 3072
-// (one group in 384 workgroups of 4 wavefronts) 6.66 / 8.04 and 7.64 / 9.63.
-constexpr int mfma_row_groups(int64_t M) { return (M + 7) / 8 <= kCUs ? 1 : 2; }
+// workgroups fill the compute units at most once (M <= 2048), else two.
+// fp16 K = 4096, µs, two groups / one, 4 and 16 vectors: 1024 rows 6.04 /
+// 4.89 and 7.02 / 5.75, 2048 6.21 / 5.17 and 7.23 / 6.04; 3072 (one group in
+// 384 workgroups of 4 wavefronts) 6.66 / 8.04 and 7.64 / 9.63.
+//
+// Four groups (32 rows, half-size chunks) for kMfmaTallMinVectors to 16
+// vectors on tall matrices: every workgroup stages the whole of X for its
+// rows, so 32-row workgroups read half as many X bytes per A byte.  The
+// time of these grids follows the largest number of workgroups a compute
+// unit runs, times their rows: four groups are taken when their grid has
+// more workgroups than compute units (so 4 wavefronts each) and no unit runs
+// more rows than with two.  fp16 K = 4096, µs, two groups / four: 16 vectors
+// 12288 rows 19.49 / 21.24 (3 against 2·2 units of 16 rows), 13312 23.75 /
+// 21.27, 14336 24.17 / 21.68, 16384 24.89 / 23.04, 20480 30.50 / 30.34 (5
+// against 6); 9 vectors 13312 21.62 / 20.40, 16384 22.97 / 22.68, 28672
+// 37.62 / 38.25 (7 against 8); 8 vectors gained less (14336 21.67 / 20.72,
+// 16384 22.70 / 22.66).  With 8 wavefronts (at most one workgroup per unit)
+// four groups were slower: 4096 rows 7.84 / 11.30, 8192 13.79 / 15.90.
+constexpr int kMfmaTallMinVectors = 9;
+constexpr int mfma_row_groups(int64_t M, int nvec) {
+    if ((M + 7) / 8 <= kCUs) return 1;
+    const int64_t g2 = (M + 15) / 16, g4 = (M + 31) / 32;
+    const bool four = nvec >= kMfmaTallMinVectors && nvec <= 16 && g4 > kCUs &&
+                      2 * ((g4 + kCUs - 1) / kCUs) <= (g2 + kCUs - 1) / kCUs;
+    return four ? 4 : 2;
+}
 // Real rows per group: 8, or, with X staged in LDS (more than
 // kMfmaFewVectors vectors), 4 (one group) while 4-row workgroups fill the
 // compute units at most once (M <= 1024).  fp16 K = 4096, µs, 8 / 4 rows per
@@ -200,11 +221,15 @@ constexpr int mfma_waves(int64_t M, int rows_per_group) {
     return (M + rows_per_group - 1) / rows_per_group > kCUs ? kMfmaManyTilesWaves : kMfmaWaves;
 }
 // 16-vector tiles for nvec vectors (1, 2 or 4); the chunk shrinks as the
-// tiles grow so that the X staged per chunk stays 16 KiB per wavefront.
+// tiles grow so that the X staged per chunk stays 16 KiB per wavefront, and
+// is halved with four row groups (twice the A loads per step: the chunk's
+// A, X and accumulators then fit the registers of two wavefronts per SIMD).
 constexpr int mfma_tiles(int nvec) { return nvec <= 16 ? 1 : (nvec <= 32 ? 2 : 4); }
-constexpr int mfma_chunk(int nvec) { return kMfmaChunk / mfma_tiles(nvec); }
-constexpr int mfma_lds_bytes(int nvec, int waves) {
-    return waves * 16 * mfma_tiles(nvec) * (mfma_chunk(nvec) * 128 + 16);
+constexpr int mfma_chunk(int nvec, int groups = 2) {
+    return kMfmaChunk / mfma_tiles(nvec) / (groups == 4 ? 2 : 1);
+}
+constexpr int mfma_lds_bytes(int nvec, int waves, int groups = 2) {
+    return waves * 16 * mfma_tiles(nvec) * (mfma_chunk(nvec, groups) * 128 + 16);
 }
 // The 64-element steps of a row that wavefront `wave` of a matrix-core
 // workgroup of `waves` wavefronts walks: steps [first, end) of the
@@ -709,12 +734,12 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
     }
     case BATCHED_MFMA:
         // each wavefront: 4 lanes per row and step, 16 rows; rows span the group
-        p.row_tiles = mfma_row_groups(M);
+        p.row_tiles = mfma_row_groups(M, nvec);
         p.rows_per_wave = mfma_group_rows(M, nvec) * p.row_tiles;
         p.waves_per_group = mfma_waves(M, p.rows_per_wave);
         p.lanes_per_row = 4 * p.waves_per_group;
-        p.batch = mfma_chunk(nvec);
-        p.lds_bytes = mfma_lds_bytes(nvec, p.waves_per_group);
+        p.batch = mfma_chunk(nvec, p.row_tiles);
+        p.lds_bytes = mfma_lds_bytes(nvec, p.waves_per_group, p.row_tiles);
         break;
     default:
         return INVALID;
@@ -744,7 +769,7 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
     switch (fam) {
     case BATCHED_MFMA: {
         int blk = nvec;
-        chain = mfma_chain(K, p.waves_per_group, mfma_chunk(blk), mfma_tiles(blk) <= 2) + 1;
+        chain = mfma_chain(K, p.waves_per_group, mfma_chunk(blk, p.row_tiles), mfma_tiles(blk) <= 2) + 1;
         if (chain > kMaxRoundingChain && mfma_tiles(nvec) > 2) {
             blk = 32;
             p.column_blocks = (int)ceil_div(nvec, (int64_t)blk);

@@ -321,12 +321,36 @@ def test_matrix_core_workgroup_shapes():
             want = 8 if nvec <= 5 and rows == 4 else rows  # X read straight from memory: 8
             q = p("f16", M, 4096, nvec=nvec)
             assert q["family"] == lg.FAMILY_BATCHED_MFMA
+            if M == 14336 and nvec == 16:  # four groups (below)
+                assert (q["row_tiles"], q["rows_per_group"], q["batch"]) == (4, 32, 4)
+                continue
             assert (q["row_tiles"], q["rows_per_group"]) == (groups, want)
             assert (q["waves_per_group"], q["block"], q["grid"]) == \
                 (waves, 64 * waves, -(-M // want))
             assert q["passes"] == 4096 // 64 // waves
             tiles = 1 if nvec <= 16 else (2 if nvec <= 32 else 4)
             assert q["lds_bytes"] == waves * 16 * tiles * (q["batch"] * 128 + 16) <= 20 * 1024 * waves
+            assert q["rounding_chain"] <= 150
+
+
+def test_matrix_core_four_row_groups():
+    """9-16 vectors on tall matrices: four groups of 8 rows (half the X
+    bytes per A byte) when their grid has more workgroups than compute units
+    and no unit runs more rows than with two groups (the largest number of
+    workgroups on one unit times their rows)."""
+    for M, nvec, groups in ((12288, 16, 2), (13312, 9, 4), (13312, 8, 2), (13313, 16, 4),
+                            (14336, 16, 4), (16384, 12, 4), (20480, 16, 2), (28672, 16, 2),
+                            (8192, 16, 2), (4096, 16, 2), (14336, 17, 2), (14336, 5, 2)):
+        q = p("f16", M, 4096, nvec=nvec)
+        assert q["family"] == lg.FAMILY_BATCHED_MFMA
+        g2, g4 = -(-M // 16), -(-M // 32)
+        assert (groups == 4) == (9 <= nvec <= 16 and g4 > 256 and
+                                 2 * -(-g4 // 256) <= -(-g2 // 256)), (M, nvec)
+        assert q["row_tiles"] == groups and q["rows_per_group"] == 8 * groups, (M, nvec)
+        if groups == 4:
+            # half-size chunks, 4 wavefronts: 33 KiB of LDS, two workgroups per unit
+            assert (q["waves_per_group"], q["batch"], q["grid"]) == (4, 4, g4)
+            assert q["lds_bytes"] == 4 * 16 * (4 * 128 + 16)
             assert q["rounding_chain"] <= 150
 
 

@@ -542,6 +542,30 @@ def test_integer_batched_workgroup_shapes(dtype, M, waves, groups, rows):
         assert_bit_exact(run_gpu(case, lg.FAMILY_AUTO, batched=True), ref, what)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_integer_batched_four_row_groups(dtype):
+    """9-16 vectors on tall matrices: workgroups of four 8-row groups (32
+    rows, 4 wavefronts, chunks of 4 steps), on row counts that leave a
+    partial last workgroup, K that leave a partial last 64-wide step or
+    steps outside whole chunks, bias or none, odd M (unaligned Y columns);
+    bit-exact.  Then random data within the bound."""
+    for M, K, nvec in ((13313, 4096, 9), (13313, 4096, 16), (14337, 1000, 12), (16384, 2680, 16),
+                       (13320, 4104, 13)):
+        q = lg.plan(dtype, M, K, K, nvec, 1 << 20, 1 << 20)
+        assert (q["family"], q["row_tiles"], q["rows_per_group"], q["waves_per_group"]) == \
+            (lg.FAMILY_BATCHED_MFMA, 4, 32, 4), q
+        case = gi.make_integer(dtype, M, K, seed=M + K + nvec, nvec=nvec, bias=nvec % 2 == 1)
+        ref, _ = run_oracle(case)
+        what = f"{dtype} {M}x{K} nvec={nvec}: four row groups, chunk {q['batch']}"
+        print(what, flush=True)
+        assert_bit_exact(run_gpu(case, lg.FAMILY_AUTO, batched=True), ref, what)
+    case = gi.make_random(dtype, 14336, 4096, seed=7, nvec=16, bias=True, dist="normal",
+                          scale=1 / 64)
+    ref, absdot = run_oracle(case)
+    assert_within_bound(run_gpu(case, lg.FAMILY_AUTO, batched=True), ref, absdot,
+                        f"{dtype} 14336x4096 nvec=16 random, four row groups")
+
+
 def test_refused_launch_reports_launch_failure():
     """A launch the runtime refuses comes back as GEMV_ERROR_LAUNCH_FAILURE
     with the runtime's error code, and leaves nothing behind: the runtime's

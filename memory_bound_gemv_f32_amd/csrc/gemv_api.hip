@@ -284,40 +284,47 @@ const void* single_fn(const Plan& p) {
 
 // ---- batched ----------------------------------------------------------------
 
-template <class D, int NV, int R, bool VEC>
+template <class D, int NV, int R, bool VEC, int KS>
 const void* batched_fn_nv() {
     constexpr int B = gemvplan::batched_batch(NV);
     constexpr int E = VEC ? gemvplan::kLoadBytes / D::bytes : 1;
     return (const void*)&gemvdev::gemv_batched_kernel<D, NV, R, B, gemvplan::batched_x_ahead(NV), VEC,
-                                                      gemvplan::batched_run(NV, B, E)>;
+                                                      gemvplan::batched_run(NV, B, E), KS>;
 }
 
-template <class D, int R, bool VEC>
+template <class D, int R, bool VEC, int KS = 1>
 const void* batched_fn(int nvec) {
     switch (nvec) {
-    case 1: return batched_fn_nv<D, 1, R, VEC>();
-    case 2: return batched_fn_nv<D, 2, R, VEC>();
-    case 3: return batched_fn_nv<D, 3, R, VEC>();
-    case 4: return batched_fn_nv<D, 4, R, VEC>();
-    case 5: return batched_fn_nv<D, 5, R, VEC>();
-    case 6: return batched_fn_nv<D, 6, R, VEC>();
-    case 7: return batched_fn_nv<D, 7, R, VEC>();
-    case 8: return batched_fn_nv<D, 8, R, VEC>();
-    case 9: return batched_fn_nv<D, 9, R, VEC>();
-    case 10: return batched_fn_nv<D, 10, R, VEC>();
-    case 11: return batched_fn_nv<D, 11, R, VEC>();
-    case 12: return batched_fn_nv<D, 12, R, VEC>();
-    case 13: return batched_fn_nv<D, 13, R, VEC>();
-    case 14: return batched_fn_nv<D, 14, R, VEC>();
-    case 15: return batched_fn_nv<D, 15, R, VEC>();
-    case 16: return batched_fn_nv<D, 16, R, VEC>();
+    case 1: return batched_fn_nv<D, 1, R, VEC, KS>();
+    case 2: return batched_fn_nv<D, 2, R, VEC, KS>();
+    case 3: return batched_fn_nv<D, 3, R, VEC, KS>();
+    case 4: return batched_fn_nv<D, 4, R, VEC, KS>();
+    case 5: return batched_fn_nv<D, 5, R, VEC, KS>();
+    case 6: return batched_fn_nv<D, 6, R, VEC, KS>();
+    case 7: return batched_fn_nv<D, 7, R, VEC, KS>();
+    case 8: return batched_fn_nv<D, 8, R, VEC, KS>();
+    case 9: return batched_fn_nv<D, 9, R, VEC, KS>();
+    case 10: return batched_fn_nv<D, 10, R, VEC, KS>();
+    case 11: return batched_fn_nv<D, 11, R, VEC, KS>();
+    case 12: return batched_fn_nv<D, 12, R, VEC, KS>();
+    case 13: return batched_fn_nv<D, 13, R, VEC, KS>();
+    case 14: return batched_fn_nv<D, 14, R, VEC, KS>();
+    case 15: return batched_fn_nv<D, 15, R, VEC, KS>();
+    case 16: return batched_fn_nv<D, 16, R, VEC, KS>();
     default: return nullptr;
     }
 }
 
-// R rows per wavefront (1 or 2), from the plan
+static_assert(gemvplan::kBatchedSplit == gemvdev::kRowsWaves && gemvplan::kBlock == gemvdev::kRowsWaves * 64,
+              "the K-split batched form splits each row over the workgroup's wavefronts");
+
+// R rows per wavefront (1 or 2), or one row per workgroup whose wavefronts
+// split K (lanes per row 64·kBatchedSplit), from the plan
 template <class D, bool VEC>
-const void* batched_fn(int nvec, int rows) {
+const void* batched_fn(int nvec, int rows, int lanes) {
+    if (lanes == gemvplan::kWave * gemvplan::kBatchedSplit && rows == 1)
+        return batched_fn<D, 1, VEC, gemvplan::kBatchedSplit>(nvec);
+    if (lanes != gemvplan::kWave) return nullptr;
     if (rows == 1) return batched_fn<D, 1, VEC>(nvec);
     if (rows == 2) return batched_fn<D, 2, VEC>(nvec);
     return nullptr;
@@ -364,8 +371,8 @@ template <class D>
 const void* batched_kernel(const Plan& p, int nvec) {
     if constexpr (D::bytes == 2) {
         if (p.family == gemvplan::BATCHED)
-            return p.vector_loads ? batched_fn<D, true>(nvec, p.rows_per_wave)
-                                  : batched_fn<D, false>(nvec, p.rows_per_wave);
+            return p.vector_loads ? batched_fn<D, true>(nvec, p.rows_per_wave, p.lanes_per_row)
+                                  : batched_fn<D, false>(nvec, p.rows_per_wave, p.lanes_per_row);
         if (p.family == gemvplan::BATCHED_MFMA && p.vector_loads) {
             if (p.waves_per_group == gemvplan::kMfmaWaves)
                 return mfma_fn<D, gemvplan::kMfmaWaves>(nvec, p.row_tiles, p.rows_per_group);

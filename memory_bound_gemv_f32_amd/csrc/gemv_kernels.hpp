@@ -655,7 +655,13 @@ gemv_splitk_reduce_kernel(const float* __restrict__ ws, int splits, const float*
 // per (row, vector) and lane u·NV + j writes Y[j·M + row u] (+ bias).  16-byte
 // loads take any row pitch and K (rows and X columns start at
 // element-aligned addresses: unaligned global loads).
-template <class D, int NV, int U, int B, bool XAHEAD, bool VEC, int RUN>
+//
+// KS = kRowsWaves splits K instead (few rows: one wavefront per row would
+// leave most of the chip idle and make the time one wavefront's walk along
+// its row): the workgroup's wavefronts share its U rows, wavefront w taking
+// batches w, w + KS, ... of each row; the per-wavefront totals meet in LDS
+// and wavefront 0 adds them in wavefront order (the same order every call).
+template <class D, int NV, int U, int B, bool XAHEAD, bool VEC, int RUN, int KS = 1>
 __global__ void __launch_bounds__(kRowsWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
                     const typename D::storage* __restrict__ X,
@@ -666,10 +672,13 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     using CT = typename C::type;
     constexpr int E = C::elems;
     static_assert(U * NV <= 64, "one writer lane per (row, vector)");
+    static_assert(KS == 1 || KS == kRowsWaves, "a row per wavefront, or per workgroup");
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t row0 = ((int64_t)blockIdx.x * kRowsWaves + wave) * U;
+    const int kw = KS > 1 ? wave : 0;  // this wavefront's share of K
+    const int64_t row0 =
+        KS > 1 ? (int64_t)blockIdx.x * U : ((int64_t)blockIdx.x * kRowsWaves + wave) * U;
     const S* rp[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -754,12 +763,11 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
             if constexpr (!XAHEAD) __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // runs of at most RUN batches per accumulator (the last, checked batch
-    // included)
-    const int nsafe = nfull - nfull % (B * 64);
-    int c0 = 0, run = 0;
+    // this wavefront's batches (every KS-th), in runs of at most RUN batches
+    // per accumulator (the last, checked batch included)
+    int c0 = kw * B * 64, run = 0;
 #pragma unroll 1
-    for (; c0 < nsafe; c0 += B * 64) {
+    for (; c0 + B * 64 <= nfull; c0 += KS * B * 64) {
         batch(c0, false);
         if (++run == RUN) {
             flush();
@@ -772,7 +780,7 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
         ++run;
     }
     if (run > 0) flush();
-    if constexpr (VEC) {
+    if (VEC && kw == 0) {
         // elements past the last whole chunk (fewer than E of them)
         float tail[U][NV];
 #pragma unroll
@@ -802,6 +810,17 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
             const float v = segment_sum<64>(sum[u][j].value());
             out = lane == u * NV + j ? v : out;
         }
+    if constexpr (KS > 1) {
+        __shared__ float part[KS][U * NV];
+        if (lane < U * NV) part[kw][lane] = out;
+        __syncthreads();
+        if (kw != 0) return;
+        if (lane < U * NV) {
+            out = part[0][lane];
+#pragma unroll
+            for (int w = 1; w < KS; ++w) out += part[w][lane];
+        }
+    }
     if (lane < U * NV) {
         const int u = lane / NV, j = lane % NV;
         const int64_t m = row0 + u;

@@ -158,6 +158,19 @@ constexpr int batched_run(int nvec, int batch, int chunk_elems) {
                ? 1
                : kBatchedRunElems / (batch * chunk_elems);
 }
+// Wavefronts per row: with one row per wavefront the time is one
+// wavefront's walk along its row, and few rows leave most of the chip idle;
+// up to kBatchedSplitMaxRows rows (one wavefront on at most every other
+// SIMD) the workgroup's 4 wavefronts share each row instead (every fourth
+// batch each, totals added in LDS).  fp16, µs, one row per wavefront / per
+// workgroup: K = 4100, 64 rows 2 vectors 3.43 / 2.63, 16 vectors 8.96 /
+// 5.47; 512 rows 2 vectors 3.69 / 3.32, 8 vectors 7.72 / 5.04, 16 vectors
+// 9.12 / 7.50; 64 × 14337 16 vectors 40.21 / 13.51; 512 × 11009 16 vectors
+// 33.05 / 19.40; at 1024 rows mixed (8 vectors 7.91 / 7.06, 16 vectors 9.48
+// / 12.19), from 1536 rows slower (2048 rows 16 vectors 16.27 / 21.25).
+constexpr int64_t kBatchedSplitMaxRows = 512;
+constexpr int kBatchedSplit = 4;
+constexpr int batched_split(int64_t M) { return M <= kBatchedSplitMaxRows ? kBatchedSplit : 1; }
 // Matrix-core batched family: up to kMfmaRows rows per workgroup (4, 8, 16
 // or 32, below), its wavefronts split K and walk their slice in chunks of
 // this many 64-wide steps (the A loads of a chunk are in flight together;
@@ -319,6 +332,25 @@ inline int valu_chain(int64_t elems, int chunk, int lanes, int wave_lanes, int b
     const int64_t first = in_batch > in_tail ? in_batch : in_tail;
     const int64_t terms = batches + (tail > 0 ? 1 : 0);
     return (int)(first + compensated_roundings(terms) + ceil_log2(wave_lanes) + (waves - 1));
+}
+
+// The vector-ALU batched kernel: rows of `elems` elements in chunks of
+// `chunk`, batches of `batch` chunks per lane (64 lanes per wavefront), a
+// wavefront taking every `split`-th batch; runs of up to `run` batches
+// accumulate in place before a compensated add (the element-wise tail is
+// one more term); then the 64-lane tree and the in-order fold of the split
+// wavefronts' totals.
+inline int batched_chain(int64_t elems, int chunk, int batch, int run, int split) {
+    const int64_t full = elems / chunk;
+    const int64_t tail = elems - full * chunk;
+    const int64_t per_block = (int64_t)batch * 64;
+    const int64_t blocks = (full + per_block - 1) / per_block;
+    const int64_t mine = (blocks + split - 1) / split;  // batches of the busiest wavefront
+    const int64_t in_run = (mine < run ? mine : run) * batch * chunk;
+    const int64_t in_tail = (tail + 63) / 64;
+    const int64_t terms = (mine + run - 1) / run + (tail > 0 ? 1 : 0);
+    return (int)((in_run > in_tail ? in_run : in_tail) + compensated_roundings(terms) + ceil_log2(64) +
+                 (split - 1));
 }
 
 // The matrix-core kernel: each wavefront's run of 64-wide steps in chunks of
@@ -713,8 +745,9 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         // kValuVectors (one launch and one pass over A each); the plan is
         // the first block's
         if (nvec > kValuVectors) nvec = kValuVectors;
-        p.lanes_per_row = kWave;
         p.rows_per_wave = batched_rows(M, nvec);
+        // (the K-split form takes one row per workgroup)
+        p.lanes_per_row = kWave * (p.rows_per_wave == 1 ? batched_split(M) : 1);
         p.waves_per_group = kBlock / kWave;
         p.batch = batched_batch(nvec);
         p.row_tiles = 1;
@@ -751,6 +784,8 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         p.rows_per_group = 1;
     else if (fam == BATCHED_MFMA)
         p.rows_per_group = p.rows_per_wave;
+    else if (fam == BATCHED)  // lanes_per_row / 64 wavefronts share each row
+        p.rows_per_group = p.rows_per_wave * (p.waves_per_group * kWave / p.lanes_per_row);
     else
         p.rows_per_group = p.rows_per_wave * p.row_tiles * p.waves_per_group;
     p.grid = ceil_div(M, p.rows_per_group);
@@ -782,8 +817,9 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
     case BATCHED:
         // one accumulator per (row, vector) per run of batches, FMA per element
         p.column_blocks = (int)ceil_div(nvec_all, (int64_t)kValuVectors);
-        chain = valu_chain(K, p.chunk_elems, kWave, kWave,
-                           p.batch * batched_run(nvec, p.batch, p.chunk_elems), 1, 1, 1) + 1;
+        chain = batched_chain(K, p.chunk_elems, p.batch, batched_run(nvec, p.batch, p.chunk_elems),
+                              p.lanes_per_row / kWave) +
+                1;
         break;
     default:
         if (p.x_in_registers)  // one batch per row, no running sum

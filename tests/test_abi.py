@@ -301,11 +301,35 @@ def test_vector_alu_batched_rows_per_wavefront():
         q = p("f16", M, 4100, nvec=nvec)
         assert q["family"] == lg.FAMILY_BATCHED, (M, nvec)
         assert q["rows_per_wave"] == rows, (M, nvec)
-        assert q["rows_per_group"] == 4 * rows and q["grid"] == -(-M // (4 * rows)), (M, nvec)
+        # up to 512 rows the workgroup's 4 wavefronts share each row
+        split = 4 if M <= 512 else 1
+        assert q["lanes_per_row"] == 64 * split, (M, nvec)
+        per_group = rows * 4 // split
+        assert q["rows_per_group"] == per_group and q["grid"] == -(-M // per_group), (M, nvec)
     # blocks of at most 16 vectors are planned one by one: 17 vectors on
     # 3000 rows run 16 on two rows per wavefront, then 1 on one
     assert p("bf16", 3000, 4100, nvec=17)["rows_per_wave"] == 2
     assert p("bf16", 3000, 4100, nvec=1, family=lg.FAMILY_BATCHED)["rows_per_wave"] == 1
+
+
+def test_vector_alu_batched_k_split():
+    """Up to 512 rows the vector-ALU batched kernel gives each row a whole
+    workgroup (4 wavefronts, every fourth batch each, then an in-order fold
+    of their totals: 3 more roundings); more rows keep a wavefront per row."""
+    for M, K, nvec in ((1, 4100, 2), (7, 100, 16), (512, 11009, 16), (64, 14337, 5), (513, 4100, 3)):
+        q = p("bf16", M, K, nvec=nvec)
+        one = p("bf16", M, K, nvec=nvec, family=lg.FAMILY_BATCHED)
+        assert q["family"] == lg.FAMILY_BATCHED and q == one
+        if M <= 512:
+            assert (q["lanes_per_row"], q["rows_per_wave"], q["rows_per_group"], q["grid"]) == \
+                (256, 1, 1, M)
+        else:
+            assert (q["lanes_per_row"], q["rows_per_group"]) == (64, 4)
+        assert q["waves_per_group"] == 4 and q["block"] == 256
+        assert q["rounding_chain"] <= 150
+    # the fold of 4 wavefronts' totals is charged to the bound
+    split, whole = p("f16", 512, 4100, nvec=2), p("f16", 513, 4100, nvec=2)
+    assert split["rounding_chain"] == whole["rounding_chain"] + 3
 
 
 def test_matrix_core_workgroup_shapes():

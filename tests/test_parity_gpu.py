@@ -333,6 +333,30 @@ def test_integer_batched_row_counts(dtype, M, nvec):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("nvec", [2, 9, 16, 17])
+def test_integer_batched_k_split(dtype, nvec):
+    """Up to 512 rows the vector-ALU batched kernel splits each row's K over
+    the workgroup's 4 wavefronts: row lengths that give some wavefronts no
+    batch, a partial last batch, an element-wise tail; 16-byte and element
+    loads; bias or none; bit-exact.  Then long random rows within the bound."""
+    for M, K in ((1, 7), (5, 1000), (64, 4100), (511, 2056), (512, 14337), (3, 16392)):
+        case = gi.make_integer(dtype, M, K, seed=M * 7 + K + nvec, nvec=nvec, bias=(M + nvec) % 2 == 1)
+        ref, _ = run_oracle(case)
+        q = lg.plan(dtype, M, K, K, nvec, 1 << 20, 1 << 20, family=lg.FAMILY_BATCHED)
+        assert q["lanes_per_row"] == 256, q
+        what = f"{dtype} {M}x{K} nvec={nvec}: K split over 4 wavefronts"
+        print(what, flush=True)
+        assert_bit_exact(run_gpu(case, lg.FAMILY_BATCHED, batched=True), ref, what)
+        assert_bit_exact(run_gpu(case, lg.FAMILY_BATCHED, batched=True, misalign=1), ref,
+                         what + ", element loads")
+    case = gi.make_random(dtype, 64, 100003, seed=nvec, nvec=nvec, bias=True, dist="normal",
+                          scale=1 / 256)
+    ref, absdot = run_oracle(case)
+    assert_within_bound(run_gpu(case, lg.FAMILY_AUTO, batched=True), ref, absdot,
+                        f"{dtype} 64x100003 nvec={nvec} random, K split")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("nvec", [2, 3, 8, 13, 16, 20, 32, 64])
 def test_random_batched(dtype, nvec):
     for M, K in ((4096, 4096), (1000, 1000), (64, 14336)):

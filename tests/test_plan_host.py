@@ -3,6 +3,7 @@ matrix-core kernel's step partition, a compiled kernel behind every
 automatic plan, and the rounding-chain bound of every plan."""
 
 import ctypes
+import math
 import shutil
 import subprocess
 from pathlib import Path
@@ -222,6 +223,66 @@ def test_rounding_chain_bounded_for_long_rows():
                         ("bf16", 1, (1 << 31) - 8)):
         q = lg.plan_splitk(dtype, M, K, A_addr=ALIGNED, x_addr=ALIGNED)
         assert q["rounding_chain"] <= 150, (dtype, M, K, q)
+
+
+def _sum2_roundings(n):
+    """Roundings a compensated running sum of n terms adds (one rounding plus
+    gamma_{n-1}^2 / u, Ogita-Rump-Oishi Sum2), written out independently."""
+    if n <= 1:
+        return 0
+    u = 2.0 ** -24
+    g = (n - 1) * u / (1 - (n - 1) * u)
+    return 1 + math.ceil(g * g / u - 1e-6)
+
+
+def _batched_schedule_chain(K, E, B, RUN, KS):
+    """Walk the vector-ALU batched kernel's schedule lane by lane: blocks of
+    B*64 chunks dealt to KS wavefronts in turn, a wavefront's 64 lanes taking
+    chunks c0 + 64*i + lane (i < B) of each of its blocks, products into one
+    accumulator for RUN blocks before a compensated add, the element-wise
+    tail (wavefront 0) as one more term; then the 64-lane tree and the fold
+    of KS totals.  Returns the most roundings any product meets."""
+    nfull = K // E
+    tail = K - nfull * E
+    worst = 0
+    for w in range(KS):
+        blocks = list(range(w * B * 64, nfull, KS * B * 64))
+        terms = -(-len(blocks) // RUN) + (1 if tail and w == 0 else 0)
+        for lane in (0, 63):
+            longest = 0
+            for r in range(0, len(blocks), RUN):
+                run = sum(E for c0 in blocks[r:r + RUN] for i in range(B)
+                          if c0 + 64 * i + lane < nfull)
+                longest = max(longest, run)
+            if w == 0 and tail:
+                longest = max(longest, len(range(lane, tail, 64)))
+            worst = max(worst, longest + _sum2_roundings(terms))
+    return worst + 6 + (KS - 1)
+
+
+def test_batched_chain_covers_the_kernel_schedule():
+    """The vector-ALU batched plan's rounding chain is never below what its
+    kernel's schedule makes a product meet (plus one for the bias), for
+    every vector count's batch and run length, with and without the K
+    split, on row lengths around the block and run boundaries."""
+    checked = 0
+    for dtype in ("f16", "bf16"):
+        for M in (64, 4096):  # K split, and a wavefront per row
+            for nvec in (2, 5, 9, 16):
+                for K in (1, 7, 8, 100, 1023, 1024, 2047, 2048, 4096, 4100, 8191, 8200, 16384,
+                          16391, 65536, 100003):
+                    for A in (ALIGNED, ALIGNED + 2):
+                        q = lg.plan(dtype, M, K, K, nvec, A, A, lg.FAMILY_BATCHED)
+                        E = q["chunk_elems"]
+                        B = q["batch"]
+                        RUN = 1 if nvec <= 8 or B * E >= 64 else 64 // (B * E)
+                        KS = q["lanes_per_row"] // 64
+                        assert KS == (4 if M <= 512 else 1)
+                        need = _batched_schedule_chain(K, E, B, RUN, KS) + 1
+                        assert q["rounding_chain"] >= need, (dtype, M, K, nvec, A, q, need)
+                        assert q["rounding_chain"] <= 150
+                        checked += 1
+    assert checked == 2 * 2 * 4 * 16 * 2
 
 
 def test_forced_wave_per_row_on_huge_rows():

@@ -49,6 +49,12 @@ def _inputs():
     u = gi.make_random("bf16", 1024, 4096, seed=5, dist="normal", scale=0.02)
     dev["Ag"] = to_device("bf16", g.A.reshape(g.M, g.lda))
     dev["Au"] = to_device("bf16", u.A.reshape(u.M, u.lda))
+    b3 = gi.make_random("bf16", 300, 2050, seed=8, nvec=12, dist="normal")  # K split over 4 wavefronts
+    dev["Ab3"] = to_device("bf16", b3.A.reshape(b3.M, b3.lda))
+    dev["Xb3"] = to_device("bf16", b3.X)
+    b4 = gi.make_random("f16", 13313, 1024, seed=9, nvec=12, dist="normal")  # 32-row MFMA workgroups
+    dev["Ab4"] = to_device("f16", b4.A.reshape(b4.M, b4.lda))
+    dev["Xb4"] = to_device("f16", b4.X)
     w = gi.make_q8_random("f16", 2048, 4096, seed=6)
     dev["Q"] = torch.from_numpy(w.Q).cuda()
     dev["scale"] = torch.from_numpy(w.scale).cuda()
@@ -61,6 +67,8 @@ def _outputs():
         "y": torch.empty(4096, device="cuda"),
         "Y": torch.empty((24, 1000), device="cuda"),
         "Y2": torch.empty((5, 1000), device="cuda"),
+        "Y3": torch.empty((12, 300), device="cuda"),
+        "Y4": torch.empty((12, 13313), device="cuda"),
         "yn": torch.empty(8, device="cuda"),
         "ys": torch.empty(8, device="cuda"),
         "yqkv": [torch.empty(M, device="cuda") for M in (512, 128, 128)],
@@ -75,6 +83,8 @@ def _calls(d, o):
     lg.gemv_batched(d["Ab"], d["Xb"], out=o["Y"])
     lg.gemv_splitk(d["As"], d["xs"], out=o["ys"], workspace=d["ws"])
     lg.gemv_batched(d["Ab2"], d["Xb2"], out=o["Y2"])  # the vector-ALU batched kernel
+    lg.gemv_batched(d["Ab3"], d["Xb3"], out=o["Y3"])  # ... with each row's K split
+    lg.gemv_batched(d["Ab4"], d["Xb4"], out=o["Y4"])  # matrix cores, four row groups
     rc = lg.gemv_splitk_noalloc(lg.DTYPE_F32, d["As"].data_ptr(), d["As"].stride(0),
                                 d["xs"].data_ptr(), None, o["yn"].data_ptr(), d["As"].shape[0],
                                 d["As"].shape[1], 0, torch.cuda.current_stream().cuda_stream)
@@ -85,8 +95,8 @@ def _calls(d, o):
 
 
 def _flat(o):
-    parts = [o["y"], o["Y"].reshape(-1), o["ys"], o["Y2"].reshape(-1), o["yn"], *o["yqkv"], o["h"],
-             o["yq"]]
+    parts = [o["y"], o["Y"].reshape(-1), o["ys"], o["Y2"].reshape(-1), o["Y3"].reshape(-1),
+             o["Y4"].reshape(-1), o["yn"], *o["yqkv"], o["h"], o["yq"]]
     return torch.cat([p.reshape(-1) for p in parts]).cpu().numpy()
 
 
@@ -97,6 +107,9 @@ def test_captured_calls_replay_like_eager_ones():
     torch.cuda.synchronize()
     want = _flat(eager)
     assert np.isfinite(want).all()
+    # the forms these calls are meant to reach
+    assert lg.plan("bf16", 300, 2050, 2050, 12, d["Ab3"].data_ptr(), d["Xb3"].data_ptr())["lanes_per_row"] == 256
+    assert lg.plan("f16", 13313, 1024, 1024, 12, d["Ab4"].data_ptr(), d["Xb4"].data_ptr())["row_tiles"] == 4
     # the allocation-free split-K gives the workspace split-K's bits
     assert torch.equal(eager["yn"], eager["ys"])
 
@@ -111,8 +124,8 @@ def test_captured_calls_replay_like_eager_ones():
         _calls(d, out)
     torch.cuda.synchronize()
     for replay in range(3):
-        for t in (out["y"], out["Y"], out["ys"], out["Y2"], out["yn"], *out["yqkv"], out["h"],
-                  out["yq"]):
+        for t in (out["y"], out["Y"], out["ys"], out["Y2"], out["Y3"], out["Y4"], out["yn"],
+                  *out["yqkv"], out["h"], out["yq"]):
             t.fill_(float("nan"))  # eager work between replays
         torch.cuda.synchronize()
         g.replay()

@@ -324,6 +324,7 @@ template <class D, bool VEC>
 const void* batched_fn(int nvec, int rows, int lanes) {
     if (lanes == gemvplan::kWave * gemvplan::kBatchedSplit && rows == 1)
         return batched_fn<D, 1, VEC, gemvplan::kBatchedSplit>(nvec);
+    if (lanes == gemvplan::kWave * 2 && rows == 1) return batched_fn<D, 1, VEC, 2>(nvec);
     if (lanes != gemvplan::kWave) return nullptr;
     if (rows == 1) return batched_fn<D, 1, VEC>(nvec);
     if (rows == 2) return batched_fn<D, 2, VEC>(nvec);

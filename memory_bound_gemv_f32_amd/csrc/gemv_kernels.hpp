@@ -656,11 +656,12 @@ gemv_splitk_reduce_kernel(const float* __restrict__ ws, int splits, const float*
 // loads take any row pitch and K (rows and X columns start at
 // element-aligned addresses: unaligned global loads).
 //
-// KS = kRowsWaves splits K instead (few rows: one wavefront per row would
-// leave most of the chip idle and make the time one wavefront's walk along
-// its row): the workgroup's wavefronts share its U rows, wavefront w taking
-// batches w, w + KS, ... of each row; the per-wavefront totals meet in LDS
-// and wavefront 0 adds them in wavefront order (the same order every call).
+// KS > 1 splits K instead (few rows: one wavefront per row would leave most
+// of the chip idle and make the time one wavefront's walk along its row):
+// KS consecutive wavefronts share U rows, the k-th of them taking batches
+// k, k + KS, ... of each row; the per-wavefront totals meet in LDS and the
+// group's first wavefront adds them in wavefront order (the same order
+// every call).
 template <class D, int NV, int U, int B, bool XAHEAD, bool VEC, int RUN, int KS = 1>
 __global__ void __launch_bounds__(kRowsWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
@@ -672,13 +673,14 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     using CT = typename C::type;
     constexpr int E = C::elems;
     static_assert(U * NV <= 64, "one writer lane per (row, vector)");
-    static_assert(KS == 1 || KS == kRowsWaves, "a row per wavefront, or per workgroup");
+    static_assert(KS == 1 || KS == 2 || KS == kRowsWaves, "1, 2 or all wavefronts per row group");
+    constexpr int kGroups = kRowsWaves / KS;  // row groups per workgroup
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int kw = KS > 1 ? wave : 0;  // this wavefront's share of K
-    const int64_t row0 =
-        KS > 1 ? (int64_t)blockIdx.x * U : ((int64_t)blockIdx.x * kRowsWaves + wave) * U;
+    const int kw = wave % KS;  // this wavefront's share of K
+    const int grp = wave / KS;
+    const int64_t row0 = ((int64_t)blockIdx.x * kGroups + grp) * U;
     const S* rp[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -811,14 +813,14 @@ gemv_batched_kernel(const typename D::storage* __restrict__ A, int64_t lda,
             out = lane == u * NV + j ? v : out;
         }
     if constexpr (KS > 1) {
-        __shared__ float part[KS][U * NV];
-        if (lane < U * NV) part[kw][lane] = out;
+        __shared__ float part[kGroups][KS][U * NV];
+        if (lane < U * NV) part[grp][kw][lane] = out;
         __syncthreads();
         if (kw != 0) return;
         if (lane < U * NV) {
-            out = part[0][lane];
+            out = part[grp][0][lane];
 #pragma unroll
-            for (int w = 1; w < KS; ++w) out += part[w][lane];
+            for (int w = 1; w < KS; ++w) out += part[grp][w][lane];
         }
     }
     if (lane < U * NV) {

@@ -159,18 +159,30 @@ constexpr int batched_run(int nvec, int batch, int chunk_elems) {
                : kBatchedRunElems / (batch * chunk_elems);
 }
 // Wavefronts per row: with one row per wavefront the time is one
-// wavefront's walk along its row, and few rows leave most of the chip idle;
-// up to kBatchedSplitMaxRows rows (one wavefront on at most every other
-// SIMD) the workgroup's 4 wavefronts share each row instead (every fourth
-// batch each, totals added in LDS).  fp16, µs, one row per wavefront / per
+// wavefront's walk along its row, and few rows leave most of the chip idle.
+// Up to kBatchedSplitMaxRows rows (one wavefront on at most every other
+// SIMD) the workgroup's 4 wavefronts share each row (every fourth batch
+// each, totals added in LDS).  fp16, µs, one row per wavefront / per
 // workgroup: K = 4100, 64 rows 2 vectors 3.43 / 2.63, 16 vectors 8.96 /
 // 5.47; 512 rows 2 vectors 3.69 / 3.32, 8 vectors 7.72 / 5.04, 16 vectors
 // 9.12 / 7.50; 64 × 14337 16 vectors 40.21 / 13.51; 512 × 11009 16 vectors
 // 33.05 / 19.40; at 1024 rows mixed (8 vectors 7.91 / 7.06, 16 vectors 9.48
 // / 12.19), from 1536 rows slower (2048 rows 16 vectors 16.27 / 21.25).
+// Up to kBatchedPairMaxRows rows with at least kBatchedPairMinVectors
+// vectors, pairs of wavefronts share each row instead (K = 4100, µs, one /
+// two wavefronts per row: 600 rows 4 vectors 5.49 / 4.48, 8 vectors 7.77 /
+// 6.89; 1024 rows 4 vectors 5.62 / 4.68, 16 vectors 9.46 / 9.56; 1536 rows
+// 8 vectors 10.46 / 8.89, 16 vectors 15.93 / 13.88; bf16 1024 rows 8
+// vectors 8.67 / 6.81); with 2 vectors pairs lost 1-4 % (1024 rows 3.89 /
+// 4.03), and at 2048 rows 3-8 % (4 vectors 6.42 / 6.89).
 constexpr int64_t kBatchedSplitMaxRows = 512;
 constexpr int kBatchedSplit = 4;
-constexpr int batched_split(int64_t M) { return M <= kBatchedSplitMaxRows ? kBatchedSplit : 1; }
+constexpr int64_t kBatchedPairMaxRows = 1536;
+constexpr int kBatchedPairMinVectors = 4;
+constexpr int batched_split(int64_t M, int nvec) {
+    if (M <= kBatchedSplitMaxRows) return kBatchedSplit;
+    return M <= kBatchedPairMaxRows && nvec >= kBatchedPairMinVectors ? 2 : 1;
+}
 // Matrix-core batched family: up to kMfmaRows rows per workgroup (4, 8, 16
 // or 32, below), its wavefronts split K and walk their slice in chunks of
 // this many 64-wide steps (the A loads of a chunk are in flight together;
@@ -746,8 +758,8 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
         // the first block's
         if (nvec > kValuVectors) nvec = kValuVectors;
         p.rows_per_wave = batched_rows(M, nvec);
-        // (the K-split form takes one row per workgroup)
-        p.lanes_per_row = kWave * (p.rows_per_wave == 1 ? batched_split(M) : 1);
+        // (the K-split forms take one row per group of wavefronts)
+        p.lanes_per_row = kWave * (p.rows_per_wave == 1 ? batched_split(M, nvec) : 1);
         p.waves_per_group = kBlock / kWave;
         p.batch = batched_batch(nvec);
         p.row_tiles = 1;

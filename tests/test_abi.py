@@ -301,8 +301,9 @@ def test_vector_alu_batched_rows_per_wavefront():
         q = p("f16", M, 4100, nvec=nvec)
         assert q["family"] == lg.FAMILY_BATCHED, (M, nvec)
         assert q["rows_per_wave"] == rows, (M, nvec)
-        # up to 512 rows the workgroup's 4 wavefronts share each row
-        split = 4 if M <= 512 else 1
+        # up to 512 rows the workgroup's 4 wavefronts share each row; up to
+        # 1536 rows with 4 or more vectors, pairs of wavefronts
+        split = 4 if M <= 512 else (2 if M <= 1536 and nvec >= 4 else 1)
         assert q["lanes_per_row"] == 64 * split, (M, nvec)
         per_group = rows * 4 // split
         assert q["rows_per_group"] == per_group and q["grid"] == -(-M // per_group), (M, nvec)
@@ -330,6 +331,15 @@ def test_vector_alu_batched_k_split():
     # the fold of 4 wavefronts' totals is charged to the bound
     split, whole = p("f16", 512, 4100, nvec=2), p("f16", 513, 4100, nvec=2)
     assert split["rounding_chain"] == whole["rounding_chain"] + 3
+    # pairs of wavefronts per row: 513-1536 rows with at least 4 vectors
+    for M, nvec, lanes in ((513, 4, 128), (600, 8, 128), (1536, 16, 128), (1536, 3, 64),
+                           (1537, 8, 64), (1024, 2, 64)):
+        q = p("f16", M, 4100, nvec=nvec)
+        assert q["family"] == lg.FAMILY_BATCHED and q["lanes_per_row"] == lanes, (M, nvec, q)
+        per_group = 4 * 64 // lanes
+        assert (q["rows_per_group"], q["grid"]) == (per_group, -(-M // per_group)), (M, nvec)
+    pair, one = p("f16", 1024, 4100, nvec=4), p("f16", 1537, 4100, nvec=4)
+    assert pair["rounding_chain"] == one["rounding_chain"] + 1
 
 
 def test_matrix_core_workgroup_shapes():

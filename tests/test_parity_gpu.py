@@ -336,15 +336,19 @@ def test_integer_batched_row_counts(dtype, M, nvec):
 @pytest.mark.parametrize("nvec", [2, 9, 16, 17])
 def test_integer_batched_k_split(dtype, nvec):
     """Up to 512 rows the vector-ALU batched kernel splits each row's K over
-    the workgroup's 4 wavefronts: row lengths that give some wavefronts no
-    batch, a partial last batch, an element-wise tail; 16-byte and element
-    loads; bias or none; bit-exact.  Then long random rows within the bound."""
-    for M, K in ((1, 7), (5, 1000), (64, 4100), (511, 2056), (512, 14337), (3, 16392)):
+    the workgroup's 4 wavefronts, up to 1536 rows (4 or more vectors) over
+    pairs of wavefronts: row lengths that give some wavefronts no batch, a
+    partial last batch, an element-wise tail, a last workgroup with one row
+    group; 16-byte and element loads; bias or none; bit-exact.  Then long
+    random rows within the bound."""
+    for M, K in ((1, 7), (5, 1000), (64, 4100), (511, 2056), (512, 14337), (3, 16392),
+                 (513, 4100), (1023, 2050), (1536, 1000)):
         case = gi.make_integer(dtype, M, K, seed=M * 7 + K + nvec, nvec=nvec, bias=(M + nvec) % 2 == 1)
         ref, _ = run_oracle(case)
         q = lg.plan(dtype, M, K, K, nvec, 1 << 20, 1 << 20, family=lg.FAMILY_BATCHED)
-        assert q["lanes_per_row"] == 256, q
-        what = f"{dtype} {M}x{K} nvec={nvec}: K split over 4 wavefronts"
+        ks = 4 if M <= 512 else (2 if nvec >= 4 else 1)  # wavefronts per row
+        assert q["lanes_per_row"] == 64 * ks, q
+        what = f"{dtype} {M}x{K} nvec={nvec}: K split over {ks} wavefronts"
         print(what, flush=True)
         assert_bit_exact(run_gpu(case, lg.FAMILY_BATCHED, batched=True), ref, what)
         assert_bit_exact(run_gpu(case, lg.FAMILY_BATCHED, batched=True, misalign=1), ref,

@@ -267,7 +267,7 @@ def test_batched_chain_covers_the_kernel_schedule():
     split, on row lengths around the block and run boundaries."""
     checked = 0
     for dtype in ("f16", "bf16"):
-        for M in (64, 4096):  # K split, and a wavefront per row
+        for M in (64, 1024, 4096):  # K over 4 or 2 wavefronts, and a wavefront per row
             for nvec in (2, 5, 9, 16):
                 for K in (1, 7, 8, 100, 1023, 1024, 2047, 2048, 4096, 4100, 8191, 8200, 16384,
                           16391, 65536, 100003):
@@ -277,12 +277,12 @@ def test_batched_chain_covers_the_kernel_schedule():
                         B = q["batch"]
                         RUN = 1 if nvec <= 8 or B * E >= 64 else 64 // (B * E)
                         KS = q["lanes_per_row"] // 64
-                        assert KS == (4 if M <= 512 else 1)
+                        assert KS == (4 if M <= 512 else (2 if M <= 1536 and nvec >= 4 else 1))
                         need = _batched_schedule_chain(K, E, B, RUN, KS) + 1
                         assert q["rounding_chain"] >= need, (dtype, M, K, nvec, A, q, need)
                         assert q["rounding_chain"] <= 150
                         checked += 1
-    assert checked == 2 * 2 * 4 * 16 * 2
+    assert checked == 2 * 3 * 4 * 16 * 2
 
 
 def test_forced_wave_per_row_on_huge_rows():

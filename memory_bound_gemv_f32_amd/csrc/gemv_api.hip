@@ -451,9 +451,40 @@ const void* q8_group_fn(int batch) {
     }
 }
 
+// int8 weights, x in registers: NX chunks of x per lane (at most
+// kQ8StreamMaxChunks, or kQ8StreamMaxChunksWideX of fp32 x), R rows
+template <class X, int NX>
+const void* q8_stream_fn_nx(int rows) {
+    constexpr int W = gemvplan::kGroupStreamWaves;
+    if constexpr (NX > (X::bytes == 4 ? gemvplan::kQ8StreamMaxChunksWideX : gemvplan::kQ8StreamMaxChunks)) {
+        return nullptr;
+    } else {
+        switch (rows) {
+        case 2: return (const void*)&gemvdev::gemv_group_stream_q8_kernel<X, W, NX, 2>;
+        case 4: return (const void*)&gemvdev::gemv_group_stream_q8_kernel<X, W, NX, 4>;
+        default: return nullptr;
+        }
+    }
+}
+template <class X>
+const void* q8_stream_fn(int chunks, int rows) {
+    static_assert(gemvplan::kQ8StreamMaxChunks == 4, "int8 streaming kernels hold up to 4 x chunks");
+    switch (chunks) {
+    case 1: return q8_stream_fn_nx<X, 1>(rows);
+    case 2: return q8_stream_fn_nx<X, 2>(rows);
+    case 3: return q8_stream_fn_nx<X, 3>(rows);
+    case 4: return q8_stream_fn_nx<X, 4>(rows);
+    default: return nullptr;
+    }
+}
+
 template <class X, bool VEC>
 const void* q8_fn(const Plan& p) {
     if (p.family == gemvplan::GROUP_PER_ROW) {
+        if (p.x_in_registers) {
+            if constexpr (VEC) return q8_stream_fn<X>(p.batch, p.row_tiles);
+            return nullptr;
+        }
         if (p.waves_per_group == gemvplan::kGroupWaves) {
             if (p.row_tiles == 1) return q8_group_fn<X, 1, VEC>(p.batch);
             // two rows per workgroup only with 16-byte loads

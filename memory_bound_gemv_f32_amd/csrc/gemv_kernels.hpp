@@ -502,7 +502,7 @@ __device__ __forceinline__ void group_stream_body(const Rows& rows,
     const float b = (rows.any_bias() && writer) ? rows.bias_of(row0 + sub) : 0.f;
     const float sc = writer ? scale_of(rows, row0 + sub) : 0.f;
 
-    CT xv[NX];
+    typename C::xtype xv[NX];
 #pragma unroll
     for (int i = 0; i < NX; ++i) xv[i] = C::load(x, i + 1 < NX ? sub + i * L : clast);
 
@@ -577,6 +577,18 @@ gemv_group_q8_kernel(const int8_t* Q, int64_t ldq, const typename X::storage* __
                      int64_t M, int K, const float* scale, const float* bias, float* y) {
     group_body<TQ8<X>, W, U, BATCH, VEC>(ScaledMatrix<int8_t>{Q, ldq, scale, bias, y, M}, x, K,
                                          blockIdx.x);
+}
+
+// Int8 weights with x held in registers across R rows: the x-in-registers
+// body on int8 rows, whose x chunks (16 elements of the x type) are 32 or 64
+// bytes against 16 of weights, so fetching x once per R rows saves more than
+// with 2-byte weights.
+template <class X, int W, int NX, int R>
+__global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4)))
+gemv_group_stream_q8_kernel(const int8_t* Q, int64_t ldq, const typename X::storage* __restrict__ x,
+                            int64_t M, int K, const float* scale, const float* bias, float* y) {
+    group_stream_body<TQ8<X>, W, NX, R>(ScaledMatrix<int8_t>{Q, ldq, scale, bias, y, M}, x, K,
+                                        blockIdx.x);
 }
 
 // Split-K, pass 1: workgroup (t, s) forms the dot products of rows t·U ..

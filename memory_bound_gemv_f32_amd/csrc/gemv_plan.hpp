@@ -118,6 +118,8 @@ constexpr int64_t kGroupStreamMinXBytes = 8 * 1024;
 constexpr int kGroupStreamWaves = 4;
 constexpr int kGroupStreamMaxChunks = 6;
 constexpr int kGroupStreamRows = 4;
+constexpr int kQ8StreamMaxChunks = 4;
+constexpr int kQ8StreamMaxChunksWideX = 3;
 // Compute units of the GPU this library is built for (MI355X).
 constexpr int64_t kCUs = 256;
 // Batched family on the vector ALUs (a wavefront per group of rows, all
@@ -720,10 +722,22 @@ inline int make_plan_vec(int dtype, int M, int K, int nvec, bool vec, int family
                 p.lanes_per_row = kWave * kQ8NarrowWaves;
                 p.batch = fitted_batch(ceil_div(full, (int64_t)p.lanes_per_row), kQ8Batch);
             }
-        } else if (xbytes > kGroupStreamMinXBytes) {
+        }
+        // x in registers across 2-4 rows for an x of more than 8 KiB that
+        // fits 6 chunks per lane (int8 weights: 4, or 3 with fp32 x, their x
+        // chunks taking 8 or 16 registers each; more spilled).  int8 weights read 2 or 4 x bytes
+        // per weight byte, so fetching x once per 4 rows pays off there too
+        // (µs, workgroup of 2 rows / x in registers over 4: fp16 x 4096 ×
+        // 11008 9.66 / 9.33, 4096 × 14336 11.81 / 11.01, 1024 × 16384 5.96 /
+        // 4.84; bf16 x 4096 × 11008 9.70 / 9.20; fp32 x 4096 × 4096 5.49 /
+        // 5.24, 4096 × 8192 9.67 / 8.14).
+        const int64_t stream_x_bytes = dtype == Q8 ? (int64_t)K * q8_x_bytes : xbytes;
+        const int max_chunks = dtype != Q8 ? kGroupStreamMaxChunks
+                                           : (q8_x_bytes == 4 ? kQ8StreamMaxChunksWideX : kQ8StreamMaxChunks);
+        if (stream_x_bytes > kGroupStreamMinXBytes) {
             const int64_t lanes = (int64_t)kWave * kGroupStreamWaves;
             const int64_t chunks = ceil_div(full, lanes);
-            if (p.vector_loads && full * p.chunk_elems == K && chunks <= kGroupStreamMaxChunks) {
+            if (p.vector_loads && full * p.chunk_elems == K && chunks <= max_chunks) {
                 int r = kGroupStreamRows < umax ? kGroupStreamRows : umax;
                 while (r > 1 && ceil_div(M, r) < kGroupTileMinGroups) r /= 2;
                 if (r > 1) {

@@ -588,6 +588,30 @@ def test_q8_validation():
                                  None) == lg.GEMV_ERROR_INVALID_VALUE
 
 
+def test_q8_x_in_registers():
+    """int8 rows whose x is longer than 8 KiB and fits 4 chunks per lane of
+    4 wavefronts (3 with fp32 x), K a whole number of 16-weight loads, and
+    enough rows for 256 workgroups of 2 or 4: x is loaded once per workgroup
+    and kept in registers while it walks its rows."""
+    for xd, M, K, rows, chunks in (("f16", 4096, 11008, 4, 3), ("bf16", 4096, 11008, 4, 3),
+                                   ("f16", 1024, 16384, 4, 4), ("f32", 4096, 8192, 4, 2),
+                                   ("f32", 4096, 12288, 4, 3), ("f16", 700, 11008, 2, 3)):
+        p = lg.plan_q8(xd, M, K, Q_addr=ALIGNED, x_addr=ALIGNED)
+        assert (p["family"], p["x_in_registers"], p["row_tiles"], p["batch"]) == \
+            (lg.FAMILY_GROUP_PER_ROW, 1, rows, chunks), (xd, M, K, p)
+        assert (p["waves_per_group"], p["lanes_per_row"], p["grid"]) == (4, 256, -(-M // rows))
+        assert p["rounding_chain"] <= 150
+    for xd, M, K in (("f16", 4096, 4096),     # an 8 KiB x: no
+                     ("f16", 4096, 16400),    # 5 chunks per lane
+                     ("f32", 4096, 12304),    # fp32 x, 4 chunks per lane
+                     ("f16", 4096, 11000),    # not whole 16-weight loads
+                     ("f16", 300, 11008)):    # too few rows for 256 workgroups of 2
+        p = lg.plan_q8(xd, M, K, Q_addr=ALIGNED, x_addr=ALIGNED)
+        assert p["x_in_registers"] == 0, (xd, M, K, p)
+    # element loads never keep x in registers
+    assert lg.plan_q8("f16", 4096, 11008, Q_addr=ALIGNED + 1, x_addr=ALIGNED)["x_in_registers"] == 0
+
+
 def test_q8_families():
     """int8 weights run the three single-vector row families only, planned by
     their 1-byte rows: 16 weights per 16-byte load."""
@@ -607,8 +631,10 @@ def test_q8_families():
         (lg.FAMILY_GROUP_PER_ROW, 2, 1, 4096)
     # (a row of at most two loads per lane of two wavefronts: two wavefronts)
     assert (p["waves_per_group"], p["lanes_per_row"], p["lds_bytes"]) == (2, 128, 8)
+    # a 16 KiB fp32 x row: x in registers across 4 rows (one chunk per lane)
     p = lg.plan_q8("f32", 4096, 4096, Q_addr=ALIGNED, x_addr=ALIGNED)
-    assert (p["family"], p["row_tiles"], p["grid"]) == (lg.FAMILY_GROUP_PER_ROW, 2, 2048)
+    assert (p["family"], p["x_in_registers"], p["row_tiles"], p["batch"], p["grid"]) == \
+        (lg.FAMILY_GROUP_PER_ROW, 1, 4, 1, 1024)
     p = lg.plan_q8("bf16", 14336, 4096, Q_addr=ALIGNED, x_addr=ALIGNED)
     assert (p["family"], p["batch"], p["row_tiles"], p["grid"]) == \
         (lg.FAMILY_GROUP_PER_ROW, 1, 2, 7168)

@@ -117,10 +117,36 @@ def test_integer_two_rows_per_workgroup(xdtype):
         shapes.append((2049, 4096, 4096))  # two rows for the 16 KiB x row alone
     for M, K, ldq in shapes:
         q = lg.plan_q8(xdtype, M, K, ldq, 1 << 20, 1 << 20)
-        assert q["family"] == lg.FAMILY_GROUP_PER_ROW and q["row_tiles"] == 2, (M, K, q)
+        # (a 16 KiB fp32 x row of whole loads is kept in registers over 4 rows)
+        rows = 4 if q["x_in_registers"] else 2
+        assert q["x_in_registers"] == (xdtype == "f32" and K % 16 == 0), (M, K, q)
+        assert q["family"] == lg.FAMILY_GROUP_PER_ROW and q["row_tiles"] == rows, (M, K, q)
         case = gi.make_q8_integer(xdtype, M, K, seed=M + K + ldq, ldq=ldq, bias=True)
         ref, _ = run_oracle_q8(case)
         assert_bit_exact(run_q8(case), ref, f"{xdtype} {M}x{K} ldq={ldq}")
+
+
+@pytest.mark.parametrize("xdtype", gi.DTYPES)
+def test_integer_x_in_registers(xdtype):
+    """int8 rows with x kept in registers while a workgroup walks 2 or 4 of
+    them: 1 to 4 x chunks per lane (3 with fp32 x), the last partly past the
+    row, a last workgroup with fewer rows, padded pitches, bias or none;
+    bit-exact.  Then random data within the bound."""
+    shapes = [(4097, 11008, 11008), (1027, 16384, 16400), (4095, 4096 if xdtype == "f32" else 8320, 8336),
+              (702, 11008, 11008)]
+    if xdtype == "f32":
+        shapes = [(4097, 11008, 11008), (1027, 8192, 8208), (4095, 4096, 4112), (702, 12288, 12288)]
+    for i, (M, K, ldq) in enumerate(shapes):
+        q = lg.plan_q8(xdtype, M, K, ldq, 1 << 20, 1 << 20)
+        assert q["family"] == lg.FAMILY_GROUP_PER_ROW and q["x_in_registers"] == 1, (M, K, q)
+        case = gi.make_q8_integer(xdtype, M, K, seed=M + K + ldq, ldq=ldq, bias=i % 2 == 0)
+        ref, _ = run_oracle_q8(case)
+        what = f"{xdtype} {M}x{K} ldq={ldq}: x in registers, {q['batch']} chunks, {q['row_tiles']} rows"
+        print(what, flush=True)
+        assert_bit_exact(run_q8(case), ref, what)
+    case = gi.make_q8_random(xdtype, 2048, 11008, seed=11, bias=True)
+    ref, absdot = run_oracle_q8(case)
+    assert_within_bound(run_q8(case), ref, absdot, f"{xdtype} 2048x11008 random, x in registers")
 
 
 RANDOM_SHAPES = [(1000, 16), (4096, 100), (2000, 1000), (513, 4096), (64, 14336),

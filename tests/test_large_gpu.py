@@ -1,4 +1,5 @@
-"""A matrix of more than 2^31 elements (needs a GPU with several GiB free).
+"""A matrix of more than 2^31 elements (needs a GPU with several GiB free):
+single-vector, batched (matrix cores and vector ALUs) and int8 weights.
 
 The pages' kernels index A with 32-bit int products (row * N + col), which
 wrap once M·K reaches 2^31; every offset here is 64-bit.  A (bf16, 4.3 GB)
@@ -70,5 +71,36 @@ def test_more_than_2_31_elements():
         got = y.cpu().numpy().astype(np.float64)
         np.testing.assert_array_equal(got[rows], ref[0], err_msg=f"family {family}")
         del y
+
+    # three right-hand vectors (x, 2x, -x): the matrix-core and vector-ALU
+    # batched kernels
+    X = torch.stack([x, 2 * x, -x]).contiguous()
+    Xr = np.concatenate([xr, _bf16_bits(2 * _x_values())[None, :], _bf16_bits(-_x_values())[None, :]])
+    refb, _ = oracle.gemv("bf16", Ar, Xr, None, len(rows), K, nvec=3)
+    for family in (lg.FAMILY_AUTO, lg.FAMILY_BATCHED):
+        print(f"batched family {family}: bf16 {M}x{K}, 3 vectors", flush=True)
+        Y = lg.gemv_batched(A, X, family=family)
+        torch.cuda.synchronize()
+        got = Y.cpu().numpy().astype(np.float64)
+        np.testing.assert_array_equal(got[:, rows], refb, err_msg=f"batched family {family}")
+        del Y
     del A
+    torch.cuda.empty_cache()
+
+    # int8 weights of the same closed form, unit scales, fp16 x
+    Q = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    for r0 in range(0, M, BLOCK):
+        r1 = min(M, r0 + BLOCK)
+        m = torch.arange(r0, r1, dtype=torch.int32, device="cuda")
+        Q[r0:r1] = ((5 * m[:, None] + 3 * k[None, :]) % 17 - 8).to(torch.int8)
+    scale = torch.ones(M, dtype=torch.float32, device="cuda")
+    xh = (torch.arange(K, device="cuda") % 13 - 6).to(torch.float16)
+    xhr = _x_values().astype(np.float16).view(np.uint16)[None, :]
+    refq, _ = oracle.gemv_q8("f16", _row_values(rows).astype(np.int8), np.ones(len(rows), np.float32),
+                             xhr, None, len(rows), K)
+    print(f"int8 {M}x{K}, fp16 x", flush=True)
+    y = lg.gemv_q8(Q, scale, xh)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y.cpu().numpy().astype(np.float64)[rows], refq[0], err_msg="int8")
+    del Q, y
     torch.cuda.empty_cache()

@@ -333,19 +333,29 @@ __device__ __forceinline__ void rows_body(const Rows& rows, const typename D::xs
     const int nsafe = nfull - nfull % (BATCH * L);
     int c0 = 0;
     for (; c0 < nsafe; c0 += BATCH * L) rows_batch<C, L, U, BATCH, false>(rp, x, c0 + sub, nfull, sum);
-    if (c0 < nfull) rows_batch<C, L, U, BATCH, true>(rp, x, c0 + sub, nfull, sum);
+    // The checked batch and the element-wise tail are marked unlikely, so
+    // the compiler places them after the kernel's end and the batches run
+    // straight into the epilogue: every wavefront reaches the epilogue at
+    // about the same time, near the end of a launch, and a jump over those
+    // blocks there fetched instruction lines no wavefront had run yet (bf16
+    // 4096 x 4096 6.643 -> 6.608 us, 1024 x 4096 3.212 -> 3.175).  Skipping
+    // an empty tail leaves every sum as it was: adding 0 to a sum that
+    // started at +0 changes no bit.
+    if (__builtin_expect(c0 < nfull, 0)) rows_batch<C, L, U, BATCH, true>(rp, x, c0 + sub, nfull, sum);
     if constexpr (VEC) {
-        // elements past the last whole chunk (fewer than E of them)
-        float tail[U];
+        if (__builtin_expect(nfull * E < K, 0)) {
+            // elements past the last whole chunk (fewer than E of them)
+            float tail[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) tail[u] = 0.f;
-        for (int k = nfull * E + sub; k < K; k += L) {
-            const float xe = widen_x(D{}, x[k]);
+            for (int u = 0; u < U; ++u) tail[u] = 0.f;
+            for (int k = nfull * E + sub; k < K; k += L) {
+                const float xe = widen_x(D{}, x[k]);
 #pragma unroll
-            for (int u = 0; u < U; ++u) tail[u] = __builtin_fmaf(widen_a(D{}, rp[u][k]), xe, tail[u]);
+                for (int u = 0; u < U; ++u) tail[u] = __builtin_fmaf(widen_a(D{}, rp[u][k]), xe, tail[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) sum[u].add(tail[u]);
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u) sum[u].add(tail[u]);
     }
 
     float v[U];
@@ -434,8 +444,10 @@ __device__ __forceinline__ void group_body(const Rows& rows, const typename D::x
     const int nsafe = nfull - nfull % (BATCH * L);
     int c0 = 0;
     for (; c0 < nsafe; c0 += BATCH * L) rows_batch<C, L, U, BATCH, false>(rp, x, c0 + sub, nfull, sum);
-    if (c0 < nfull) rows_batch<C, L, U, BATCH, true>(rp, x, c0 + sub, nfull, sum);
-    if constexpr (VEC) {
+    // (rare paths out of line, as in the rows body: 512 x 4096 2.730 ->
+    // 2.687 us, 4096 x 14336 18.01 -> 17.90)
+    if (__builtin_expect(c0 < nfull, 0)) rows_batch<C, L, U, BATCH, true>(rp, x, c0 + sub, nfull, sum);
+    if (VEC && __builtin_expect(nfull * E < K, 0)) {
         float tail[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) tail[u] = 0.f;
@@ -1091,7 +1103,7 @@ gemv_batched_mfma_kernel(const typename D::storage* __restrict__ A, int64_t lda,
     for (int t = 0; t < NT; ++t) xq[t] = X + (int64_t)(16 * t + r < nvec ? 16 * t + r : 0) * K + 8 * g;
     const int c_left = c;
 #pragma unroll 1
-    for (; c < rg.end; ++c) {
+    for (; __builtin_expect(c < rg.end, 0); ++c) {  // (out of line: rare)
         const int e = c * 64;
         const bool ina = e + 32 * half + 8 * g < K;
         quad a[Q];

@@ -276,8 +276,8 @@ typedef enum {
     GEMV_FAMILY_ROWS_PER_WAVE = 0, /* 64/L rows per wavefront, L lanes per row */
     GEMV_FAMILY_WAVE_PER_ROW = 1,  /* one 64-lane wavefront per row */
     GEMV_FAMILY_GROUP_PER_ROW = 2, /* one workgroup per row, LDS reduction */
-    GEMV_FAMILY_BATCHED = 3,       /* several rows × nvec vectors per wave */
-    GEMV_FAMILY_BATCHED_MFMA = 4,  /* 8 or 16 rows × 16 vectors on the matrix cores */
+    GEMV_FAMILY_BATCHED = 3,       /* 1-2 rows × nvec vectors per wave, or few rows split over 2-4 waves */
+    GEMV_FAMILY_BATCHED_MFMA = 4,  /* 4-32 rows × 16 vectors per tile on the matrix cores */
     GEMV_FAMILY_GATED_SILU = 5,    /* a row of A_gate and of A_up per workgroup */
     GEMV_FAMILY_SPLIT_K = 6        /* a workgroup per two rows and K-slice, then a reduce */
 } gemv_family_t;
@@ -286,13 +286,16 @@ typedef struct {
     int family;          /* gemv_family_t */
     int vector_loads;    /* 1: 16-byte loads; 0: one element per load */
     int chunk_elems;     /* elements per load (16/size, or 1) */
-    int lanes_per_row;   /* lanes that share one row's dot product */
+    int lanes_per_row;   /* lanes that share one row's dot product (batched
+                            on the vector ALUs: 128 or 256 when a row's K
+                            is split over 2 or 4 wavefronts) */
     int rows_per_wave;   /* rows one wavefront covers per row tile (matrix
                             cores: the workgroup's rows, which its wavefronts
                             share, each taking a slice of K) */
     int row_tiles;       /* row tiles each wavefront takes in one pass
                             (workgroup per row: rows per workgroup; matrix
-                            cores: groups of 8 rows per workgroup) */
+                            cores: groups of 4 or 8 rows per workgroup, 1,
+                            2 or 4 of them) */
     int waves_per_group; /* wavefronts per workgroup */
     int rows_per_group;  /* rows one workgroup produces */
     int batch;           /* loads per lane kept in flight per row */

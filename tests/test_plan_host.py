@@ -171,8 +171,10 @@ def test_every_automatic_int8_plan_has_a_kernel(xdtype):
     """Int8 rows of 17-24 loads on very tall matrices (K 257..384 at 2^19 rows
     and more) had a plan with no kernel behind it; now every shape has one."""
     for M in ROW_COUNTS:
+        # (4112-16384: x kept in registers over 2-4 rows, 1-4 chunks per lane,
+        # 16400 just past it; with fp32 x 12288 is the last)
         for K in [0, 1, 16, 17, 48, 100, 256, 257, 272, 320, 368, 384, 385, 512, 1000, 4096,
-                  14336, 100000]:
+                  4112, 8192, 8320, 11008, 12288, 12304, 14336, 16384, 16400, 100000]:
             for ldq, Q in ((K, ALIGNED), (K + 3, ALIGNED), (K, ALIGNED + 1)):
                 q = lg.plan_q8(xdtype, M, K, ldq, Q, ALIGNED)
                 assert q["batch"] == 1 or q["lanes_per_row"] == 64 or \

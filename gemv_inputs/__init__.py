@@ -398,6 +398,7 @@ Q8_WORKLOADS = {
     # name: (xdtype, M, K, seed)
     "q8_f16_4096": ("f16", 4096, 4096, 68),
     "q8_bf16_14336x4096": ("bf16", 14336, 4096, 69),
+    "q8_f16_4096x11008": ("f16", 4096, 11008, 70),
 }
 
 

@@ -214,7 +214,7 @@ constexpr int kMfmaManyTilesWaves = 4;
 // 4.89 and 7.02 / 5.75, 2048 6.21 / 5.17 and 7.23 / 6.04; 3072 (one group in
 // 384 workgroups of 4 wavefronts) 6.66 / 8.04 and 7.64 / 9.63.
 //
-// Four groups (32 rows, half-size chunks) for kMfmaTallMinVectors to 16
+// Four groups (32 rows, half-size chunks) for kMfmaTallMinVectors (6) to 16
 // vectors on tall matrices: every workgroup stages the whole of X for its
 // rows, so 32-row workgroups read half as many X bytes per A byte.  The
 // time of these grids follows the largest number of workgroups a compute
@@ -224,10 +224,14 @@ constexpr int kMfmaManyTilesWaves = 4;
 // 12288 rows 19.49 / 21.24 (3 against 2·2 units of 16 rows), 13312 23.75 /
 // 21.27, 14336 24.17 / 21.68, 16384 24.89 / 23.04, 20480 30.50 / 30.34 (5
 // against 6); 9 vectors 13312 21.62 / 20.40, 16384 22.97 / 22.68, 28672
-// 37.62 / 38.25 (7 against 8); 8 vectors gained less (14336 21.67 / 20.72,
-// 16384 22.70 / 22.66).  With 8 wavefronts (at most one workgroup per unit)
-// four groups were slower: 4096 rows 7.84 / 11.30, 8192 13.79 / 15.90.
-constexpr int kMfmaTallMinVectors = 9;
+// 37.62 / 38.25 (7 against 8); 6-8 vectors gained less (13312 rows 6
+// vectors 20.93 / 20.14, 8 vectors 21.32 / 20.31; 14336 rows 6 vectors
+// 21.27 / 20.69; bf16 14336 rows 8 vectors 21.73 / 20.82; 16384 rows, both
+// grids even, 6 vectors 22.34 / 22.61, 8 vectors 22.77 / 22.66).  With 8
+// wavefronts (at most one workgroup per unit) four groups were slower: 4096
+// rows 7.84 / 11.30, 8192 13.79 / 15.90.  (Up to kMfmaFewVectors vectors X
+// is read straight from memory and the kernel takes at most two groups.)
+constexpr int kMfmaTallMinVectors = kMfmaFewVectors + 1;
 constexpr int mfma_row_groups(int64_t M, int nvec) {
     if ((M + 7) / 8 <= kCUs) return 1;
     const int64_t g2 = (M + 15) / 16, g4 = (M + 31) / 32;

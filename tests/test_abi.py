@@ -368,17 +368,18 @@ def test_matrix_core_workgroup_shapes():
 
 
 def test_matrix_core_four_row_groups():
-    """9-16 vectors on tall matrices: four groups of 8 rows (half the X
-    bytes per A byte) when their grid has more workgroups than compute units
-    and no unit runs more rows than with two groups (the largest number of
-    workgroups on one unit times their rows)."""
-    for M, nvec, groups in ((12288, 16, 2), (13312, 9, 4), (13312, 8, 2), (13313, 16, 4),
-                            (14336, 16, 4), (16384, 12, 4), (20480, 16, 2), (28672, 16, 2),
-                            (8192, 16, 2), (4096, 16, 2), (14336, 17, 2), (14336, 5, 2)):
+    """6-16 vectors (X staged in LDS) on tall matrices: four groups of 8 rows
+    (half the X bytes per A byte) when their grid has more workgroups than
+    compute units and no unit runs more rows than with two groups (the
+    largest number of workgroups on one unit times their rows)."""
+    for M, nvec, groups in ((12288, 16, 2), (13312, 9, 4), (13312, 8, 4), (13313, 16, 4),
+                            (14336, 16, 4), (14336, 6, 4), (16384, 12, 4), (20480, 16, 2),
+                            (28672, 16, 2), (8192, 16, 2), (4096, 16, 2), (14336, 17, 2),
+                            (14336, 5, 2)):
         q = p("f16", M, 4096, nvec=nvec)
         assert q["family"] == lg.FAMILY_BATCHED_MFMA
         g2, g4 = -(-M // 16), -(-M // 32)
-        assert (groups == 4) == (9 <= nvec <= 16 and g4 > 256 and
+        assert (groups == 4) == (6 <= nvec <= 16 and g4 > 256 and
                                  2 * -(-g4 // 256) <= -(-g2 // 256)), (M, nvec)
         assert q["row_tiles"] == groups and q["rows_per_group"] == 8 * groups, (M, nvec)
         if groups == 4:

@@ -572,13 +572,13 @@ def test_integer_batched_workgroup_shapes(dtype, M, waves, groups, rows):
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_integer_batched_four_row_groups(dtype):
-    """9-16 vectors on tall matrices: workgroups of four 8-row groups (32
+    """6-16 vectors on tall matrices: workgroups of four 8-row groups (32
     rows, 4 wavefronts, chunks of 4 steps), on row counts that leave a
     partial last workgroup, K that leave a partial last 64-wide step or
     steps outside whole chunks, bias or none, odd M (unaligned Y columns);
     bit-exact.  Then random data within the bound."""
     for M, K, nvec in ((13313, 4096, 9), (13313, 4096, 16), (14337, 1000, 12), (16384, 2680, 16),
-                       (13320, 4104, 13)):
+                       (13320, 4104, 13), (14336, 4096, 6), (13313, 1000, 8)):
         q = lg.plan(dtype, M, K, K, nvec, 1 << 20, 1 << 20)
         assert (q["family"], q["row_tiles"], q["rows_per_group"], q["waves_per_group"]) == \
             (lg.FAMILY_BATCHED_MFMA, 4, 32, 4), q
